@@ -1,0 +1,167 @@
+"""Benchmark of the block-scaled small-M decode GEMV on one MI355X.
+
+One step = one qgemv_run call (dispatch + kernel) over one batch of synthetic input:
+Y[M, N] = A[M, K] . dequant(W)^T. The weights are cold: the timed loop rotates
+through enough copies of the weight (>= 1 GiB together, several times the 256 MB
+last-level cache) that every call streams its weight from HBM. Inputs are resident in
+HBM before the timed region starts.
+
+Prints one JSON line. `value` is achieved GB/s = weight bytes (codes + block scales +
+zero points) per call / average time per call. The roofline object reports the same
+bytes against the 8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "u8_m1_k4096_n4096"
+HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--m", type=int, default=None, help="rows of A (default: the workload's first M)")
+    p.add_argument("--flags", type=int, default=0, help="qgemv_desc.flags (force a family, K split)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
+    p.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm; not the metric)")
+    return p.parse_args()
+
+
+def cpu_baseline(prob, M, target_s):
+    """Time the CPU oracle (as it stands) on a bounded column sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from block_quantized_weight_amd import synth
+
+    # pick a column count that takes roughly target_s, after a short calibration
+    ncal = min(prob.N, 256)
+    sub = synth.Problem(**{**prob.__dict__, "N": ncal, "W": prob.W[:ncal], "scales": prob.scales[:ncal],
+                           "zp": None if prob.zp is None else prob.zp[:ncal]})
+    t0 = time.perf_counter()
+    oracle.gemv(sub, M=M)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    ncols = int(min(prob.N, max(ncal, ncal * target_s / dt)))
+    reps = max(1, int(math.ceil(ncal * target_s / dt / max(ncols, 1))))
+    sub = synth.Problem(**{**prob.__dict__, "N": ncols, "W": prob.W[:ncols], "scales": prob.scales[:ncols],
+                           "zp": None if prob.zp is None else prob.zp[:ncols]})
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.gemv(sub, M=M)
+    el = (time.perf_counter() - t0) / reps
+    bytes_per_col = prob.weight_bytes() / prob.N
+    return {"value": round(bytes_per_col * ncols / el / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{ncols} of {prob.N} columns x {reps} repetition(s), M={M}, fp64 plain loops, "
+                      f"{el * 1e3:.1f} ms per sample pass"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the weight would be split by "
+              "output columns, one shard per GPU, with no communication in the product). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_weight_amd as bqw
+    from block_quantized_weight_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    prob = synth.workload(args.workload)
+    M = args.m if args.m is not None else prob.ms[0]
+    wbytes = prob.weight_bytes()
+    copies = 1 if args.warm else max(2, int(math.ceil(COLD_BYTES / wbytes)))
+
+    # device buffers: one copy of each input per rotation slot
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    W0 = dev_t(prob.W)
+    S0 = dev_t(prob.scales if prob.scales.dtype == np.float32 else prob.scales.view(np.uint8))
+    Z0 = None if prob.zp is None else dev_t(prob.zp)
+    tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
+    A = dev_t(prob.A[:M].view(np.int16)).view(tdt).contiguous()
+    Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
+    slots = []
+    for i in range(copies):
+        W = W0 if i == 0 else W0.clone()
+        S = S0 if i == 0 else S0.clone()
+        Z = Z0 if (i == 0 or Z0 is None) else Z0.clone()
+        q = bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, W, S, Z, prob.tensor_scale, args.flags)
+        slots.append((q, W, S, Z))
+    plan = slots[0][0].plan(M)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        slots[i % copies][0].run(A, Y, M, stream)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        slots[i % copies][0].run(A, Y, M, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per = ms_total / args.steps
+    gbs = wbytes / (ms_per * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob, M, args.cpu_seconds)
+
+    spec = synth.WORKLOADS[args.workload]
+    out = {
+        "metric": "achieved HBM GB/s (weight bytes / kernel time), cold weights",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per, 6),
+        "us_per_call": round(ms_per * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{prob.fmt} x {prob.act} -> f32 acc",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
+                   "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
+                   "plan": plan, "flags": args.flags, "seed": spec["seed"]},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+    }
+    for q, *_ in slots:
+        q.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

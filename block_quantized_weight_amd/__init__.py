@@ -1,1 +1,201 @@
-"""MI355X-native block-scaled small-M decode GEMV (placeholder; binding added with the library)."""
+"""Python binding of libqgemv, the block-scaled small-M decode GEMV for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in include/qgemv.h. PyTorch supplies device memory and
+streams. If the shared library has not been built the first call raises; there is
+no fallback path of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Any, Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+FORMATS = {"u4": 1, "u8": 2, "fp8": 3, "nvfp4": 4}
+ACT_DTYPES = {"f16": 1, "bf16": 2}
+FAMILIES = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3}
+FAMILY_NAMES = {v: k for k, v in FAMILIES.items()}
+
+QGEMV_OK = 0
+FLAG_FAMILY_MASK = 0x0000000F
+FLAG_KSPLIT_SHIFT = 8
+FLAG_NO_MFMA = 0x00010000
+MAX_M = 16
+
+_lock = threading.Lock()
+_lib = None
+
+
+class QGemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: qgemv status {status} ({status_str(status)})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("format", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("W", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zero_points", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("family", ctypes.c_int32),
+        ("rows_per_pass", ctypes.c_int32),
+        ("passes", ctypes.c_int32),
+        ("cols_per_wave", ctypes.c_int32),
+        ("ksplit", ctypes.c_int32),
+        ("waves_per_wg", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("lds_bytes", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
+    ]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgemv.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with block_quantized_weight_amd.build.build()")
+            L = ctypes.CDLL(LIB_PATH)
+            vp = ctypes.c_void_p
+            L.qgemv_create.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(Desc), ctypes.c_int]
+            L.qgemv_create.restype = ctypes.c_int
+            L.qgemv_run.argtypes = [vp, vp, vp, ctypes.c_int, vp]
+            L.qgemv_run.restype = ctypes.c_int
+            L.qgemv_plan.argtypes = [vp, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+            L.qgemv_plan.restype = ctypes.c_int
+            L.qgemv_select.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+            L.qgemv_select.restype = ctypes.c_int
+            L.qgemv_destroy.argtypes = [vp]
+            L.qgemv_destroy.restype = None
+            L.qgemv_status_str.argtypes = [ctypes.c_int]
+            L.qgemv_status_str.restype = ctypes.c_char_p
+            L.qgemv_abi_version.restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().qgemv_status_str(int(status)).decode()
+
+
+def _ptr(x: Any) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def make_desc(fmt: str, act: str, N: int, K: int, block_size: int, W: Any, scales: Any,
+              zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0) -> Desc:
+    return Desc(ctypes.sizeof(Desc), FORMATS.get(fmt, 0) if isinstance(fmt, str) else int(fmt),
+                ACT_DTYPES.get(act, 0) if isinstance(act, str) else int(act), int(block_size), int(N), int(K),
+                _ptr(W), _ptr(scales), _ptr(zero_points), float(tensor_scale), int(flags))
+
+
+def _plan_dict(p: PlanInfo) -> Dict[str, Any]:
+    return {"family": FAMILY_NAMES.get(p.family, p.family), "rows_per_pass": p.rows_per_pass,
+            "passes": p.passes, "cols_per_wave": p.cols_per_wave, "ksplit": p.ksplit,
+            "waves_per_wg": p.waves_per_wg, "grid": p.grid, "lds_bytes": p.lds_bytes, "variant": p.variant}
+
+
+def select(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count: int = 256,
+           flags: int = 0, W: Any = 0x1000, scales: Any = 0x1000, zero_points: Any = None) -> Dict[str, Any]:
+    """Pure host dispatcher query (no GPU): the launch for M rows at cu_count CUs."""
+    d = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, 1.0, flags)
+    out = PlanInfo()
+    rc = lib().qgemv_select(ctypes.byref(d), int(M), int(cu_count), ctypes.byref(out))
+    if rc != QGEMV_OK:
+        raise QGemvError(rc, "qgemv_select")
+    return _plan_dict(out)
+
+
+class QGemv:
+    """A quantized weight resident on the GPU, ready to multiply activations.
+
+    W, scales and zero_points are device buffers (torch tensors or raw device
+    pointers) in the layouts documented in include/qgemv.h; they must stay alive
+    as long as this object.
+    """
+
+    def __init__(self, fmt: str, act: str, N: int, K: int, block_size: int, W: Any, scales: Any,
+                 zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0, device: int = -1):
+        self.fmt, self.act, self.N, self.K, self.block_size = fmt, act, int(N), int(K), int(block_size)
+        self._keep = (W, scales, zero_points)
+        self._desc = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, tensor_scale, flags)
+        h = ctypes.c_void_p()
+        rc = lib().qgemv_create(ctypes.byref(h), ctypes.byref(self._desc), int(device))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_create")
+        self._h = h
+
+    def run(self, A: Any, Y: Any, M: Optional[int] = None, stream: Any = None) -> None:
+        """Enqueue Y[M, N] = A[M, K] . dequant(W)^T on `stream` (torch stream, raw
+        hipStream_t int, or None for torch's current stream)."""
+        if M is None:
+            M = int(A.shape[0])
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        rc = lib().qgemv_run(self._h, _ptr(A), _ptr(Y), int(M), ctypes.c_void_p(stream))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_run")
+
+    def plan(self, M: int) -> Dict[str, Any]:
+        out = PlanInfo()
+        rc = lib().qgemv_plan(self._h, int(M), ctypes.byref(out))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_plan")
+        return _plan_dict(out)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().qgemv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def upload(problem, device: str = "cuda:0", flags: int = 0) -> "tuple[QGemv, dict]":
+    """Copy a numpy-side problem (see synth.Problem) to device tensors and build the
+    handle. Returns (QGemv, tensors) where tensors holds A (as an activation tensor of
+    the problem's dtype) and the weight buffers."""
+    import numpy as np
+    import torch
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    t = {"W": dev(problem.W), "scales": dev(problem.scales.view(np.uint8) if problem.scales.dtype != np.float32
+                                              else problem.scales)}
+    t["zp"] = None if problem.zp is None else dev(problem.zp)
+    tdt = torch.float16 if problem.act == "f16" else torch.bfloat16
+    t["A"] = dev(problem.A.view(np.int16)).view(tdt)
+    q = QGemv(problem.fmt, problem.act, problem.N, problem.K, problem.bs, t["W"], t["scales"], t["zp"],
+              problem.tensor_scale, flags)
+    return q, t

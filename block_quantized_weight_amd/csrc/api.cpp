@@ -1,0 +1,167 @@
+// C ABI of qgemv (declarations and contracts in include/qgemv.h).
+//
+// The op layer of the pages passes device properties in at construction and reads
+// its environment switches once per instance, never per call ("[CUDA] Block-scaled
+// MatMul decode GEMV", review fixes; "[CUDA] MatMul: add an opt-in split-K GEMV",
+// Kernel and dispatch). The handle here does the same: qgemv_create captures the
+// compute-unit count and the environment overrides, and qgemv_run only validates the
+// per-call arguments, picks the launch and enqueues it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/qgemv.h"
+#include "launch.h"
+#include "select.h"
+
+struct qgemv_handle {
+    qgemv_desc d;
+    int device;
+    int cu_count;
+    uint32_t env_flags;
+    bool weights_fast_ok;
+};
+
+namespace {
+
+bool env_true(const char *name) {
+    const char *v = getenv(name);
+    if (!v || !*v) return false;
+    return !(strcmp(v, "0") == 0 || strcmp(v, "false") == 0 || strcmp(v, "False") == 0 ||
+             strcmp(v, "FALSE") == 0 || strcmp(v, "off") == 0 || strcmp(v, "no") == 0);
+}
+
+uint32_t read_env_flags() {
+    uint32_t f = 0;
+    const char *fam = getenv("QGEMV_FORCE_FAMILY");
+    if (fam && *fam) {
+        if (!strcmp(fam, "stream") || !strcmp(fam, "1")) f |= QGEMV_FAMILY_STREAM;
+        else if (!strcmp(fam, "mfma") || !strcmp(fam, "2")) f |= QGEMV_FAMILY_MFMA;
+        else if (!strcmp(fam, "generic") || !strcmp(fam, "3")) f |= QGEMV_FAMILY_GENERIC;
+    }
+    const char *ks = getenv("QGEMV_FORCE_KSPLIT");
+    if (ks && *ks) {
+        long v = strtol(ks, nullptr, 10);
+        if (v > 0 && v <= 64) f |= ((uint32_t)v << QGEMV_FLAG_KSPLIT_SHIFT);
+    }
+    if (env_true("QGEMV_NO_MFMA")) f |= QGEMV_FLAG_NO_MFMA;
+    return f;
+}
+
+void fill_args(const qgemv_handle *h, const void *A, void *Y, int M, qgemv::KArgs *a) {
+    const qgemv_desc &d = h->d;
+    a->W = (const uint8_t *)d.W;
+    a->scales = d.scales;
+    a->zp = (const uint8_t *)d.zero_points;
+    a->A = A;
+    a->Y = Y;
+    a->N = d.N;
+    a->K = d.K;
+    a->col_bytes = (d.format == QGEMV_FMT_U4 || d.format == QGEMV_FMT_NVFP4) ? d.K / 2 : d.K;
+    a->nchunks = a->col_bytes / 16;
+    a->bs = d.block_size;
+    a->nblk = (int32_t)(d.K / d.block_size);
+    a->zstride = (d.format == QGEMV_FMT_U4) ? (a->nblk + 1) / 2 : a->nblk;
+    a->M = M;
+    a->ksplit = 1;
+    a->tscale = (d.format == QGEMV_FMT_NVFP4) ? d.tensor_scale : 1.0f;
+}
+
+void to_info(const qgemv::LaunchCfg &c, qgemv_plan_info *o) {
+    o->family = c.family;
+    o->rows_per_pass = c.rows_per_pass;
+    o->passes = c.passes;
+    o->cols_per_wave = c.cols_per_wave;
+    o->ksplit = c.ksplit;
+    o->waves_per_wg = c.waves_per_wg;
+    o->grid = c.grid;
+    o->lds_bytes = c.lds_bytes;
+    o->variant = c.variant;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_abi_version(void) { return QGEMV_ABI_VERSION; }
+
+const char *qgemv_status_str(int s) {
+    switch (s) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_E_NULL: return "a required pointer is NULL";
+    case QGEMV_E_SHAPE: return "invalid shape (M outside [1,16], N or K < 1, or K not a multiple of the block size)";
+    case QGEMV_E_BLOCK: return "block size not supported for this format";
+    case QGEMV_E_FORMAT: return "unknown format or activation dtype, or zero points given for FP8/NVFP4";
+    case QGEMV_E_DEVICE: return "no usable gfx950 device";
+    case QGEMV_E_LAUNCH: return "kernel launch failed";
+    case QGEMV_E_ARG: return "invalid argument";
+    case QGEMV_E_ALLOC: return "host allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
+    if (!out) return QGEMV_E_NULL;
+    *out = nullptr;
+    int rc = qgemv::validate_desc(d);
+    if (rc) return rc;
+    int dev = device;
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return QGEMV_E_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QGEMV_E_DEVICE;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return QGEMV_E_DEVICE;
+    qgemv_handle *h = new (std::nothrow) qgemv_handle;
+    if (!h) return QGEMV_E_ALLOC;
+    h->d = *d;
+    h->device = dev;
+    h->cu_count = prop.multiProcessorCount;
+    h->env_flags = read_env_flags();
+    h->weights_fast_ok = qgemv::pointers_fast_ok(d, nullptr, nullptr);
+    *out = h;
+    return QGEMV_OK;
+}
+
+int qgemv_plan(const qgemv_handle *h, int M, qgemv_plan_info *out) {
+    if (!h || !out) return QGEMV_E_NULL;
+    qgemv::LaunchCfg c;
+    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, &c);
+    if (rc) return rc;
+    to_info(c, out);
+    return QGEMV_OK;
+}
+
+int qgemv_select(const qgemv_desc *d, int M, int cu_count, qgemv_plan_info *out) {
+    if (!out) return QGEMV_E_NULL;
+    qgemv::LaunchCfg c;
+    int rc = qgemv::select_plan(d, M, cu_count, d ? qgemv::pointers_fast_ok(d, nullptr, nullptr) : false, 0u, &c);
+    if (rc) return rc;
+    to_info(c, out);
+    return QGEMV_OK;
+}
+
+int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream) {
+    if (!h || !A || !Y) return QGEMV_E_NULL;
+    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
+    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
+    qgemv::LaunchCfg c;
+    int rc = qgemv::select_plan(&h->d, M, h->cu_count, fast, h->env_flags, &c);
+    if (rc) return rc;
+    qgemv::KArgs a;
+    fill_args(h, A, Y, M, &a);
+    a.ksplit = c.ksplit;
+    hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e;
+    switch (c.family) {
+    case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(c, a, s); break;
+    case QGEMV_FAMILY_MFMA: e = qgemv::launch_mfma(c, a, s); break;
+    default: e = qgemv::launch_generic(c, a, s); break;
+    }
+    return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
+}
+
+void qgemv_destroy(qgemv_handle *h) { delete h; }
+
+}  // extern "C"

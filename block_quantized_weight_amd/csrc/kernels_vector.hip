@@ -1,0 +1,241 @@
+// Vector kernels of qgemv for gfx950: the streaming family and the generic fallback.
+//
+// Streaming family ("[CUDA] MatMulNBits 8-bit: wide fp16 M=1 kernel", Description;
+// "[CUDA] Block-scaled MatMul decode GEMV", FP4 row-tiling paragraph):
+//  - a wave owns CPW output columns; each lane takes 16-byte chunks of every column
+//    (chunk c = lane + 64*j), so a wave-wide load moves 1 KiB of contiguous codes;
+//  - UNR chunks per lane are issued before any is consumed, and the block scales and
+//    zero points are read straight from global memory (no LDS staging, no barrier);
+//  - MT rows of A share every weight load, decode and scale (row tiling), and the
+//    whole M range is covered in ceil(M/MT) passes, so each weight byte is read once
+//    per pass, never once per row;
+//  - per-row arithmetic (decode, dot order, scale application, wave reduction) does
+//    not depend on MT, CPW or the row's position, so a row's result is bit-identical
+//    whatever tile carries it;
+//  - the 64 lane partials of a column are summed with a fixed DPP tree.
+//
+// Generic family: one wave per column, one element per lane step, any alignment and
+// any K that is a multiple of the block size. Correct and slow; used only when the
+// streaming family's preconditions do not hold.
+#include "chunk_ops.h"
+#include "launch.h"
+
+namespace qgemv {
+
+template <int FMT, int ACT, int MT, int CPW, int UNR>
+__global__ void __launch_bounds__(256) k_stream(KArgs a) {
+    using Ops = ChunkOps<FMT, ACT>;
+    constexpr int H = Ops::HALVES;
+    constexpr int WD = 4 / H;  // code dwords per half
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nbase = wave * CPW;
+    if (nbase >= a.N) return;  // uniform per wave
+
+    int64_t col[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) col[i] = (nbase + i < a.N) ? nbase + i : a.N - 1;
+
+    for (int m0 = 0; m0 < a.M; m0 += MT) {
+        float acc[CPW][MT];
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+
+        for (int64_t c0 = 0; c0 < a.nchunks; c0 += 64 * UNR) {
+            u4v w[UNR][CPW];
+            HalfMeta meta[UNR][CPW][2];
+            bool valid[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int64_t c = c0 + 64 * u + lane;
+                valid[u] = c < a.nchunks;
+                if (valid[u]) {
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) w[u][i] = load16_stream(a.W + col[i] * a.col_bytes + c * 16);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int64_t c = c0 + 64 * u + lane;
+                if (valid[u]) {
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) load_meta<FMT>(a, col[i], c, meta[u][i]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                if (!valid[u]) continue;
+                const int64_t c = c0 + 64 * u + lane;
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    HalfAct act[MT];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        uint32_t x[8];
+                        if (m0 + m < a.M) {
+                            load_act_half(a, m0 + m, c * Ops::KPC + 16 * h, x);
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) x[t] = 0u;
+                        }
+                        Ops::prep(x, act[m]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) {
+                        uint32_t wh[WD];
+#pragma unroll
+                        for (int t = 0; t < WD; ++t) wh[t] = w[u][i][h * WD + t];
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            float v = Ops::dot(wh, act[m]);
+                            if constexpr (FMT == FMT_U4 || FMT == FMT_U8) v = __builtin_fmaf(-meta[u][i][h].zero, act[m].asum, v);
+                            acc[i][m] = __builtin_fmaf(meta[u][i][h].scale, v, acc[i][m]);
+                        }
+                    }
+                }
+            }
+        }
+
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float s = wave_sum(acc[i][m]) * a.tscale;
+                if (lane == 0 && nbase + i < a.N && m0 + m < a.M) store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, s);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// generic element-wise kernel
+
+template <int ACT>
+__device__ __forceinline__ float act_at(const KArgs &a, int m, int64_t k) {
+    const uint16_t bits = ((const uint16_t *)a.A)[(int64_t)m * a.K + k];
+    if constexpr (ACT == ACT_F16) return (float)__builtin_bit_cast(_Float16, bits);
+    else return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+
+template <int FMT>
+__device__ __forceinline__ float weight_at(const KArgs &a, int64_t n, int64_t k) {
+    const int64_t b = k / a.bs;
+    if constexpr (FMT == FMT_U4) {
+        const uint8_t byte = a.W[n * a.col_bytes + (k >> 1)];
+        const int q = (k & 1) ? (byte >> 4) : (byte & 0x0F);
+        int z = 8;
+        if (a.zp) {
+            const uint8_t zb = a.zp[n * a.zstride + (b >> 1)];
+            z = (b & 1) ? (zb >> 4) : (zb & 0x0F);
+        }
+        return half_bits_to_float(((const uint16_t *)a.scales)[n * a.nblk + b]) * (float)(q - z);
+    } else if constexpr (FMT == FMT_U8) {
+        const int q = a.W[n * a.col_bytes + k];
+        const int z = a.zp ? a.zp[n * a.nblk + b] : 128;
+        return half_bits_to_float(((const uint16_t *)a.scales)[n * a.nblk + b]) * (float)(q - z);
+    } else if constexpr (FMT == FMT_FP8) {
+        return ((const float *)a.scales)[n * a.nblk + b] * e4m3_to_float(a.W[n * a.col_bytes + k]);
+    } else {
+        const uint8_t byte = a.W[n * a.col_bytes + (k >> 1)];
+        const uint32_t code = (k & 1) ? (byte >> 4) : (byte & 0x0F);
+        const uint32_t pair = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0));
+        const float e2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFFu));
+        return e4m3_to_float(((const uint8_t *)a.scales)[n * (a.K / 16) + k / 16]) * e2;
+    }
+}
+
+template <int FMT, int ACT>
+__global__ void __launch_bounds__(256) k_generic(KArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t n = wave; n < a.N; n += nwaves) {
+        float acc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
+        for (int64_t k = lane; k < a.K; k += 64) {
+            const float w = weight_at<FMT>(a, n, k);
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                if (m < a.M) acc[m] = __builtin_fmaf(act_at<ACT>(a, m, k), w, acc[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            if (m < a.M) {
+                const float s = wave_sum(acc[m]) * a.tscale;
+                if (lane == 0) store_out<ACT>(a.Y, (int64_t)m * a.N + n, s);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// launchers
+
+namespace {
+
+template <int FMT, int ACT, int MT, int CPW>
+hipError_t go_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int ACT, int MT>
+hipError_t pick_cpw(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.cols_per_wave) {
+    case 1: return go_stream<FMT, ACT, MT, 1>(cfg, a, s);
+    case 2: return go_stream<FMT, ACT, MT, 2>(cfg, a, s);
+    case 4: return go_stream<FMT, ACT, MT, 4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT, int ACT>
+hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.rows_per_pass) {
+    case 1: return pick_cpw<FMT, ACT, 1>(cfg, a, s);
+    case 2: return pick_cpw<FMT, ACT, 2>(cfg, a, s);
+    case 4: return pick_cpw<FMT, ACT, 4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+hipError_t pick_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    return cfg.act == ACT_F16 ? pick_mt<FMT, ACT_F16>(cfg, a, s) : pick_mt<FMT, ACT_BF16>(cfg, a, s);
+}
+
+template <int FMT>
+hipError_t generic_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    if (cfg.act == ACT_F16)
+        hipLaunchKernelGGL((k_generic<FMT, ACT_F16>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_generic<FMT, ACT_BF16>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.fmt) {
+    case FMT_U4: return pick_act<FMT_U4>(cfg, a, s);
+    case FMT_U8: return pick_act<FMT_U8>(cfg, a, s);
+    case FMT_FP8: return pick_act<FMT_FP8>(cfg, a, s);
+    case FMT_NVFP4: return pick_act<FMT_NVFP4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_generic(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.fmt) {
+    case FMT_U4: return generic_act<FMT_U4>(cfg, a, s);
+    case FMT_U8: return generic_act<FMT_U8>(cfg, a, s);
+    case FMT_FP8: return generic_act<FMT_FP8>(cfg, a, s);
+    case FMT_NVFP4: return generic_act<FMT_NVFP4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qgemv

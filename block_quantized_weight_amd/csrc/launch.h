@@ -1,0 +1,46 @@
+// Host-side launch description shared by the dispatcher and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+// Arguments every kernel receives (by value).
+struct KArgs {
+    const uint8_t *W;        // packed codes
+    const void *scales;      // block scales
+    const uint8_t *zp;       // zero points or nullptr
+    const void *A;           // [M, K] activations
+    void *Y;                 // [M, N] output
+    int64_t N;
+    int64_t K;
+    int64_t col_bytes;       // bytes of codes per column
+    int64_t nchunks;         // 16-byte chunks per column
+    int32_t bs;              // block size along K
+    int32_t nblk;            // K / bs
+    int32_t zstride;         // bytes of zero points per column
+    int32_t M;
+    int32_t ksplit;          // waves sharing one column tile's K range
+    float tscale;            // nvfp4 tensor scale (1 otherwise)
+};
+
+struct LaunchCfg {
+    int fmt;            // Fmt
+    int act;            // Act
+    int family;         // qgemv_family
+    int rows_per_pass;  // MT
+    int passes;
+    int cols_per_wave;
+    int ksplit;
+    int waves_per_wg;
+    int64_t grid;
+    int lds_bytes;
+    int variant;
+};
+
+hipError_t launch_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
+hipError_t launch_generic(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
+hipError_t launch_mfma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
+
+}  // namespace qgemv

@@ -1,0 +1,120 @@
+// Device-side building blocks shared by the qgemv kernels (gfx950 / CDNA4 only).
+//
+// Decoders turn 16-byte chunks of packed codes into fp16/bf16 operand pairs that
+// feed v_dot2_f32_{f16,bf16} (vector family) or v_mfma_f32_16x16x32_{f16,bf16}
+// (matrix family). Every decode here is exact:
+//  - 4-/8-bit codes q become fp16 subnormals q*2^-24 (4-bit codes in the upper
+//    nibble of a half become q*2^-20), or bf16 integers q through the E4M3
+//    converter (codes 0..15 of E4M3 are exactly q*2^-9; the converter's power-of-two
+//    scale 2^9 restores q). The zero point is applied as z * sum(a) on the fp32
+//    block sum, so (q - zp) never needs a packed subtract.
+//  - E4M3 and E2M1 use the hardware converters, which decode OCP E4M3FN and
+//    E2M1 exactly (E4M3 to fp16/bf16 widening is lossless: "[CUDA] Block-scaled
+//    MatMul decode GEMV", FP8 mma paragraph).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace qgemv {
+
+enum Fmt : int { FMT_U4 = 1, FMT_U8 = 2, FMT_FP8 = 3, FMT_NVFP4 = 4 };
+enum Act : int { ACT_F16 = 1, ACT_BF16 = 2 };
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+
+// ---------------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    // v_perm_b32: selector bytes 0..3 pick bytes of `lo`, 4..7 bytes of `hi`, 0x0c gives 0.
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <int ACT>
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float c) {
+    if constexpr (ACT == ACT_F16) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, x), __builtin_bit_cast(h2, y), c, false);
+    } else {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, x), __builtin_bit_cast(b2, y), c, false);
+    }
+}
+
+// Pair (1, 1) in the activation type, for sums of activations through dot2.
+template <int ACT>
+__device__ __forceinline__ constexpr uint32_t ones2() {
+    return ACT == ACT_F16 ? 0x3C003C00u : 0x3F803F80u;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float e4m3_to_float(uint32_t byte) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// E4M3 -> fp16/bf16 pairs: bytes (2*word, 2*word+1) of w.
+template <int ACT, bool WORD>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+    if constexpr (ACT == ACT_F16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, WORD));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, WORD));
+}
+
+// E2M1 -> fp16/bf16 pair from byte `sel` of w (low nibble -> element 0).
+template <int ACT, int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
+    if constexpr (ACT == ACT_F16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// bf16 pair of integers (q_a, q_b) from bytes (2*word, 2*word+1) of w holding 0..15.
+template <bool WORD>
+__device__ __forceinline__ uint32_t small_int_bf16_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, WORD));
+}
+
+template <int ACT>
+__device__ __forceinline__ void store_out(void *Y, int64_t idx, float v) {
+    if constexpr (ACT == ACT_F16) {
+        ((_Float16 *)Y)[idx] = (_Float16)v;
+    } else {
+        ((__bf16 *)Y)[idx] = (__bf16)v;
+    }
+}
+
+// Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 and is
+// returned to every lane through readlane. Fixed order: the result depends only on
+// the 64 inputs.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));  // row_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false)); // row_bcast:15
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false)); // row_bcast:31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ u4v load16(const void *p) {
+    return *(const u4v *)p;
+}
+
+// Streaming load of weight bytes: read once, so keep them out of the caches' way.
+__device__ __forceinline__ u4v load16_stream(const void *p) {
+    return __builtin_nontemporal_load((const u4v *)p);
+}
+
+}  // namespace qgemv

@@ -1,0 +1,161 @@
+/*
+ * qgemv — block-scaled small-M decode GEMV for AMD Instinct MI355X (gfx950)
+ *
+ *     Y[M, N] = A[M, K] . dequant(W)[N, K]^T,   1 <= M <= 16,
+ *
+ * with A and Y in fp16 or bf16 and fp32 accumulation. The weight W is quantized
+ * in blocks along K in one of four formats:
+ *
+ *   QGEMV_FMT_U4     4-bit unsigned codes, fp16 scale and 4-bit zero point per
+ *                    block: w = s * (q - zp). Layout [N, K/bs, bs/2] bytes, two
+ *                    codes per byte with the lower k in the low nibble.
+ *                    ("[CUDA] Batched small-M GEMV for MatMulNBits (4-bit/8-bit)",
+ *                    Description: the [N, blocks, blob] layout.)
+ *   QGEMV_FMT_U8     8-bit unsigned codes, fp16 scale and 8-bit zero point per
+ *                    block. Layout [N, K/bs, bs] bytes. ("[CUDA] MatMulNBits
+ *                    8-bit: wide fp16 M=1 kernel for decode GEMVs", Description:
+ *                    per-block scale and zero point, (q - zp) exact.)
+ *   QGEMV_FMT_FP8    OCP E4M3FN codes, row-major [N, K] bytes, one fp32 scale per
+ *                    block of bs consecutive k: w = s * e4m3(q). ("[CUDA]
+ *                    Block-scaled MatMul decode GEMV", FP8 mma paragraph.)
+ *   QGEMV_FMT_NVFP4  packed E2M1 codes [N, K/2] bytes (lower k in the low nibble),
+ *                    one E4M3 scale byte per 16 consecutive k, one fp32 tensor
+ *                    scale: w = t * e4m3(s) * e2m1(q). (Same page, FP4 mma
+ *                    paragraph.)
+ *
+ * Scales are row-major [N, K/bs]: fp16 bit patterns for U4/U8, float32 for FP8,
+ * E4M3 bytes for NVFP4. Zero points: U4 packs two per byte, even block in the low
+ * nibble, ceil((K/bs)/2) bytes per column; U8 has one byte per block, [N, K/bs].
+ * A NULL zero-point pointer means the midpoint 2^(bits-1). FP8 and NVFP4 take no
+ * zero points.
+ *
+ * All pointers passed to qgemv_create and qgemv_run are DEVICE pointers, owned by
+ * the caller. The handle keeps the weight pointers (not copies) and the caller
+ * keeps them alive until qgemv_destroy. The library allocates no device memory.
+ *
+ * Every call returns QGEMV_OK (0) or a positive status; nothing aborts, prints or
+ * throws across this interface. Arguments are validated before anything is
+ * launched.
+ */
+#ifndef QGEMV_H_
+#define QGEMV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QGEMV_ABI_VERSION 1
+#define QGEMV_MAX_M 16
+
+/* Weight formats. */
+enum qgemv_format {
+    QGEMV_FMT_U4 = 1,
+    QGEMV_FMT_U8 = 2,
+    QGEMV_FMT_FP8 = 3,
+    QGEMV_FMT_NVFP4 = 4
+};
+
+/* Activation (and output) element type. */
+enum qgemv_act_dtype {
+    QGEMV_ACT_F16 = 1,
+    QGEMV_ACT_BF16 = 2
+};
+
+/* Status codes. */
+enum qgemv_status {
+    QGEMV_OK = 0,
+    QGEMV_E_NULL = 1,     /* a required pointer is NULL */
+    QGEMV_E_SHAPE = 2,    /* M outside [1, 16], N < 1, K < 1 or K % block_size != 0 */
+    QGEMV_E_BLOCK = 3,    /* block size not supported for the format */
+    QGEMV_E_FORMAT = 4,   /* unknown format / dtype, or zero points given for FP8/NVFP4 */
+    QGEMV_E_DEVICE = 5,   /* no usable device, or the device is not gfx950 */
+    QGEMV_E_LAUNCH = 6,   /* the kernel launch reported an error */
+    QGEMV_E_ARG = 7,      /* other invalid argument (struct size, flags, plan request) */
+    QGEMV_E_ALLOC = 8     /* host memory for the handle could not be allocated */
+};
+
+/* Kernel families (qgemv_plan_info.family; also usable in QGEMV_FLAG_FORCE). */
+enum qgemv_family {
+    QGEMV_FAMILY_AUTO = 0,
+    QGEMV_FAMILY_STREAM = 1,   /* vector kernel: wave per column group, fp32 dot products */
+    QGEMV_FAMILY_MFMA = 2,     /* matrix-core kernel: 16-column tiles, rows in 4-row groups */
+    QGEMV_FAMILY_GENERIC = 3   /* element-wise kernel for any shape / alignment */
+};
+
+/* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
+ * Bits 8..15: forced K split (0 = automatic; otherwise 1..64 waves per workgroup
+ * share the K range of a column tile). Bit 16: never pick the MFMA family. */
+#define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
+#define QGEMV_FLAG_KSPLIT_SHIFT 8
+#define QGEMV_FLAG_KSPLIT_MASK 0x0000FF00u
+#define QGEMV_FLAG_NO_MFMA 0x00010000u
+
+/* Problem description. struct_size must be sizeof(qgemv_desc). */
+typedef struct qgemv_desc {
+    uint32_t struct_size;
+    int32_t format;        /* enum qgemv_format */
+    int32_t act_dtype;     /* enum qgemv_act_dtype, for A and Y */
+    int32_t block_size;    /* U4/U8/FP8: 16, 32, 64, 128 or 256; NVFP4: 16 */
+    int64_t N;             /* output columns (weight rows) */
+    int64_t K;             /* reduction length */
+    const void *W;         /* device: packed codes (layout above) */
+    const void *scales;    /* device: block scales [N, K/bs] */
+    const void *zero_points; /* device: zero points, or NULL */
+    float tensor_scale;    /* NVFP4 tensor scale (multiplies); ignored otherwise */
+    uint32_t flags;        /* QGEMV_FLAG_* */
+} qgemv_desc;
+
+/* What qgemv_plan / qgemv_select report about a launch. */
+typedef struct qgemv_plan_info {
+    int32_t family;          /* enum qgemv_family actually used */
+    int32_t rows_per_pass;   /* rows of A carried by one pass over the weight */
+    int32_t passes;          /* passes over the weight for this M */
+    int32_t cols_per_wave;   /* output columns one wave owns at a time */
+    int32_t ksplit;          /* waves of a workgroup sharing one column tile's K */
+    int32_t waves_per_wg;    /* waves per workgroup */
+    int64_t grid;            /* workgroups launched */
+    int32_t lds_bytes;       /* dynamic LDS per workgroup */
+    int32_t variant;         /* family-specific kernel variant id */
+} qgemv_plan_info;
+
+typedef struct qgemv_handle qgemv_handle;
+
+/* Validate d, read the device's properties (device index, or -1 for the current
+ * device), and return a handle in *out. The weight pointers are kept, not copied.
+ * Environment overrides (QGEMV_FORCE_FAMILY, QGEMV_FORCE_KSPLIT, QGEMV_NO_MFMA) are
+ * read here once, never per call. */
+int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device);
+
+/* Enqueue Y[M, N] = A[M, K] . dequant(W)^T on hip_stream (a hipStream_t; NULL = the
+ * default stream). A is [M, K] row-major and Y is [M, N] row-major, both device
+ * pointers in the handle's activation dtype. Asynchronous: no host sync, no
+ * allocation, no environment read. Safe to call concurrently on different streams
+ * (the handle is immutable after create). The call must be made with the
+ * handle's device current. */
+int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream);
+
+/* The launch qgemv_run would make for M rows (pointers as given at create; A and Y
+ * assumed 16-byte aligned). */
+int qgemv_plan(const qgemv_handle *h, int M, qgemv_plan_info *out);
+
+/* Pure host selector, no device needed: the plan for d at M rows on a device with
+ * cu_count compute units, assuming 16-byte aligned pointers. Used to test the
+ * dispatcher at fixed CU counts. */
+int qgemv_select(const qgemv_desc *d, int M, int cu_count, qgemv_plan_info *out);
+
+/* Release the handle (NULL is ignored). Does not touch the caller's buffers. */
+void qgemv_destroy(qgemv_handle *h);
+
+/* Static English text for a status code. */
+const char *qgemv_status_str(int status);
+
+/* ABI version of the loaded library (QGEMV_ABI_VERSION it was built with). */
+int qgemv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H_ */

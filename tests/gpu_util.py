@@ -1,0 +1,75 @@
+"""Helpers for the GPU tests: upload a problem, run it through the C ABI, compare
+with the oracle. Imported only by tests marked ``gpu``."""
+
+from __future__ import annotations
+
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import block_quantized_weight_amd as bqw
+import oracle
+from block_quantized_weight_amd import synth
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 device"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(prob: synth.Problem, M: int, flags: int = 0, A: Optional[np.ndarray] = None,
+            a_offset_elems: int = 0, repeat: int = 1):
+    """Run Y = A[:M] . dequant(W)^T on cuda:0; returns (Y as float64 [M, N], plan)."""
+    q, t = bqw.upload(prob, flags=flags)
+    tdt = t["A"].dtype
+    if A is not None:
+        t["A"] = torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).cuda().view(tdt)
+    Am = t["A"][:M].contiguous()
+    if a_offset_elems:
+        buf = torch.empty(M * prob.K + a_offset_elems, dtype=tdt, device="cuda")
+        buf[a_offset_elems:] = Am.reshape(-1)
+        Am = buf[a_offset_elems:]
+    outs = []
+    for _ in range(repeat):
+        Y = torch.full((M, prob.N), float("nan"), dtype=tdt, device="cuda")
+        q.run(Am, Y, M=M)
+        torch.cuda.synchronize()
+        outs.append(Y.float().cpu().numpy().astype(np.float64))
+    plan = q.plan(M)
+    q.close()
+    return (outs if repeat > 1 else outs[0]), plan
+
+
+def sample_points(M: int, N: int, count: int, seed: int = 0):
+    """Random (m, n) points plus every row at the first and the last 40 columns."""
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, size=count)
+    ns = rng.integers(0, N, size=count)
+    edge = np.unique(np.concatenate([np.arange(min(40, N)), np.arange(max(0, N - 40), N)]))
+    em = np.repeat(np.arange(M), edge.size)
+    en = np.tile(edge, M)
+    return np.concatenate([ms, em]).astype(np.int32), np.concatenate([ns, en]).astype(np.int64)
+
+
+def check_full(prob, M, Y, A=None, strict=True):
+    """Compare every output. strict=False allows the output type's final rounding on
+    top of the accumulation bound (used for synthetic cases outside the named
+    workloads, where |y| can approach S and bf16 rounding alone exceeds 1e-3 * S)."""
+    Yr, S = oracle.gemv(prob, A=A, M=M)
+    ok, ratio = oracle.within_tolerance(Y, Yr, S, out_dtype=None if strict else prob.act)
+    return ok, ratio, Yr, S
+
+
+def check_points(prob, M, Y, count=3000, seed=0, A=None):
+    ms, ns = sample_points(M, prob.N, count, seed)
+    yr, s = oracle.gemv_points(prob, ms, ns, A=A, M=M)
+    ok, ratio = oracle.within_tolerance(Y[ms, ns], yr, s)
+    return ok, ratio

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports every declared entry point, and
+its pure-host pieces (validation, status strings, dispatcher) behave. No GPU needed."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_weight_amd as bqw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:int|void|const char \*)\s*\**\s*(qgemv_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"qgemv_create", "qgemv_run", "qgemv_plan", "qgemv_select", "qgemv_destroy",
+            "qgemv_status_str", "qgemv_abi_version"} <= names
+    L = bqw.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_abi_version_and_struct_layout():
+    assert bqw.lib().qgemv_abi_version() == 1
+    # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields
+    assert ctypes.sizeof(bqw.Desc) == 64
+    assert bqw.Desc.N.offset == 16 and bqw.Desc.W.offset == 32 and bqw.Desc.flags.offset == 60
+
+
+def test_status_strings():
+    for s in range(0, 9):
+        assert bqw.status_str(s)
+    assert bqw.status_str(0) == "ok"
+    assert "unknown" in bqw.status_str(99)
+
+
+def _sel(**kw):
+    base = dict(fmt="u4", act="bf16", N=151936, K=4096, block_size=32, M=1, cu_count=256)
+    base.update(kw)
+    return bqw.select(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), 2), (dict(M=17), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=4010), 2),
+    (dict(block_size=48), 3), (dict(block_size=8), 3), (dict(fmt="nvfp4", block_size=32), 3),
+    (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
+    (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
+    (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=1 << 20), 7),
+    (dict(cu_count=0), 7),
+])
+def test_select_rejects_invalid_arguments(kw, status):
+    with pytest.raises(bqw.QGemvError) as e:
+        _sel(**kw)
+    assert e.value.status == status
+
+
+def test_null_pointers_are_rejected_before_anything_else():
+    L = bqw.lib()
+    assert L.qgemv_select(None, 1, 256, None) == 1
+    out = bqw.PlanInfo()
+    assert L.qgemv_select(None, 1, 256, ctypes.byref(out)) == 1
+    assert L.qgemv_create(None, None, 0) == 1
+    h = ctypes.c_void_p()
+    assert L.qgemv_create(ctypes.byref(h), None, 0) == 1
+    assert L.qgemv_run(None, None, None, 1, None) == 1
+    L.qgemv_destroy(None)  # ignored
+
+
+def test_create_validates_before_touching_the_device():
+    L = bqw.lib()
+    d = bqw.make_desc("u4", "f16", 16, 100, 32, 0x1000, 0x1000)  # K not a multiple of bs
+    h = ctypes.c_void_p()
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 0) == 2
+    d.struct_size = 8
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(d), 0) == 7
+
+
+def test_select_families_and_fallback():
+    assert _sel()["family"] in ("stream", "mfma")
+    # misaligned weight pointer -> generic kernel, never an error
+    assert _sel(W=0x1001)["family"] == "generic"
+    # K not a multiple of a 16-byte chunk -> generic
+    assert _sel(fmt="u4", K=16 * 3, block_size=16)["family"] == "generic"
+    assert _sel(flags=3)["family"] == "generic"
+    with pytest.raises(bqw.QGemvError):
+        _sel(W=0x1001, flags=1)  # a forced fast family needs its preconditions
+
+
+def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
+    for fmt, act, N, K, bs in [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128),
+                               ("nvfp4", "bf16", 248320, 2048, 16), ("u8", "f16", 4096, 4096, 128),
+                               ("u4", "f16", 1024, 2048, 32)]:
+        plans = [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=m) for m in range(1, 17)]
+        for key in ("ksplit", "variant"):
+            fams = {}
+            for p in plans:
+                fams.setdefault(p["family"], set()).add(p[key])
+            assert all(len(v) == 1 for v in fams.values()), (fmt, key, fams)
+
+
+def test_select_covers_the_machine():
+    # every automatic plan for the named shapes launches at least a full wave of
+    # work groups on 256 CUs, or is limited by the number of columns itself
+    for fmt, act, N, K, bs in [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128),
+                               ("nvfp4", "bf16", 248320, 2048, 16), ("u8", "f16", 4096, 4096, 128)]:
+        for M in (1, 4, 8):
+            p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)
+            assert p["grid"] * p["waves_per_wg"] >= 256 * 4 or p["grid"] * p["cols_per_wave"] * p["waves_per_wg"] >= N

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: |y - y_ref| <= 1e-3 * sum|a*w| + 1e-3 per output (fp32 accumulation), checked
+element by element on every output for the small workloads and on sampled outputs
+(random points plus every row of the first and last 40 columns) at full size.
+Integer-valued and one-hot cases must match bit for bit; rows must come out
+bit-identical whatever tile carries them; repeated runs must be bitwise equal.
+"""
+
+import numpy as np
+import pytest
+
+import block_quantized_weight_amd as bqw
+import oracle
+from block_quantized_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from tests import gpu_util as gu
+
+FAMILY_FLAG = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+# ----------------------------------------------------------------------------------
+# named workloads
+
+
+SMALL = [("u4_m1_k512_n256", 1), ("u8_m1_k4096_n4096", 1), ("fp8_k6144_n5120", 1), ("fp8_k6144_n5120", 4),
+         ("fp8_k6144_n5120", 8), ("nvfp4_m4_k2048_n2048", 4), ("u4_m8_k2048_n1024", 8)]
+
+
+@pytest.mark.parametrize("name,M", SMALL)
+def test_named_workload_full_parity(name, M):
+    prob = synth.workload(name)
+    gu.say(f"[parity] {name} M={M}")
+    Y, plan = gu.run_gpu(prob, M)
+    ok, ratio, Yr, S = gu.check_full(prob, M, Y)
+    gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
+    assert ok, (name, M, ratio, plan)
+
+
+@pytest.fixture(scope="module")
+def lm_head_u4():
+    return synth.workload("u4_k4096_n151936")
+
+
+@pytest.fixture(scope="module")
+def lm_head_nvfp4():
+    return synth.workload("nvfp4_m4_k2048_n248320")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_u4_lm_head_sampled_parity(lm_head_u4, M):
+    gu.say(f"[parity] u4 lm_head M={M}")
+    Y, plan = gu.run_gpu(lm_head_u4, M)
+    assert np.all(np.isfinite(Y))
+    ok, ratio = gu.check_points(lm_head_u4, M, Y, seed=M)
+    gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
+    assert ok, (M, ratio, plan)
+
+
+def test_nvfp4_lm_head_sampled_parity(lm_head_nvfp4):
+    gu.say("[parity] nvfp4 lm_head M=4")
+    Y, plan = gu.run_gpu(lm_head_nvfp4, 4)
+    assert np.all(np.isfinite(Y))
+    ok, ratio = gu.check_points(lm_head_nvfp4, 4, Y)
+    gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
+    assert ok, ratio
+
+
+# ----------------------------------------------------------------------------------
+# every family, every format, ragged shapes
+
+
+FMT_CASES = [("u4", "f16", 32), ("u4", "bf16", 32), ("u4", "f16", 16), ("u4", "bf16", 128),
+             ("u8", "f16", 128), ("u8", "bf16", 32), ("u8", "f16", 16),
+             ("fp8", "f16", 128), ("fp8", "bf16", 32), ("nvfp4", "bf16", 16), ("nvfp4", "f16", 16)]
+
+
+@pytest.mark.parametrize("family", ["auto", "stream", "generic"])
+@pytest.mark.parametrize("fmt,act,bs", FMT_CASES)
+def test_families_ragged_shapes(family, fmt, act, bs):
+    for N, K, M in [(1, 256, 1), (17, 512, 3), (36, 1024, 5), (1169, 768, 16), (300, 4096, 2)]:
+        if K % bs:
+            continue
+        prob = synth.make_problem(fmt, act, N, K, bs, M, seed=N + K, zp_range=(0, 15) if fmt == "u4" else (96, 160),
+                                  scale_sigma=0.02 if fmt == "u4" else 0.004)
+        gu.say(f"[ragged] {family} {fmt}/{act} bs={bs} N={N} K={K} M={M}")
+        Y, plan = gu.run_gpu(prob, M, flags=FAMILY_FLAG[family])
+        if family != "auto":
+            assert plan["family"] == family
+        ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
+        assert ok, (family, fmt, act, bs, N, K, M, ratio, plan)
+
+
+@pytest.mark.parametrize("fmt,act", [("u4", "f16"), ("u8", "f16"), ("u4", "bf16")])
+def test_missing_zero_points_mean_midpoint(fmt, act):
+    prob = synth.make_problem(fmt, act, 200, 512, 32, 4, seed=9, with_zp=False)
+    assert prob.zp is None
+    Y, _ = gu.run_gpu(prob, 4)
+    ok, ratio, _, _ = gu.check_full(prob, 4, Y, strict=False)
+    assert ok, ratio
+
+
+# ----------------------------------------------------------------------------------
+# bit-exact properties
+
+
+@pytest.mark.parametrize("family", ["stream", "generic"])
+@pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u4", "f16", 32), ("fp8", "f16", 128),
+                                         ("nvfp4", "bf16", 16), ("u8", "f16", 128)])
+def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
+    """Row i of an M-row call equals the same row run alone, and in any other M."""
+    prob = synth.make_problem(fmt, act, 777, 2048, bs, 16, seed=21)
+    flags = FAMILY_FLAG[family]
+    gu.say(f"[rows] {family} {fmt}/{act}")
+    Y16, _ = gu.run_gpu(prob, 16, flags=flags)
+    for M in (1, 2, 3, 4, 5, 8):
+        A = np.ascontiguousarray(prob.A[16 - M:])  # rows land in different slots
+        Ym, _ = gu.run_gpu(prob, M, flags=flags, A=A)
+        assert np.array_equal(Ym.view(np.int64), Y16[16 - M:].view(np.int64)), (family, fmt, M)
+
+
+def test_repeated_runs_are_bitwise_equal():
+    prob = synth.workload("u4_m8_k2048_n1024")
+    outs, _ = gu.run_gpu(prob, 8, repeat=4)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("fmt,act", [("u4", "f16"), ("u4", "bf16"), ("u8", "f16"), ("u8", "bf16")])
+def test_integer_special_case_is_exact(fmt, act):
+    """Scale 1, zero point 0, small integer activations: fp32 holds the integer result
+    exactly, so the output must be that integer rounded once to the output type."""
+    rng = np.random.default_rng(1)
+    M, N, K, bs = 5, 333, 512, 32
+    nblk = K // bs
+    a_int = rng.integers(-2, 3, size=(M, K))
+    hi = 16 if fmt == "u4" else 4
+    q = rng.integers(0, hi, size=(N, K)).astype(np.uint8)
+    W = synth.pack_nibbles(q).reshape(N, nblk, bs // 2) if fmt == "u4" else q.reshape(N, nblk, bs)
+    zp = synth.pack_nibbles(np.zeros((N, nblk), np.uint8)) if fmt == "u4" else np.zeros((N, nblk), np.uint8)
+    prob = synth.Problem(name="int", fmt=fmt, act=act, N=N, K=K, bs=bs, W=W,
+                         scales=np.full((N, nblk), 0x3C00, dtype=np.uint16), zp=zp, tensor_scale=1.0,
+                         A=synth.activation_bits(a_int.astype(np.float64), act))
+    exact = (a_int @ q.astype(np.int64).T).astype(np.float64)
+    assert np.abs(exact).max() > 256  # some results need rounding in bf16
+    want = oracle.decode_activation_bits(synth.activation_bits(exact, act), act)
+    for fam in ("stream", "generic"):
+        Y, _ = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam])
+        assert np.array_equal(Y, want), fam
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4", "u4", "u8"])
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_one_hot_probes_decode_every_code_exactly(fmt, act):
+    """One-hot activations pick single weights; every code of the format appears, so
+    each decoded value (times its scale) must come out exactly. Catches any lane,
+    byte, nibble or k permutation and any decoder error."""
+    rng = np.random.default_rng(2)
+    N, K = 48, 512
+    bs = 16 if fmt == "nvfp4" else 32
+    nblk = K // bs
+    if fmt == "fp8":
+        codes = np.resize(synth.FP8_FINITE_CODES, (N, K)).astype(np.uint8)
+        for n in range(N):
+            codes[n] = np.roll(codes[n], 5 * n)
+        W = codes
+        scales = np.ones((N, nblk), np.float32)
+        zp = None
+    elif fmt == "nvfp4":
+        codes = (np.arange(N * K).reshape(N, K) + np.arange(N)[:, None]) % 16
+        W = synth.pack_nibbles(codes.astype(np.uint8))
+        scales = np.full((N, K // 16), 0x38, np.uint8)  # E4M3 1.0
+        zp = None
+    elif fmt == "u4":
+        codes = ((np.arange(K)[None, :] * 3 + np.arange(N)[:, None]) % 16).astype(np.uint8)
+        W = synth.pack_nibbles(codes).reshape(N, nblk, bs // 2)
+        zp = synth.pack_nibbles(rng.integers(0, 16, size=(N, nblk)).astype(np.uint8))
+        scales = np.full((N, nblk), 0x3C00, np.uint16)
+    else:
+        codes = ((np.arange(K)[None, :] + 37 * np.arange(N)[:, None]) % 256).astype(np.uint8)
+        W = codes.reshape(N, nblk, bs)
+        zp = rng.integers(0, 256, size=(N, nblk)).astype(np.uint8)
+        scales = np.full((N, nblk), 0x3C00, np.uint16)
+    base = synth.Problem(name="onehot", fmt=fmt, act=act, N=N, K=K, bs=bs, W=W, scales=scales, zp=zp,
+                         tensor_scale=1.0, A=np.zeros((16, K), np.uint16))
+    one = 0x3C00 if act == "f16" else 0x3F80
+    deq = oracle.dequant_columns(base)  # [N, K] exact values
+    for fam in ("stream", "generic"):
+        for k0 in range(0, K, 16):
+            A = np.zeros((16, K), np.uint16)
+            A[np.arange(16), k0 + np.arange(16)] = one
+            Y, _ = gu.run_gpu(base, 16, flags=FAMILY_FLAG[fam], A=A)
+            want = deq[:, k0:k0 + 16].T  # exact in fp16 and bf16
+            assert np.array_equal(Y, want), (fam, fmt, act, k0)
+
+
+def test_misaligned_activations_fall_back_and_stay_correct():
+    prob = synth.workload("u4_m8_k2048_n1024", n_override=256)
+    Y, plan = gu.run_gpu(prob, 8, a_offset_elems=1)  # A 2 bytes off a 16-byte boundary
+    ok, ratio, _, _ = gu.check_full(prob, 8, Y)
+    assert ok, ratio
+
+
+def test_run_rejects_bad_arguments():
+    import torch
+    prob = synth.workload("u4_m1_k512_n256")
+    q, t = bqw.upload(prob)
+    Y = torch.empty((16, prob.N), dtype=t["A"].dtype, device="cuda")
+    for M in (0, 17, -1):
+        with pytest.raises(bqw.QGemvError) as e:
+            q.run(t["A"], Y, M=M)
+        assert e.value.status == 2
+    with pytest.raises(bqw.QGemvError) as e:
+        q.run(0, Y, M=1)
+    assert e.value.status == 1
+    q.close()
