@@ -63,6 +63,8 @@ void fill_args(const qgemv_handle *h, const void *A, void *Y, int M, qgemv::KArg
     a->col_bytes = (d.format == QGEMV_FMT_U4 || d.format == QGEMV_FMT_NVFP4) ? d.K / 2 : d.K;
     a->nchunks = a->col_bytes / 16;
     a->bs = d.block_size;
+    a->bs_shift = 0;
+    while ((1 << a->bs_shift) < d.block_size) ++a->bs_shift;
     a->nblk = (int32_t)(d.K / d.block_size);
     a->zstride = (d.format == QGEMV_FMT_U4) ? (a->nblk + 1) / 2 : a->nblk;
     a->M = M;

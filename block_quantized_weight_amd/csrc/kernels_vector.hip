@@ -22,76 +22,88 @@
 
 namespace qgemv {
 
-template <int FMT, int ACT, int MT, int CPW, int UNR>
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
 __global__ void __launch_bounds__(256) k_stream(KArgs a) {
-    using Ops = ChunkOps<FMT, ACT>;
-    constexpr int H = Ops::HALVES;
-    constexpr int WD = 4 / H;  // code dwords per half
+    using Ops = ChunkOps<FMT, ACT, H>;
+    constexpr bool ZP = (FMT == FMT_U4 || FMT == FMT_U8);
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t nbase = wave * CPW;
     if (nbase >= a.N) return;  // uniform per wave
 
-    int64_t col[CPW];
+    ColPtrs cp[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) col[i] = (nbase + i < a.N) ? nbase + i : a.N - 1;
+    for (int i = 0; i < CPW; ++i) cp[i] = col_ptrs<FMT>(a, (nbase + i < a.N) ? nbase + i : a.N - 1);
+    const int nch = (int)a.nchunks;
 
     for (int m0 = 0; m0 < a.M; m0 += MT) {
+        const uint16_t *arow[MT];
+        bool rlive[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            rlive[m] = m0 + m < a.M;
+            arow[m] = (const uint16_t *)a.A + (int64_t)(rlive[m] ? m0 + m : 0) * a.K;
+        }
         float acc[CPW][MT];
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
 
-        for (int64_t c0 = 0; c0 < a.nchunks; c0 += 64 * UNR) {
+        for (int base = 0; base < nch; base += 64 * UNR) {
             u4v w[UNR][CPW];
-            HalfMeta meta[UNR][CPW][2];
+            float sc[UNR][CPW][H], zr[UNR][CPW][H];
             bool valid[UNR];
+            // all weight loads of this round first, then the block metadata
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int64_t c = c0 + 64 * u + lane;
-                valid[u] = c < a.nchunks;
+                const int c = base + 64 * u + lane;
+                valid[u] = c < nch;
                 if (valid[u]) {
 #pragma unroll
-                    for (int i = 0; i < CPW; ++i) w[u][i] = load16_stream(a.W + col[i] * a.col_bytes + c * 16);
+                    for (int i = 0; i < CPW; ++i) w[u][i] = load16_stream(cp[i].w + (uint32_t)c * 16u);
                 }
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int64_t c = c0 + 64 * u + lane;
+                const int c = base + 64 * u + lane;
                 if (valid[u]) {
 #pragma unroll
-                    for (int i = 0; i < CPW; ++i) load_meta<FMT>(a, col[i], c, meta[u][i]);
+                    for (int i = 0; i < CPW; ++i) chunk_meta<FMT, H>(a, cp[i], c, sc[u][i], zr[u][i]);
                 }
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 if (!valid[u]) continue;
-                const int64_t c = c0 + 64 * u + lane;
+                const int c = base + 64 * u + lane;
+                ChunkAct act[MT];
 #pragma unroll
-                for (int h = 0; h < H; ++h) {
-                    HalfAct act[MT];
+                for (int m = 0; m < MT; ++m) {
+                    uint32_t x[Ops::ND];
+                    if (rlive[m]) {
+                        const uint16_t *ap = arow[m] + (uint32_t)c * (uint32_t)Ops::KPC;
+#pragma unroll
+                        for (int q = 0; q < Ops::ND / 4; ++q) {
+                            const u4v v = load16(ap + 8 * q);
+                            x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < Ops::ND; ++q) x[q] = 0u;
+                    }
+                    Ops::prep(x, act[m]);
+                }
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        uint32_t x[8];
-                        if (m0 + m < a.M) {
-                            load_act_half(a, m0 + m, c * Ops::KPC + 16 * h, x);
-                        } else {
+                        float part[H];
+                        Ops::dot(w[u][i], act[m], part);
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) x[t] = 0u;
-                        }
-                        Ops::prep(x, act[m]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < CPW; ++i) {
-                        uint32_t wh[WD];
-#pragma unroll
-                        for (int t = 0; t < WD; ++t) wh[t] = w[u][i][h * WD + t];
-#pragma unroll
-                        for (int m = 0; m < MT; ++m) {
-                            float v = Ops::dot(wh, act[m]);
-                            if constexpr (FMT == FMT_U4 || FMT == FMT_U8) v = __builtin_fmaf(-meta[u][i][h].zero, act[m].asum, v);
-                            acc[i][m] = __builtin_fmaf(meta[u][i][h].scale, v, acc[i][m]);
+                        for (int h = 0; h < H; ++h) {
+                            float v = part[h];
+                            if constexpr (ZP) v = __builtin_fmaf(-zr[u][i][h], act[m].asum[h], v);
+                            acc[i][m] = __builtin_fmaf(sc[u][i][h], v, acc[i][m]);
                         }
                     }
                 }
@@ -103,7 +115,7 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const float s = wave_sum(acc[i][m]) * a.tscale;
-                if (lane == 0 && nbase + i < a.N && m0 + m < a.M) store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, s);
+                if (lane == 0 && nbase + i < a.N && rlive[m]) store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, s);
             }
         }
     }
@@ -121,7 +133,7 @@ __device__ __forceinline__ float act_at(const KArgs &a, int m, int64_t k) {
 
 template <int FMT>
 __device__ __forceinline__ float weight_at(const KArgs &a, int64_t n, int64_t k) {
-    const int64_t b = k / a.bs;
+    const int64_t b = k >> a.bs_shift;
     if constexpr (FMT == FMT_U4) {
         const uint8_t byte = a.W[n * a.col_bytes + (k >> 1)];
         const int q = (k & 1) ? (byte >> 4) : (byte & 0x0F);
@@ -178,7 +190,17 @@ namespace {
 
 template <int FMT, int ACT, int MT, int CPW>
 hipError_t go_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    // two scale blocks per chunk: every NVFP4 chunk, and U4 chunks with 16-wide blocks
+    if constexpr (FMT == FMT_NVFP4) {
+        hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    } else if constexpr (FMT == FMT_U4) {
+        if (a.bs == 16)
+            hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 1>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 1>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

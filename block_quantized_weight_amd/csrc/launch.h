@@ -17,7 +17,8 @@ struct KArgs {
     int64_t K;
     int64_t col_bytes;       // bytes of codes per column
     int64_t nchunks;         // 16-byte chunks per column
-    int32_t bs;              // block size along K
+    int32_t bs;              // block size along K (a power of two)
+    int32_t bs_shift;        // log2(bs)
     int32_t nblk;            // K / bs
     int32_t zstride;         // bytes of zero points per column
     int32_t M;

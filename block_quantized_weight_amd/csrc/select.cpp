@@ -55,10 +55,34 @@ static int k_per_chunk(int fmt) { return (fmt == QGEMV_FMT_U4 || fmt == QGEMV_FM
 
 static bool stream_shape_ok(const qgemv_desc *d) {
     // every column's codes start on a 16-byte boundary and split into whole chunks
-    if (d->K % k_per_chunk(d->format)) return false;
-    // NVFP4 scale pairs are read as two bytes per chunk; U4 with 16-wide blocks
-    // reads two scales per chunk
+    return d->K % k_per_chunk(d->format) == 0;
+}
+
+// The matrix family walks K in steps of four 16-byte chunks per column, and takes
+// 8-bit codes only with fp16 activations (1024 + q is an exact fp16 integer; bf16
+// has no room for an offset 8-bit code).
+static bool mfma_shape_ok(const qgemv_desc *d) {
+    if (d->K % (4 * k_per_chunk(d->format))) return false;
+    if (d->format == QGEMV_FMT_U8 && d->act_dtype != QGEMV_ACT_F16) return false;
     return true;
+}
+
+// Waves that share one 16-column tile's K range. Chosen from N and K only so that
+// the summation order of a row never depends on M: enough waves to fill the
+// machine (about eight per CU), no more than one K step of four chunks per wave.
+static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
+    const uint32_t forced = (flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
+    const int64_t tiles = (d->N + 15) / 16;
+    const int64_t steps = d->K / (4 * k_per_chunk(d->format));
+    int ks = 1;
+    if (forced) {
+        ks = (int)forced;
+    } else {
+        while (ks < 16 && tiles * ks < 8LL * cu_count && 2 * ks <= steps) ks *= 2;
+    }
+    if (ks > 16) ks = 16;
+    if (ks > steps) ks = (int)steps;
+    return ks < 1 ? 1 : ks;
 }
 
 int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t extra_flags, LaunchCfg *out) {
@@ -77,21 +101,38 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
     c.lds_bytes = 0;
     c.variant = 0;
 
-    int forced = (int)(flags & QGEMV_FLAG_FAMILY_MASK);
+    const int forced = (int)(flags & QGEMV_FLAG_FAMILY_MASK);
     const bool stream_ok = fast_ok && stream_shape_ok(d);
+    const bool mfma_ok = fast_ok && mfma_shape_ok(d) && !(flags & QGEMV_FLAG_NO_MFMA);
     int family;
-    if (forced == QGEMV_FAMILY_GENERIC || (forced == QGEMV_FAMILY_AUTO && !stream_ok)) {
+    if (forced == QGEMV_FAMILY_GENERIC) {
         family = QGEMV_FAMILY_GENERIC;
-    } else if (forced == QGEMV_FAMILY_STREAM || forced == QGEMV_FAMILY_MFMA) {
+    } else if (forced == QGEMV_FAMILY_STREAM) {
         if (!stream_ok) return QGEMV_E_ARG;  // a forced fast family needs its preconditions
-        family = QGEMV_FAMILY_STREAM;        // matrix family not built yet: stream serves it
-    } else {
         family = QGEMV_FAMILY_STREAM;
+    } else if (forced == QGEMV_FAMILY_MFMA) {
+        if (!(fast_ok && mfma_shape_ok(d))) return QGEMV_E_ARG;
+        family = QGEMV_FAMILY_MFMA;
+    } else if (mfma_ok && M >= 2) {
+        family = QGEMV_FAMILY_MFMA;
+    } else if (stream_ok) {
+        family = QGEMV_FAMILY_STREAM;
+    } else {
+        family = QGEMV_FAMILY_GENERIC;
     }
     c.family = family;
 
     const int64_t wave_target = 8LL * cu_count;  // two waves per SIMD
-    if (family == QGEMV_FAMILY_GENERIC) {
+    if (family == QGEMV_FAMILY_MFMA) {
+        const int rg = (M + 3) / 4;
+        c.rows_per_pass = 4 * rg;
+        c.passes = 1;
+        c.cols_per_wave = 16;
+        c.ksplit = mfma_ksplit(d, cu_count, flags);
+        c.waves_per_wg = c.ksplit;
+        c.grid = (d->N + 15) / 16;
+        c.lds_bytes = c.ksplit > 1 ? c.ksplit * rg * 4 * 64 * 4 : 0;
+    } else if (family == QGEMV_FAMILY_GENERIC) {
         c.rows_per_pass = M;
         c.passes = 1;
         c.cols_per_wave = 1;

@@ -82,9 +82,15 @@ FMT_CASES = [("u4", "f16", 32), ("u4", "bf16", 32), ("u4", "f16", 16), ("u4", "b
              ("fp8", "f16", 128), ("fp8", "bf16", 32), ("nvfp4", "bf16", 16), ("nvfp4", "f16", 16)]
 
 
-@pytest.mark.parametrize("family", ["auto", "stream", "generic"])
+def mfma_supports(fmt, act):
+    return not (fmt == "u8" and act == "bf16")
+
+
+@pytest.mark.parametrize("family", ["auto", "stream", "mfma", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", FMT_CASES)
 def test_families_ragged_shapes(family, fmt, act, bs):
+    if family == "mfma" and not mfma_supports(fmt, act):
+        pytest.skip("the matrix family takes 8-bit codes with fp16 activations only")
     for N, K, M in [(1, 256, 1), (17, 512, 3), (36, 1024, 5), (1169, 768, 16), (300, 4096, 2)]:
         if K % bs:
             continue
@@ -111,26 +117,36 @@ def test_missing_zero_points_mean_midpoint(fmt, act):
 # bit-exact properties
 
 
-@pytest.mark.parametrize("family", ["stream", "generic"])
+@pytest.mark.parametrize("family", ["stream", "mfma", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u4", "f16", 32), ("fp8", "f16", 128),
-                                         ("nvfp4", "bf16", 16), ("u8", "f16", 128)])
+                                         ("nvfp4", "bf16", 16), ("u8", "f16", 128), ("u4", "f16", 16)])
 def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
     """Row i of an M-row call equals the same row run alone, and in any other M."""
     prob = synth.make_problem(fmt, act, 777, 2048, bs, 16, seed=21)
     flags = FAMILY_FLAG[family]
     gu.say(f"[rows] {family} {fmt}/{act}")
     Y16, _ = gu.run_gpu(prob, 16, flags=flags)
-    for M in (1, 2, 3, 4, 5, 8):
+    for M in (1, 2, 3, 4, 5, 8, 13):
         A = np.ascontiguousarray(prob.A[16 - M:])  # rows land in different slots
         Ym, _ = gu.run_gpu(prob, M, flags=flags, A=A)
         assert np.array_equal(Ym.view(np.int64), Y16[16 - M:].view(np.int64)), (family, fmt, M)
 
 
-def test_repeated_runs_are_bitwise_equal():
-    prob = synth.workload("u4_m8_k2048_n1024")
-    outs, _ = gu.run_gpu(prob, 8, repeat=4)
+@pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
+def test_repeated_runs_are_bitwise_equal(name, M):
+    prob = synth.workload(name)
+    outs, plan = gu.run_gpu(prob, M, repeat=4)
     for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+        assert np.array_equal(o, outs[0]), plan
+
+
+@pytest.mark.parametrize("ks", [1, 2, 4, 16])
+def test_forced_k_split_is_correct(ks):
+    prob = synth.make_problem("u4", "bf16", 100, 4096, 32, 6, seed=4)
+    Y, plan = gu.run_gpu(prob, 6, flags=2 | (ks << 8))
+    assert plan["ksplit"] == ks
+    ok, ratio, _, _ = gu.check_full(prob, 6, Y, strict=False)
+    assert ok, (ks, ratio)
 
 
 @pytest.mark.parametrize("fmt,act", [("u4", "f16"), ("u4", "bf16"), ("u8", "f16"), ("u8", "bf16")])
@@ -149,9 +165,9 @@ def test_integer_special_case_is_exact(fmt, act):
                          scales=np.full((N, nblk), 0x3C00, dtype=np.uint16), zp=zp, tensor_scale=1.0,
                          A=synth.activation_bits(a_int.astype(np.float64), act))
     exact = (a_int @ q.astype(np.int64).T).astype(np.float64)
-    assert np.abs(exact).max() > 256  # some results need rounding in bf16
+    assert np.abs(exact).max() > 128  # large enough that bf16 must round some results
     want = oracle.decode_activation_bits(synth.activation_bits(exact, act), act)
-    for fam in ("stream", "generic"):
+    for fam in ("stream", "generic") + (("mfma",) if mfma_supports(fmt, act) else ()):
         Y, _ = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam])
         assert np.array_equal(Y, want), fam
 
@@ -192,7 +208,7 @@ def test_one_hot_probes_decode_every_code_exactly(fmt, act):
                          tensor_scale=1.0, A=np.zeros((16, K), np.uint16))
     one = 0x3C00 if act == "f16" else 0x3F80
     deq = oracle.dequant_columns(base)  # [N, K] exact values
-    for fam in ("stream", "generic"):
+    for fam in ("stream", "generic") + (("mfma",) if mfma_supports(fmt, act) else ()):
         for k0 in range(0, K, 16):
             A = np.zeros((16, K), np.uint16)
             A[np.arange(16), k0 + np.arange(16)] = one
