@@ -25,6 +25,10 @@ QGEMV_OK = 0
 FLAG_FAMILY_MASK = 0x0000000F
 FLAG_KSPLIT_SHIFT = 8
 FLAG_NO_MFMA = 0x00010000
+FLAG_STAGE_A_OFF = 0x00020000
+FLAG_STAGE_A_ON = 0x00040000
+FLAG_RING_OFF = 0x00080000
+FLAG_RING_ON = 0x00100000
 MAX_M = 16
 
 _lock = threading.Lock()

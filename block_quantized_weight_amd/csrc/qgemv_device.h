@@ -108,6 +108,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding. Written
+// as volatile asm with a memory clobber so that it is also a compiler barrier: no LDS
+// read of a DMA destination may be hoisted above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land at
+// lds + l * BYTES (global_load_lds_dword / _dwordx4). Counted by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void *src, void *lds) {
+    static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4 copies");
+    if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 4, 0, 0);
+    else __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ u4v load16(const void *p) {
     return *(const u4v *)p;
 }

@@ -16,6 +16,9 @@
 
 namespace qgemv {
 
+// LDS of one gfx950 compute unit (bytes).
+static const int64_t kLdsBytes = 160 * 1024;
+
 static bool valid_block(int fmt, int bs) {
     if (fmt == QGEMV_FMT_NVFP4) return bs == 16;
     return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
@@ -31,12 +34,16 @@ int validate_desc(const qgemv_desc *d) {
     if (d->N < 1 || d->K < 1) return QGEMV_E_SHAPE;
     if (!valid_block(d->format, d->block_size)) return QGEMV_E_BLOCK;
     if (d->K % d->block_size) return QGEMV_E_SHAPE;
-    const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA;
+    const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA |
+                           QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
+                           QGEMV_FLAG_RING_ON;
     if (d->flags & ~known) return QGEMV_E_ARG;
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
     const uint32_t ks = (d->flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
-    if (ks > 64) return QGEMV_E_ARG;
+    if (ks > 16) return QGEMV_E_ARG;
+    if ((d->flags & QGEMV_FLAG_STAGE_A_OFF) && (d->flags & QGEMV_FLAG_STAGE_A_ON)) return QGEMV_E_ARG;
+    if ((d->flags & QGEMV_FLAG_RING_OFF) && (d->flags & QGEMV_FLAG_RING_ON)) return QGEMV_E_ARG;
     return QGEMV_OK;
 }
 
@@ -67,9 +74,27 @@ static bool mfma_shape_ok(const qgemv_desc *d) {
     return true;
 }
 
+// The LDS DMA ring copies whole dwords of the scale and zero-point arrays; they must
+// be 4-byte aligned and a whole number of dwords long so no copy leaves them.
+static bool meta_dwords_ok(const qgemv_desc *d) {
+    const int64_t nblk = d->K / d->block_size;
+    int64_t sbytes;
+    if (d->format == QGEMV_FMT_FP8) sbytes = d->N * nblk * 4;
+    else if (d->format == QGEMV_FMT_NVFP4) sbytes = d->N * (d->K / 16);
+    else sbytes = d->N * nblk * 2;
+    if ((uintptr_t)d->scales % 4 || sbytes % 4) return false;
+    if (d->zero_points) {
+        const int64_t zbytes = d->format == QGEMV_FMT_U4 ? d->N * ((nblk + 1) / 2) : d->N * nblk;
+        if ((uintptr_t)d->zero_points % 4 || zbytes % 4) return false;
+    }
+    return true;
+}
+
 // Waves that share one 16-column tile's K range. Chosen from N and K only so that
 // the summation order of a row never depends on M: enough waves to fill the
-// machine (about eight per CU), no more than one K step of four chunks per wave.
+// machine (about eight per CU), at least two K steps of four chunks per wave, and
+// at most 8 (a 16-wave workgroup caps every wave at 128 VGPRs). A forced split may
+// go to 16.
 static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     const uint32_t forced = (flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     const int64_t tiles = (d->N + 15) / 16;
@@ -78,7 +103,7 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     if (forced) {
         ks = (int)forced;
     } else {
-        while (ks < 16 && tiles * ks < 8LL * cu_count && 2 * ks <= steps) ks *= 2;
+        while (ks < 8 && tiles * ks < 8LL * cu_count && 2 * ks <= steps) ks *= 2;
     }
     if (ks > 16) ks = 16;
     if (ks > steps) ks = (int)steps;
@@ -129,9 +154,49 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         c.passes = 1;
         c.cols_per_wave = 16;
         c.ksplit = mfma_ksplit(d, cu_count, flags);
-        c.waves_per_wg = c.ksplit;
-        c.grid = (d->N + 15) / 16;
-        c.lds_bytes = c.ksplit > 1 ? c.ksplit * rg * 4 * 64 * 4 : 0;
+        // a workgroup holds nw / ksplit tiles of ksplit waves each
+        const int nw = c.ksplit > 8 ? c.ksplit : 8;
+        c.waves_per_wg = nw;
+        const int64_t tiles = (d->N + 15) / 16;
+        const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
+        const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
+        const int64_t lds_a = (int64_t)M * (d->K + 8) * 2;
+        // LDS DMA ring: 8 waves, 8 (or 4) slots each of one KiB of codes plus 256 B per
+        // block-metadata dword stream; only without a K split
+        const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
+        const int64_t slot = 1024 + 256 * (zpp ? 2 : 1);
+        const int64_t abytes16 = 16 + ((lds_a + 15) & ~15LL);  // zero block + staged rows
+        const bool ring_ok = c.ksplit == 1 && meta_dwords_ok(d) && abytes16 + 8 * 4 * slot <= kLdsBytes;
+        bool ring = ring_ok && M <= 8 && groups > cu_count;
+        if (flags & QGEMV_FLAG_RING_ON) ring = ring_ok;
+        if (flags & QGEMV_FLAG_RING_OFF) ring = false;
+        if (ring) {
+            const bool deep = abytes16 + 8 * 8 * slot <= kLdsBytes;
+            c.waves_per_wg = 8;
+            c.variant = 2 | (deep ? 4 : 0);
+            c.lds_bytes = (int)(abytes16 + 8 * (deep ? 8 : 4) * slot);
+            int64_t per_cu = kLdsBytes / c.lds_bytes;
+            if (per_cu < 1) per_cu = 1;
+            if (per_cu > 4) per_cu = 4;
+            c.grid = groups < per_cu * cu_count ? groups : per_cu * cu_count;
+            *out = c;
+            return QGEMV_OK;
+        }
+        // Stage the activations when they fit and the workgroups then walk many tiles
+        // (no K split): the staging is paid once per workgroup.
+        bool stage = lds_a + lds_red <= kLdsBytes && c.ksplit == 1 && groups > 2LL * cu_count;
+        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_a + lds_red <= kLdsBytes;
+        if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
+        c.variant = stage ? 1 : 0;
+        c.lds_bytes = (int)(lds_red + (stage ? 16 + ((lds_a + 15) & ~15LL) : 0));
+        int64_t grid = groups;
+        if (stage) {
+            int64_t per_cu = c.lds_bytes > 0 ? kLdsBytes / c.lds_bytes : 8;
+            if (per_cu > 32 / nw) per_cu = 32 / nw;
+            if (per_cu < 1) per_cu = 1;
+            if (grid > per_cu * cu_count) grid = per_cu * cu_count;
+        }
+        c.grid = grid;
     } else if (family == QGEMV_FAMILY_GENERIC) {
         c.rows_per_pass = M;
         c.passes = 1;

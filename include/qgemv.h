@@ -85,12 +85,19 @@ enum qgemv_family {
 };
 
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
- * Bits 8..15: forced K split (0 = automatic; otherwise 1..64 waves per workgroup
- * share the K range of a column tile). Bit 16: never pick the MFMA family. */
+ * Bits 8..15: forced K split of the MFMA family (0 = automatic; otherwise 1..16 waves
+ * share the K range of a column tile). Bit 16: never pick the MFMA family.
+ * Bits 17/18: MFMA family never / always stages the activations in LDS (when they
+ * fit); neither set = automatic. Bits 19/20: MFMA family never / always (when
+ * eligible) streams the weights through the LDS DMA ring. For A/B comparisons. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
 #define QGEMV_FLAG_KSPLIT_MASK 0x0000FF00u
 #define QGEMV_FLAG_NO_MFMA 0x00010000u
+#define QGEMV_FLAG_STAGE_A_OFF 0x00020000u
+#define QGEMV_FLAG_STAGE_A_ON 0x00040000u
+#define QGEMV_FLAG_RING_OFF 0x00080000u
+#define QGEMV_FLAG_RING_ON 0x00100000u
 
 /* Problem description. struct_size must be sizeof(qgemv_desc). */
 typedef struct qgemv_desc {
@@ -117,7 +124,8 @@ typedef struct qgemv_plan_info {
     int32_t waves_per_wg;    /* waves per workgroup */
     int64_t grid;            /* workgroups launched */
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
-    int32_t variant;         /* family-specific kernel variant id */
+    int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
+                                LDS, bit 1 = weights through the LDS DMA ring, bit 2 = 8-slot ring */
 } qgemv_plan_info;
 
 typedef struct qgemv_handle qgemv_handle;

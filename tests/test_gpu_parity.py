@@ -18,7 +18,10 @@ pytestmark = pytest.mark.gpu
 
 from tests import gpu_util as gu
 
-FAMILY_FLAG = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3}
+FAMILY_FLAG = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3,
+               "mfma_lds": 2 | bqw.FLAG_STAGE_A_ON | bqw.FLAG_RING_OFF,
+               "mfma_nolds": 2 | bqw.FLAG_STAGE_A_OFF | bqw.FLAG_RING_OFF,
+               "mfma_ring": 2 | bqw.FLAG_RING_ON | (1 << 8)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -82,14 +85,20 @@ FMT_CASES = [("u4", "f16", 32), ("u4", "bf16", 32), ("u4", "f16", 16), ("u4", "b
              ("fp8", "f16", 128), ("fp8", "bf16", 32), ("nvfp4", "bf16", 16), ("nvfp4", "f16", 16)]
 
 
+def meta_whole_dwords(prob):
+    """The LDS DMA ring copies whole dwords of the scale / zero-point arrays, so the
+    dispatcher takes it only when those arrays are a whole number of dwords."""
+    return prob.scales.nbytes % 4 == 0 and (prob.zp is None or prob.zp.nbytes % 4 == 0)
+
+
 def mfma_supports(fmt, act):
     return not (fmt == "u8" and act == "bf16")
 
 
-@pytest.mark.parametrize("family", ["auto", "stream", "mfma", "generic"])
+@pytest.mark.parametrize("family", ["auto", "stream", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", FMT_CASES)
 def test_families_ragged_shapes(family, fmt, act, bs):
-    if family == "mfma" and not mfma_supports(fmt, act):
+    if family.startswith("mfma") and not mfma_supports(fmt, act):
         pytest.skip("the matrix family takes 8-bit codes with fp16 activations only")
     for N, K, M in [(1, 256, 1), (17, 512, 3), (36, 1024, 5), (1169, 768, 16), (300, 4096, 2)]:
         if K % bs:
@@ -99,7 +108,11 @@ def test_families_ragged_shapes(family, fmt, act, bs):
         gu.say(f"[ragged] {family} {fmt}/{act} bs={bs} N={N} K={K} M={M}")
         Y, plan = gu.run_gpu(prob, M, flags=FAMILY_FLAG[family])
         if family != "auto":
-            assert plan["family"] == family
+            assert plan["family"] == family.split("_")[0]
+        if family == "mfma_lds":
+            assert plan["variant"] & 1
+        if family == "mfma_ring" and meta_whole_dwords(prob):
+            assert plan["variant"] & 2
         ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
         assert ok, (family, fmt, act, bs, N, K, M, ratio, plan)
 
@@ -117,19 +130,26 @@ def test_missing_zero_points_mean_midpoint(fmt, act):
 # bit-exact properties
 
 
-@pytest.mark.parametrize("family", ["stream", "mfma", "generic"])
+@pytest.mark.parametrize("family", ["stream", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u4", "f16", 32), ("fp8", "f16", 128),
                                          ("nvfp4", "bf16", 16), ("u8", "f16", 128), ("u4", "f16", 16)])
 def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
-    """Row i of an M-row call equals the same row run alone, and in any other M."""
+    """Row i of an M-row call equals the same row run alone, and in any other M. The
+    two activation paths of the matrix family must also agree bit for bit."""
     prob = synth.make_problem(fmt, act, 777, 2048, bs, 16, seed=21)
     flags = FAMILY_FLAG[family]
     gu.say(f"[rows] {family} {fmt}/{act}")
-    Y16, _ = gu.run_gpu(prob, 16, flags=flags)
+    Y16, plan16 = gu.run_gpu(prob, 16, flags=flags)
     for M in (1, 2, 3, 4, 5, 8, 13):
         A = np.ascontiguousarray(prob.A[16 - M:])  # rows land in different slots
         Ym, _ = gu.run_gpu(prob, M, flags=flags, A=A)
         assert np.array_equal(Ym.view(np.int64), Y16[16 - M:].view(np.int64)), (family, fmt, M)
+    if family in ("mfma_lds", "mfma_ring"):
+        # same K split (it orders the fp32 sums), other activation / weight paths
+        ks = plan16["ksplit"]
+        Yo, po = gu.run_gpu(prob, 16, flags=FAMILY_FLAG["mfma_nolds"] | (ks << 8))
+        assert po["ksplit"] == ks and not (po["variant"] & 3)
+        assert np.array_equal(Yo.view(np.int64), Y16.view(np.int64))
 
 
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
@@ -140,11 +160,13 @@ def test_repeated_runs_are_bitwise_equal(name, M):
         assert np.array_equal(o, outs[0]), plan
 
 
+@pytest.mark.parametrize("stage", [False, True])
 @pytest.mark.parametrize("ks", [1, 2, 4, 16])
-def test_forced_k_split_is_correct(ks):
+def test_forced_k_split_is_correct(ks, stage):
     prob = synth.make_problem("u4", "bf16", 100, 4096, 32, 6, seed=4)
-    Y, plan = gu.run_gpu(prob, 6, flags=2 | (ks << 8))
-    assert plan["ksplit"] == ks
+    flags = 2 | (ks << 8) | (bqw.FLAG_STAGE_A_ON if stage else bqw.FLAG_STAGE_A_OFF)
+    Y, plan = gu.run_gpu(prob, 6, flags=flags)
+    assert plan["ksplit"] == ks and bool(plan["variant"] & 1) == stage
     ok, ratio, _, _ = gu.check_full(prob, 6, Y, strict=False)
     assert ok, (ks, ratio)
 
@@ -167,7 +189,7 @@ def test_integer_special_case_is_exact(fmt, act):
     exact = (a_int @ q.astype(np.int64).T).astype(np.float64)
     assert np.abs(exact).max() > 128  # large enough that bf16 must round some results
     want = oracle.decode_activation_bits(synth.activation_bits(exact, act), act)
-    for fam in ("stream", "generic") + (("mfma",) if mfma_supports(fmt, act) else ()):
+    for fam in ("stream", "generic") + (("mfma_nolds", "mfma_lds", "mfma_ring") if mfma_supports(fmt, act) else ()):
         Y, _ = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam])
         assert np.array_equal(Y, want), fam
 
@@ -208,7 +230,7 @@ def test_one_hot_probes_decode_every_code_exactly(fmt, act):
                          tensor_scale=1.0, A=np.zeros((16, K), np.uint16))
     one = 0x3C00 if act == "f16" else 0x3F80
     deq = oracle.dequant_columns(base)  # [N, K] exact values
-    for fam in ("stream", "generic") + (("mfma",) if mfma_supports(fmt, act) else ()):
+    for fam in ("stream", "generic") + (("mfma_nolds", "mfma_lds", "mfma_ring") if mfma_supports(fmt, act) else ()):
         for k0 in range(0, K, 16):
             A = np.zeros((16, K), np.uint16)
             A[np.arange(16), k0 + np.arange(16)] = one
