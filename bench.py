@@ -8,16 +8,28 @@ HBM before the timed region starts.
 
 Prints one JSON line. `value` is achieved GB/s = weight bytes (codes + block scales +
 zero points) per call / average time per call. The roofline object reports the same
-bytes against the 8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload on this host.
+bytes against the 8 TB/s HBM peak; its `traffic` is the HBM bytes per launch that two
+rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) measured for this workload, read from
+the summaries under profiles/ and only while the kernel sources still hash to what
+was profiled (null otherwise). `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload on this host.
+
+Profiling helpers (no GPU needed):
+  --calib-copy-mib X      also run one plain copy kernel of X MiB (torch.neg on fp32)
+                          before the warmup, so a counter run can scale its readings
+  --trace-summary DIR     per-kernel durations from a rocprofv3 --kernel-trace database
+  --traffic-record F W    FETCH_SIZE run dir F and WRITE_SIZE run dir W -> traffic record
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
+import sqlite3
 import sys
 import time
 
@@ -27,6 +39,8 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "u8_m1_k4096_n4096"
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_quantized_weight_amd", "csrc")
 
 
 def parse():
@@ -40,7 +54,121 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
     p.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm; not the metric)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one plain copy kernel of this many MiB before the warmup (counter calibration)")
+    p.add_argument("--trace-summary", metavar="DIR", default=None)
+    p.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     return p.parse_args()
+
+
+# ----------------------------------------------------------------------------------
+# rocprofv3 databases (rocpd SQLite) -> short text summaries
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources and the dispatcher: a traffic figure is valid only for
+    the kernels it was measured on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _dbs(d):
+    out = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not out:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return out
+
+
+def trace_durations(d):
+    """{kernel name: [durations in ns]} from --kernel-trace databases under d."""
+    res = {}
+    for db in _dbs(d):
+        con = sqlite3.connect(db)
+        for name, start, end in con.execute("select name, start, end from kernels"):
+            res.setdefault(name, []).append(end - start)
+        con.close()
+    return res
+
+
+def counter_means(d):
+    """{kernel name: {counter: (mean per dispatch, dispatches)}} from --pmc databases."""
+    acc = {}
+    for db in _dbs(d):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+        con.close()
+        for name, ctr, v in rows:
+            acc.setdefault(name, {}).setdefault(ctr, []).append(float(v))
+    return {k: {c: (sum(v) / len(v), len(v)) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def print_trace_summary(d):
+    rows = sorted(trace_durations(d).items(), key=lambda kv: -sum(kv[1]))
+    tot = sum(sum(v) for _, v in rows) or 1
+    print(f"{'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'time %':>7}  kernel")
+    for name, v in rows:
+        print(f"{len(v):6d} {sum(v) / len(v) / 1e3:9.3f} {min(v) / 1e3:9.3f} {max(v) / 1e3:9.3f} "
+              f"{100.0 * sum(v) / tot:7.2f}  {name}")
+
+
+def _is_qgemv(name):
+    return "qgemv::" in name
+
+
+def _is_calib(name):
+    return "neg" in name.lower()
+
+
+def traffic_record(fetch_dir, write_dir, args):
+    """Scale the qgemv kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as the
+    counters report them) by what the same counters read for the calibration copy
+    kernel, whose true traffic is known (it reads and writes X MiB)."""
+    if args.calib_copy_mib <= 0:
+        raise SystemExit("--traffic-record needs --calib-copy-mib (the size the runs used)")
+    from block_quantized_weight_amd import synth
+
+    true_bytes = args.calib_copy_mib * (1 << 20)
+    M = args.m if args.m is not None else synth.WORKLOADS[args.workload]["ms"][0]
+    rec = {"workload": args.workload, "M": M, "flags": args.flags, "src_hash": kernel_source_hash(),
+           "calib_bytes": true_bytes}
+    for key, d, ctr in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        cm = counter_means(d)
+        q = [(k, v[ctr]) for k, v in cm.items() if _is_qgemv(k) and ctr in v]
+        c = [(k, v[ctr]) for k, v in cm.items() if _is_calib(k) and ctr in v]
+        if len(q) != 1 or len(c) != 1:
+            raise SystemExit(f"{ctr}: expected one qgemv kernel and one calibration kernel, got {q} / {c}")
+        (qk, (qv, qn)), (ck, (cv, cn)) = q[0], c[0]
+        factor = true_bytes / cv  # bytes per counter unit
+        rec[key] = {"kernel": qk, "counter_kib": round(qv, 3), "dispatches": qn,
+                    "calib_counter_kib": round(cv, 3), "bytes_per_unit": round(factor, 4),
+                    "bytes": round(qv * factor)}
+        rec["calib_kernel"] = ck.split("(")[0][:60] + " (torch.neg, fp32)"
+    rec["traffic_bytes"] = rec["fetch"]["bytes"] + rec["write"]["bytes"]
+    print("traffic_record: " + json.dumps(rec, sort_keys=True))
+
+
+def lookup_traffic(workload, M, flags):
+    """HBM bytes per launch from a committed counter summary, or None when there is
+    none for this workload or the kernel sources changed since it was taken."""
+    want = kernel_source_hash()
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md")) + glob.glob(os.path.join(PROFILES, "*.txt"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("traffic_record: "):
+                    continue
+                try:
+                    rec = json.loads(line[len("traffic_record: "):])
+                except ValueError:
+                    continue
+                if (rec.get("workload"), rec.get("M"), rec.get("flags"), rec.get("src_hash")) == \
+                        (workload, M, flags, want):
+                    return rec["traffic_bytes"]
+    return None
 
 
 def cpu_baseline(prob, M, target_s):
@@ -74,6 +202,12 @@ def cpu_baseline(prob, M, target_s):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print_trace_summary(args.trace_summary)
+        return
+    if args.traffic_record:
+        traffic_record(*args.traffic_record, args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the weight would be split by "
               "output columns, one shard per GPU, with no communication in the product). Run with --gpus 1.",
@@ -112,6 +246,14 @@ def main():
         slots.append((q, W, S, Z))
     plan = slots[0][0].plan(M)
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib > 0:
+        # one plain copy kernel of known size, for scaling counter readings
+        csrc = torch.ones(args.calib_copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        cdst = torch.empty_like(csrc)
+        torch.cuda.synchronize()
+        torch.neg(csrc, out=cdst)
+        torch.cuda.synchronize()
+        del csrc, cdst
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -154,7 +296,7 @@ def main():
                    "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
                    "plan": plan, "flags": args.flags, "seed": spec["seed"]},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": lookup_traffic(args.workload, M, args.flags)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
     }
