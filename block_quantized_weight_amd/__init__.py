@@ -29,6 +29,11 @@ FLAG_STAGE_A_OFF = 0x00020000
 FLAG_STAGE_A_ON = 0x00040000
 FLAG_RING_OFF = 0x00080000
 FLAG_RING_ON = 0x00100000
+FLAG_STREAM_CPW_SHIFT = 21
+FLAG_STREAM_UNR_SHIFT = 23
+FLAG_STREAM_WPC_SHIFT = 25
+FLAG_STREAM_CLASSIC = 0x10000000
+FLAG_MFMA_DEPTH_SHIFT = 29
 MAX_M = 16
 
 _lock = threading.Lock()

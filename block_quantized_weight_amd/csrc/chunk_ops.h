@@ -9,6 +9,8 @@
 // fp32 sum with v_dot2; the block scale then multiplies that sum, and for the integer
 // formats the zero point enters as -z * sum(a) over the same k:
 //     s * sum_k a_k (q_k - z) = s * (sum_k a_k q_k - z * sum_k a_k)
+// A decode may carry a constant offset Z0 in every code (q + Z0 is what it feeds to
+// v_dot2); the zero point then enters as z + Z0.
 // ("[CUDA] MatMulNBits 8-bit: wide fp16 M=1 kernel", Description: exact (q - zp),
 // scale applied once per chunk to an fp32 partial; "[CUDA] Block-scaled MatMul decode
 // GEMV", FP4 row-tiling paragraph: load, decode and scales shared by the rows).
@@ -47,6 +49,7 @@ template <int H>
 struct ChunkOps<FMT_U4, ACT_F16, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;  // activation dwords per chunk
+    static constexpr float Z0 = 0.0f;
 
     // x: natural pairs (a0,a1),(a2,a3),...; weight dword d (k = 8d..8d+7) decodes to
     // pairs (k0,k4), (k2,k6) [low nibbles] and (k1,k5), (k3,k7) [high nibbles].
@@ -86,22 +89,24 @@ struct ChunkOps<FMT_U4, ACT_F16, H> {
     }
 };
 
-// U4, bf16 activations. Each nibble moves into its own byte and is widened by the E4M3
-// converter (E4M3 codes 0..15 are exactly q * 2^-9; the converter's 2^9 scale gives q).
+// U4, bf16 activations. A nibble q placed in the low mantissa bits of bf16 0x4300
+// (= 128) reads as the exact integer 128 + q, so each dword of codes becomes four
+// bf16 pairs with one shift and one and-or each; the offset 128 joins the zero point.
 template <int H>
 struct ChunkOps<FMT_U4, ACT_BF16, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;
+    static constexpr float Z0 = 128.0f;
 
-    // decode yields (k0,k2), (k4,k6) from the low nibbles and (k1,k3), (k5,k7) from the high.
+    // same pairing as the fp16 decode: (a0,a4), (a2,a6), (a1,a5), (a3,a7) per 8 k
     __device__ static void prep(const uint32_t x[16], ChunkAct &h) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t x0 = x[4 * d], x1 = x[4 * d + 1], x2 = x[4 * d + 2], x3 = x[4 * d + 3];
-            h.p[4 * d + 0] = perm(x1, x0, 0x05040100u);  // (a0, a2)
-            h.p[4 * d + 1] = perm(x3, x2, 0x05040100u);  // (a4, a6)
-            h.p[4 * d + 2] = perm(x1, x0, 0x07060302u);  // (a1, a3)
-            h.p[4 * d + 3] = perm(x3, x2, 0x07060302u);  // (a5, a7)
+            h.p[4 * d + 0] = perm(x2, x0, 0x05040100u);  // (a0, a4)
+            h.p[4 * d + 1] = perm(x3, x1, 0x05040100u);  // (a2, a6)
+            h.p[4 * d + 2] = perm(x2, x0, 0x07060302u);  // (a1, a5)
+            h.p[4 * d + 3] = perm(x3, x1, 0x07060302u);  // (a3, a7)
         }
         if constexpr (H == 2) {
             h.asum[0] = sum_pairs<ACT_BF16>(x, 8);
@@ -111,18 +116,20 @@ struct ChunkOps<FMT_U4, ACT_BF16, H> {
         }
     }
 
+    // sum_k a_k (128 + q_k) per half
     __device__ static void dot(const u4v &w, const ChunkAct &h, float out[H]) {
+        constexpr uint32_t MAGIC = 0x43004300u;
         float s[H];
 #pragma unroll
         for (int i = 0; i < H; ++i) s[i] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int i = (H == 2) ? (d >> 1) : 0;
-            const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
-            s[i] = dot2<ACT_BF16>(small_int_bf16_pair<false>(lo), h.p[4 * d + 0], s[i]);
-            s[i] = dot2<ACT_BF16>(small_int_bf16_pair<true>(lo), h.p[4 * d + 1], s[i]);
-            s[i] = dot2<ACT_BF16>(small_int_bf16_pair<false>(hi), h.p[4 * d + 2], s[i]);
-            s[i] = dot2<ACT_BF16>(small_int_bf16_pair<true>(hi), h.p[4 * d + 3], s[i]);
+            const uint32_t wv = w[d];
+            s[i] = dot2<ACT_BF16>((wv & 0x000F000Fu) | MAGIC, h.p[4 * d + 0], s[i]);
+            s[i] = dot2<ACT_BF16>(((wv >> 8) & 0x000F000Fu) | MAGIC, h.p[4 * d + 1], s[i]);
+            s[i] = dot2<ACT_BF16>(((wv >> 4) & 0x000F000Fu) | MAGIC, h.p[4 * d + 2], s[i]);
+            s[i] = dot2<ACT_BF16>(((wv >> 12) & 0x000F000Fu) | MAGIC, h.p[4 * d + 3], s[i]);
         }
 #pragma unroll
         for (int i = 0; i < H; ++i) out[i] = s[i];
@@ -135,6 +142,7 @@ template <int H>
 struct ChunkOps<FMT_U8, ACT_F16, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
+    static constexpr float Z0 = 0.0f;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
@@ -158,6 +166,7 @@ template <int H>
 struct ChunkOps<FMT_U8, ACT_BF16, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
+    static constexpr float Z0 = 0.0f;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
@@ -187,6 +196,7 @@ template <int ACT, int H>
 struct ChunkOps<FMT_FP8, ACT, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
+    static constexpr float Z0 = 0.0f;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
@@ -209,6 +219,7 @@ template <int ACT, int H>
 struct ChunkOps<FMT_NVFP4, ACT, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;
+    static constexpr float Z0 = 0.0f;
 
     __device__ static void prep(const uint32_t x[16], ChunkAct &h) {
 #pragma unroll
@@ -236,7 +247,7 @@ struct ChunkOps<FMT_NVFP4, ACT, H> {
 struct ColPtrs {
     const uint8_t *w;   // codes of the column
     const void *s;      // scale row
-    const uint8_t *z;   // zero-point row (or nullptr)
+    const uint8_t *z;   // zero-point row (the scale row when there are no zero points)
 };
 
 template <int FMT>
@@ -246,38 +257,85 @@ __device__ __forceinline__ ColPtrs col_ptrs(const KArgs &a, int64_t n) {
     if constexpr (FMT == FMT_NVFP4) p.s = (const uint8_t *)a.scales + n * (a.K >> 4);
     else if constexpr (FMT == FMT_FP8) p.s = (const float *)a.scales + n * a.nblk;
     else p.s = (const uint16_t *)a.scales + n * a.nblk;
-    p.z = a.zp ? a.zp + n * a.zstride : nullptr;
+    // without zero points p.z aliases the scale row (valid memory, at least as long as
+    // a zero-point row) so zero-point loads never sit behind a branch; the decode then
+    // takes the midpoint
+    p.z = a.zp ? a.zp + n * a.zstride : (const uint8_t *)p.s;
     return p;
 }
 
-// Scale and zero point of each of the H halves of chunk c.
+// Raw block metadata of chunk c (scale bits and zero-point byte per half), loaded
+// ahead of use; decoded by meta_decode_s once the loads have landed.
+template <int H>
+struct MetaS {
+    uint32_t s[H];
+    uint32_t z[H];
+};
+
+template <int FMT>
+__device__ __forceinline__ int chunk_block(const KArgs &a, int c, int h) {
+    if constexpr (FMT == FMT_U4 || FMT == FMT_NVFP4) return ((c << 5) + 16 * h) >> a.bs_shift;
+    else return (c << 4) >> a.bs_shift;
+}
+
 template <int FMT, int H>
-__device__ __forceinline__ void chunk_meta(const KArgs &a, const ColPtrs &p, int c, float sc[H], float zr[H]) {
+__device__ __forceinline__ void meta_load_s(const KArgs &a, const ColPtrs &p, int c, MetaS<H> &m) {
     if constexpr (FMT == FMT_U4) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-            const int b = ((c << 5) + 16 * h) >> a.bs_shift;
-            sc[h] = half_bits_to_float(((const uint16_t *)p.s)[b]);
-            int z = 8;
-            if (p.z) {
-                const uint32_t zb = p.z[b >> 1];
-                z = (b & 1) ? (int)(zb >> 4) : (int)(zb & 0x0Fu);
-            }
-            zr[h] = (float)z;
+            const int b = chunk_block<FMT>(a, c, h);
+            m.s[h] = ((const uint16_t *)p.s)[b];
+            m.z[h] = p.z[b >> 1];
         }
     } else if constexpr (FMT == FMT_U8) {
-        const int b = (c << 4) >> a.bs_shift;
-        sc[0] = half_bits_to_float(((const uint16_t *)p.s)[b]);
-        zr[0] = p.z ? (float)p.z[b] : 128.0f;
+        const int b = chunk_block<FMT>(a, c, 0);
+        m.s[0] = ((const uint16_t *)p.s)[b];
+        m.z[0] = p.z[b];
     } else if constexpr (FMT == FMT_FP8) {
-        sc[0] = ((const float *)p.s)[(c << 4) >> a.bs_shift];
+        m.s[0] = ((const uint32_t *)p.s)[chunk_block<FMT>(a, c, 0)];
+        m.z[0] = 0u;
+    } else {
+        const uint8_t *S = (const uint8_t *)p.s + 2 * c;  // the two E4M3 scales of the chunk
+        m.s[0] = (uint32_t)S[0] | ((uint32_t)S[1] << 8);
+        m.z[0] = 0u;
+        if constexpr (H == 2) m.s[1] = 0u, m.z[1] = 0u;
+    }
+}
+
+// Scale and zero point (plus the decode's offset Z0) of each half of chunk c; zs is
+// zsel(a.zp, midpoint byte) (0x88 for U4, 128 for U8).
+template <int FMT, int H>
+__device__ __forceinline__ void meta_decode_s(const KArgs &a, int c, const MetaS<H> &m, float z0, ZSel zs,
+                                              float sc[H], float zr[H]) {
+    if constexpr (FMT == FMT_U4) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            const int b = chunk_block<FMT>(a, c, h);
+            sc[h] = half_bits_to_float((uint16_t)m.s[h]);
+            const uint32_t zb = (m.z[h] & zs.keep) | zs.fill;
+            const uint32_t z = (b & 1) ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu);
+            zr[h] = (float)z + z0;
+        }
+    } else if constexpr (FMT == FMT_U8) {
+        sc[0] = half_bits_to_float((uint16_t)m.s[0]);
+        zr[0] = (float)(((m.z[0] & zs.keep) | zs.fill) & 0xFFu) + z0;
+    } else if constexpr (FMT == FMT_FP8) {
+        sc[0] = __builtin_bit_cast(float, m.s[0]);
         zr[0] = 0.0f;
     } else {
-        const uint8_t *S = (const uint8_t *)p.s + 2 * c;
-        sc[0] = e4m3_to_float(S[0]);
-        sc[1] = e4m3_to_float(S[1]);
+        sc[0] = e4m3_to_float(m.s[0] & 0xFFu);
+        sc[1] = e4m3_to_float((m.s[0] >> 8) & 0xFFu);
         zr[0] = zr[1] = 0.0f;
     }
+}
+
+// Scale and zero point of each of the H halves of chunk c, loaded and decoded.
+template <int FMT, int H>
+__device__ __forceinline__ void chunk_meta(const KArgs &a, const ColPtrs &p, int c, float z0, float sc[H],
+                                           float zr[H]) {
+    MetaS<H> m;
+    meta_load_s<FMT, H>(a, p, c, m);
+    meta_decode_s<FMT, H>(a, c, m, z0, zsel(a.zp, FMT == FMT_U4 ? 0x88u : 128u), sc, zr);
 }
 
 }  // namespace qgemv

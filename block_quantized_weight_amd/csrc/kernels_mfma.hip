@@ -116,16 +116,19 @@ __device__ __forceinline__ op4 load_a(const uint16_t *arow, bool live, uint32_t 
     return r;
 }
 
-// Block metadata of one chunk kept raw (one or two dwords) while it waits in the
-// prefetch ring, decoded only when the chunk is consumed.
-//   U4, one block per chunk : fp16 scale bits | zero-point nibble << 16
-//   U4, two blocks per chunk: both fp16 scales | the zero-point byte of the pair
-//   U8                      : fp16 scale bits | zero-point byte << 16
-//   FP8                     : fp32 scale bits
-//   NVFP4                   : the two E4M3 scale bytes
+// Block metadata of one chunk kept raw while it waits in the prefetch ring: the
+// loaded values as they are (nothing is computed from a load until the chunk is
+// consumed, so a prefetch never waits for its own data), decoded by meta_decode.
+//   U4, one block per chunk : v0 = fp16 scale bits, v1 = the zero-point byte holding the block
+//   U4, two blocks per chunk: v0 = both fp16 scales, v1 = the zero-point byte of the pair
+//   U8                      : v0 = fp16 scale bits, v1 = zero-point byte
+//   FP8                     : v0 = fp32 scale bits
+//   NVFP4                   : v0 = the two E4M3 scale bytes
+// (without zero points v1 holds whatever the aliased address held; meta_decode then
+// uses the midpoint, 8 for U4 and 128 for U8)
 template <int H>
 struct MetaRaw {
-    uint32_t v[H];
+    uint32_t v[2];
 };
 
 struct MfCol {
@@ -134,6 +137,10 @@ struct MfCol {
     const uint8_t *z;
 };
 
+// Column pointers. Without zero points p.z aliases the column's scale row (at least
+// as many bytes as a zero-point row), so that every zero-point load is issued
+// unconditionally from a valid address and the midpoint is selected at decode: no
+// branch around a load keeps the compiler's load-counter waits exact in the rings.
 template <int FMT>
 __device__ __forceinline__ MfCol mf_col(const KArgs &a, int64_t n) {
     MfCol p;
@@ -141,30 +148,28 @@ __device__ __forceinline__ MfCol mf_col(const KArgs &a, int64_t n) {
     if constexpr (FMT == FMT_NVFP4) p.s = (const uint8_t *)a.scales + n * (a.K >> 4);
     else if constexpr (FMT == FMT_FP8) p.s = (const float *)a.scales + n * a.nblk;
     else p.s = (const uint16_t *)a.scales + n * a.nblk;
-    p.z = a.zp ? a.zp + n * a.zstride : nullptr;
+    p.z = a.zp ? a.zp + n * a.zstride : (const uint8_t *)p.s;
     return p;
 }
 
 template <int FMT, int H>
 __device__ __forceinline__ MetaRaw<H> load_meta_raw(const KArgs &a, const MfCol &p, int c) {
     MetaRaw<H> m;
+    m.v[1] = 0u;
     if constexpr (FMT == FMT_U4) {
         if constexpr (H == 1) {
             const int b = (c << 5) >> a.bs_shift;
-            uint32_t z = 8u;
-            if (p.z) {
-                const uint32_t zb = p.z[b >> 1];
-                z = (b & 1) ? (zb >> 4) : (zb & 0x0Fu);
-            }
-            m.v[0] = (uint32_t)((const uint16_t *)p.s)[b] | (z << 16);
+            m.v[0] = ((const uint16_t *)p.s)[b];
+            m.v[1] = p.z[b >> 1];
         } else {
             // 16-wide blocks: blocks 2c and 2c+1, adjacent scales, one zero-point byte
             m.v[0] = *(const uint32_t *)((const uint16_t *)p.s + 2 * c);
-            m.v[1] = p.z ? (uint32_t)p.z[c] : 0x88u;
+            m.v[1] = p.z[c];
         }
     } else if constexpr (FMT == FMT_U8) {
         const int b = (c << 4) >> a.bs_shift;
-        m.v[0] = (uint32_t)((const uint16_t *)p.s)[b] | ((p.z ? (uint32_t)p.z[b] : 128u) << 16);
+        m.v[0] = ((const uint16_t *)p.s)[b];
+        m.v[1] = p.z[b];
     } else if constexpr (FMT == FMT_FP8) {
         m.v[0] = ((const uint32_t *)p.s)[(c << 4) >> a.bs_shift];
     } else {
@@ -173,25 +178,30 @@ __device__ __forceinline__ MetaRaw<H> load_meta_raw(const KArgs &a, const MfCol 
     return m;
 }
 
-// Scale and (M0 + zero point) of half h from the raw metadata.
+// Scale and (M0 + zero point) of half h of chunk c from the raw metadata.
 template <int FMT, int ACT, int H>
-__device__ __forceinline__ void meta_decode(const MetaRaw<H> &m, int h, float &s, float &zoff) {
+__device__ __forceinline__ void meta_decode(const KArgs &a, const MetaRaw<H> &m, int c, int h, float &s,
+                                            float &zoff) {
     if constexpr (FMT == FMT_U4) {
+        const ZSel zs = zsel(a.zp, 0x88u);
+        const uint32_t zb = (m.v[1] & zs.keep) | zs.fill;
         if constexpr (H == 1) {
+            const int b = (c << 5) >> a.bs_shift;
             s = half_bits_to_float((uint16_t)(m.v[0] & 0xFFFFu));
-            zoff = U4Magic<ACT>::off + (float)(m.v[0] >> 16);
+            zoff = U4Magic<ACT>::off + (float)((b & 1) ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu));
         } else {
             s = half_bits_to_float((uint16_t)(h ? (m.v[0] >> 16) : (m.v[0] & 0xFFFFu)));
-            zoff = U4Magic<ACT>::off + (float)(h ? (m.v[1] >> 4) : (m.v[1] & 0x0Fu));
+            zoff = U4Magic<ACT>::off + (float)(h ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu));
         }
     } else if constexpr (FMT == FMT_U8) {
+        const ZSel zs = zsel(a.zp, 128u);
         s = half_bits_to_float((uint16_t)(m.v[0] & 0xFFFFu));
-        zoff = 1024.0f + (float)(m.v[0] >> 16);
+        zoff = 1024.0f + (float)(((m.v[1] & zs.keep) | zs.fill) & 0xFFu);
     } else if constexpr (FMT == FMT_FP8) {
         s = __builtin_bit_cast(float, m.v[0]);
         zoff = 0.0f;
     } else {
-        s = e4m3_to_float(h ? (m.v[0] >> 8) : (m.v[0] & 0xFFu));
+        s = e4m3_to_float(h ? ((m.v[0] >> 8) & 0xFFu) : (m.v[0] & 0xFFu));
         zoff = 0.0f;
     }
 }
@@ -241,26 +251,20 @@ __device__ __forceinline__ MetaRaw<H> meta_from_lds(const KArgs &a, const MfCol 
                                                     const uint32_t *meta1) {
     const int lane = threadIdx.x & 63;
     MetaRaw<H> m;
+    m.v[1] = 0u;
     if constexpr (FMT == FMT_U4) {
         if constexpr (H == 1) {
             const int b = (c << 5) >> a.bs_shift;
-            const uint16_t *sp = (const uint16_t *)p.s + b;
-            const uint32_t sbits = (meta0[lane] >> byte_shift(sp)) & 0xFFFFu;
-            uint32_t z = 8u;
-            if constexpr (ZPP) {
-                const uint32_t zb = (meta1[lane] >> byte_shift(p.z + (b >> 1))) & 0xFFu;
-                z = (b & 1) ? (zb >> 4) : (zb & 0x0Fu);
-            }
-            m.v[0] = sbits | (z << 16);
+            m.v[0] = (meta0[lane] >> byte_shift((const uint16_t *)p.s + b)) & 0xFFFFu;
+            m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + (b >> 1))) & 0xFFu) : 0x88u;
         } else {
             m.v[0] = meta0[lane];
             m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + c)) & 0xFFu) : 0x88u;
         }
     } else if constexpr (FMT == FMT_U8) {
         const int b = (c << 4) >> a.bs_shift;
-        const uint32_t sbits = (meta0[lane] >> byte_shift((const uint16_t *)p.s + b)) & 0xFFFFu;
-        const uint32_t z = ZPP ? ((meta1[lane] >> byte_shift(p.z + b)) & 0xFFu) : 128u;
-        m.v[0] = sbits | (z << 16);
+        m.v[0] = (meta0[lane] >> byte_shift((const uint16_t *)p.s + b)) & 0xFFFFu;
+        m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + b)) & 0xFFu) : 128u;
     } else if constexpr (FMT == FMT_FP8) {
         m.v[0] = meta0[lane];
     } else {
@@ -290,14 +294,37 @@ constexpr int kAPad = 8;
 // One K step of one wave: the chunk c = 4t + g of each of the 16 columns (already in
 // w, with its raw block metadata m), multiplied by every row group of A. Shared by
 // both kernels below so that they compute bit-identical results.
+// A operands of one K step for every row group, loaded from global memory (used ahead
+// of time by the register-ring kernel when the activations are not staged in LDS).
+template <int FMT, int RG>
+struct AOps {
+    op4 v[RG][MfFmt<FMT>::MF];
+};
+
+// Every lane loads (rows past M read row M - 1); lanes off the block diagonal or past
+// M are zeroed when the operands are used (mfma_step), so the loads themselves are
+// unconditional.
+template <int FMT, int RG>
+__device__ __forceinline__ void load_a_ops(const KArgs &a, int c, int ar, AOps<FMT, RG> &o) {
+    using F = MfFmt<FMT>;
+    const uint16_t *A16 = (const uint16_t *)a.A;
+    const uint32_t kbase = (uint32_t)c * F::KPC;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int row = 4 * rg + ar;
+        const uint16_t *arow = A16 + (int64_t)(row < a.M ? row : a.M - 1) * a.K;
+#pragma unroll
+        for (int j = 0; j < F::MF; ++j) o.v[rg][j] = load_a<FMT>(arow, true, kbase + 8 * j);
+    }
+}
+
 template <int FMT, int ACT, int RG, int H, bool LDSA>
 __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const MetaRaw<H> &m, int c, int ar,
                                           bool a_live_grp, const uint16_t *sA, const uint16_t *sZero, int astride,
-                                          f4 acc[RG]) {
+                                          const AOps<FMT, RG> &areg, bool valid, f4 acc[RG]) {
     using F = MfFmt<FMT>;
     constexpr uint32_t ONE = (ACT == ACT_F16) ? 0x3C003C00u : 0x3F803F80u;
     const op4 ones = {ONE, ONE, ONE, ONE};
-    const uint16_t *A16 = (const uint16_t *)a.A;
     // with one row group the B operands are decoded right before their MFMA; with
     // more they are decoded once and shared by the groups
     op4 bv[RG == 1 ? 1 : F::MF];
@@ -332,7 +359,8 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             if constexpr (LDSA) {
                 av = avs[j];
             } else {
-                av = load_a<FMT>(A16 + (int64_t)(live ? row : 0) * a.K, live, kbase + 8 * j);
+                const op4 z = {0u, 0u, 0u, 0u};
+                av = live ? areg.v[rg][j] : z;
             }
             const int h = (H == 2) ? (j / (F::MF / 2)) : 0;
             op4 b;
@@ -350,39 +378,65 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             float sc, zoff;
-            meta_decode<FMT, ACT, H>(m, h, sc, zoff);
+            meta_decode<FMT, ACT, H>(a, m, c, h, sc, zoff);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = d[h][r];
                 if constexpr (F::ZP) v = __builtin_fmaf(-zoff, sa[h][r], v);
-                acc[rg][r] = __builtin_fmaf(sc, v, acc[rg][r]);
+                const float t = __builtin_fmaf(sc, v, acc[rg][r]);
+                acc[rg][r] = valid ? t : acc[rg][r];
             }
         }
     }
 }
 
+// Compiler fence for the register rings: the accumulators are produced before this
+// point and no memory operation moves across it. Emits no instruction.
+template <int RG>
+__device__ __forceinline__ void pin_accumulators(f4 acc[RG]) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) asm volatile("" : "+v"(acc[r])::"memory");
+}
+
 // Stage the M activation rows into LDS once per workgroup, permuted into the MFMA
-// slot order (row stride K + kAPad elements).
-template <int FMT>
+// slot order (row stride K + kAPad elements). Each thread handles 16-byte pieces
+// it, it + blockDim, ... in batches of SB whose loads are all issued before the first
+// store, so the staging costs about one load latency per batch, not one per piece.
+template <int FMT, int SB = 8>
 __device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astride) {
     using F = MfFmt<FMT>;
     const uint16_t *A16 = (const uint16_t *)a.A;
     const int K = (int)a.K;
-    const int items = a.M * (K >> 3);
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-        const int m = it / (K >> 3);
-        const int k8 = (it - m * (K >> 3)) << 3;
-        const u4v v = load16(A16 + (int64_t)m * K + k8);
-        u4v o;
-        if constexpr (F::PERM) {
-            o.x = perm(v.z, v.x, 0x05040100u);  // (a0, a4)
-            o.y = perm(v.z, v.x, 0x07060302u);  // (a1, a5)
-            o.z = perm(v.w, v.y, 0x05040100u);  // (a2, a6)
-            o.w = perm(v.w, v.y, 0x07060302u);  // (a3, a7)
-        } else {
-            o = v;
+    const int k8n = K >> 3;
+    const int items = a.M * k8n;
+    const int last = items - 1;
+    for (int base = threadIdx.x; base < items; base += SB * (int)blockDim.x) {
+        u4v v[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            int it = base + j * (int)blockDim.x;
+            it = it < items ? it : last;
+            const int m = it / k8n;
+            v[j] = load16(A16 + (int64_t)m * K + ((it - m * k8n) << 3));
         }
-        *(u4v *)(sA + m * astride + k8) = o;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int it = base + j * (int)blockDim.x;
+            if (it < items) {
+                const int m = it / k8n;
+                const int k8 = (it - m * k8n) << 3;
+                u4v o;
+                if constexpr (F::PERM) {
+                    o.x = perm(v[j].z, v[j].x, 0x05040100u);  // (a0, a4)
+                    o.y = perm(v[j].z, v[j].x, 0x07060302u);  // (a1, a5)
+                    o.z = perm(v[j].w, v[j].y, 0x05040100u);  // (a2, a6)
+                    o.w = perm(v[j].w, v[j].y, 0x07060302u);  // (a3, a7)
+                } else {
+                    o = v[j];
+                }
+                *(u4v *)(sA + m * astride + k8) = o;
+            }
+        }
     }
 }
 
@@ -423,11 +477,27 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
     }
 }
 
+// Register-ring kernel. A workgroup of 8 waves holds 8 / ksplit tiles of ksplit waves
+// each and walks tile groups g = blockIdx.x, + gridDim.x, ...; within a tile, wave
+// kslice takes K steps t = kslice, kslice + ksplit, ... Every wave runs the same
+// S = ceil(ceil(steps / ksplit) / P) * P slots per tile (a slot past the last step, or
+// of a tile past N, computes on a clamped valid address and its accumulator update is
+// discarded), so all waves reach the K-split barriers of finish_tile together. The
+// (tile, slot) sequence is one pipeline: a register ring of P slots holds the codes and
+// raw metadata of the next P - 1 slots in flight, across tile boundaries. Activations
+// are either staged once per workgroup in LDS (LDSA) or, when they are not, fetched
+// into the same ring with the codes of their slot.
+//
+// Load-wait discipline: no load and no use of a slot sits behind a branch, a slot is
+// consumed before it is refilled (a scheduling barrier keeps the refill below the last
+// use), and the slot loop is a whole number of ring turns per tile, so each slot keeps
+// its registers and the compiler's wait before a slot leaves the later P - 1 slots in
+// flight.
 // Register budget: four waves per SIMD (<= 128 VGPRs) for one row group, two waves
-// per SIMD (<= 256) beyond. A 16-wave workgroup needs four waves per SIMD whatever the
-// bound says, so the automatic K split stays at 8 waves or fewer.
-template <int FMT, int ACT, int RG, int H, bool LDSA, int P, int NW>
-__global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
+// per SIMD (<= 256) beyond.
+template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
+__global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
+    constexpr int NW = 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int ks = a.ksplit;
     const int tpw = NW / ks;
@@ -439,6 +509,7 @@ __global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     const int ar = lane & 3;
     const bool a_live_grp = ((lane & 15) >> 2) == g;
     const int nsteps = (int)(a.nchunks >> 2);
+    const int S = ((nsteps + ks - 1) / ks + P - 1) / P * P;
     const int astride = (int)a.K + kAPad;
     const int64_t ntiles = (a.N + 15) >> 4;
     const int64_t ngroups = (ntiles + tpw - 1) / tpw;
@@ -446,51 +517,76 @@ __global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     uint16_t *sA = (uint16_t *)(smem + 16);
     float *sR = (float *)(smem + 16 + (LDSA ? (((size_t)a.M * astride * 2 + 15) & ~(size_t)15) : 0));
 
+    // issue cursor: tile group, slot within the tile, and the column the lane loads
+    int64_t itg = blockIdx.x;
+    int is = 0;
+    auto icol = [&]() {
+        const int64_t n = (itg * tpw + slot) * 16 + (lane & 15);
+        return mf_col<FMT>(a, n < a.N ? n : a.N - 1);
+    };
+    MfCol col = icol();
+    u4v wb[P];
+    MetaRaw<H> mb[P];
+    AOps<FMT, RG> ab[LDSA ? 1 : P];  // activations in the ring when they are not staged
+    auto issue = [&](int p) {
+        const int t0 = kslice + is * ks;
+        const int c = 4 * (t0 < nsteps ? t0 : nsteps - 1) + g;
+        wb[p] = load16_stream(col.w + (uint32_t)c * 16u);
+        mb[p] = load_meta_raw<FMT, H>(a, col, c);
+        if constexpr (!LDSA) load_a_ops<FMT, RG>(a, c, ar, ab[p]);
+        if (++is == S) {
+            is = 0;
+            itg += gridDim.x;
+            col = icol();
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(p);
+
     if constexpr (LDSA) {
         if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
         stage_a<FMT>(a, sA, astride);
         __syncthreads();
     }
 
-    for (int64_t tg = blockIdx.x; tg < ngroups; tg += gridDim.x) {
+    // One ring turn = P slots. Every turn but the last consumes and refills each slot;
+    // the last turn only drains the ring, so nothing is fetched past the wave's work.
+    // Tile boundaries fall on turn boundaries (S is a multiple of P).
+    const int64_t G = blockIdx.x < ngroups ? (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+    const int64_t turns = G * (S / P);
+    const int tpt = S / P;  // turns per tile
+    int64_t tg = blockIdx.x;
+    int tt = 0;  // turn within the tile
+    f4 acc[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
+    auto turn = [&](bool refill) {
         const int64_t tile = tg * tpw + slot;
         const bool tile_ok = tile < ntiles;
-        const int64_t n = tile * 16 + (lane & 15);
-        f4 acc[RG];
 #pragma unroll
-        for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
-        if (tile_ok) {
-            const MfCol col = mf_col<FMT>(a, n < a.N ? n : a.N - 1);
-            u4v wb[P];
-            MetaRaw<H> mb[P];
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int t = kslice + p * ks;
-                if (t < nsteps) {
-                    const int c = 4 * t + g;
-                    wb[p] = load16_stream(col.w + (uint32_t)c * 16u);
-                    mb[p] = load_meta_raw<FMT, H>(a, col, c);
-                }
-            }
-            for (int tb = kslice; tb < nsteps; tb += P * ks) {
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    const int t = tb + p * ks;
-                    if (t >= nsteps) break;
-                    const u4v w = wb[p];
-                    const MetaRaw<H> m = mb[p];
-                    const int tn = t + P * ks;
-                    if (tn < nsteps) {
-                        const int cn = 4 * tn + g;
-                        wb[p] = load16_stream(col.w + (uint32_t)cn * 16u);
-                        mb[p] = load_meta_raw<FMT, H>(a, col, cn);
-                    }
-                    mfma_step<FMT, ACT, RG, H, LDSA>(a, w, m, 4 * t + g, ar, a_live_grp, sA, sZero, astride, acc);
-                }
+        for (int p = 0; p < P; ++p) {
+            const int t = kslice + (tt * P + p) * ks;
+            const int tc = t < nsteps ? t : nsteps - 1;
+            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * tc + g, ar, a_live_grp, sA, sZero, astride,
+                                             ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
+            if (refill) {
+                // the slot's accumulation completes here (nothing of it may sink below
+                // the refill), then the refill reuses the slot's registers
+                pin_accumulators<RG>(acc);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(p);
             }
         }
-        finish_tile<ACT, RG>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, n);
-    }
+        if (++tt == tpt) {
+            finish_tile<ACT, RG>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15));
+#pragma unroll
+            for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
+            tt = 0;
+            tg += gridDim.x;
+        }
+    };
+    for (int64_t i = 0; i + 1 < turns; ++i) turn(true);
+    if (turns > 0) turn(false);
 }
 
 // LDS-ring kernel: each K step's 16-byte code chunk and its block-metadata dword(s)
@@ -551,7 +647,7 @@ __global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma_ring(KArgs 
         }
         if (!staged) {
             if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
-            stage_a<FMT>(a, sA, astride);
+            stage_a<FMT, 4>(a, sA, astride);  // smaller batches: the ring's state is live here
             __syncthreads();
             staged = true;
         }
@@ -574,7 +670,8 @@ __global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma_ring(KArgs 
                     dma_to_lds<16>(col.w + (uint32_t)cn * 16u, sn);
                     meta_dma<FMT, H, ZPP>(a, col, cn, (uint32_t *)(sn + 1024), (uint32_t *)(sn + 1280));
                 }
-                mfma_step<FMT, ACT, RG, H, true>(a, w, m, c, ar, a_live_grp, sA, sZero, astride, acc);
+                mfma_step<FMT, ACT, RG, H, true>(a, w, m, c, ar, a_live_grp, sA, sZero, astride, AOps<FMT, RG>{}, true,
+                                                 acc);
             }
         }
         finish_tile<ACT, RG>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, n);
@@ -583,22 +680,43 @@ __global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma_ring(KArgs 
 
 namespace {
 
-constexpr int kPrefetch = 2;
-
-template <int FMT, int ACT, int RG, int H, bool LDSA, int NW>
-hipError_t go_nw(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    auto kern = k_mfma<FMT, ACT, RG, H, LDSA, kPrefetch, NW>;
+template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
+hipError_t go_p(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    auto kern = k_mfma<FMT, ACT, RG, H, LDSA, P>;
     if (cfg.lds_bytes > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(64u * NW), (size_t)cfg.lds_bytes, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }
 
+// Ring depth when the activations travel in the ring too: as deep as the register
+// budget allows without spilling (each slot then holds RG * MF activation operands).
+template <int FMT, int RG>
+constexpr int ring_depth_with_a() {
+    return (MfFmt<FMT>::MF == 2 && RG <= 3) ? 4 : ((MfFmt<FMT>::MF == 4 && RG == 4) ? 1 : 2);
+}
+
+// Depth with staged activations: variant bit 3 asks for 8 slots, which one row group
+// with one scale block per chunk affords; larger tiles take 4 (2 for three or four row
+// groups with two scale blocks per chunk), the most that fit without spilling.
+template <int RG, int H>
+constexpr int ring_depth_staged(bool deep) {
+    return (RG <= 2 && H == 1) ? (deep ? 8 : 4) : ((RG <= 2 || H == 1) ? 4 : 2);
+}
+
+// register-ring depth (ring_depth_staged / ring_depth_with_a); 8-wave workgroups
 template <int FMT, int ACT, int RG, int H, bool LDSA>
 hipError_t go(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    return cfg.waves_per_wg == 16 ? go_nw<FMT, ACT, RG, H, LDSA, 16>(cfg, a, s) : go_nw<FMT, ACT, RG, H, LDSA, 8>(cfg, a, s);
+    if (cfg.waves_per_wg != 8) return hipErrorInvalidValue;
+    if constexpr (LDSA) {
+        constexpr int PD = ring_depth_staged<RG, H>(true), PS = ring_depth_staged<RG, H>(false);
+        return ((cfg.variant >> 3) & 1) ? go_p<FMT, ACT, RG, H, LDSA, PD>(cfg, a, s)
+                                        : go_p<FMT, ACT, RG, H, LDSA, PS>(cfg, a, s);
+    } else {
+        return go_p<FMT, ACT, RG, H, LDSA, ring_depth_with_a<FMT, RG>()>(cfg, a, s);
+    }
 }
 
 template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int NW>
@@ -617,7 +735,9 @@ hipError_t go_ring_nw(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 template <int FMT, int ACT, int RG, int H, bool ZPP>
 hipError_t go_ring(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.waves_per_wg != 8 || cfg.ksplit != 1) return hipErrorInvalidValue;
-    return ((cfg.variant >> 2) & 1) ? go_ring_nw<FMT, ACT, RG, H, ZPP, 8, 8>(cfg, a, s)
+    // two scale blocks per chunk (and zero points) do not fit an 8-slot ring's registers
+    constexpr int RD = (H == 2 && ZPP) ? 4 : 8;
+    return ((cfg.variant >> 2) & 1) ? go_ring_nw<FMT, ACT, RG, H, ZPP, RD, 8>(cfg, a, s)
                                     : go_ring_nw<FMT, ACT, RG, H, ZPP, 4, 8>(cfg, a, s);
 }
 

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
                 const int c = base + 64 * u + lane;
                 if (valid[u]) {
 #pragma unroll
-                    for (int i = 0; i < CPW; ++i) chunk_meta<FMT, H>(a, cp[i], c, sc[u][i], zr[u][i]);
+                    for (int i = 0; i < CPW; ++i) chunk_meta<FMT, H>(a, cp[i], c, Ops::Z0, sc[u][i], zr[u][i]);
                 }
             }
 #pragma unroll
@@ -118,6 +118,207 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
                 if (lane == 0 && nbase + i < a.N && rlive[m]) store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, s);
             }
         }
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// Persistent one-row streaming kernel (M = 1).
+//
+// The same per-row arithmetic as k_stream (same lanes per chunk, same chunk order per
+// lane, same decode, zero-point and scale steps, same wave reduction), so results are
+// bit-identical to it; what differs is how the latency is covered:
+//  - the activation row is staged once per workgroup in LDS, already in the decode's
+//    pair order and laid out so that the 64 lanes of a wave read consecutive 16-byte
+//    pieces, together with sum(a) of every chunk (half);
+//  - each wave walks column groups g = wave, wave + nwaves, ... and the batches of one
+//    group (UNR chunks per lane of each of its CPW columns); the codes and raw block
+//    metadata of the next batch are in flight while the current one is computed
+//    (two register buffers, the loop unrolled by two);
+//  - every load is issued for a clamped, valid chunk index, so the loads never
+//    diverge; a chunk past the end of K is simply not accumulated.
+
+template <int FMT, int H, int UNR, int CPW>
+struct SBatch {
+    u4v w[UNR][CPW];
+    MetaS<H> m[UNR][CPW];
+};
+
+// Index (in 16-byte pieces) of piece q of chunk c of the staged activation row.
+template <int NQ>
+__device__ __forceinline__ int stage_index(int c, int q) {
+    return (((c >> 6) * NQ + q) << 6) + (c & 63);
+}
+
+// Stage the activation row: each thread prepares chunks c, c + blockDim, ... two at a
+// time, with both chunks' loads issued before either is used.
+template <int FMT, int ACT, int H>
+__device__ __forceinline__ void stage_row(const KArgs &a, u4v *sP, float *sS) {
+    using Ops = ChunkOps<FMT, ACT, H>;
+    constexpr int NQ = Ops::ND / 4;
+    constexpr int SB = 2;
+    const uint16_t *A16 = (const uint16_t *)a.A;
+    const int nch = (int)a.nchunks;
+    for (int c0 = threadIdx.x; c0 < nch; c0 += SB * (int)blockDim.x) {
+        uint32_t x[SB][Ops::ND];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            int c = c0 + j * (int)blockDim.x;
+            c = c < nch ? c : nch - 1;
+            const uint16_t *ap = A16 + (uint32_t)c * (uint32_t)Ops::KPC;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const u4v v = load16(ap + 8 * q);
+                x[j][4 * q] = v.x; x[j][4 * q + 1] = v.y; x[j][4 * q + 2] = v.z; x[j][4 * q + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int c = c0 + j * (int)blockDim.x;
+            if (c < nch) {
+                ChunkAct act;
+                Ops::prep(x[j], act);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    sP[stage_index<NQ>(c, q)] = u4v{act.p[4 * q], act.p[4 * q + 1], act.p[4 * q + 2], act.p[4 * q + 3]};
+                if constexpr (FMT == FMT_U4 || FMT == FMT_U8) {
+#pragma unroll
+                    for (int h = 0; h < H; ++h) sS[c * H + h] = act.asum[h];
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int ACT, int CPW, int UNR, int H>
+__global__ void __launch_bounds__(256) k_stream1(KArgs a) {
+    using Ops = ChunkOps<FMT, ACT, H>;
+    using B = SBatch<FMT, H, UNR, CPW>;
+    constexpr bool ZP = (FMT == FMT_U4 || FMT == FMT_U8);
+    constexpr int NQ = Ops::ND / 4;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = (int)a.nchunks;
+    const int nch64 = (nch + 63) & ~63;
+    u4v *sP = (u4v *)smem;
+    float *sS = (float *)(smem + (size_t)nch64 * Ops::ND * 4);
+    const int64_t ngroups = (a.N + CPW - 1) / CPW;
+    const int rounds = (nch + 64 * UNR - 1) / (64 * UNR);
+    const int mine = gw < ngroups ? (int)((ngroups - gw + nw - 1) / nw) : 0;
+    const int total = mine * rounds;
+    const ZSel zs = zsel(a.zp, FMT == FMT_U4 ? 0x88u : 128u);
+
+    // issue cursor (group, round)
+    int64_t ig = gw;
+    int ir = 0;
+    auto issue = [&](B &b) {
+        ColPtrs cp[CPW];
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int64_t n = ig * CPW + i;
+            cp[i] = col_ptrs<FMT>(a, n < a.N ? n : a.N - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = ir * (64 * UNR) + 64 * u + lane;
+            const int cc = c < nch ? c : nch - 1;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) b.w[u][i] = load16_stream(cp[i].w + (uint32_t)cc * 16u);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = ir * (64 * UNR) + 64 * u + lane;
+            const int cc = c < nch ? c : nch - 1;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) meta_load_s<FMT, H>(a, cp[i], cc, b.m[u][i]);
+        }
+        if (++ir == rounds) {
+            ir = 0;
+            ig += nw;
+        }
+    };
+
+    // consume cursor and the accumulators of the group being computed
+    int64_t cg = gw;
+    int cr = 0;
+    float acc[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) acc[i] = 0.0f;
+    // branch-free: a chunk past the end is computed on the clamped chunk and its
+    // update of the accumulator is discarded by a select (acc keeps its bits)
+    auto consume = [&](const B &b) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = cr * (64 * UNR) + 64 * u + lane;
+            const bool valid = c < nch;
+            const int cc = valid ? c : nch - 1;
+            ChunkAct act;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const u4v v = sP[stage_index<NQ>(cc, q)];
+                act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
+            }
+            if constexpr (ZP) {
+#pragma unroll
+                for (int h = 0; h < H; ++h) act.asum[h] = sS[cc * H + h];
+            }
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                float sc[H], zr[H], part[H];
+                meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc, zr);
+                Ops::dot(b.w[u][i], act, part);
+                float t = acc[i];
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    float v = part[h];
+                    if constexpr (ZP) v = __builtin_fmaf(-zr[h], act.asum[h], v);
+                    t = __builtin_fmaf(sc[h], v, t);
+                }
+                acc[i] = valid ? t : acc[i];
+            }
+        }
+        // the batch's accumulation completes here (nothing of it may sink below the
+        // next refill of this buffer); emits no instruction
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) asm volatile("" : "+v"(acc[i])::"memory");
+        if (++cr == rounds) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int64_t n = cg * CPW + i;
+                const float v = wave_sum(acc[i]) * a.tscale;
+                if (lane == 0 && n < a.N) store_out<ACT>(a.Y, n, v);
+                acc[i] = 0.0f;
+            }
+            cr = 0;
+            cg += nw;
+        }
+    };
+
+    // Two buffers, refilled in turn; the steady-state loop has no branch around a load
+    // or a use, so the compiler's wait before a batch is consumed leaves the other
+    // batch in flight. The last one or two batches are drained without refills, so
+    // nothing is fetched past the wave's work. (Scheduling barriers keep each refill
+    // below the last use of the buffer's old contents.)
+    B b0, b1;
+    if (total > 0) issue(b0);  // the first batch's fetch overlaps the staging below
+    stage_row<FMT, ACT, H>(a, sP, sS);
+    __syncthreads();
+    int i = 0;
+    for (; i + 2 < total; i += 2) {
+        issue(b1);
+        consume(b0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(b0);
+        consume(b1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (total - i == 2) {
+        issue(b1);
+        consume(b0);
+        consume(b1);
+    } else if (total - i == 1) {
+        consume(b0);
     }
 }
 
@@ -224,8 +425,49 @@ hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     }
 }
 
+// One-row persistent kernel: cols_per_wave 1/2/4; unroll 2/3/4 from variant bits 1..2
+// (2 -> 2, 3 -> 3, 0 -> 4).
+template <int FMT, int ACT, int CPW, int UNR>
+hipError_t go_stream1_h(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)cfg.grid), block(256);
+    const size_t lds = (size_t)cfg.lds_bytes;
+    if constexpr (FMT == FMT_NVFP4) {
+        hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 2>), grid, block, lds, s, a);
+    } else if constexpr (FMT == FMT_U4) {
+        if (a.bs == 16)
+            hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 2>), grid, block, lds, s, a);
+        else
+            hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 1>), grid, block, lds, s, a);
+    } else {
+        hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 1>), grid, block, lds, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int FMT, int ACT, int CPW>
+hipError_t go_stream1_u(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch ((cfg.variant >> 1) & 3) {
+    case 2: return go_stream1_h<FMT, ACT, CPW, 2>(cfg, a, s);
+    case 3: return go_stream1_h<FMT, ACT, CPW, 3>(cfg, a, s);
+    case 0: return go_stream1_h<FMT, ACT, CPW, 4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT, int ACT>
+hipError_t go_stream1(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.cols_per_wave) {
+    case 1: return go_stream1_u<FMT, ACT, 1>(cfg, a, s);
+    case 2: return go_stream1_u<FMT, ACT, 2>(cfg, a, s);
+    case 4: return go_stream1_u<FMT, ACT, 4>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int FMT>
 hipError_t pick_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    if (cfg.variant & 1)
+        return cfg.act == ACT_F16 ? go_stream1<FMT, ACT_F16>(cfg, a, s) : go_stream1<FMT, ACT_BF16>(cfg, a, s);
     return cfg.act == ACT_F16 ? pick_mt<FMT, ACT_F16>(cfg, a, s) : pick_mt<FMT, ACT_BF16>(cfg, a, s);
 }
 

@@ -117,6 +117,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Zero-point presence as bit masks: byte = (loaded & keep) | fill gives the loaded
+// zero point, or the midpoint when the weight has none. The mask is laundered through
+// an empty asm so the optimizer cannot turn the selection back into a branch on the
+// (uniform) kernel argument, which would move zero-point decodes next to their loads
+// and make a prefetch wait for its own data.
+struct ZSel {
+    uint32_t keep, fill;
+};
+
+__device__ __forceinline__ ZSel zsel(const void *zp, uint32_t midpoint) {
+    uint32_t keep = zp ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(keep));
+    return ZSel{keep, ~keep & midpoint};
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land at

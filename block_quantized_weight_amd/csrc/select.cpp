@@ -36,12 +36,14 @@ int validate_desc(const qgemv_desc *d) {
     if (d->K % d->block_size) return QGEMV_E_SHAPE;
     const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA |
                            QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
-                           QGEMV_FLAG_RING_ON;
+                           QGEMV_FLAG_RING_ON | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
+                           QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK;
     if (d->flags & ~known) return QGEMV_E_ARG;
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
     const uint32_t ks = (d->flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
-    if (ks > 16) return QGEMV_E_ARG;
+    if (ks > 8) return QGEMV_E_ARG;
+    if (((d->flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT) > 2) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_STAGE_A_OFF) && (d->flags & QGEMV_FLAG_STAGE_A_ON)) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_RING_OFF) && (d->flags & QGEMV_FLAG_RING_ON)) return QGEMV_E_ARG;
     return QGEMV_OK;
@@ -92,9 +94,9 @@ static bool meta_dwords_ok(const qgemv_desc *d) {
 
 // Waves that share one 16-column tile's K range. Chosen from N and K only so that
 // the summation order of a row never depends on M: enough waves to fill the
-// machine (about eight per CU), at least two K steps of four chunks per wave, and
-// at most 8 (a 16-wave workgroup caps every wave at 128 VGPRs). A forced split may
-// go to 16.
+// machine (about four per CU: the split's LDS reduction and the per-workgroup
+// activation copy cost more than further waves bring), at least two K steps of four
+// chunks per wave, and at most 8, the waves of one workgroup.
 static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     const uint32_t forced = (flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     const int64_t tiles = (d->N + 15) / 16;
@@ -103,11 +105,62 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     if (forced) {
         ks = (int)forced;
     } else {
-        while (ks < 8 && tiles * ks < 8LL * cu_count && 2 * ks <= steps) ks *= 2;
+        while (ks < 8 && tiles * ks < 4LL * cu_count && 2 * ks <= steps) ks *= 2;
     }
-    if (ks > 16) ks = 16;
+    if (ks > 8) ks = 8;
     if (ks > steps) ks = (int)steps;
     return ks < 1 ? 1 : ks;
+}
+
+// Persistent one-row streaming kernel: the activation row (in the decode's pair order)
+// and per-chunk sums of it live in LDS; each wave walks column groups with the next
+// batch of codes in flight. Returns false when the staged row does not fit.
+//  - chunks per lane per batch (UNR 2, 3 or 4): the fewest idle load slots over the
+//    column's chunks, ties to the larger batch;
+//  - columns per wave: 1 while every column can have a wave of its own within ~24
+//    resident waves per CU, else 2;
+//  - grid: one group per wave when that fits in 24 waves per CU, else a persistent
+//    grid of 24 waves per CU.
+static bool stream1_plan(const qgemv_desc *d, int cu_count, uint32_t flags, LaunchCfg *c) {
+    const int kpc = k_per_chunk(d->format);
+    const int64_t nch = d->K / kpc;
+    const int64_t nch64 = (nch + 63) / 64 * 64;
+    const int nd = kpc == 32 ? 16 : 8;
+    const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
+    const int64_t lds = nch64 * nd * 4 + nch64 * h * 4;
+    if (lds > 48 * 1024) return false;
+    const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
+    int unr = 0;
+    const uint32_t fu = (flags & QGEMV_FLAG_STREAM_UNR_MASK) >> QGEMV_FLAG_STREAM_UNR_SHIFT;
+    if (fu) {
+        unr = (int)fu + 1;
+    } else {
+        int64_t best = -1;
+        for (int u = 4; u >= 2; --u) {
+            const int64_t idle = (cpl + u - 1) / u * u - cpl;
+            if (best < 0 || idle < best) best = idle, unr = u;
+        }
+    }
+    const uint32_t fc = (flags & QGEMV_FLAG_STREAM_CPW_MASK) >> QGEMV_FLAG_STREAM_CPW_SHIFT;
+    int cpw;
+    if (fc) cpw = fc == 3 ? 4 : (int)fc;
+    else cpw = d->N <= 24LL * cu_count ? 1 : 2;
+    const int64_t groups = (d->N + cpw - 1) / cpw;
+    const uint32_t fw = (flags & QGEMV_FLAG_STREAM_WPC_MASK) >> QGEMV_FLAG_STREAM_WPC_SHIFT;
+    int64_t wpc;
+    if (fw) wpc = 4 * (int64_t)fw;
+    else wpc = 24;
+    const int64_t wgs = (groups + 3) / 4;
+    const int64_t cap = (int64_t)cu_count * wpc / 4;
+    c->rows_per_pass = 1;
+    c->passes = 1;
+    c->cols_per_wave = cpw;
+    c->ksplit = 1;
+    c->waves_per_wg = 4;
+    c->grid = wgs < cap ? wgs : (cap > 0 ? cap : 1);
+    c->lds_bytes = (int)lds;
+    c->variant = 1 | ((unr & 3) << 1);
+    return true;
 }
 
 int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t extra_flags, LaunchCfg *out) {
@@ -154,8 +207,8 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         c.passes = 1;
         c.cols_per_wave = 16;
         c.ksplit = mfma_ksplit(d, cu_count, flags);
-        // a workgroup holds nw / ksplit tiles of ksplit waves each
-        const int nw = c.ksplit > 8 ? c.ksplit : 8;
+        // a workgroup holds 8 / ksplit tiles of ksplit waves each
+        const int nw = 8;
         c.waves_per_wg = nw;
         const int64_t tiles = (d->N + 15) / 16;
         const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
@@ -171,7 +224,10 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         if (flags & QGEMV_FLAG_RING_ON) ring = ring_ok;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {
-            const bool deep = abytes16 + 8 * 8 * slot <= kLdsBytes;
+            // 8 slots when they fit (not for 16-wide 4-bit blocks with zero points,
+            // whose registers take only 4)
+            const bool deep = abytes16 + 8 * 8 * slot <= kLdsBytes &&
+                              !(zpp && d->format == QGEMV_FMT_U4 && d->block_size == 16);
             c.waves_per_wg = 8;
             c.variant = 2 | (deep ? 4 : 0);
             c.lds_bytes = (int)(abytes16 + 8 * (deep ? 8 : 4) * slot);
@@ -182,12 +238,19 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
             *out = c;
             return QGEMV_OK;
         }
-        // Stage the activations when they fit and the workgroups then walk many tiles
-        // (no K split): the staging is paid once per workgroup.
-        bool stage = lds_a + lds_red <= kLdsBytes && c.ksplit == 1 && groups > 2LL * cu_count;
-        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_a + lds_red <= kLdsBytes;
+        // Stage the activations in LDS when they fit and every wave has enough K steps
+        // per tile (8 or more) to amortize the copy; with fewer, the activations travel
+        // with the codes in the register ring instead.
+        const int64_t steps = d->K / (4 * k_per_chunk(d->format));
+        const int64_t spw = (steps + c.ksplit - 1) / c.ksplit;
+        bool stage = lds_a + 16 + lds_red <= kLdsBytes && spw >= 8;
+        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_a + 16 + lds_red <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
-        c.variant = stage ? 1 : 0;
+        // register-ring depth: 8 slots when a wave's steps per tile are a multiple of 8
+        // or many (no idle padded slots to speak of), else 4; or forced
+        const uint32_t fdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
+        const bool deep8 = fdep ? fdep == 2 : (spw % 8 == 0 || spw >= 32);
+        c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
         c.lds_bytes = (int)(lds_red + (stage ? 16 + ((lds_a + 15) & ~15LL) : 0));
         int64_t grid = groups;
         if (stage) {
@@ -204,6 +267,8 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t wgs = (d->N + 3) / 4;
         const int64_t cap = 8LL * cu_count;
         c.grid = wgs < cap ? wgs : cap;
+    } else if (M == 1 && !(flags & QGEMV_FLAG_STREAM_CLASSIC) && stream1_plan(d, cu_count, flags, &c)) {
+        // persistent one-row kernel (plan filled in)
     } else {
         c.rows_per_pass = (M == 1) ? 1 : (M == 2 ? 2 : 4);
         c.passes = (M + c.rows_per_pass - 1) / c.rows_per_pass;

@@ -85,11 +85,18 @@ enum qgemv_family {
 };
 
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
- * Bits 8..15: forced K split of the MFMA family (0 = automatic; otherwise 1..16 waves
+ * Bits 8..15: forced K split of the MFMA family (0 = automatic; otherwise 1..8 waves
  * share the K range of a column tile). Bit 16: never pick the MFMA family.
  * Bits 17/18: MFMA family never / always stages the activations in LDS (when they
  * fit); neither set = automatic. Bits 19/20: MFMA family never / always (when
- * eligible) streams the weights through the LDS DMA ring. For A/B comparisons. */
+ * eligible) streams the weights through the LDS DMA ring.
+ * Streaming family at M = 1 (the persistent one-row kernel): bits 21..22 force the
+ * columns per wave (1 -> 1, 2 -> 2, 3 -> 4), bits 23..24 the chunks per lane per
+ * batch (1 -> 2, 2 -> 3, 3 -> 4), bits 25..27 the resident waves per CU the grid is
+ * sized for (v -> 4v); 0 = automatic. Bit 28: use the non-persistent streaming kernel
+ * at M = 1 as well. Bits 29..30: MFMA register-ring depth (1 -> 4 slots, 2 -> 8;
+ * 0 = automatic). None of these changes a result's bits except the family choice and
+ * the K split; they exist for A/B comparisons and tuning. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
 #define QGEMV_FLAG_KSPLIT_MASK 0x0000FF00u
@@ -98,6 +105,15 @@ enum qgemv_family {
 #define QGEMV_FLAG_STAGE_A_ON 0x00040000u
 #define QGEMV_FLAG_RING_OFF 0x00080000u
 #define QGEMV_FLAG_RING_ON 0x00100000u
+#define QGEMV_FLAG_STREAM_CPW_SHIFT 21
+#define QGEMV_FLAG_STREAM_CPW_MASK 0x00600000u
+#define QGEMV_FLAG_STREAM_UNR_SHIFT 23
+#define QGEMV_FLAG_STREAM_UNR_MASK 0x01800000u
+#define QGEMV_FLAG_STREAM_WPC_SHIFT 25
+#define QGEMV_FLAG_STREAM_WPC_MASK 0x0E000000u
+#define QGEMV_FLAG_STREAM_CLASSIC 0x10000000u
+#define QGEMV_FLAG_MFMA_DEPTH_SHIFT 29
+#define QGEMV_FLAG_MFMA_DEPTH_MASK 0x60000000u
 
 /* Problem description. struct_size must be sizeof(qgemv_desc). */
 typedef struct qgemv_desc {
@@ -125,7 +141,10 @@ typedef struct qgemv_plan_info {
     int64_t grid;            /* workgroups launched */
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
     int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
-                                LDS, bit 1 = weights through the LDS DMA ring, bit 2 = 8-slot ring */
+                                LDS, bit 1 = weights through the LDS DMA ring, bit 2 = 8-slot DMA
+                                ring, bit 3 = 8-slot register ring (else 4).
+                                Streaming: bit 0 = persistent one-row kernel, bits 1..2 = chunks
+                                per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
 } qgemv_plan_info;
 
 typedef struct qgemv_handle qgemv_handle;

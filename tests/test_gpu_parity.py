@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 from tests import gpu_util as gu
 
-FAMILY_FLAG = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3,
+FAMILY_FLAG = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3, "stream_classic": 1 | bqw.FLAG_STREAM_CLASSIC,
                "mfma_lds": 2 | bqw.FLAG_STAGE_A_ON | bqw.FLAG_RING_OFF,
                "mfma_nolds": 2 | bqw.FLAG_STAGE_A_OFF | bqw.FLAG_RING_OFF,
                "mfma_ring": 2 | bqw.FLAG_RING_ON | (1 << 8)}
@@ -130,7 +130,7 @@ def test_missing_zero_points_mean_midpoint(fmt, act):
 # bit-exact properties
 
 
-@pytest.mark.parametrize("family", ["stream", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
+@pytest.mark.parametrize("family", ["stream", "stream_classic", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u4", "f16", 32), ("fp8", "f16", 128),
                                          ("nvfp4", "bf16", 16), ("u8", "f16", 128), ("u4", "f16", 16)])
 def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
@@ -152,6 +152,43 @@ def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
         assert np.array_equal(Yo.view(np.int64), Y16.view(np.int64))
 
 
+def _stream1_flags(cpw, unr, wpc):
+    code = {1: 1, 2: 2, 4: 3}[cpw]
+    return (1 | (code << bqw.FLAG_STREAM_CPW_SHIFT) | ((unr - 1) << bqw.FLAG_STREAM_UNR_SHIFT)
+            | (wpc << bqw.FLAG_STREAM_WPC_SHIFT))
+
+
+@pytest.mark.parametrize("fmt,act,bs,N,K", [("u4", "bf16", 32, 1001, 4000 // 32 * 32 + 32 * 3),
+                                            ("u4", "f16", 16, 517, 64 * 32 * 3 + 32),
+                                            ("u8", "f16", 128, 333, 128 * 37),
+                                            ("u8", "bf16", 64, 700, 64 * 40),
+                                            ("fp8", "f16", 128, 1234, 128 * 41),
+                                            ("nvfp4", "bf16", 16, 999, 32 * 97),
+                                            ("nvfp4", "f16", 16, 64, 32 * 128),
+                                            ("u4", "bf16", 32, 20011, 1024),
+                                            ("fp8", "bf16", 128, 9001, 2048)])
+def test_one_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act, bs, N, K):
+    """The persistent M = 1 streaming kernel keeps the streaming family's per-row
+    arithmetic: every columns-per-wave / batch / grid choice (including grids small
+    enough that each wave walks many column groups, and ragged chunk counts) must give
+    the classic kernel's bits, and both must meet the oracle bound."""
+    prob = synth.make_problem(fmt, act, N, K, bs, 1, seed=31)
+    gu.say(f"[stream1] {fmt}/{act} bs{bs} N={N} K={K}")
+    Yc, pc = gu.run_gpu(prob, 1, flags=FAMILY_FLAG["stream_classic"])
+    assert not (pc["variant"] & 1)
+    ok, ratio, _, _ = gu.check_full(prob, 1, Yc, strict=False)
+    assert ok, ratio
+    Ya, pa = gu.run_gpu(prob, 1, flags=FAMILY_FLAG["stream"])
+    assert pa["variant"] & 1, pa
+    assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64))
+    for cpw in (1, 2, 4):
+        for unr in (2, 3, 4):
+            for wpc in (0, 1):
+                Yv, pv = gu.run_gpu(prob, 1, flags=_stream1_flags(cpw, unr, wpc))
+                assert pv["variant"] & 1 and pv["cols_per_wave"] == cpw, pv
+                assert np.array_equal(Yv.view(np.int64), Yc.view(np.int64)), (cpw, unr, wpc, pv)
+
+
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
 def test_repeated_runs_are_bitwise_equal(name, M):
     prob = synth.workload(name)
@@ -161,7 +198,7 @@ def test_repeated_runs_are_bitwise_equal(name, M):
 
 
 @pytest.mark.parametrize("stage", [False, True])
-@pytest.mark.parametrize("ks", [1, 2, 4, 16])
+@pytest.mark.parametrize("ks", [1, 2, 4, 8])
 def test_forced_k_split_is_correct(ks, stage):
     prob = synth.make_problem("u4", "bf16", 100, 4096, 32, 6, seed=4)
     flags = 2 | (ks << 8) | (bqw.FLAG_STAGE_A_ON if stage else bqw.FLAG_STAGE_A_OFF)
