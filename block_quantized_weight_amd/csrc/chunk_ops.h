@@ -126,10 +126,10 @@ struct ChunkOps<FMT_U4, ACT_BF16, H> {
         for (int d = 0; d < 4; ++d) {
             const int i = (H == 2) ? (d >> 1) : 0;
             const uint32_t wv = w[d];
-            s[i] = dot2<ACT_BF16>((wv & 0x000F000Fu) | MAGIC, h.p[4 * d + 0], s[i]);
-            s[i] = dot2<ACT_BF16>(((wv >> 8) & 0x000F000Fu) | MAGIC, h.p[4 * d + 1], s[i]);
-            s[i] = dot2<ACT_BF16>(((wv >> 4) & 0x000F000Fu) | MAGIC, h.p[4 * d + 2], s[i]);
-            s[i] = dot2<ACT_BF16>(((wv >> 12) & 0x000F000Fu) | MAGIC, h.p[4 * d + 3], s[i]);
+            s[i] = dot2<ACT_BF16>(and_or(wv, 0x000F000Fu, MAGIC), h.p[4 * d + 0], s[i]);
+            s[i] = dot2<ACT_BF16>(and_or(wv >> 8, 0x000F000Fu, MAGIC), h.p[4 * d + 1], s[i]);
+            s[i] = dot2<ACT_BF16>(and_or(wv >> 4, 0x000F000Fu, MAGIC), h.p[4 * d + 2], s[i]);
+            s[i] = dot2<ACT_BF16>(and_or(wv >> 12, 0x000F000Fu, MAGIC), h.p[4 * d + 3], s[i]);
         }
 #pragma unroll
         for (int i = 0; i < H; ++i) out[i] = s[i];

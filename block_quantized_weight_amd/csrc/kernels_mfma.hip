@@ -69,10 +69,10 @@ __device__ __forceinline__ op4 decode_b(const u4v &w) {
         // dword J holds k = 8J..8J+7: slots (k0,k4),(k1,k5),(k2,k6),(k3,k7)
         const uint32_t x = w[J];
         constexpr uint32_t M = U4Magic<ACT>::bits;
-        r.x = (x & 0x000F000Fu) | M;
-        r.y = ((x >> 4) & 0x000F000Fu) | M;
-        r.z = ((x >> 8) & 0x000F000Fu) | M;
-        r.w = ((x >> 12) & 0x000F000Fu) | M;
+        r.x = and_or(x, 0x000F000Fu, M);
+        r.y = and_or(x >> 4, 0x000F000Fu, M);
+        r.z = and_or(x >> 8, 0x000F000Fu, M);
+        r.w = and_or(x >> 12, 0x000F000Fu, M);
     } else if constexpr (FMT == FMT_U8) {
         // dwords 2J, 2J+1 hold k = 8J..8J+7 in natural order; (1024 + q) as fp16
         constexpr uint32_t MB = 0x64646464u;
@@ -204,73 +204,6 @@ __device__ __forceinline__ void meta_decode(const KArgs &a, const MetaRaw<H> &m,
         s = e4m3_to_float(h ? ((m.v[0] >> 8) & 0xFFu) : (m.v[0] & 0xFFu));
         zoff = 0.0f;
     }
-}
-
-// Block metadata through the DMA ring: the aligned dword(s) holding a chunk's scale
-// (and zero point) are copied to LDS next to the chunk's codes, then unpacked into
-// the same raw form as load_meta_raw. The dispatcher only takes this path when the
-// scale and zero-point arrays are 4-byte aligned and whole dwords long, so every
-// dword read lies inside them.
-template <int FMT, bool ZPP>
-struct MetaDma {
-    static constexpr int NM = ((FMT == FMT_U4 || FMT == FMT_U8) && ZPP) ? 2 : 1;
-};
-
-__device__ __forceinline__ const uint32_t *dword_of(const void *p) {
-    return (const uint32_t *)((uintptr_t)p & ~(uintptr_t)3);
-}
-
-__device__ __forceinline__ uint32_t byte_shift(const void *p) { return 8u * (uint32_t)((uintptr_t)p & 3); }
-
-template <int FMT, int H, bool ZPP>
-__device__ __forceinline__ void meta_dma(const KArgs &a, const MfCol &p, int c, uint32_t *meta0, uint32_t *meta1) {
-    const int lane = threadIdx.x & 63;
-    if constexpr (FMT == FMT_U4) {
-        if constexpr (H == 1) {
-            const int b = (c << 5) >> a.bs_shift;
-            dma_to_lds<4>(dword_of((const uint16_t *)p.s + b), meta0);
-            if constexpr (ZPP) dma_to_lds<4>(dword_of(p.z + (b >> 1)), meta1);
-        } else {
-            dma_to_lds<4>((const uint16_t *)p.s + 2 * c, meta0);
-            if constexpr (ZPP) dma_to_lds<4>(dword_of(p.z + c), meta1);
-        }
-    } else if constexpr (FMT == FMT_U8) {
-        const int b = (c << 4) >> a.bs_shift;
-        dma_to_lds<4>(dword_of((const uint16_t *)p.s + b), meta0);
-        if constexpr (ZPP) dma_to_lds<4>(dword_of(p.z + b), meta1);
-    } else if constexpr (FMT == FMT_FP8) {
-        dma_to_lds<4>((const uint32_t *)p.s + ((c << 4) >> a.bs_shift), meta0);
-    } else {
-        dma_to_lds<4>(dword_of((const uint8_t *)p.s + 2 * c), meta0);
-    }
-    (void)lane;
-}
-
-template <int FMT, int H, bool ZPP>
-__device__ __forceinline__ MetaRaw<H> meta_from_lds(const KArgs &a, const MfCol &p, int c, const uint32_t *meta0,
-                                                    const uint32_t *meta1) {
-    const int lane = threadIdx.x & 63;
-    MetaRaw<H> m;
-    m.v[1] = 0u;
-    if constexpr (FMT == FMT_U4) {
-        if constexpr (H == 1) {
-            const int b = (c << 5) >> a.bs_shift;
-            m.v[0] = (meta0[lane] >> byte_shift((const uint16_t *)p.s + b)) & 0xFFFFu;
-            m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + (b >> 1))) & 0xFFu) : 0x88u;
-        } else {
-            m.v[0] = meta0[lane];
-            m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + c)) & 0xFFu) : 0x88u;
-        }
-    } else if constexpr (FMT == FMT_U8) {
-        const int b = (c << 4) >> a.bs_shift;
-        m.v[0] = (meta0[lane] >> byte_shift((const uint16_t *)p.s + b)) & 0xFFFFu;
-        m.v[1] = ZPP ? ((meta1[lane] >> byte_shift(p.z + b)) & 0xFFu) : 128u;
-    } else if constexpr (FMT == FMT_FP8) {
-        m.v[0] = meta0[lane];
-    } else {
-        m.v[0] = (meta0[lane] >> byte_shift((const uint8_t *)p.s + 2 * c)) & 0xFFFFu;
-    }
-    return m;
 }
 
 // Sum over the four lane groups (lanes n, n+16, n+32, n+48); every lane gets the
@@ -589,92 +522,191 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     if (turns > 0) turn(false);
 }
 
-// LDS-ring kernel: each K step's 16-byte code chunk and its block-metadata dword(s)
-// travel global -> LDS by DMA (global_load_lds), R slots per wave and R - 1 steps in
-// flight, so the prefetch depth costs no VGPRs. The activations are staged in LDS as
-// well, which leaves these DMAs as the only vector-memory operations of the K loop;
-// they complete in issue order, so the wait before a slot is read is an exact vmcnt.
-template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int NW>
-__global__ void __launch_bounds__(64 * NW, (RG == 1 ? 4 : 2)) k_mfma_ring(KArgs a) {
-    constexpr int P = R - 1;
-    constexpr int NM = MetaDma<FMT, ZPP>::NM;
-    constexpr int OPS = 1 + NM;                 // DMAs per step
-    constexpr int STEADY = (P - 1) * OPS;       // later steps' DMAs still in flight
-    constexpr int SLOT = 1024 + 256 * NM;       // bytes per slot
+// DMA-ring kernel for wide N without a K split. Each wave owns 16-column tiles
+// (tiles gw, gw + nwaves, ...) over the whole of K. Codes and block metadata travel
+// global -> LDS by DMA (global_load_lds) in slots of SS K steps (CS = 4 * SS chunks
+// of each of the 16 columns), R slots per wave and R - 1 in flight, so the prefetch
+// depth costs no VGPRs and the waits are exact load counts.
+//  - Coalescing: one code DMA instruction moves 64 / CS whole columns' CS chunks
+//    (CS * 16 contiguous bytes each, whole cache lines), not 16 columns' 64-byte
+//    pieces. Which lane fetches which chunk is permuted (chunk j of column n lands
+//    at position j ^ (n mod CS)), so that the MFMA-order reads of a step, where the
+//    16 columns ask for the same chunk, fall in 16 distinct LDS bank groups.
+//  - Metadata: each column's scale bytes of the slot (and zero-point bytes) are one
+//    contiguous window of the row, copied as whole dwords; a chunk's raw metadata is
+//    then cut from LDS in the form load_meta_raw gives.
+//  - Every K step keeps the chunk -> (step, lane group) assignment of k_mfma (step t,
+//    lane group g: chunk 4t + g) and calls the same mfma_step, so results are
+//    bit-identical to k_mfma with no K split.
+template <int FMT, int SS>
+struct DmaGeom {
+    static constexpr int CS = 4 * SS;                      // chunks per column per slot
+    static constexpr int CPD = 64 / CS;                    // columns per code DMA
+    static constexpr int DSTRIDE = SS == 4 ? 1024 : 1152;  // bytes per code DMA block (+pad)
+    static constexpr int CODEB = (16 / CPD) * DSTRIDE;     // code bytes per slot
+    // scale-window DMAs per slot (upper bound over the block sizes the format takes)
+    static constexpr int NSD =
+        (FMT == FMT_FP8) ? (SS == 4 ? 4 : 2) : ((FMT == FMT_U4 || FMT == FMT_NVFP4) ? (SS == 4 ? 4 : 2) : (SS == 4 ? 2 : 1));
+};
+
+template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int SS>
+__global__ void __launch_bounds__(512, 2) k_mfma_dma(KArgs a) {
+    using Gm = DmaGeom<FMT, SS>;
+    using F = MfFmt<FMT>;
+    constexpr int NW = 8;
+    constexpr int CS = Gm::CS;
+    constexpr int SLOT = Gm::CODEB + 256 * Gm::NSD + (ZPP ? 256 : 0);
+    constexpr int SB = (FMT == FMT_FP8) ? 4 : ((FMT == FMT_NVFP4) ? 1 : 2);  // scale bytes
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int ks = a.ksplit;
-    const int tpw = NW / ks;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int slot = wave / ks;
-    const int kslice = wave - slot * ks;
+    const int n = lane & 15;
     const int g = lane >> 4;
     const int ar = lane & 3;
-    const bool a_live_grp = ((lane & 15) >> 2) == g;
-    const int nsteps = (int)(a.nchunks >> 2);
+    const bool a_live_grp = (n >> 2) == g;
+    const int nch = (int)a.nchunks;
+    const int nslots = (nch + CS - 1) / CS;
     const int astride = (int)a.K + kAPad;
     const int64_t ntiles = (a.N + 15) >> 4;
-    const int64_t ngroups = (ntiles + tpw - 1) / tpw;
+    const int64_t nw = (int64_t)gridDim.x * NW;
+    const int64_t gw = (int64_t)blockIdx.x * NW + wave;
+    const int64_t mytiles = gw < ntiles ? (ntiles - gw + nw - 1) / nw : 0;
+    const int64_t total = mytiles * nslots;
     const size_t abytes = 16 + (((size_t)a.M * astride * 2 + 15) & ~(size_t)15);
     uint16_t *sZero = (uint16_t *)smem;
     uint16_t *sA = (uint16_t *)(smem + 16);
     unsigned char *ring = smem + abytes + (size_t)wave * R * SLOT;
-    float *sR = (float *)(smem + abytes + (size_t)NW * R * SLOT);
-    // this wave's steps: t = kslice + i * ks, i < nmine
-    const int nmine = kslice < nsteps ? (nsteps - kslice + ks - 1) / ks : 0;
 
-    bool staged = false;
-    for (int64_t tg = blockIdx.x; tg < ngroups; tg += gridDim.x) {
-        const int64_t tile = tg * tpw + slot;
-        const bool tile_ok = tile < ntiles;
-        const int64_t n = tile * 16 + (lane & 15);
-        const MfCol col = mf_col<FMT>(a, n < a.N ? n : a.N - 1);
-        f4 acc[RG];
+    // per-slot metadata windows (uniform): blocks per slot (slots hold whole blocks:
+    // the dispatcher ensures CS * KPC >= block size), bytes per column, dwords
+    const int bps = (H == 2) ? 2 * CS : ((CS * F::KPC) >> a.bs_shift);
+    const int sbc = bps * SB;
+    const int mds = sbc >= 4 ? sbc / 4 : 1;
+    const int nsd = (16 * mds + 63) / 64;
+    const int zbc = (FMT == FMT_U4) ? (bps >> 1) : bps;
+    const int mdz = zbc >= 4 ? zbc / 4 : 1;
+    const int srow = a.nblk * SB;                                     // scale row bytes
+    const int zrow = a.zstride;                                       // zero-point row bytes
+    const int ops = SS + nsd + (ZPP ? 1 : 0);                         // DMAs per slot
+
+    // issue cursor
+    int64_t itile = gw;
+    int isl = 0;
+    auto issue = [&](int r) {
+        unsigned char *slot = ring + r * SLOT;
+        const int64_t t0 = itile * 16;
+        // codes: DMA d moves columns d*CPD .. d*CPD + CPD - 1
 #pragma unroll
-        for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
-        // prologue: the first P steps in flight (on the first tile before the
-        // activations are staged, so that the copy overlaps the weight fetch)
-        if (tile_ok) {
+        for (int d = 0; d < 16 / Gm::CPD; ++d) {
+            const int cn = d * Gm::CPD + lane / CS;
+            const int jp = lane % CS;
+            const int j = jp ^ (cn % CS);
+            int64_t col = t0 + cn;
+            col = col < a.N ? col : a.N - 1;
+            int c = isl * CS + j;
+            c = c < nch ? c : nch - 1;
+            dma_to_lds<16>(a.W + col * a.col_bytes + (int64_t)c * 16, slot + d * Gm::DSTRIDE);
+        }
+        // scale windows: dword q of column cn's window
+        const int wbs = (isl * sbc) & ~3;
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                if (p < nmine) {
-                    const int c = 4 * (kslice + p * ks) + g;
-                    unsigned char *sl = ring + p * SLOT;
-                    dma_to_lds<16>(col.w + (uint32_t)c * 16u, sl);
-                    meta_dma<FMT, H, ZPP>(a, col, c, (uint32_t *)(sl + 1024), (uint32_t *)(sl + 1280));
-                }
+        for (int e = 0; e < Gm::NSD; ++e) {
+            if (e < nsd) {
+                const int idx = e * 64 + lane;
+                int cn = idx / mds, q = idx - (idx / mds) * mds;
+                if (cn > 15) cn = 15, q = mds - 1;
+                if (wbs + 4 * q + 4 > srow) q = (srow - wbs) / 4 - 1;
+                int64_t col = t0 + cn;
+                col = col < a.N ? col : a.N - 1;
+                const uint8_t *row = (const uint8_t *)a.scales + col * srow;
+                dma_to_lds<4>(row + wbs + 4 * q, slot + Gm::CODEB + e * 256);
             }
         }
-        if (!staged) {
-            if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
-            stage_a<FMT, 4>(a, sA, astride);  // smaller batches: the ring's state is live here
-            __syncthreads();
-            staged = true;
+        if constexpr (ZPP) {
+            const int zb0 = (FMT == FMT_U4) ? ((isl * bps) >> 1) : isl * bps;
+            const int wbz = zb0 & ~3;
+            int cn = lane / mdz, q = lane - (lane / mdz) * mdz;
+            if (cn > 15) cn = 15, q = mdz - 1;
+            if (wbz + 4 * q + 4 > zrow) q = (zrow - wbz) / 4 - 1;
+            int64_t col = t0 + cn;
+            col = col < a.N ? col : a.N - 1;
+            dma_to_lds<4>(a.zp + col * zrow + wbz + 4 * q, slot + Gm::CODEB + Gm::NSD * 256);
         }
-        if (tile_ok) {
-            // one step per iteration, slots addressed at run time: nothing from
-            // another step is live across the wait
+        if (++isl == nslots) {
+            isl = 0;
+            itile += nw;
+        }
+    };
+
+    // the first R - 1 slots in flight, then the activations staged (the copy overlaps
+    // the weight fetch)
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r)
+        if (r < total) issue(r);
+    if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
+    stage_a<FMT, 4>(a, sA, astride);
+    __syncthreads();
+
+    // Byte offsets, within a slot's scale / zero-point window of the lane's column, of
+    // the metadata of the lane's chunk 4s + g (the same in every slot; a window shorter
+    // than a dword adds the slot's position in its dword)
+    int sbyte[SS], zbyte[SS];
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+        const int j = 4 * s + g;
+        const int lb = (H == 2) ? 2 * j : ((j * F::KPC) >> a.bs_shift);  // first block of the chunk
+        sbyte[s] = lb * SB;
+        zbyte[s] = (FMT == FMT_U4) ? (lb >> 1) : lb;
+    }
+
+    int64_t ctile = gw;
+    int csl = 0;
+    f4 acc[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-            for (int i = 0; i < nmine; ++i) {
-                if (i + P - 1 < nmine) wait_vmcnt<STEADY>();
-                else wait_vmcnt<0>();
-                const int c = 4 * (kslice + i * ks) + g;
-                const unsigned char *sl = ring + (i % R) * SLOT;
-                const u4v w = ((const u4v *)sl)[lane];
-                const MetaRaw<H> m = meta_from_lds<FMT, H, ZPP>(a, col, c, (const uint32_t *)(sl + 1024),
-                                                                (const uint32_t *)(sl + 1280));
-                if (i + P < nmine) {
-                    // refill the slot consumed one step ago
-                    const int cn = 4 * (kslice + (i + P) * ks) + g;
-                    unsigned char *sn = ring + ((i + P) % R) * SLOT;
-                    dma_to_lds<16>(col.w + (uint32_t)cn * 16u, sn);
-                    meta_dma<FMT, H, ZPP>(a, col, cn, (uint32_t *)(sn + 1024), (uint32_t *)(sn + 1280));
-                }
-                mfma_step<FMT, ACT, RG, H, true>(a, w, m, c, ar, a_live_grp, sA, sZero, astride, AOps<FMT, RG>{}, true,
-                                                 acc);
+    for (int64_t i = 0; i < total; ++i) {
+        // slot i's DMAs are done once at most the later issued slots' remain
+        const int64_t later = total - 1 - i < R - 2 ? total - 1 - i : R - 2;
+        wait_vmcnt_dyn((int)later * ops);
+        const unsigned char *slot = ring + (i % R) * SLOT;
+        const uint32_t *ms = (const uint32_t *)(slot + Gm::CODEB);
+        const uint32_t *mz = (const uint32_t *)(slot + Gm::CODEB + Gm::NSD * 256);
+        // refill the slot consumed in the previous iteration (its reads are done)
+        if (i + R - 1 < total) issue((int)((i + R - 1) % R));
+        const bool tile_ok = ctile < ntiles;
+        const int ssub = (csl * sbc) & 3;            // nonzero only for windows under a dword
+        const int zsub = ((FMT == FMT_U4) ? ((csl * bps) >> 1) : csl * bps) & 3;
+        const uint32_t *msn = ms + n * mds;
+        const uint32_t *mzn = mz + n * mdz;
+#pragma unroll
+        for (int s = 0; s < SS; ++s) {
+            const int j = 4 * s + g;                 // chunk within the slot
+            const int cg = csl * CS + j;             // chunk within the column
+            const bool valid = tile_ok && csl * CS + 4 * s < nch;
+            const int c = cg < nch ? cg : nch - 1;
+            const u4v w = *(const u4v *)(slot + (n / Gm::CPD) * Gm::DSTRIDE +
+                                         ((n % Gm::CPD) * CS + (j ^ (n % CS))) * 16);
+            MetaRaw<H> m;
+            const int sb = sbyte[s] + ssub;
+            const uint32_t dw = msn[sb >> 2];
+            if constexpr (SB == 4 || (FMT == FMT_U4 && H == 2)) m.v[0] = dw;  // aligned dword
+            else m.v[0] = (dw >> (8 * (sb & 3))) & 0xFFFFu;
+            m.v[1] = 0u;
+            if constexpr (ZPP) {
+                const int zb = zbyte[s] + zsub;
+                m.v[1] = (mzn[zb >> 2] >> (8 * (zb & 3))) & 0xFFu;
             }
+            mfma_step<FMT, ACT, RG, H, true>(a, w, m, c, ar, a_live_grp, sA, sZero, astride, AOps<FMT, RG>{},
+                                             valid, acc);
         }
-        finish_tile<ACT, RG>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, n);
+        if (++csl == nslots) {
+            finish_tile<ACT, RG>(a, acc, nullptr, wave, lane, 1, 0, g, tile_ok, ctile * 16 + n);
+#pragma unroll
+            for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
+            csl = 0;
+            ctile += nw;
+        }
     }
 }
 
@@ -698,12 +730,14 @@ constexpr int ring_depth_with_a() {
     return (MfFmt<FMT>::MF == 2 && RG <= 3) ? 4 : ((MfFmt<FMT>::MF == 4 && RG == 4) ? 1 : 2);
 }
 
-// Depth with staged activations: variant bit 3 asks for 8 slots, which one row group
-// with one scale block per chunk affords; larger tiles take 4 (2 for three or four row
-// groups with two scale blocks per chunk), the most that fit without spilling.
-template <int RG, int H>
+// Depth with staged activations: variant bit 3 asks for 8 slots, which tiles of one or
+// two row groups with one scale block per chunk afford (not one row group of a 32-k
+// chunk format, whose decode constants take the room); the rest take 4 (2 for three or
+// four row groups with two scale blocks per chunk), the most that fit without spilling.
+template <int FMT, int RG, int H>
 constexpr int ring_depth_staged(bool deep) {
-    return (RG <= 2 && H == 1) ? (deep ? 8 : 4) : ((RG <= 2 || H == 1) ? 4 : 2);
+    return (RG <= 2 && H == 1 && !(MfFmt<FMT>::MF == 4 && RG == 1)) ? (deep ? 8 : 4)
+                                                                     : ((RG <= 2 || H == 1) ? 4 : 2);
 }
 
 // register-ring depth (ring_depth_staged / ring_depth_with_a); 8-wave workgroups
@@ -711,7 +745,7 @@ template <int FMT, int ACT, int RG, int H, bool LDSA>
 hipError_t go(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.waves_per_wg != 8) return hipErrorInvalidValue;
     if constexpr (LDSA) {
-        constexpr int PD = ring_depth_staged<RG, H>(true), PS = ring_depth_staged<RG, H>(false);
+        constexpr int PD = ring_depth_staged<FMT, RG, H>(true), PS = ring_depth_staged<FMT, RG, H>(false);
         return ((cfg.variant >> 3) & 1) ? go_p<FMT, ACT, RG, H, LDSA, PD>(cfg, a, s)
                                         : go_p<FMT, ACT, RG, H, LDSA, PS>(cfg, a, s);
     } else {
@@ -719,35 +753,41 @@ hipError_t go(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     }
 }
 
-template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int NW>
-hipError_t go_ring_nw(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    auto kern = k_mfma_ring<FMT, ACT, RG, H, ZPP, R, NW>;
+template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int SS>
+hipError_t go_dma_rs(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    auto kern = k_mfma_dma<FMT, ACT, RG, H, ZPP, R, SS>;
     if (cfg.lds_bytes > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(64u * NW), (size_t)cfg.lds_bytes, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }
 
-// ring depth (bit 2 of the variant: 0 -> 4 slots, 1 -> 8 slots); the ring runs
-// without a K split, always with 8-wave workgroups
+// DMA ring shape from variant bits 4..5: 0 -> 4-step slots x 3, 1 -> 2-step slots x 5,
+// 2 -> 2-step slots x 4; one or two row groups only
 template <int FMT, int ACT, int RG, int H, bool ZPP>
-hipError_t go_ring(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+hipError_t go_dma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.waves_per_wg != 8 || cfg.ksplit != 1) return hipErrorInvalidValue;
-    // two scale blocks per chunk (and zero points) do not fit an 8-slot ring's registers
-    constexpr int RD = (H == 2 && ZPP) ? 4 : 8;
-    return ((cfg.variant >> 2) & 1) ? go_ring_nw<FMT, ACT, RG, H, ZPP, RD, 8>(cfg, a, s)
-                                    : go_ring_nw<FMT, ACT, RG, H, ZPP, 4, 8>(cfg, a, s);
+    if constexpr (RG <= 2) {
+        switch ((cfg.variant >> 4) & 3) {
+        case 0: return go_dma_rs<FMT, ACT, RG, H, ZPP, 3, 4>(cfg, a, s);
+        case 1: return go_dma_rs<FMT, ACT, RG, H, ZPP, 5, 2>(cfg, a, s);
+        case 2: return go_dma_rs<FMT, ACT, RG, H, ZPP, 4, 2>(cfg, a, s);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
 }
 
 template <int FMT, int ACT, int RG, int H>
 hipError_t pick_lds(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.variant & 2) {
         if constexpr (FMT == FMT_U4 || FMT == FMT_U8)
-            return a.zp ? go_ring<FMT, ACT, RG, H, true>(cfg, a, s) : go_ring<FMT, ACT, RG, H, false>(cfg, a, s);
+            return a.zp ? go_dma<FMT, ACT, RG, H, true>(cfg, a, s) : go_dma<FMT, ACT, RG, H, false>(cfg, a, s);
         else
-            return go_ring<FMT, ACT, RG, H, false>(cfg, a, s);
+            return go_dma<FMT, ACT, RG, H, false>(cfg, a, s);
     }
     return (cfg.variant & 1) ? go<FMT, ACT, RG, H, true>(cfg, a, s) : go<FMT, ACT, RG, H, false>(cfg, a, s);
 }

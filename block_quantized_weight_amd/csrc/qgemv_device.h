@@ -86,6 +86,12 @@ __device__ __forceinline__ uint32_t small_int_bf16_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, WORD));
 }
 
+// (x & mask) | bits in one v_bitop3 (truth table 0xEA: bit i is the result for
+// inputs x = i>>2 & 1, mask = i>>1 & 1, bits = i & 1).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    return __builtin_amdgcn_bitop3_b32(x, mask, bits, 0xEA);
+}
+
 template <int ACT>
 __device__ __forceinline__ void store_out(void *Y, int64_t idx, float v) {
     if constexpr (ACT == ACT_F16) {
@@ -130,6 +136,24 @@ __device__ __forceinline__ ZSel zsel(const void *zp, uint32_t midpoint) {
     uint32_t keep = zp ? 0xFFFFFFFFu : 0u;
     asm volatile("" : "+v"(keep));
     return ZSel{keep, ~keep & midpoint};
+}
+
+// The same wait for a count known only at run time (uniform); counts above 31 wait
+// for everything.
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    switch (n) {
+#define QGEMV_WAIT_CASE(k) \
+    case k: wait_vmcnt<k>(); break;
+        QGEMV_WAIT_CASE(1) QGEMV_WAIT_CASE(2) QGEMV_WAIT_CASE(3) QGEMV_WAIT_CASE(4) QGEMV_WAIT_CASE(5)
+        QGEMV_WAIT_CASE(6) QGEMV_WAIT_CASE(7) QGEMV_WAIT_CASE(8) QGEMV_WAIT_CASE(9) QGEMV_WAIT_CASE(10)
+        QGEMV_WAIT_CASE(11) QGEMV_WAIT_CASE(12) QGEMV_WAIT_CASE(13) QGEMV_WAIT_CASE(14) QGEMV_WAIT_CASE(15)
+        QGEMV_WAIT_CASE(16) QGEMV_WAIT_CASE(17) QGEMV_WAIT_CASE(18) QGEMV_WAIT_CASE(19) QGEMV_WAIT_CASE(20)
+        QGEMV_WAIT_CASE(21) QGEMV_WAIT_CASE(22) QGEMV_WAIT_CASE(23) QGEMV_WAIT_CASE(24) QGEMV_WAIT_CASE(25)
+        QGEMV_WAIT_CASE(26) QGEMV_WAIT_CASE(27) QGEMV_WAIT_CASE(28) QGEMV_WAIT_CASE(29) QGEMV_WAIT_CASE(30)
+        QGEMV_WAIT_CASE(31)
+#undef QGEMV_WAIT_CASE
+    default: wait_vmcnt<0>(); break;
+    }
 }
 
 typedef __attribute__((address_space(3))) void lds_void;

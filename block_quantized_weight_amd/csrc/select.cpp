@@ -76,20 +76,37 @@ static bool mfma_shape_ok(const qgemv_desc *d) {
     return true;
 }
 
-// The LDS DMA ring copies whole dwords of the scale and zero-point arrays; they must
-// be 4-byte aligned and a whole number of dwords long so no copy leaves them.
-static bool meta_dwords_ok(const qgemv_desc *d) {
+// DMA-ring shape for the matrix family: 0 = 4-step slots x 3, 1 = 2-step slots x 5,
+// 2 = 2-step slots x 4 (the first that fits in LDS next to abytes of staged
+// activations), or -1 when the ring cannot take the problem: the scale (and zero-point)
+// rows must be whole dwords on 4-byte aligned arrays, a slot must hold whole blocks,
+// and a 4-bit slot at least two, so its zero points fill whole bytes. lds_out gets
+// the LDS bytes.
+static int dma_ring_shape(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t *lds_out) {
+    const int kpc = k_per_chunk(d->format);
     const int64_t nblk = d->K / d->block_size;
-    int64_t sbytes;
-    if (d->format == QGEMV_FMT_FP8) sbytes = d->N * nblk * 4;
-    else if (d->format == QGEMV_FMT_NVFP4) sbytes = d->N * (d->K / 16);
-    else sbytes = d->N * nblk * 2;
-    if ((uintptr_t)d->scales % 4 || sbytes % 4) return false;
-    if (d->zero_points) {
-        const int64_t zbytes = d->format == QGEMV_FMT_U4 ? d->N * ((nblk + 1) / 2) : d->N * nblk;
-        if ((uintptr_t)d->zero_points % 4 || zbytes % 4) return false;
+    const int sb = d->format == QGEMV_FMT_FP8 ? 4 : (d->format == QGEMV_FMT_NVFP4 ? 1 : 2);
+    if ((nblk * sb) % 4 || (uintptr_t)d->scales % 4) return -1;
+    if (zpp) {
+        const int64_t zrow = d->format == QGEMV_FMT_U4 ? (nblk + 1) / 2 : nblk;
+        if (zrow % 4 || (uintptr_t)d->zero_points % 4) return -1;
     }
-    return true;
+    // (steps per slot, slots); shallower rings measured slower than the register ring
+    static const int shapes[3][2] = {{4, 3}, {2, 5}, {2, 4}};
+    for (int i = 0; i < 3; ++i) {
+        const int ss = shapes[i][0], r = shapes[i][1];
+        if (4 * ss * kpc < d->block_size) continue;  // a slot holds whole blocks
+        if (d->format == QGEMV_FMT_U4 && (4 * ss * kpc) / d->block_size < 2) continue;
+        const int codeb = ss == 4 ? 4 * 1024 : 2 * 1152;
+        const int nsd = d->format == QGEMV_FMT_U8 ? (ss == 4 ? 2 : 1) : (ss == 4 ? 4 : 2);
+        const int64_t slot = codeb + 256 * nsd + (zpp ? 256 : 0);
+        const int64_t lds = abytes + 8 * r * slot;
+        if (lds <= kLdsBytes) {
+            *lds_out = (int32_t)lds;
+            return i;
+        }
+    }
+    return -1;
 }
 
 // Waves that share one 16-column tile's K range. Chosen from N and K only so that
@@ -214,30 +231,24 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
         const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
         const int64_t lds_a = (int64_t)M * (d->K + 8) * 2;
-        // LDS DMA ring: 8 waves, 8 (or 4) slots each of one KiB of codes plus 256 B per
-        // block-metadata dword stream; only without a K split
-        const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
-        const int64_t slot = 1024 + 256 * (zpp ? 2 : 1);
+        // DMA ring (no K split, one or two row groups, metadata rows in whole dwords):
+        // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
+        // fits in LDS next to the staged activations.
         const int64_t abytes16 = 16 + ((lds_a + 15) & ~15LL);  // zero block + staged rows
-        const bool ring_ok = c.ksplit == 1 && meta_dwords_ok(d) && abytes16 + 8 * 4 * slot <= kLdsBytes;
-        bool ring = ring_ok && M <= 8 && groups > cu_count;
-        if (flags & QGEMV_FLAG_RING_ON) ring = ring_ok;
+        const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
+        const int ring_shape = dma_ring_shape(d, abytes16, zpp, &c.lds_bytes);
+        bool ring = c.ksplit == 1 && rg <= 2 && ring_shape >= 0 && groups > cu_count;
+        if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && rg <= 2 && ring_shape >= 0;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {
-            // 8 slots when they fit (not for 16-wide 4-bit blocks with zero points,
-            // whose registers take only 4)
-            const bool deep = abytes16 + 8 * 8 * slot <= kLdsBytes &&
-                              !(zpp && d->format == QGEMV_FMT_U4 && d->block_size == 16);
             c.waves_per_wg = 8;
-            c.variant = 2 | (deep ? 4 : 0);
-            c.lds_bytes = (int)(abytes16 + 8 * (deep ? 8 : 4) * slot);
-            int64_t per_cu = kLdsBytes / c.lds_bytes;
-            if (per_cu < 1) per_cu = 1;
-            if (per_cu > 4) per_cu = 4;
-            c.grid = groups < per_cu * cu_count ? groups : per_cu * cu_count;
+            c.variant = 2 | (ring_shape << 4);
+            const int64_t wgs = (tiles + 7) / 8;
+            c.grid = wgs < cu_count ? wgs : cu_count;
             *out = c;
             return QGEMV_OK;
         }
+        c.lds_bytes = 0;
         // Stage the activations in LDS when they fit and every wave has enough K steps
         // per tile (8 or more) to amortize the copy; with fewer, the activations travel
         // with the codes in the register ring instead.

@@ -85,10 +85,14 @@ FMT_CASES = [("u4", "f16", 32), ("u4", "bf16", 32), ("u4", "f16", 16), ("u4", "b
              ("fp8", "f16", 128), ("fp8", "bf16", 32), ("nvfp4", "bf16", 16), ("nvfp4", "f16", 16)]
 
 
-def meta_whole_dwords(prob):
-    """The LDS DMA ring copies whole dwords of the scale / zero-point arrays, so the
-    dispatcher takes it only when those arrays are a whole number of dwords."""
-    return prob.scales.nbytes % 4 == 0 and (prob.zp is None or prob.zp.nbytes % 4 == 0)
+def ring_eligible(prob, M):
+    """The DMA ring copies each column's metadata window as whole dwords, so the
+    dispatcher takes it only when every scale (and zero-point) row is a whole number
+    of dwords, and only for one or two row groups (M <= 8)."""
+    nblk = prob.K // prob.bs
+    sb = {"u4": 2, "u8": 2, "fp8": 4, "nvfp4": 1}[prob.fmt]
+    zrow = 0 if prob.zp is None else ((nblk + 1) // 2 if prob.fmt == "u4" else nblk)
+    return M <= 8 and (nblk * sb) % 4 == 0 and zrow % 4 == 0
 
 
 def mfma_supports(fmt, act):
@@ -111,8 +115,8 @@ def test_families_ragged_shapes(family, fmt, act, bs):
             assert plan["family"] == family.split("_")[0]
         if family == "mfma_lds":
             assert plan["variant"] & 1
-        if family == "mfma_ring" and meta_whole_dwords(prob):
-            assert plan["variant"] & 2
+        if family == "mfma_ring" and ring_eligible(prob, M):
+            assert plan["variant"] & 2, plan
         ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
         assert ok, (family, fmt, act, bs, N, K, M, ratio, plan)
 
