@@ -34,6 +34,7 @@ FLAG_STREAM_UNR_SHIFT = 23
 FLAG_STREAM_WPC_SHIFT = 25
 FLAG_STREAM_CLASSIC = 0x10000000
 FLAG_MFMA_DEPTH_SHIFT = 29
+FLAG_STREAM_WIDE_WG = 0x80000000
 MAX_M = 16
 
 _lock = threading.Lock()

@@ -70,19 +70,31 @@ struct ChunkOps<FMT_U4, ACT_F16, H> {
         }
     }
 
+    // decoded operand words of a chunk (exact), shared by every row of a tile
+    static constexpr int NWD = 16;
+    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t wv = w[d], w8 = w[d] >> 8;
+            wd[4 * d + 0] = wv & 0x000F000Fu;
+            wd[4 * d + 1] = w8 & 0x000F000Fu;
+            wd[4 * d + 2] = wv & 0x00F000F0u;
+            wd[4 * d + 3] = w8 & 0x00F000F0u;
+        }
+    }
+
     // sum_k a_k q_k per half
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[H]) {
+    __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[H]) {
         float lo[H], hi[H];
 #pragma unroll
         for (int i = 0; i < H; ++i) lo[i] = hi[i] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int i = (H == 2) ? (d >> 1) : 0;
-            const uint32_t wv = w[d], w8 = w[d] >> 8;
-            lo[i] = dot2<ACT_F16>(wv & 0x000F000Fu, h.p[4 * d + 0], lo[i]);
-            lo[i] = dot2<ACT_F16>(w8 & 0x000F000Fu, h.p[4 * d + 1], lo[i]);
-            hi[i] = dot2<ACT_F16>(wv & 0x00F000F0u, h.p[4 * d + 2], hi[i]);
-            hi[i] = dot2<ACT_F16>(w8 & 0x00F000F0u, h.p[4 * d + 3], hi[i]);
+            lo[i] = dot2<ACT_F16>(wd[4 * d + 0], h.p[4 * d + 0], lo[i]);
+            lo[i] = dot2<ACT_F16>(wd[4 * d + 1], h.p[4 * d + 1], lo[i]);
+            hi[i] = dot2<ACT_F16>(wd[4 * d + 2], h.p[4 * d + 2], hi[i]);
+            hi[i] = dot2<ACT_F16>(wd[4 * d + 3], h.p[4 * d + 3], hi[i]);
         }
 #pragma unroll
         for (int i = 0; i < H; ++i) out[i] = __builtin_fmaf(hi[i], 0.0625f, lo[i]) * 16777216.0f;
@@ -116,20 +128,29 @@ struct ChunkOps<FMT_U4, ACT_BF16, H> {
         }
     }
 
-    // sum_k a_k (128 + q_k) per half
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[H]) {
+    static constexpr int NWD = 16;
+    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
         constexpr uint32_t MAGIC = 0x43004300u;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t wv = w[d];
+            wd[4 * d + 0] = and_or(wv, 0x000F000Fu, MAGIC);
+            wd[4 * d + 1] = and_or(wv >> 8, 0x000F000Fu, MAGIC);
+            wd[4 * d + 2] = and_or(wv >> 4, 0x000F000Fu, MAGIC);
+            wd[4 * d + 3] = and_or(wv >> 12, 0x000F000Fu, MAGIC);
+        }
+    }
+
+    // sum_k a_k (128 + q_k) per half
+    __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[H]) {
         float s[H];
 #pragma unroll
         for (int i = 0; i < H; ++i) s[i] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int i = (H == 2) ? (d >> 1) : 0;
-            const uint32_t wv = w[d];
-            s[i] = dot2<ACT_BF16>(and_or(wv, 0x000F000Fu, MAGIC), h.p[4 * d + 0], s[i]);
-            s[i] = dot2<ACT_BF16>(and_or(wv >> 8, 0x000F000Fu, MAGIC), h.p[4 * d + 1], s[i]);
-            s[i] = dot2<ACT_BF16>(and_or(wv >> 4, 0x000F000Fu, MAGIC), h.p[4 * d + 2], s[i]);
-            s[i] = dot2<ACT_BF16>(and_or(wv >> 12, 0x000F000Fu, MAGIC), h.p[4 * d + 3], s[i]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s[i] = dot2<ACT_BF16>(wd[4 * d + k], h.p[4 * d + k], s[i]);
         }
 #pragma unroll
         for (int i = 0; i < H; ++i) out[i] = s[i];
@@ -150,13 +171,19 @@ struct ChunkOps<FMT_U8, ACT_F16, H> {
         h.asum[0] = sum_pairs<ACT_F16>(x, 8);
     }
 
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[1]) {
-        float s = 0.0f;
+    static constexpr int NWD = 8;
+    __device__ static void decode(const u4v &w, uint32_t wd[8]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            s = dot2<ACT_F16>(perm(0u, w[d], 0x0C010C00u), h.p[2 * d], s);
-            s = dot2<ACT_F16>(perm(0u, w[d], 0x0C030C02u), h.p[2 * d + 1], s);
+            wd[2 * d] = perm(0u, w[d], 0x0C010C00u);
+            wd[2 * d + 1] = perm(0u, w[d], 0x0C030C02u);
         }
+    }
+
+    __device__ static void dotd(const uint32_t wd[8], const ChunkAct &h, float out[1]) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = dot2<ACT_F16>(wd[i], h.p[i], s);
         out[0] = s * 16777216.0f;
     }
 };
@@ -174,7 +201,19 @@ struct ChunkOps<FMT_U8, ACT_BF16, H> {
         h.asum[0] = sum_pairs<ACT_BF16>(x, 8);
     }
 
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[1]) {
+    // decoded words: the 16 bytes as float bits
+    static constexpr int NWD = 16;
+    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            wd[4 * d + 0] = __builtin_bit_cast(uint32_t, (float)(w[d] & 0xFFu));
+            wd[4 * d + 1] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 8) & 0xFFu));
+            wd[4 * d + 2] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 16) & 0xFFu));
+            wd[4 * d + 3] = __builtin_bit_cast(uint32_t, (float)(w[d] >> 24));
+        }
+    }
+
+    __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[1]) {
         float s = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -182,10 +221,10 @@ struct ChunkOps<FMT_U8, ACT_BF16, H> {
             const float a1 = __builtin_bit_cast(float, h.p[2 * d] & 0xFFFF0000u);
             const float a2 = __builtin_bit_cast(float, h.p[2 * d + 1] << 16);
             const float a3 = __builtin_bit_cast(float, h.p[2 * d + 1] & 0xFFFF0000u);
-            s = __builtin_fmaf(a0, (float)(w[d] & 0xFFu), s);
-            s = __builtin_fmaf(a1, (float)((w[d] >> 8) & 0xFFu), s);
-            s = __builtin_fmaf(a2, (float)((w[d] >> 16) & 0xFFu), s);
-            s = __builtin_fmaf(a3, (float)(w[d] >> 24), s);
+            s = __builtin_fmaf(a0, __builtin_bit_cast(float, wd[4 * d + 0]), s);
+            s = __builtin_fmaf(a1, __builtin_bit_cast(float, wd[4 * d + 1]), s);
+            s = __builtin_fmaf(a2, __builtin_bit_cast(float, wd[4 * d + 2]), s);
+            s = __builtin_fmaf(a3, __builtin_bit_cast(float, wd[4 * d + 3]), s);
         }
         out[0] = s;
     }
@@ -203,13 +242,19 @@ struct ChunkOps<FMT_FP8, ACT, H> {
         for (int i = 0; i < 8; ++i) h.p[i] = x[i];
     }
 
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[1]) {
-        float s = 0.0f;
+    static constexpr int NWD = 8;
+    __device__ static void decode(const u4v &w, uint32_t wd[8]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            s = dot2<ACT>(fp8_pair<ACT, false>(w[d]), h.p[2 * d], s);
-            s = dot2<ACT>(fp8_pair<ACT, true>(w[d]), h.p[2 * d + 1], s);
+            wd[2 * d] = fp8_pair<ACT, false>(w[d]);
+            wd[2 * d + 1] = fp8_pair<ACT, true>(w[d]);
         }
+    }
+
+    __device__ static void dotd(const uint32_t wd[8], const ChunkAct &h, float out[1]) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = dot2<ACT>(wd[i], h.p[i], s);
         out[0] = s;
     }
 };
@@ -226,20 +271,40 @@ struct ChunkOps<FMT_NVFP4, ACT, H> {
         for (int i = 0; i < 16; ++i) h.p[i] = x[i];
     }
 
-    __device__ static void dot(const u4v &w, const ChunkAct &h, float out[2]) {
+    static constexpr int NWD = 16;
+    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            wd[4 * d + 0] = fp4_pair<ACT, 0>(w[d]);
+            wd[4 * d + 1] = fp4_pair<ACT, 1>(w[d]);
+            wd[4 * d + 2] = fp4_pair<ACT, 2>(w[d]);
+            wd[4 * d + 3] = fp4_pair<ACT, 3>(w[d]);
+        }
+    }
+
+    __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[2]) {
         float s[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int i = d >> 1;
-            s[i] = dot2<ACT>(fp4_pair<ACT, 0>(w[d]), h.p[4 * d + 0], s[i]);
-            s[i] = dot2<ACT>(fp4_pair<ACT, 1>(w[d]), h.p[4 * d + 1], s[i]);
-            s[i] = dot2<ACT>(fp4_pair<ACT, 2>(w[d]), h.p[4 * d + 2], s[i]);
-            s[i] = dot2<ACT>(fp4_pair<ACT, 3>(w[d]), h.p[4 * d + 3], s[i]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s[i] = dot2<ACT>(wd[4 * d + k], h.p[4 * d + k], s[i]);
         }
         out[0] = s[0];
         out[1] = s[1];
     }
 };
+
+// sum over a chunk (per half) of activations times decoded codes: decode, then the
+// dot products in the format's fixed order. Splitting the two lets a tile of rows
+// share one decode without changing any row's arithmetic.
+template <int FMT, int ACT, int H>
+__device__ __forceinline__ void chunk_dot(const u4v &w, const ChunkAct &h, float out[H]) {
+    using Ops = ChunkOps<FMT, ACT, H>;
+    uint32_t wd[Ops::NWD];
+    Ops::decode(w, wd);
+    Ops::dotd(wd, h, out);
+}
 
 // ----------------------------------------------------------------------------------
 // Per-column pointers, computed once per wave, and the block metadata of a chunk.

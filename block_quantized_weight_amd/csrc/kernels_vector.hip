@@ -95,10 +95,12 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
+                    uint32_t wd[Ops::NWD];
+                    Ops::decode(w[u][i], wd);  // once per chunk, shared by the rows
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         float part[H];
-                        Ops::dot(w[u][i], act[m], part);
+                        Ops::dotd(wd, act[m], part);
 #pragma unroll
                         for (int h = 0; h < H; ++h) {
                             float v = part[h];
@@ -122,20 +124,20 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 }
 
 // ----------------------------------------------------------------------------------
-// Persistent one-row streaming kernel (M = 1).
+// Persistent streaming kernel for MT = 1, 2 or 4 rows in one pass.
 //
 // The same per-row arithmetic as k_stream (same lanes per chunk, same chunk order per
 // lane, same decode, zero-point and scale steps, same wave reduction), so results are
 // bit-identical to it; what differs is how the latency is covered:
-//  - the activation row is staged once per workgroup in LDS, already in the decode's
-//    pair order and laid out so that the 64 lanes of a wave read consecutive 16-byte
-//    pieces, together with sum(a) of every chunk (half);
+//  - the activation rows are staged once per workgroup in LDS, already in the
+//    decode's pair order and laid out so that the 64 lanes of a wave read consecutive
+//    16-byte pieces, together with sum(a) of every chunk (half);
 //  - each wave walks column groups g = wave, wave + nwaves, ... and the batches of one
 //    group (UNR chunks per lane of each of its CPW columns); the codes and raw block
 //    metadata of the next batch are in flight while the current one is computed
-//    (two register buffers, the loop unrolled by two);
-//  - every load is issued for a clamped, valid chunk index, so the loads never
-//    diverge; a chunk past the end of K is simply not accumulated.
+//    (two register buffers); a chunk's codes are decoded once for all rows;
+//  - no load and no use sits behind a branch (clamped indexes, selected updates), so
+//    the compiler's wait before a batch leaves the other batch in flight.
 
 template <int FMT, int H, int UNR, int CPW>
 struct SBatch {
@@ -143,28 +145,31 @@ struct SBatch {
     MetaS<H> m[UNR][CPW];
 };
 
-// Index (in 16-byte pieces) of piece q of chunk c of the staged activation row.
+// Index (in 16-byte pieces) of piece q of chunk c of a staged activation row.
 template <int NQ>
 __device__ __forceinline__ int stage_index(int c, int q) {
     return (((c >> 6) * NQ + q) << 6) + (c & 63);
 }
 
-// Stage the activation row: each thread prepares chunks c, c + blockDim, ... two at a
-// time, with both chunks' loads issued before either is used.
+// Stage the M activation rows: each thread prepares chunks c, c + blockDim, ... of
+// every row, two at a time, with both chunks' loads issued before either is used.
+// Row m's pieces start at sP + m * rowq, its chunk sums at sS + m * rows.
 template <int FMT, int ACT, int H>
-__device__ __forceinline__ void stage_row(const KArgs &a, u4v *sP, float *sS) {
+__device__ __forceinline__ void stage_rows(const KArgs &a, u4v *sP, float *sS, int rowq, int rows) {
     using Ops = ChunkOps<FMT, ACT, H>;
     constexpr int NQ = Ops::ND / 4;
     constexpr int SB = 2;
     const uint16_t *A16 = (const uint16_t *)a.A;
     const int nch = (int)a.nchunks;
-    for (int c0 = threadIdx.x; c0 < nch; c0 += SB * (int)blockDim.x) {
+    const int items = a.M * nch;
+    for (int i0 = threadIdx.x; i0 < items; i0 += SB * (int)blockDim.x) {
         uint32_t x[SB][Ops::ND];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            int c = c0 + j * (int)blockDim.x;
-            c = c < nch ? c : nch - 1;
-            const uint16_t *ap = A16 + (uint32_t)c * (uint32_t)Ops::KPC;
+            int it = i0 + j * (int)blockDim.x;
+            it = it < items ? it : items - 1;
+            const int m = it / nch, c = it - (it / nch) * nch;
+            const uint16_t *ap = A16 + (int64_t)m * a.K + (uint32_t)c * (uint32_t)Ops::KPC;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const u4v v = load16(ap + 8 * q);
@@ -173,24 +178,26 @@ __device__ __forceinline__ void stage_row(const KArgs &a, u4v *sP, float *sS) {
         }
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            const int c = c0 + j * (int)blockDim.x;
-            if (c < nch) {
+            const int it = i0 + j * (int)blockDim.x;
+            if (it < items) {
+                const int m = it / nch, c = it - (it / nch) * nch;
                 ChunkAct act;
                 Ops::prep(x[j], act);
 #pragma unroll
                 for (int q = 0; q < NQ; ++q)
-                    sP[stage_index<NQ>(c, q)] = u4v{act.p[4 * q], act.p[4 * q + 1], act.p[4 * q + 2], act.p[4 * q + 3]};
+                    sP[m * rowq + stage_index<NQ>(c, q)] =
+                        u4v{act.p[4 * q], act.p[4 * q + 1], act.p[4 * q + 2], act.p[4 * q + 3]};
                 if constexpr (FMT == FMT_U4 || FMT == FMT_U8) {
 #pragma unroll
-                    for (int h = 0; h < H; ++h) sS[c * H + h] = act.asum[h];
+                    for (int h = 0; h < H; ++h) sS[m * rows + c * H + h] = act.asum[h];
                 }
             }
         }
     }
 }
 
-template <int FMT, int ACT, int CPW, int UNR, int H>
-__global__ void __launch_bounds__(256) k_stream1(KArgs a) {
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
+__global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     using Ops = ChunkOps<FMT, ACT, H>;
     using B = SBatch<FMT, H, UNR, CPW>;
     constexpr bool ZP = (FMT == FMT_U4 || FMT == FMT_U8);
@@ -201,8 +208,10 @@ __global__ void __launch_bounds__(256) k_stream1(KArgs a) {
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = (int)a.nchunks;
     const int nch64 = (nch + 63) & ~63;
+    const int rowq = nch64 * NQ;          // 16-byte pieces per staged row
+    const int rows = nch64 * H;           // chunk sums per staged row
     u4v *sP = (u4v *)smem;
-    float *sS = (float *)(smem + (size_t)nch64 * Ops::ND * 4);
+    float *sS = (float *)(smem + (size_t)MT * rowq * 16);
     const int64_t ngroups = (a.N + CPW - 1) / CPW;
     const int rounds = (nch + 64 * UNR - 1) / (64 * UNR);
     const int mine = gw < ngroups ? (int)((ngroups - gw + nw - 1) / nw) : 0;
@@ -242,9 +251,11 @@ __global__ void __launch_bounds__(256) k_stream1(KArgs a) {
     // consume cursor and the accumulators of the group being computed
     int64_t cg = gw;
     int cr = 0;
-    float acc[CPW];
+    float acc[CPW][MT];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
     // branch-free: a chunk past the end is computed on the clamped chunk and its
     // update of the accumulator is discarded by a select (acc keeps its bits)
     auto consume = [&](const B &b) {
@@ -253,42 +264,89 @@ __global__ void __launch_bounds__(256) k_stream1(KArgs a) {
             const int c = cr * (64 * UNR) + 64 * u + lane;
             const bool valid = c < nch;
             const int cc = valid ? c : nch - 1;
-            ChunkAct act;
+            if constexpr (MT == 1) {
+                // one row: the activations are read once and each column's codes are
+                // decoded right before their dot products
+                ChunkAct act;
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const u4v v = sP[stage_index<NQ>(cc, q)];
-                act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
-            }
-            if constexpr (ZP) {
-#pragma unroll
-                for (int h = 0; h < H; ++h) act.asum[h] = sS[cc * H + h];
-            }
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                float sc[H], zr[H], part[H];
-                meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc, zr);
-                Ops::dot(b.w[u][i], act, part);
-                float t = acc[i];
-#pragma unroll
-                for (int h = 0; h < H; ++h) {
-                    float v = part[h];
-                    if constexpr (ZP) v = __builtin_fmaf(-zr[h], act.asum[h], v);
-                    t = __builtin_fmaf(sc[h], v, t);
+                for (int q = 0; q < NQ; ++q) {
+                    const u4v v = sP[stage_index<NQ>(cc, q)];
+                    act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
                 }
-                acc[i] = valid ? t : acc[i];
+                if constexpr (ZP) {
+#pragma unroll
+                    for (int h = 0; h < H; ++h) act.asum[h] = sS[cc * H + h];
+                }
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    float sc[H], zr[H], part[H];
+                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc, zr);
+                    chunk_dot<FMT, ACT, H>(b.w[u][i], act, part);
+                    float t = acc[i][0];
+#pragma unroll
+                    for (int h = 0; h < H; ++h) {
+                        float v = part[h];
+                        if constexpr (ZP) v = __builtin_fmaf(-zr[h], act.asum[h], v);
+                        t = __builtin_fmaf(sc[h], v, t);
+                    }
+                    acc[i][0] = valid ? t : acc[i][0];
+                }
+            } else {
+                // several rows: every column's codes are decoded once and shared
+                uint32_t wd[CPW][Ops::NWD];
+                float sc[CPW][H], zr[CPW][H];
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    Ops::decode(b.w[u][i], wd[i]);
+                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc[i], zr[i]);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m >= a.M) break;  // uniform; no memory operation is skipped
+                    ChunkAct act;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const u4v v = sP[m * rowq + stage_index<NQ>(cc, q)];
+                        act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
+                    }
+                    if constexpr (ZP) {
+#pragma unroll
+                        for (int h = 0; h < H; ++h) act.asum[h] = sS[m * rows + cc * H + h];
+                    }
+#pragma unroll
+                    for (int i = 0; i < CPW; ++i) {
+                        float part[H];
+                        Ops::dotd(wd[i], act, part);
+                        float t = acc[i][m];
+#pragma unroll
+                        for (int h = 0; h < H; ++h) {
+                            float v = part[h];
+                            if constexpr (ZP) v = __builtin_fmaf(-zr[i][h], act.asum[h], v);
+                            t = __builtin_fmaf(sc[i][h], v, t);
+                        }
+                        acc[i][m] = valid ? t : acc[i][m];
+                    }
+                }
             }
         }
         // the batch's accumulation completes here (nothing of it may sink below the
         // next refill of this buffer); emits no instruction
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) asm volatile("" : "+v"(acc[i])::"memory");
+        for (int i = 0; i < CPW; ++i)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(acc[i][m])::"memory");
         if (++cr == rounds) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
                 const int64_t n = cg * CPW + i;
-                const float v = wave_sum(acc[i]) * a.tscale;
-                if (lane == 0 && n < a.N) store_out<ACT>(a.Y, n, v);
-                acc[i] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (MT == 1 || m < a.M) {
+                        const float v = wave_sum(acc[i][m]) * a.tscale;
+                        if (lane == 0 && n < a.N) store_out<ACT>(a.Y, (int64_t)m * a.N + n, v);
+                    }
+                    acc[i][m] = 0.0f;
+                }
             }
             cr = 0;
             cg += nw;
@@ -302,7 +360,7 @@ __global__ void __launch_bounds__(256) k_stream1(KArgs a) {
     // below the last use of the buffer's old contents.)
     B b0, b1;
     if (total > 0) issue(b0);  // the first batch's fetch overlaps the staging below
-    stage_row<FMT, ACT, H>(a, sP, sS);
+    stage_rows<FMT, ACT, H>(a, sP, sS, rowq, rows);
     __syncthreads();
     int i = 0;
     for (; i + 2 < total; i += 2) {
@@ -427,39 +485,72 @@ hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 
 // One-row persistent kernel: cols_per_wave 1/2/4; unroll 2/3/4 from variant bits 1..2
 // (2 -> 2, 3 -> 3, 0 -> 4).
-template <int FMT, int ACT, int CPW, int UNR>
-hipError_t go_stream1_h(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    const dim3 grid((unsigned)cfg.grid), block(256);
-    const size_t lds = (size_t)cfg.lds_bytes;
-    if constexpr (FMT == FMT_NVFP4) {
-        hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 2>), grid, block, lds, s, a);
-    } else if constexpr (FMT == FMT_U4) {
-        if (a.bs == 16)
-            hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 2>), grid, block, lds, s, a);
-        else
-            hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 1>), grid, block, lds, s, a);
-    } else {
-        hipLaunchKernelGGL((k_stream1<FMT, ACT, CPW, UNR, 1>), grid, block, lds, s, a);
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
+hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    auto kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG>;
+    if (cfg.lds_bytes > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
+        if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(64 * NWG), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }
 
-template <int FMT, int ACT, int CPW>
+// workgroups of 4 waves, or of 16 (one row, one column per wave) when variant bit 3
+// asks for them
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
+hipError_t go_stream1_k(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    if constexpr (MT == 1 && CPW == 1) {
+        if (cfg.waves_per_wg == 16) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+    }
+    if (cfg.waves_per_wg != 4) return hipErrorInvalidValue;
+    return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 4>(cfg, a, s);
+}
+
+template <int FMT, int ACT, int MT, int CPW, int UNR>
+hipError_t go_stream1_h(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    if constexpr (FMT == FMT_NVFP4) return go_stream1_k<FMT, ACT, MT, CPW, UNR, 2>(cfg, a, s);
+    else if constexpr (FMT == FMT_U4)
+        return a.bs == 16 ? go_stream1_k<FMT, ACT, MT, CPW, UNR, 2>(cfg, a, s)
+                          : go_stream1_k<FMT, ACT, MT, CPW, UNR, 1>(cfg, a, s);
+    else return go_stream1_k<FMT, ACT, MT, CPW, UNR, 1>(cfg, a, s);
+}
+
+// unroll 2/3/4 from variant bits 1..2 (2 -> 2, 3 -> 3, 0 -> 4) for one row; two or
+// four rows take 2 chunks per lane and 1 or 2 columns per wave
+template <int FMT, int ACT, int MT, int CPW>
 hipError_t go_stream1_u(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    switch ((cfg.variant >> 1) & 3) {
-    case 2: return go_stream1_h<FMT, ACT, CPW, 2>(cfg, a, s);
-    case 3: return go_stream1_h<FMT, ACT, CPW, 3>(cfg, a, s);
-    case 0: return go_stream1_h<FMT, ACT, CPW, 4>(cfg, a, s);
+    if constexpr (MT > 1) {
+        if (((cfg.variant >> 1) & 3) != 2) return hipErrorInvalidValue;
+        return go_stream1_h<FMT, ACT, MT, CPW, 2>(cfg, a, s);
+    } else {
+        switch ((cfg.variant >> 1) & 3) {
+        case 2: return go_stream1_h<FMT, ACT, MT, CPW, 2>(cfg, a, s);
+        case 3: return go_stream1_h<FMT, ACT, MT, CPW, 3>(cfg, a, s);
+        case 0: return go_stream1_h<FMT, ACT, MT, CPW, 4>(cfg, a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+}
+
+template <int FMT, int ACT, int MT>
+hipError_t go_stream1_c(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
+    switch (cfg.cols_per_wave) {
+    case 1: return go_stream1_u<FMT, ACT, MT, 1>(cfg, a, s);
+    case 2: return go_stream1_u<FMT, ACT, MT, 2>(cfg, a, s);
+    case 4:
+        if constexpr (MT == 1) return go_stream1_u<FMT, ACT, MT, 4>(cfg, a, s);
+        else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int FMT, int ACT>
 hipError_t go_stream1(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    switch (cfg.cols_per_wave) {
-    case 1: return go_stream1_u<FMT, ACT, 1>(cfg, a, s);
-    case 2: return go_stream1_u<FMT, ACT, 2>(cfg, a, s);
-    case 4: return go_stream1_u<FMT, ACT, 4>(cfg, a, s);
+    switch (cfg.rows_per_pass) {
+    case 1: return go_stream1_c<FMT, ACT, 1>(cfg, a, s);
+    case 2: return go_stream1_c<FMT, ACT, 2>(cfg, a, s);
+    case 4: return go_stream1_c<FMT, ACT, 4>(cfg, a, s);
     default: return hipErrorInvalidValue;
     }
 }

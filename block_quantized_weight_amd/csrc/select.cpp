@@ -37,7 +37,8 @@ int validate_desc(const qgemv_desc *d) {
     const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA |
                            QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
                            QGEMV_FLAG_RING_ON | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
-                           QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK;
+                           QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK |
+                           QGEMV_FLAG_STREAM_WIDE_WG;
     if (d->flags & ~known) return QGEMV_E_ARG;
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
@@ -129,27 +130,32 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     return ks < 1 ? 1 : ks;
 }
 
-// Persistent one-row streaming kernel: the activation row (in the decode's pair order)
-// and per-chunk sums of it live in LDS; each wave walks column groups with the next
-// batch of codes in flight. Returns false when the staged row does not fit.
+// Persistent streaming kernel for M <= 4 rows in one pass (2 or 4 rows per pass for
+// M = 2 or 3..4): the activation rows (in the decode's pair order) and per-chunk sums
+// of them live in LDS; each wave walks column groups with the next batch of codes in
+// flight. Returns false when the staged rows do not fit.
 //  - chunks per lane per batch (UNR 2, 3 or 4): the fewest idle load slots over the
 //    column's chunks, ties to the larger batch;
 //  - columns per wave: 1 while every column can have a wave of its own within ~24
 //    resident waves per CU, else 2;
-//  - grid: one group per wave when that fits in 24 waves per CU, else a persistent
-//    grid of 24 waves per CU.
-static bool stream1_plan(const qgemv_desc *d, int cu_count, uint32_t flags, LaunchCfg *c) {
+//  - grid: one group per wave when that fits in 24 waves per CU (16 for several
+//    rows, whose waves hold more registers), else a persistent grid of as many.
+static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flags, LaunchCfg *c) {
+    if (M > 4) return false;
+    const int mt = M == 1 ? 1 : (M == 2 ? 2 : 4);  // rows per pass (one pass)
     const int kpc = k_per_chunk(d->format);
     const int64_t nch = d->K / kpc;
     const int64_t nch64 = (nch + 63) / 64 * 64;
     const int nd = kpc == 32 ? 16 : 8;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
-    const int64_t lds = nch64 * nd * 4 + nch64 * h * 4;
-    if (lds > 48 * 1024) return false;
+    const int64_t lds = mt * (nch64 * nd * 4 + nch64 * h * 4);
+    if (lds > (mt > 1 ? 64 : 48) * 1024) return false;
     const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
     int unr = 0;
     const uint32_t fu = (flags & QGEMV_FLAG_STREAM_UNR_MASK) >> QGEMV_FLAG_STREAM_UNR_SHIFT;
-    if (fu) {
+    if (mt > 1) {
+        unr = 2;  // several rows: 2 chunks per lane per batch
+    } else if (fu) {
         unr = (int)fu + 1;
     } else {
         int64_t best = -1;
@@ -161,23 +167,46 @@ static bool stream1_plan(const qgemv_desc *d, int cu_count, uint32_t flags, Laun
     const uint32_t fc = (flags & QGEMV_FLAG_STREAM_CPW_MASK) >> QGEMV_FLAG_STREAM_CPW_SHIFT;
     int cpw;
     if (fc) cpw = fc == 3 ? 4 : (int)fc;
-    else cpw = d->N <= 24LL * cu_count ? 1 : 2;
+    else cpw = (mt > 1 || d->N <= 24LL * cu_count) ? 1 : 2;
+    if (mt > 1 && cpw > 2) cpw = 2;
     const int64_t groups = (d->N + cpw - 1) / cpw;
     const uint32_t fw = (flags & QGEMV_FLAG_STREAM_WPC_MASK) >> QGEMV_FLAG_STREAM_WPC_SHIFT;
     int64_t wpc;
     if (fw) wpc = 4 * (int64_t)fw;
-    else wpc = 24;
-    const int64_t wgs = (groups + 3) / 4;
-    const int64_t cap = (int64_t)cu_count * wpc / 4;
-    c->rows_per_pass = 1;
+    else wpc = mt > 1 ? 16 : 24;
+    // 16-wave workgroups (one row, one column per wave) when asked for
+    const int nwg = (flags & QGEMV_FLAG_STREAM_WIDE_WG) && mt == 1 && cpw == 1 ? 16 : 4;
+    const int64_t wgs = (groups + nwg - 1) / nwg;
+    int64_t cap = (int64_t)cu_count * wpc / nwg;
+    if (cap < 1) cap = 1;
+    c->rows_per_pass = mt;
     c->passes = 1;
     c->cols_per_wave = cpw;
     c->ksplit = 1;
-    c->waves_per_wg = 4;
+    c->waves_per_wg = nwg;
     c->grid = wgs < cap ? wgs : (cap > 0 ? cap : 1);
     c->lds_bytes = (int)lds;
     c->variant = 1 | ((unr & 3) << 1);
     return true;
+}
+
+// Where the persistent streaming kernel with 2 or 4 rows per pass beats the matrix
+// family (measured on MI355X): at M = 2 for 4- and 8-bit integer and FP8 codes, and at
+// M = 3..4 for 8-bit codes or while the weight is small enough (under 64 MB) that the
+// call is latency-bound rather than bandwidth-bound. NVFP4's converter-based decode
+// keeps wide NVFP4 weights on the matrix family from M = 2.
+static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
+    if (!stream_ok || M > 4 || M < 2) return false;
+    const int kpc = k_per_chunk(d->format);
+    const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
+    const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
+    const int mt = M == 2 ? 2 : 4;
+    if (mt * (nch64 * (kpc == 32 ? 16 : 8) * 4 + nch64 * h * 4) > 64 * 1024) return false;
+    const double wbytes = (double)d->N * d->K * (kpc == 32 ? 0.5 : 1.0);
+    const bool small = wbytes < 64.0 * 1024 * 1024;
+    const bool byte_codes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
+    if (M == 2) return d->format != QGEMV_FMT_NVFP4 || small;
+    return byte_codes || small;
 }
 
 int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t extra_flags, LaunchCfg *out) {
@@ -208,7 +237,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
     } else if (forced == QGEMV_FAMILY_MFMA) {
         if (!(fast_ok && mfma_shape_ok(d))) return QGEMV_E_ARG;
         family = QGEMV_FAMILY_MFMA;
-    } else if (mfma_ok && M >= 2) {
+    } else if (mfma_ok && M >= 2 && !stream_rows_win(d, M, stream_ok)) {
         family = QGEMV_FAMILY_MFMA;
     } else if (stream_ok) {
         family = QGEMV_FAMILY_STREAM;
@@ -278,7 +307,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t wgs = (d->N + 3) / 4;
         const int64_t cap = 8LL * cu_count;
         c.grid = wgs < cap ? wgs : cap;
-    } else if (M == 1 && !(flags & QGEMV_FLAG_STREAM_CLASSIC) && stream1_plan(d, cu_count, flags, &c)) {
+    } else if (!(flags & QGEMV_FLAG_STREAM_CLASSIC) && stream1_plan(d, M, cu_count, flags, &c)) {
         // persistent one-row kernel (plan filled in)
     } else {
         c.rows_per_pass = (M == 1) ? 1 : (M == 2 ? 2 : 4);

@@ -95,7 +95,8 @@ enum qgemv_family {
  * batch (1 -> 2, 2 -> 3, 3 -> 4), bits 25..27 the resident waves per CU the grid is
  * sized for (v -> 4v); 0 = automatic. Bit 28: use the non-persistent streaming kernel
  * at M = 1 as well. Bits 29..30: MFMA register-ring depth (1 -> 4 slots, 2 -> 8;
- * 0 = automatic). None of these changes a result's bits except the family choice and
+ * 0 = automatic). Bit 31: 16-wave workgroups for the one-row streaming kernel with one
+ * column per wave. None of these changes a result's bits except the family choice and
  * the K split; they exist for A/B comparisons and tuning. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
@@ -114,6 +115,7 @@ enum qgemv_family {
 #define QGEMV_FLAG_STREAM_CLASSIC 0x10000000u
 #define QGEMV_FLAG_MFMA_DEPTH_SHIFT 29
 #define QGEMV_FLAG_MFMA_DEPTH_MASK 0x60000000u
+#define QGEMV_FLAG_STREAM_WIDE_WG 0x80000000u
 
 /* Problem description. struct_size must be sizeof(qgemv_desc). */
 typedef struct qgemv_desc {

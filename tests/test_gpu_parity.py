@@ -191,6 +191,28 @@ def test_one_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act, 
                 Yv, pv = gu.run_gpu(prob, 1, flags=_stream1_flags(cpw, unr, wpc))
                 assert pv["variant"] & 1 and pv["cols_per_wave"] == cpw, pv
                 assert np.array_equal(Yv.view(np.int64), Yc.view(np.int64)), (cpw, unr, wpc, pv)
+    for unr in (2, 3, 4):  # 16-wave workgroups
+        Yv, pv = gu.run_gpu(prob, 1, flags=_stream1_flags(1, unr, 0) | bqw.FLAG_STREAM_WIDE_WG)
+        assert pv["waves_per_wg"] == 16, pv
+        assert np.array_equal(Yv.view(np.int64), Yc.view(np.int64)), (unr, pv)
+
+
+@pytest.mark.parametrize("fmt,act,bs,N,K", [("u4", "bf16", 32, 1001, 4064), ("u8", "f16", 64, 333, 64 * 37),
+                                            ("fp8", "bf16", 128, 700, 128 * 41), ("nvfp4", "bf16", 16, 517, 32 * 97),
+                                            ("u4", "f16", 16, 9001, 1024)])
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_multi_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act, bs, N, K, M):
+    """Two or four rows per pass in the persistent streaming kernel: each row equals
+    the classic streaming kernel's bits, and the oracle bound holds."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=32)
+    gu.say(f"[stream-rows] {fmt}/{act} bs{bs} N={N} K={K} M={M}")
+    Yc, pc = gu.run_gpu(prob, M, flags=FAMILY_FLAG["stream_classic"])
+    ok, ratio, _, _ = gu.check_full(prob, M, Yc, strict=False)
+    assert ok, ratio
+    for cpw in (1, 2):
+        Ya, pa = gu.run_gpu(prob, M, flags=1 | ({1: 1, 2: 2}[cpw] << bqw.FLAG_STREAM_CPW_SHIFT))
+        assert pa["variant"] & 1 and pa["rows_per_pass"] >= M and pa["cols_per_wave"] == cpw, pa
+        assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, pa)
 
 
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
