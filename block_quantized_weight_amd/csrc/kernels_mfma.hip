@@ -269,6 +269,11 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             bv[3] = decode_b<FMT, ACT, 3>(w);
         }
     }
+    // A discarded step (past K, or a tile past N, both on clamped valid addresses)
+    // gets a zero scale: it adds 0 * (a finite value) to the accumulators, which
+    // leaves them as they are, with one select per step instead of one per element.
+    MetaRaw<H> mv = m;
+    mv.v[0] = valid ? m.v[0] : 0u;
     const uint32_t kbase = (uint32_t)c * F::KPC;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -311,13 +316,12 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             float sc, zoff;
-            meta_decode<FMT, ACT, H>(a, m, c, h, sc, zoff);
+            meta_decode<FMT, ACT, H>(a, mv, c, h, sc, zoff);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = d[h][r];
                 if constexpr (F::ZP) v = __builtin_fmaf(-zoff, sa[h][r], v);
-                const float t = __builtin_fmaf(sc, v, acc[rg][r]);
-                acc[rg][r] = valid ? t : acc[rg][r];
+                acc[rg][r] = __builtin_fmaf(sc, v, acc[rg][r]);
             }
         }
     }
@@ -589,48 +593,72 @@ __global__ void __launch_bounds__(512, 2) k_mfma_dma(KArgs a) {
     const int zrow = a.zstride;                                       // zero-point row bytes
     const int ops = SS + nsd + (ZPP ? 1 : 0);                         // DMAs per slot
 
+    // Lane constants of the DMA sources, relative to a uniform per-slot base address
+    // (the tile's first column at the slot's first chunk or metadata dword): the
+    // column part and the chunk (or dword) part, each clamped per slot with one min
+    // against a uniform limit, so that a ragged tile re-reads column N - 1 and a
+    // ragged slot the column's last chunk, as every load here stays in bounds.
+    uint32_t ccol[16 / Gm::CPD], cchk[16 / Gm::CPD];
+#pragma unroll
+    for (int d = 0; d < 16 / Gm::CPD; ++d) {
+        const int cn = d * Gm::CPD + lane / CS;
+        ccol[d] = (uint32_t)cn * (uint32_t)a.col_bytes;
+        cchk[d] = (uint32_t)((lane % CS) ^ (cn % CS)) * 16u;
+    }
+    uint32_t scol[Gm::NSD], sq4[Gm::NSD];
+#pragma unroll
+    for (int e = 0; e < Gm::NSD; ++e) {
+        const int idx = e * 64 + lane;
+        int cn = idx / mds, q = idx - (idx / mds) * mds;
+        if (cn > 15) cn = 15, q = mds - 1;
+        scol[e] = (uint32_t)(cn * srow);
+        sq4[e] = (uint32_t)(4 * q);
+    }
+    uint32_t zcol = 0, zq4 = 0;
+    if constexpr (ZPP) {
+        int cn = lane / mdz, q = lane - (lane / mdz) * mdz;
+        if (cn > 15) cn = 15, q = mdz - 1;
+        zcol = (uint32_t)(cn * zrow);
+        zq4 = (uint32_t)(4 * q);
+    }
+
     // issue cursor
     int64_t itile = gw;
     int isl = 0;
     auto issue = [&](int r) {
         unsigned char *slot = ring + r * SLOT;
         const int64_t t0 = itile * 16;
+        const int64_t lastc = a.N - 1 - t0;
+        const uint32_t limc = (uint32_t)(lastc < 15 ? lastc : 15);  // last column in the tile
         // codes: DMA d moves columns d*CPD .. d*CPD + CPD - 1
+        const uint8_t *wbase = a.W + t0 * a.col_bytes + (int64_t)isl * (CS * 16);
+        const uint32_t limcw = limc * (uint32_t)a.col_bytes;
+        const uint32_t limj = (uint32_t)(nch - 1 - isl * CS) * 16u;
 #pragma unroll
         for (int d = 0; d < 16 / Gm::CPD; ++d) {
-            const int cn = d * Gm::CPD + lane / CS;
-            const int jp = lane % CS;
-            const int j = jp ^ (cn % CS);
-            int64_t col = t0 + cn;
-            col = col < a.N ? col : a.N - 1;
-            int c = isl * CS + j;
-            c = c < nch ? c : nch - 1;
-            dma_to_lds<16>(a.W + col * a.col_bytes + (int64_t)c * 16, slot + d * Gm::DSTRIDE);
+            const uint32_t off = (ccol[d] < limcw ? ccol[d] : limcw) + (cchk[d] < limj ? cchk[d] : limj);
+            dma_to_lds<16>(wbase + off, slot + d * Gm::DSTRIDE);
         }
         // scale windows: dword q of column cn's window
         const int wbs = (isl * sbc) & ~3;
+        const uint8_t *sbase = (const uint8_t *)a.scales + t0 * srow + wbs;
+        const uint32_t limcs = limc * (uint32_t)srow;
+        const uint32_t limq = (uint32_t)(srow - wbs - 4);
 #pragma unroll
         for (int e = 0; e < Gm::NSD; ++e) {
             if (e < nsd) {
-                const int idx = e * 64 + lane;
-                int cn = idx / mds, q = idx - (idx / mds) * mds;
-                if (cn > 15) cn = 15, q = mds - 1;
-                if (wbs + 4 * q + 4 > srow) q = (srow - wbs) / 4 - 1;
-                int64_t col = t0 + cn;
-                col = col < a.N ? col : a.N - 1;
-                const uint8_t *row = (const uint8_t *)a.scales + col * srow;
-                dma_to_lds<4>(row + wbs + 4 * q, slot + Gm::CODEB + e * 256);
+                const uint32_t off = (scol[e] < limcs ? scol[e] : limcs) + (sq4[e] < limq ? sq4[e] : limq);
+                dma_to_lds<4>(sbase + off, slot + Gm::CODEB + e * 256);
             }
         }
         if constexpr (ZPP) {
             const int zb0 = (FMT == FMT_U4) ? ((isl * bps) >> 1) : isl * bps;
             const int wbz = zb0 & ~3;
-            int cn = lane / mdz, q = lane - (lane / mdz) * mdz;
-            if (cn > 15) cn = 15, q = mdz - 1;
-            if (wbz + 4 * q + 4 > zrow) q = (zrow - wbz) / 4 - 1;
-            int64_t col = t0 + cn;
-            col = col < a.N ? col : a.N - 1;
-            dma_to_lds<4>(a.zp + col * zrow + wbz + 4 * q, slot + Gm::CODEB + Gm::NSD * 256);
+            const uint8_t *zbase = a.zp + t0 * zrow + wbz;
+            const uint32_t limcz = limc * (uint32_t)zrow;
+            const uint32_t limqz = (uint32_t)(zrow - wbz - 4);
+            const uint32_t off = (zcol < limcz ? zcol : limcz) + (zq4 < limqz ? zq4 : limqz);
+            dma_to_lds<4>(zbase + off, slot + Gm::CODEB + Gm::NSD * 256);
         }
         if (++isl == nslots) {
             isl = 0;

@@ -96,7 +96,8 @@ enum qgemv_family {
  * sized for (v -> 4v); 0 = automatic. Bit 28: use the non-persistent streaming kernel
  * at M = 1 as well. Bits 29..30: MFMA register-ring depth (1 -> 4 slots, 2 -> 8;
  * 0 = automatic). Bit 31: 16-wave workgroups for the one-row streaming kernel with one
- * column per wave. None of these changes a result's bits except the family choice and
+ * column per wave (also chosen automatically when the columns fill 8 to 16 waves per
+ * CU and neither bits 21..22 nor 25..27 are set). None of these changes a result's bits except the family choice and
  * the K split; they exist for A/B comparisons and tuning. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
