@@ -118,13 +118,13 @@ __device__ __forceinline__ op4 load_a(const uint16_t *arow, bool live, uint32_t 
 
 // Block metadata of one chunk kept raw while it waits in the prefetch ring: the
 // loaded values as they are (nothing is computed from a load until the chunk is
-// consumed, so a prefetch never waits for its own data), decoded by meta_decode.
+// consumed, so a prefetch never waits for its own data), decoded by meta_values.
 //   U4, one block per chunk : v0 = fp16 scale bits, v1 = the zero-point byte holding the block
 //   U4, two blocks per chunk: v0 = both fp16 scales, v1 = the zero-point byte of the pair
 //   U8                      : v0 = fp16 scale bits, v1 = zero-point byte
 //   FP8                     : v0 = fp32 scale bits
 //   NVFP4                   : v0 = the two E4M3 scale bytes
-// (without zero points v1 holds whatever the aliased address held; meta_decode then
+// (without zero points v1 holds whatever the aliased address held; meta_values then
 // uses the midpoint, 8 for U4 and 128 for U8)
 template <int H>
 struct MetaRaw {
@@ -178,31 +178,49 @@ __device__ __forceinline__ MetaRaw<H> load_meta_raw(const KArgs &a, const MfCol 
     return m;
 }
 
-// Scale and (M0 + zero point) of half h of chunk c from the raw metadata.
+// Scale and (M0 + zero point) of half h of a chunk from its raw metadata (v0, v1 as
+// MetaRaw holds them). zsh is the bit position of the chunk's zero-point nibble in v1
+// for 4-bit codes with one block per chunk (4 for an odd block index, else 0).
 template <int FMT, int ACT, int H>
-__device__ __forceinline__ void meta_decode(const KArgs &a, const MetaRaw<H> &m, int c, int h, float &s,
+__device__ __forceinline__ void meta_values(const KArgs &a, uint32_t v0, uint32_t v1, int zsh, int h, float &s,
                                             float &zoff) {
     if constexpr (FMT == FMT_U4) {
         const ZSel zs = zsel(a.zp, 0x88u);
-        const uint32_t zb = (m.v[1] & zs.keep) | zs.fill;
+        const uint32_t zb = (v1 & zs.keep) | zs.fill;
         if constexpr (H == 1) {
-            const int b = (c << 5) >> a.bs_shift;
-            s = half_bits_to_float((uint16_t)(m.v[0] & 0xFFFFu));
-            zoff = U4Magic<ACT>::off + (float)((b & 1) ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu));
+            s = half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
+            zoff = U4Magic<ACT>::off + (float)((zb >> zsh) & 0x0Fu);
         } else {
-            s = half_bits_to_float((uint16_t)(h ? (m.v[0] >> 16) : (m.v[0] & 0xFFFFu)));
+            s = half_bits_to_float((uint16_t)(h ? (v0 >> 16) : (v0 & 0xFFFFu)));
             zoff = U4Magic<ACT>::off + (float)(h ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu));
         }
     } else if constexpr (FMT == FMT_U8) {
         const ZSel zs = zsel(a.zp, 128u);
-        s = half_bits_to_float((uint16_t)(m.v[0] & 0xFFFFu));
-        zoff = 1024.0f + (float)(((m.v[1] & zs.keep) | zs.fill) & 0xFFu);
+        s = half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
+        zoff = 1024.0f + (float)(((v1 & zs.keep) | zs.fill) & 0xFFu);
     } else if constexpr (FMT == FMT_FP8) {
-        s = __builtin_bit_cast(float, m.v[0]);
+        s = __builtin_bit_cast(float, v0);
         zoff = 0.0f;
     } else {
-        s = e4m3_to_float(h ? ((m.v[0] >> 8) & 0xFFu) : (m.v[0] & 0xFFu));
+        s = e4m3_to_float(h ? ((v0 >> 8) & 0xFFu) : (v0 & 0xFFu));
         zoff = 0.0f;
+    }
+}
+
+// Zero-point nibble position of chunk c (4-bit codes, one block per chunk).
+__device__ __forceinline__ int u4_zshift(const KArgs &a, int c) {
+    return (((c << 5) >> a.bs_shift) & 1) << 2;
+}
+
+// One output group's epilogue: acc += s * (d - zoff * sa) (the zero-point term only
+// for formats with zero points). Shared by every matrix-family kernel.
+template <bool ZP>
+__device__ __forceinline__ void epilogue(const f4 &d, const f4 &sa, float sc, float zoff, f4 &acc) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = d[r];
+        if constexpr (ZP) v = __builtin_fmaf(-zoff, sa[r], v);
+        acc[r] = __builtin_fmaf(sc, v, acc[r]);
     }
 }
 
@@ -220,6 +238,21 @@ __device__ __forceinline__ float sum_groups(float v) {
 // Padding of a staged activation row in LDS (elements): shifts consecutive rows by
 // 16 bytes so the 16 live lanes of an A-operand read hit distinct banks.
 constexpr int kAPad = 8;
+
+// LDS layout of the kernels that stage the activations: a 64-byte zero block (the A
+// operand of lanes off the block diagonal, MF reads of 16 bytes), the staged rows,
+// then for formats with zero points the per-chunk activation sums (f4 entries indexed
+// (chunk * RG + row group) * H + half), then the kernel's own area.
+constexpr int kZeroBytes = 64;
+
+__device__ __forceinline__ size_t staged_rows_bytes(const KArgs &a, int astride) {
+    return ((size_t)a.M * astride * 2 + 15) & ~(size_t)15;
+}
+
+template <int FMT, int RG, int H>
+__device__ __forceinline__ size_t sums_bytes(const KArgs &a) {
+    return MfFmt<FMT>::ZP ? (size_t)a.nchunks * RG * H * 16 : 0;
+}
 
 // One wave owns the 16 columns of a tile for one K slice. A workgroup of nw waves
 // holds nw / ksplit tiles; the ksplit waves of a tile take K steps t = kslice,
@@ -251,13 +284,31 @@ __device__ __forceinline__ void load_a_ops(const KArgs &a, int c, int ar, AOps<F
     }
 }
 
-template <int FMT, int ACT, int RG, int H, bool LDSA>
-__device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const MetaRaw<H> &m, int c, int ar,
-                                          bool a_live_grp, const uint16_t *sA, const uint16_t *sZero, int astride,
-                                          const AOps<FMT, RG> &areg, bool valid, f4 acc[RG]) {
+// The ones-operand MFMA chain that sums the activations of one row group over a
+// chunk (per half h with two scale blocks per chunk): element r of lane (n, g) gets
+// row 4 * rg + r of chunk 4t + g. Run per K step by the kernels that load the
+// activations into registers, and once per chunk into the LDS sum table by the ones
+// that stage them, so both see the same bits.
+template <int FMT, int ACT, int H>
+__device__ __forceinline__ void chunk_sums(const op4 (&av)[MfFmt<FMT>::MF], f4 (&sa)[H]) {
     using F = MfFmt<FMT>;
     constexpr uint32_t ONE = (ACT == ACT_F16) ? 0x3C003C00u : 0x3F803F80u;
     const op4 ones = {ONE, ONE, ONE, ONE};
+#pragma unroll
+    for (int h = 0; h < H; ++h) sa[h] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < F::MF; ++j) {
+        const int h = (H == 2) ? (j / (F::MF / 2)) : 0;
+        sa[h] = mfma<ACT>(av[j], ones, sa[h]);
+    }
+}
+
+template <int FMT, int ACT, int RG, int H, bool LDSA>
+__device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const MetaRaw<H> &m, int c, int ar,
+                                          bool a_live_grp, const uint16_t *sA, const uint16_t *sZero,
+                                          const f4 *sSum, int astride, const AOps<FMT, RG> &areg, bool valid,
+                                          f4 acc[RG]) {
+    using F = MfFmt<FMT>;
     // with one row group the B operands are decoded right before their MFMA; with
     // more they are decoded once and shared by the groups
     op4 bv[RG == 1 ? 1 : F::MF];
@@ -272,8 +323,8 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
     // A discarded step (past K, or a tile past N, both on clamped valid addresses)
     // gets a zero scale: it adds 0 * (a finite value) to the accumulators, which
     // leaves them as they are, with one select per step instead of one per element.
-    MetaRaw<H> mv = m;
-    mv.v[0] = valid ? m.v[0] : 0u;
+    const uint32_t v0 = valid ? m.v[0] : 0u;
+    const int zsh = (FMT == FMT_U4 && H == 1) ? u4_zshift(a, c) : 0;
     const uint32_t kbase = (uint32_t)c * F::KPC;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -281,25 +332,26 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
         const bool live = a_live_grp && row < a.M;
         f4 d[H], sa[H];
 #pragma unroll
-        for (int h = 0; h < H; ++h) d[h] = sa[h] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < H; ++h) d[h] = f4{0.f, 0.f, 0.f, 0.f};
         // staged activations: every lane reads (lanes outside the block diagonal read
-        // a 16-byte zero block), so the MF reads issue back to back without predication
+        // the zero block), so the MF reads issue back to back without predication
         op4 avs[F::MF];
         if constexpr (LDSA) {
             const uint16_t *abase = live ? sA + row * astride + kbase : sZero;
-            const int jstride = live ? 8 : 0;
 #pragma unroll
-            for (int j = 0; j < F::MF; ++j) avs[j] = *(const op4 *)(abase + jstride * j);
+            for (int j = 0; j < F::MF; ++j) avs[j] = *(const op4 *)(abase + 8 * j);
+            if constexpr (F::ZP) {
+#pragma unroll
+                for (int h = 0; h < H; ++h) sa[h] = sSum[((size_t)c * RG + rg) * H + h];
+            }
+        } else {
+            const op4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < F::MF; ++j) avs[j] = live ? areg.v[rg][j] : z;
+            if constexpr (F::ZP) chunk_sums<FMT, ACT, H>(avs, sa);
         }
 #pragma unroll
         for (int j = 0; j < F::MF; ++j) {
-            op4 av;
-            if constexpr (LDSA) {
-                av = avs[j];
-            } else {
-                const op4 z = {0u, 0u, 0u, 0u};
-                av = live ? areg.v[rg][j] : z;
-            }
             const int h = (H == 2) ? (j / (F::MF / 2)) : 0;
             op4 b;
             if constexpr (RG == 1) {
@@ -310,18 +362,47 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             } else {
                 b = bv[j];
             }
-            d[h] = mfma<ACT>(av, b, d[h]);
-            if constexpr (F::ZP) sa[h] = mfma<ACT>(av, ones, sa[h]);
+            d[h] = mfma<ACT>(avs[j], b, d[h]);
         }
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             float sc, zoff;
-            meta_decode<FMT, ACT, H>(a, mv, c, h, sc, zoff);
+            meta_values<FMT, ACT, H>(a, v0, m.v[1], zsh, h, sc, zoff);
+            epilogue<F::ZP>(d[h], sa[h], sc, zoff, acc[rg]);
+        }
+    }
+}
+
+// Fill the per-chunk activation-sum table (formats with zero points) from the staged
+// rows: the waves of the workgroup take K steps in turn and run chunk_sums on the
+// same A operands mfma_step reads; lane (0, g) of each lane group stores its chunk's
+// entry. The caller synchronizes the workgroup before and after.
+template <int FMT, int ACT, int RG, int H>
+__device__ __forceinline__ void stage_sums(const KArgs &a, const uint16_t *sA, const uint16_t *sZero, int astride,
+                                           f4 *sSum) {
+    using F = MfFmt<FMT>;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwv = (int)(blockDim.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int ar = lane & 3;
+    const bool a_live_grp = ((lane & 15) >> 2) == g;
+    const int nsteps = (int)(a.nchunks >> 2);
+    for (int t = wave; t < nsteps; t += nwv) {
+        const int c = 4 * t + g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = d[h][r];
-                if constexpr (F::ZP) v = __builtin_fmaf(-zoff, sa[h][r], v);
-                acc[rg][r] = __builtin_fmaf(sc, v, acc[rg][r]);
+        for (int rg = 0; rg < RG; ++rg) {
+            const int row = 4 * rg + ar;
+            const bool live = a_live_grp && row < a.M;
+            const uint16_t *abase = live ? sA + row * astride + (uint32_t)c * F::KPC : sZero;
+            op4 avs[F::MF];
+#pragma unroll
+            for (int j = 0; j < F::MF; ++j) avs[j] = *(const op4 *)(abase + 8 * j);
+            f4 sa[H];
+            chunk_sums<FMT, ACT, H>(avs, sa);
+            if ((lane & 15) == 0) {
+#pragma unroll
+                for (int h = 0; h < H; ++h) sSum[((size_t)c * RG + rg) * H + h] = sa[h];
             }
         }
     }
@@ -450,9 +531,13 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     const int astride = (int)a.K + kAPad;
     const int64_t ntiles = (a.N + 15) >> 4;
     const int64_t ngroups = (ntiles + tpw - 1) / tpw;
+    // LDS: [zero block | staged rows | activation sums] when staged, then the K-split
+    // reduction area
     uint16_t *sZero = (uint16_t *)smem;
-    uint16_t *sA = (uint16_t *)(smem + 16);
-    float *sR = (float *)(smem + 16 + (LDSA ? (((size_t)a.M * astride * 2 + 15) & ~(size_t)15) : 0));
+    uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
+    f4 *sSum = (f4 *)(smem + kZeroBytes + (LDSA ? staged_rows_bytes(a, astride) : 0));
+    float *sR = (float *)(LDSA ? smem + kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>(a)
+                               : smem);
 
     // issue cursor: tile group, slot within the tile, and the column the lane loads
     int64_t itg = blockIdx.x;
@@ -481,9 +566,13 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     for (int p = 0; p < P; ++p) issue(p);
 
     if constexpr (LDSA) {
-        if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
+        if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
         stage_a<FMT>(a, sA, astride);
         __syncthreads();
+        if constexpr (MfFmt<FMT>::ZP) {
+            stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum);
+            __syncthreads();
+        }
     }
 
     // One ring turn = P slots. Every turn but the last consumes and refills each slot;
@@ -504,8 +593,8 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         for (int p = 0; p < P; ++p) {
             const int t = kslice + (tt * P + p) * ks;
             const int tc = t < nsteps ? t : nsteps - 1;
-            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * tc + g, ar, a_live_grp, sA, sZero, astride,
-                                             ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
+            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * tc + g, ar, a_live_grp, sA, sZero, sSum,
+                                             astride, ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
             if (refill) {
                 // the slot's accumulation completes here (nothing of it may sink below
                 // the refill), then the refill reuses the slot's registers
@@ -542,20 +631,21 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
 //  - Every K step keeps the chunk -> (step, lane group) assignment of k_mfma (step t,
 //    lane group g: chunk 4t + g) and calls the same mfma_step, so results are
 //    bit-identical to k_mfma with no K split.
-template <int FMT, int SS>
+template <int FMT, int SS, int H>
 struct DmaGeom {
     static constexpr int CS = 4 * SS;                      // chunks per column per slot
     static constexpr int CPD = 64 / CS;                    // columns per code DMA
     static constexpr int DSTRIDE = SS == 4 ? 1024 : 1152;  // bytes per code DMA block (+pad)
     static constexpr int CODEB = (16 / CPD) * DSTRIDE;     // code bytes per slot
-    // scale-window DMAs per slot (upper bound over the block sizes the format takes)
-    static constexpr int NSD =
-        (FMT == FMT_FP8) ? (SS == 4 ? 4 : 2) : ((FMT == FMT_U4 || FMT == FMT_NVFP4) ? (SS == 4 ? 4 : 2) : (SS == 4 ? 2 : 1));
+    // scale-window DMAs per slot: the most the format's block sizes need (16 columns
+    // x the slot's scale bytes, 256 bytes per DMA); FP8 takes 16-wide blocks, 4-bit
+    // codes with one block per chunk at most 16 per 512 k
+    static constexpr int NSD = (FMT == FMT_FP8 || (FMT == FMT_U4 && H == 2)) ? (SS == 4 ? 4 : 2) : (SS == 4 ? 2 : 1);
 };
 
 template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int SS>
-__global__ void __launch_bounds__(512, 2) k_mfma_dma(KArgs a) {
-    using Gm = DmaGeom<FMT, SS>;
+__global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
+    using Gm = DmaGeom<FMT, SS, H>;
     using F = MfFmt<FMT>;
     constexpr int NW = 8;
     constexpr int CS = Gm::CS;
@@ -576,9 +666,10 @@ __global__ void __launch_bounds__(512, 2) k_mfma_dma(KArgs a) {
     const int64_t gw = (int64_t)blockIdx.x * NW + wave;
     const int64_t mytiles = gw < ntiles ? (ntiles - gw + nw - 1) / nw : 0;
     const int64_t total = mytiles * nslots;
-    const size_t abytes = 16 + (((size_t)a.M * astride * 2 + 15) & ~(size_t)15);
+    const size_t abytes = kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>(a);
     uint16_t *sZero = (uint16_t *)smem;
-    uint16_t *sA = (uint16_t *)(smem + 16);
+    uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
+    f4 *sSum = (f4 *)(smem + kZeroBytes + staged_rows_bytes(a, astride));
     unsigned char *ring = smem + abytes + (size_t)wave * R * SLOT;
 
     // per-slot metadata windows (uniform): blocks per slot (slots hold whole blocks:
@@ -671,65 +762,153 @@ __global__ void __launch_bounds__(512, 2) k_mfma_dma(KArgs a) {
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         if (r < total) issue(r);
-    if (threadIdx.x == 0) *(u4v *)sZero = u4v{0u, 0u, 0u, 0u};
+    if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
     stage_a<FMT, 4>(a, sA, astride);
     __syncthreads();
-
-    // Byte offsets, within a slot's scale / zero-point window of the lane's column, of
-    // the metadata of the lane's chunk 4s + g (the same in every slot; a window shorter
-    // than a dword adds the slot's position in its dword)
-    int sbyte[SS], zbyte[SS];
-#pragma unroll
-    for (int s = 0; s < SS; ++s) {
-        const int j = 4 * s + g;
-        const int lb = (H == 2) ? 2 * j : ((j * F::KPC) >> a.bs_shift);  // first block of the chunk
-        sbyte[s] = lb * SB;
-        zbyte[s] = (FMT == FMT_U4) ? (lb >> 1) : lb;
+    if constexpr (F::ZP) {
+        stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum);
+        __syncthreads();
     }
 
-    int64_t ctile = gw;
-    int csl = 0;
+    // Consumer lane constants. Step s of a slot is the lane's chunk j = 4s + g of the
+    // slot's CS: its code bytes at cofs[s] in the slot, its scale (zero-point) bytes at
+    // sofs[s] (zofs[s]) from the start of the slot plus the window's sub-dword start,
+    // the bit of its zero-point nibble zsh[s]; the A operands of row group rg at
+    // abase[rg] plus the step's K offset (kept at the zero block off the block diagonal
+    // by amask), the activation sums at sumb plus the step's chunk.
+    uint32_t cofs[SS], sofs[SS], zofs[SS];
+    int zsh[SS];
+#pragma unroll
+    for (int st = 0; st < SS; ++st) {
+        const int j = 4 * st + g;
+        const int lb = (H == 2) ? 2 * j : ((j * F::KPC) >> a.bs_shift);  // first block of the chunk
+        cofs[st] = (uint32_t)((n / Gm::CPD) * Gm::DSTRIDE + ((n % Gm::CPD) * CS + (j ^ (n % CS))) * 16);
+        sofs[st] = (uint32_t)(Gm::CODEB + n * mds * 4 + lb * SB);
+        zofs[st] = (uint32_t)(Gm::CODEB + Gm::NSD * 256 + n * mdz * 4 + ((FMT == FMT_U4) ? (lb >> 1) : lb));
+        zsh[st] = (FMT == FMT_U4 && H == 1) ? ((lb & 1) << 2) : 0;
+    }
+    const unsigned char *abase[RG];
+    uint32_t amask[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int row = 4 * rg + ar;
+        const bool live = a_live_grp && row < a.M;
+        abase[rg] = live ? (const unsigned char *)(sA + row * astride + g * F::KPC) : (const unsigned char *)sZero;
+        amask[rg] = live ? 0xFFFFFFFFu : 0u;
+    }
+    const f4 *sumb = sSum + g * (RG * H);
+
+    // Operands of one K step, read from LDS one step ahead of their use (the A
+    // operands too, except with two row groups and two scale blocks per chunk, where
+    // a second set would not fit in the registers: those are read at their use).
+    constexpr bool PREA = !(RG == 2 && H == 2);
+    struct In {
+        u4v w;
+        uint32_t sv, zv;
+        int kc;
+        op4 av[PREA ? RG : 1][F::MF];
+        f4 sa[RG][H];
+    };
+    auto read_a = [&](int kc, int rg, op4 (&av)[F::MF]) {
+        const unsigned char *ap = abase[rg] + (((uint32_t)kc * (F::KPC * 2)) & amask[rg]);
+#pragma unroll
+        for (int j = 0; j < F::MF; ++j) av[j] = *(const op4 *)(ap + 16 * j);
+    };
+    // st: step within the slot; kc: the step's first chunk in the column (uniform)
+    auto read_step = [&](const unsigned char *slot, int st, int kc, int ssub, int zsub, In &o) {
+        o.w = *(const u4v *)(slot + cofs[st]);
+        if constexpr (SB == 4 || (FMT == FMT_U4 && H == 2)) o.sv = *(const uint32_t *)(slot + sofs[st] + ssub);
+        else o.sv = *(const uint16_t *)(slot + sofs[st] + ssub);
+        o.zv = 0u;
+        if constexpr (ZPP) o.zv = *(const uint8_t *)(slot + zofs[st] + zsub);
+        // a step past K (ragged last slot) reads the last step's activations and sums:
+        // finite values, discarded by the zero scale (nch is a multiple of 4)
+        kc = kc < nch - 4 ? kc : nch - 4;
+        o.kc = kc;
+        if constexpr (PREA) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) read_a(kc, rg, o.av[rg]);
+        }
+        if constexpr (F::ZP) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int h = 0; h < H; ++h) o.sa[rg][h] = sumb[(size_t)kc * (RG * H) + rg * H + h];
+        }
+    };
+    // The arithmetic of mfma_step on the operands read (valid: the step lies within K)
     f4 acc[RG];
 #pragma unroll
     for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int64_t i = 0; i < total; ++i) {
-        // slot i's DMAs are done once at most the later issued slots' remain
+    auto compute = [&](const In &o, int st, bool valid) {
+        const uint32_t v0 = valid ? o.sv : 0u;
+        op4 bv[F::MF];
+        bv[0] = decode_b<FMT, ACT, 0>(o.w);
+        bv[1] = decode_b<FMT, ACT, 1>(o.w);
+        if constexpr (F::MF == 4) {
+            bv[2] = decode_b<FMT, ACT, 2>(o.w);
+            bv[3] = decode_b<FMT, ACT, 3>(o.w);
+        }
+        float sc[H], zo[H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) meta_values<FMT, ACT, H>(a, v0, o.zv, zsh[st], h, sc[h], zo[h]);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            f4 d[H];
+#pragma unroll
+            for (int h = 0; h < H; ++h) d[h] = f4{0.f, 0.f, 0.f, 0.f};
+            op4 avl[F::MF];
+            if constexpr (!PREA) read_a(o.kc, rg, avl);
+#pragma unroll
+            for (int j = 0; j < F::MF; ++j) {
+                const int h = (H == 2) ? (j / (F::MF / 2)) : 0;
+                d[h] = mfma<ACT>(PREA ? o.av[PREA ? rg : 0][j] : avl[j], bv[j], d[h]);
+            }
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+                epilogue<F::ZP>(d[h], F::ZP ? o.sa[rg][h] : z4, sc[h], zo[h], acc[rg]);
+            }
+        }
+    };
+
+    // slot i's DMAs are done once at most the later issued slots' remain
+    auto wait_slot = [&](int64_t i) {
         const int64_t later = total - 1 - i < R - 2 ? total - 1 - i : R - 2;
         wait_vmcnt_dyn((int)later * ops);
+    };
+    auto win_ssub = [&](int sl) { return (sl * sbc) & 3; };  // nonzero only for windows under a dword
+    auto win_zsub = [&](int sl) { return ((FMT == FMT_U4) ? ((sl * bps) >> 1) : sl * bps) & 3; };
+
+    int64_t ctile = gw;
+    int csl = 0;
+    In cur, nxt;
+    if (total > 0) {
+        wait_slot(0);
+        read_step(ring, 0, 0, win_ssub(0), win_zsub(0), cur);
+    }
+#pragma unroll 1
+    for (int64_t i = 0; i < total; ++i) {
         const unsigned char *slot = ring + (i % R) * SLOT;
-        const uint32_t *ms = (const uint32_t *)(slot + Gm::CODEB);
-        const uint32_t *mz = (const uint32_t *)(slot + Gm::CODEB + Gm::NSD * 256);
-        // refill the slot consumed in the previous iteration (its reads are done)
+        // refill the slot consumed in the previous iteration (all its reads have
+        // returned: the last was waited for by that iteration's last step)
         if (i + R - 1 < total) issue((int)((i + R - 1) % R));
-        const bool tile_ok = ctile < ntiles;
-        const int ssub = (csl * sbc) & 3;            // nonzero only for windows under a dword
-        const int zsub = ((FMT == FMT_U4) ? ((csl * bps) >> 1) : csl * bps) & 3;
-        const uint32_t *msn = ms + n * mds;
-        const uint32_t *mzn = mz + n * mdz;
+        const int ssub = win_ssub(csl), zsub = win_zsub(csl);
 #pragma unroll
-        for (int s = 0; s < SS; ++s) {
-            const int j = 4 * s + g;                 // chunk within the slot
-            const int cg = csl * CS + j;             // chunk within the column
-            const bool valid = tile_ok && csl * CS + 4 * s < nch;
-            const int c = cg < nch ? cg : nch - 1;
-            const u4v w = *(const u4v *)(slot + (n / Gm::CPD) * Gm::DSTRIDE +
-                                         ((n % Gm::CPD) * CS + (j ^ (n % CS))) * 16);
-            MetaRaw<H> m;
-            const int sb = sbyte[s] + ssub;
-            const uint32_t dw = msn[sb >> 2];
-            if constexpr (SB == 4 || (FMT == FMT_U4 && H == 2)) m.v[0] = dw;  // aligned dword
-            else m.v[0] = (dw >> (8 * (sb & 3))) & 0xFFFFu;
-            m.v[1] = 0u;
-            if constexpr (ZPP) {
-                const int zb = zbyte[s] + zsub;
-                m.v[1] = (mzn[zb >> 2] >> (8 * (zb & 3))) & 0xFFu;
+        for (int st = 0; st < SS; ++st) {
+            if (st + 1 < SS) {
+                read_step(slot, st + 1, csl * CS + 4 * (st + 1), ssub, zsub, nxt);
+            } else if (i + 1 < total) {
+                // the next slot's first step: wait for its DMAs, then read it
+                const int nsl = csl + 1 == nslots ? 0 : csl + 1;
+                wait_slot(i + 1);
+                read_step(ring + ((i + 1) % R) * SLOT, 0, nsl * CS, win_ssub(nsl), win_zsub(nsl), nxt);
             }
-            mfma_step<FMT, ACT, RG, H, true>(a, w, m, c, ar, a_live_grp, sA, sZero, astride, AOps<FMT, RG>{},
-                                             valid, acc);
+            compute(cur, st, csl * CS + 4 * st < nch);
+            cur = nxt;
         }
         if (++csl == nslots) {
-            finish_tile<ACT, RG>(a, acc, nullptr, wave, lane, 1, 0, g, tile_ok, ctile * 16 + n);
+            finish_tile<ACT, RG>(a, acc, nullptr, wave, lane, 1, 0, g, true, ctile * 16 + n);
 #pragma unroll
             for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
             csl = 0;

@@ -99,7 +99,8 @@ static int dma_ring_shape(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t
         if (4 * ss * kpc < d->block_size) continue;  // a slot holds whole blocks
         if (d->format == QGEMV_FMT_U4 && (4 * ss * kpc) / d->block_size < 2) continue;
         const int codeb = ss == 4 ? 4 * 1024 : 2 * 1152;
-        const int nsd = d->format == QGEMV_FMT_U8 ? (ss == 4 ? 2 : 1) : (ss == 4 ? 4 : 2);
+        const bool wide_meta = d->format == QGEMV_FMT_FP8 || (d->format == QGEMV_FMT_U4 && d->block_size == 16);
+        const int nsd = wide_meta ? (ss == 4 ? 4 : 2) : (ss == 4 ? 2 : 1);
         const int64_t slot = codeb + 256 * nsd + (zpp ? 256 : 0);
         const int64_t lds = abytes + 8 * r * slot;
         if (lds <= kLdsBytes) {
@@ -196,10 +197,10 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 }
 
 // Where the persistent streaming kernel with 2 or 4 rows per pass beats the matrix
-// family (measured on MI355X): at M = 2 for 4- and 8-bit integer and FP8 codes, and at
-// M = 3..4 for 8-bit codes or while the weight is small enough (under 64 MB) that the
-// call is latency-bound rather than bandwidth-bound. NVFP4's converter-based decode
-// keeps wide NVFP4 weights on the matrix family from M = 2.
+// family (measured on MI355X): at M = 2..4 for 8-bit integer and FP8 codes, and for
+// 4-bit codes while the weight is small enough (under 64 MB) that the call is
+// latency-bound rather than bandwidth-bound. Wide 4-bit weights take the matrix
+// family's DMA ring from M = 2 (4-bit lm_head, M = 2: 90 us against 101 us).
 static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
     if (!stream_ok || M > 4 || M < 2) return false;
     const int kpc = k_per_chunk(d->format);
@@ -210,7 +211,6 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
     const double wbytes = (double)d->N * d->K * (kpc == 32 ? 0.5 : 1.0);
     const bool small = wbytes < 64.0 * 1024 * 1024;
     const bool byte_codes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
-    if (M == 2) return d->format != QGEMV_FMT_NVFP4 || small;
     return byte_codes || small;
 }
 
@@ -264,11 +264,17 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t tiles = (d->N + 15) / 16;
         const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
         const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
+        // staged activations: a 64-byte zero block, the rows (stride K + 8 elements), and
+        // for formats with zero points one 16-byte activation-sum entry per chunk, row
+        // group and scale block of the chunk
         const int64_t lds_a = (int64_t)M * (d->K + 8) * 2;
+        const bool zp_fmt = d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8;
+        const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
+        const int64_t lds_sums = zp_fmt ? (d->K / k_per_chunk(d->format)) * rg * hh * 16 : 0;
+        const int64_t abytes16 = 64 + ((lds_a + 15) & ~15LL) + lds_sums;
         // DMA ring (no K split, one or two row groups, metadata rows in whole dwords):
         // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
         // fits in LDS next to the staged activations.
-        const int64_t abytes16 = 16 + ((lds_a + 15) & ~15LL);  // zero block + staged rows
         const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
         const int ring_shape = dma_ring_shape(d, abytes16, zpp, &c.lds_bytes);
         bool ring = c.ksplit == 1 && rg <= 2 && ring_shape >= 0 && groups > cu_count;
@@ -288,15 +294,15 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // with the codes in the register ring instead.
         const int64_t steps = d->K / (4 * k_per_chunk(d->format));
         const int64_t spw = (steps + c.ksplit - 1) / c.ksplit;
-        bool stage = lds_a + 16 + lds_red <= kLdsBytes && spw >= 8;
-        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_a + 16 + lds_red <= kLdsBytes;
+        bool stage = abytes16 + lds_red <= kLdsBytes && spw >= 8;
+        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = abytes16 + lds_red <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
         // register-ring depth: 8 slots when a wave's steps per tile are a multiple of 8
         // or many (no idle padded slots to speak of), else 4; or forced
         const uint32_t fdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
         const bool deep8 = fdep ? fdep == 2 : (spw % 8 == 0 || spw >= 32);
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
-        c.lds_bytes = (int)(lds_red + (stage ? 16 + ((lds_a + 15) & ~15LL) : 0));
+        c.lds_bytes = (int)(lds_red + (stage ? abytes16 : 0));
         int64_t grid = groups;
         if (stage) {
             int64_t per_cu = c.lds_bytes > 0 ? kLdsBytes / c.lds_bytes : 8;
