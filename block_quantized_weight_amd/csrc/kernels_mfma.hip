@@ -682,7 +682,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     const int mdz = zbc >= 4 ? zbc / 4 : 1;
     const int srow = a.nblk * SB;                                     // scale row bytes
     const int zrow = a.zstride;                                       // zero-point row bytes
-    const int ops = SS + nsd + (ZPP ? 1 : 0);                         // DMAs per slot
+    constexpr int OPS = SS + Gm::NSD + (ZPP ? 1 : 0);                  // DMAs per slot
 
     // Lane constants of the DMA sources, relative to a uniform per-slot base address
     // (the tile's first column at the slot's first chunk or metadata dword): the
@@ -696,10 +696,13 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
         ccol[d] = (uint32_t)cn * (uint32_t)a.col_bytes;
         cchk[d] = (uint32_t)((lane % CS) ^ (cn % CS)) * 16u;
     }
+    // every slot issues all NSD scale DMAs (a DMA past the window's nsd repeats the
+    // last one into an unused part of the area), so the DMA count per slot is a
+    // compile-time constant and the waits are immediates
     uint32_t scol[Gm::NSD], sq4[Gm::NSD];
 #pragma unroll
     for (int e = 0; e < Gm::NSD; ++e) {
-        const int idx = e * 64 + lane;
+        const int idx = (e < nsd ? e : nsd - 1) * 64 + lane;
         int cn = idx / mds, q = idx - (idx / mds) * mds;
         if (cn > 15) cn = 15, q = mds - 1;
         scol[e] = (uint32_t)(cn * srow);
@@ -713,17 +716,26 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
         zq4 = (uint32_t)(4 * q);
     }
 
-    // issue cursor
+    // issue cursor: tile, slot within the column, ring buffer, and the tile's
+    // first-column addresses and column clamps (uniform; advanced per tile)
     int64_t itile = gw;
-    int isl = 0;
-    auto issue = [&](int r) {
-        unsigned char *slot = ring + r * SLOT;
-        const int64_t t0 = itile * 16;
-        const int64_t lastc = a.N - 1 - t0;
+    int isl = 0, iring = 0;
+    const uint8_t *wt = a.W + gw * 16 * a.col_bytes;
+    const uint8_t *st = (const uint8_t *)a.scales + gw * 16 * srow;
+    const uint8_t *zt = ZPP ? a.zp + gw * 16 * zrow : nullptr;
+    uint32_t limcw = 0, limcs = 0, limcz = 0;
+    auto tile_limits = [&]() {
+        const int64_t lastc = a.N - 1 - itile * 16;
         const uint32_t limc = (uint32_t)(lastc < 15 ? lastc : 15);  // last column in the tile
+        limcw = limc * (uint32_t)a.col_bytes;
+        limcs = limc * (uint32_t)srow;
+        limcz = limc * (uint32_t)zrow;
+    };
+    tile_limits();
+    auto issue = [&]() {
+        unsigned char *slot = ring + iring * SLOT;
         // codes: DMA d moves columns d*CPD .. d*CPD + CPD - 1
-        const uint8_t *wbase = a.W + t0 * a.col_bytes + (int64_t)isl * (CS * 16);
-        const uint32_t limcw = limc * (uint32_t)a.col_bytes;
+        const uint8_t *wbase = wt + isl * (CS * 16);
         const uint32_t limj = (uint32_t)(nch - 1 - isl * CS) * 16u;
 #pragma unroll
         for (int d = 0; d < 16 / Gm::CPD; ++d) {
@@ -732,28 +744,29 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
         }
         // scale windows: dword q of column cn's window
         const int wbs = (isl * sbc) & ~3;
-        const uint8_t *sbase = (const uint8_t *)a.scales + t0 * srow + wbs;
-        const uint32_t limcs = limc * (uint32_t)srow;
+        const uint8_t *sbase = st + wbs;
         const uint32_t limq = (uint32_t)(srow - wbs - 4);
 #pragma unroll
         for (int e = 0; e < Gm::NSD; ++e) {
-            if (e < nsd) {
-                const uint32_t off = (scol[e] < limcs ? scol[e] : limcs) + (sq4[e] < limq ? sq4[e] : limq);
-                dma_to_lds<4>(sbase + off, slot + Gm::CODEB + e * 256);
-            }
+            const uint32_t off = (scol[e] < limcs ? scol[e] : limcs) + (sq4[e] < limq ? sq4[e] : limq);
+            dma_to_lds<4>(sbase + off, slot + Gm::CODEB + e * 256);
         }
         if constexpr (ZPP) {
             const int zb0 = (FMT == FMT_U4) ? ((isl * bps) >> 1) : isl * bps;
             const int wbz = zb0 & ~3;
-            const uint8_t *zbase = a.zp + t0 * zrow + wbz;
-            const uint32_t limcz = limc * (uint32_t)zrow;
+            const uint8_t *zbase = zt + wbz;
             const uint32_t limqz = (uint32_t)(zrow - wbz - 4);
             const uint32_t off = (zcol < limcz ? zcol : limcz) + (zq4 < limqz ? zq4 : limqz);
             dma_to_lds<4>(zbase + off, slot + Gm::CODEB + Gm::NSD * 256);
         }
+        if (++iring == R) iring = 0;
         if (++isl == nslots) {
             isl = 0;
             itile += nw;
+            wt += nw * 16 * a.col_bytes;
+            st += nw * 16 * srow;
+            if constexpr (ZPP) zt += nw * 16 * zrow;
+            tile_limits();
         }
     };
 
@@ -761,7 +774,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     // the weight fetch)
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
-        if (r < total) issue(r);
+        if (r < total) issue();
     if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
     stage_a<FMT, 4>(a, sA, astride);
     __syncthreads();
@@ -873,15 +886,12 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     };
 
     // slot i's DMAs are done once at most the later issued slots' remain
-    auto wait_slot = [&](int64_t i) {
-        const int64_t later = total - 1 - i < R - 2 ? total - 1 - i : R - 2;
-        wait_vmcnt_dyn((int)later * ops);
-    };
+    auto wait_slot = [&](int64_t i) { wait_slots<R - 2, OPS>(total - 1 - i); };
     auto win_ssub = [&](int sl) { return (sl * sbc) & 3; };  // nonzero only for windows under a dword
     auto win_zsub = [&](int sl) { return ((FMT == FMT_U4) ? ((sl * bps) >> 1) : sl * bps) & 3; };
 
     int64_t ctile = gw;
-    int csl = 0;
+    int csl = 0, cring = 0;
     In cur, nxt;
     if (total > 0) {
         wait_slot(0);
@@ -889,10 +899,11 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     }
 #pragma unroll 1
     for (int64_t i = 0; i < total; ++i) {
-        const unsigned char *slot = ring + (i % R) * SLOT;
+        const unsigned char *slot = ring + cring * SLOT;
+        const int nring = cring + 1 == R ? 0 : cring + 1;
         // refill the slot consumed in the previous iteration (all its reads have
         // returned: the last was waited for by that iteration's last step)
-        if (i + R - 1 < total) issue((int)((i + R - 1) % R));
+        if (i + R - 1 < total) issue();
         const int ssub = win_ssub(csl), zsub = win_zsub(csl);
 #pragma unroll
         for (int st = 0; st < SS; ++st) {
@@ -902,11 +913,12 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
                 // the next slot's first step: wait for its DMAs, then read it
                 const int nsl = csl + 1 == nslots ? 0 : csl + 1;
                 wait_slot(i + 1);
-                read_step(ring + ((i + 1) % R) * SLOT, 0, nsl * CS, win_ssub(nsl), win_zsub(nsl), nxt);
+                read_step(ring + nring * SLOT, 0, nsl * CS, win_ssub(nsl), win_zsub(nsl), nxt);
             }
             compute(cur, st, csl * CS + 4 * st < nch);
             cur = nxt;
         }
+        cring = nring;
         if (++csl == nslots) {
             finish_tile<ACT, RG>(a, acc, nullptr, wave, lane, 1, 0, g, true, ctile * 16 + n);
 #pragma unroll

@@ -156,6 +156,19 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     }
 }
 
+// Wait until at most min(left, K) groups of OPS loads remain in flight (uniform
+// left >= 0): a compile-time count in each branch.
+template <int K, int OPS>
+__device__ __forceinline__ void wait_slots(int64_t left) {
+    static_assert(K * OPS <= 63, "vmcnt holds at most 63");
+    if constexpr (K <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (left >= K) wait_vmcnt<K * OPS>();
+        else wait_slots<K - 1, OPS>(left);
+    }
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land at
