@@ -772,10 +772,12 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 
     // the first R - 1 slots in flight, then the activations staged (the copy overlaps
     // the weight fetch)
+    // (the zero block is stored first: an LDS store after the DMAs waits for them, as
+    // the compiler cannot tell the DMAs' LDS writes from the store's address)
+    if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         if (r < total) issue();
-    if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
     stage_a<FMT, 4>(a, sA, astride);
     __syncthreads();
     if constexpr (F::ZP) {
