@@ -24,6 +24,7 @@ FAMILY_NAMES = {v: k for k, v in FAMILIES.items()}
 QGEMV_OK = 0
 FLAG_FAMILY_MASK = 0x0000000F
 FLAG_KSPLIT_SHIFT = 8
+FLAG_STREAM_NWG_SHIFT = 12
 FLAG_NO_MFMA = 0x00010000
 FLAG_STAGE_A_OFF = 0x00020000
 FLAG_STAGE_A_ON = 0x00040000

@@ -496,12 +496,21 @@ hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// workgroups of 4 waves, or of 16 (one row, one column per wave) when variant bit 3
-// asks for them
+// workgroups of 4 waves; of 16 for one row with one column per wave; of 4, 8, 12 or
+// 16 for several rows
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
 hipError_t go_stream1_k(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    if constexpr (MT == 1 && CPW == 1) {
-        if (cfg.waves_per_wg == 16) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+    if constexpr (MT == 1) {
+        if constexpr (CPW == 1) {
+            if (cfg.waves_per_wg == 16) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+        }
+    } else {
+        switch (cfg.waves_per_wg) {
+        case 8: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 8>(cfg, a, s);
+        case 12: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 12>(cfg, a, s);
+        case 16: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+        default: break;
+        }
     }
     if (cfg.waves_per_wg != 4) return hipErrorInvalidValue;
     return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 4>(cfg, a, s);

@@ -38,12 +38,13 @@ int validate_desc(const qgemv_desc *d) {
                            QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
                            QGEMV_FLAG_RING_ON | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
                            QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK |
-                           QGEMV_FLAG_STREAM_WIDE_WG;
+                           QGEMV_FLAG_STREAM_WIDE_WG | QGEMV_FLAG_STREAM_NWG_MASK;
     if (d->flags & ~known) return QGEMV_E_ARG;
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
     const uint32_t ks = (d->flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     if (ks > 8) return QGEMV_E_ARG;
+    if (((d->flags & QGEMV_FLAG_STREAM_NWG_MASK) >> QGEMV_FLAG_STREAM_NWG_SHIFT) > 4) return QGEMV_E_ARG;
     if (((d->flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT) > 2) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_STAGE_A_OFF) && (d->flags & QGEMV_FLAG_STAGE_A_ON)) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_RING_OFF) && (d->flags & QGEMV_FLAG_RING_ON)) return QGEMV_E_ARG;
@@ -181,9 +182,27 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     // 4096 x 4096 8-bit codes); past 16 per CU the 16-wave groups no longer spread
     // evenly over the CUs and lose.
     const bool wide_auto = !fc && !fw && groups >= 8LL * cu_count && groups <= 16LL * cu_count;
-    const int nwg = ((flags & QGEMV_FLAG_STREAM_WIDE_WG) || wide_auto) && mt == 1 && cpw == 1 ? 16 : 4;
+    int nwg = ((flags & QGEMV_FLAG_STREAM_WIDE_WG) || wide_auto) && mt == 1 && cpw == 1 ? 16 : 4;
+    // Several rows: 4, 8, 12 or 16 waves share one staged copy of the rows. The staged
+    // rows bound the workgroups resident per CU (res); when 16-wave workgroups would
+    // hold every column group at once, the fewest waves per workgroup that do are
+    // taken and the grid is one group per wave. (FP8 5120 x 6144 at M = 4: 4-wave
+    // workgroups hold 8 waves per CU and run 2.5 rounds, 15.6 us; 12-wave ones hold
+    // all 5120 columns, 11.5 us.)
+    const uint32_t fn = (flags & QGEMV_FLAG_STREAM_NWG_MASK) >> QGEMV_FLAG_STREAM_NWG_SHIFT;
+    int64_t res = kLdsBytes / (lds > 0 ? lds : 1);
+    if (res < 1) res = 1;
+    const int64_t need = (groups + cu_count - 1) / cu_count;  // column groups per CU
+    bool one_round = false;
+    if (mt > 1 && fn) {
+        nwg = 4 * (int)fn;
+    } else if (mt > 1 && !fw && 16 * res >= need) {
+        nwg = 4;
+        while (nwg * res < need) nwg += 4;
+        one_round = true;
+    }
     const int64_t wgs = (groups + nwg - 1) / nwg;
-    int64_t cap = (int64_t)cu_count * wpc / nwg;
+    int64_t cap = one_round ? res * cu_count : (int64_t)cu_count * wpc / nwg;
     if (cap < 1) cap = 1;
     c->rows_per_pass = mt;
     c->passes = 1;

@@ -85,8 +85,10 @@ enum qgemv_family {
 };
 
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
- * Bits 8..15: forced K split of the MFMA family (0 = automatic; otherwise 1..8 waves
- * share the K range of a column tile). Bit 16: never pick the MFMA family.
+ * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1..8 waves
+ * share the K range of a column tile). Bits 12..14: waves per workgroup of the
+ * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
+ * automatic). Bit 15: reserved (0). Bit 16: never pick the MFMA family.
  * Bits 17/18: MFMA family never / always stages the activations in LDS (when they
  * fit); neither set = automatic. Bits 19/20: MFMA family never / always (when
  * eligible) streams the weights through the LDS DMA ring.
@@ -101,7 +103,9 @@ enum qgemv_family {
  * the K split; they exist for A/B comparisons and tuning. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
-#define QGEMV_FLAG_KSPLIT_MASK 0x0000FF00u
+#define QGEMV_FLAG_KSPLIT_MASK 0x00000F00u
+#define QGEMV_FLAG_STREAM_NWG_SHIFT 12
+#define QGEMV_FLAG_STREAM_NWG_MASK 0x00007000u
 #define QGEMV_FLAG_NO_MFMA 0x00010000u
 #define QGEMV_FLAG_STAGE_A_OFF 0x00020000u
 #define QGEMV_FLAG_STAGE_A_ON 0x00040000u

@@ -210,9 +210,12 @@ def test_multi_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act
     ok, ratio, _, _ = gu.check_full(prob, M, Yc, strict=False)
     assert ok, ratio
     for cpw in (1, 2):
-        Ya, pa = gu.run_gpu(prob, M, flags=1 | ({1: 1, 2: 2}[cpw] << bqw.FLAG_STREAM_CPW_SHIFT))
-        assert pa["variant"] & 1 and pa["rows_per_pass"] >= M and pa["cols_per_wave"] == cpw, pa
-        assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, pa)
+        for nwg in (0, 1, 2, 3, 4):  # automatic, then 4, 8, 12 and 16 waves per workgroup
+            Ya, pa = gu.run_gpu(prob, M, flags=1 | ({1: 1, 2: 2}[cpw] << bqw.FLAG_STREAM_CPW_SHIFT)
+                                | (nwg << bqw.FLAG_STREAM_NWG_SHIFT))
+            assert pa["variant"] & 1 and pa["rows_per_pass"] >= M and pa["cols_per_wave"] == cpw, pa
+            assert nwg == 0 or pa["waves_per_wg"] == 4 * nwg, pa
+            assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, nwg, pa)
 
 
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
