@@ -357,7 +357,9 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     // or a use, so the compiler's wait before a batch is consumed leaves the other
     // batch in flight. The last one or two batches are drained without refills, so
     // nothing is fetched past the wave's work. (Scheduling barriers keep each refill
-    // below the last use of the buffer's old contents.)
+    // below the last use of the buffer's old contents.) A third buffer (two batches in
+    // flight) measured slower: the registers it takes cost more resident waves than
+    // the extra depth brings.
     B b0, b1;
     if (total > 0) issue(b0);  // the first batch's fetch overlaps the staging below
     stage_rows<FMT, ACT, H>(a, sP, sS, rowq, rows);
@@ -496,8 +498,15 @@ hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// workgroups of 4 waves; of 16 for one row with one column per wave; of 4, 8, 12 or
-// 16 for several rows
+// Workgroups of 4 waves; of 16 for one row with one column per wave; of 4, 8, 12 or
+// 16 for several rows, as far as the kernel fits the register share that many waves
+// per CU leave without spilling (the dispatcher picks within the same limits): 8 with
+// two columns per wave, 12 for four rows of 4-bit codes with two blocks per chunk.
+template <int FMT, int MT, int CPW, int H>
+constexpr int stream_rows_max_wg() {
+    return CPW == 2 ? 8 : ((FMT == FMT_U4 && H == 2 && MT == 4) ? 12 : 16);
+}
+
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
 hipError_t go_stream1_k(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if constexpr (MT == 1) {
@@ -505,10 +514,16 @@ hipError_t go_stream1_k(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
             if (cfg.waves_per_wg == 16) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
         }
     } else {
+        constexpr int MX = stream_rows_max_wg<FMT, MT, CPW, H>();
+        if (cfg.waves_per_wg > MX) return hipErrorInvalidValue;
         switch (cfg.waves_per_wg) {
         case 8: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 8>(cfg, a, s);
-        case 12: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 12>(cfg, a, s);
-        case 16: return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+        case 12:
+            if constexpr (MX >= 12) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 12>(cfg, a, s);
+            break;
+        case 16:
+            if constexpr (MX >= 16) return go_stream1_w<FMT, ACT, MT, CPW, UNR, H, 16>(cfg, a, s);
+            break;
         default: break;
         }
     }

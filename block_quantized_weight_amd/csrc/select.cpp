@@ -194,9 +194,13 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     if (res < 1) res = 1;
     const int64_t need = (groups + cu_count - 1) / cu_count;  // column groups per CU
     bool one_round = false;
+    // the most waves per workgroup the kernel fits without spilling (kernel side:
+    // stream_rows_max_wg)
+    const bool u4_two_blocks = d->format == QGEMV_FMT_U4 && d->block_size == 16;
+    const int max_wg = cpw == 2 ? 8 : ((u4_two_blocks && mt == 4) ? 12 : 16);
     if (mt > 1 && fn) {
-        nwg = 4 * (int)fn;
-    } else if (mt > 1 && !fw && 16 * res >= need) {
+        nwg = 4 * (int)fn < max_wg ? 4 * (int)fn : max_wg;
+    } else if (mt > 1 && !fw && max_wg * res >= need) {
         nwg = 4;
         while (nwg * res < need) nwg += 4;
         one_round = true;

@@ -88,7 +88,10 @@ enum qgemv_family {
  * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1..8 waves
  * share the K range of a column tile). Bits 12..14: waves per workgroup of the
  * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
- * automatic). Bit 15: reserved (0). Bit 16: never pick the MFMA family.
+ * automatic; capped at 8 with two columns per wave and at 12 for four rows of 4-bit
+ * codes in 16-wide blocks, the most those fit without spilling registers). Bit 15:
+ * reserved (0).
+ * Bit 16: never pick the MFMA family.
  * Bits 17/18: MFMA family never / always stages the activations in LDS (when they
  * fit); neither set = automatic. Bits 19/20: MFMA family never / always (when
  * eligible) streams the weights through the LDS DMA ring.
@@ -151,8 +154,8 @@ typedef struct qgemv_plan_info {
                                 LDS, bit 1 = weights through the LDS DMA ring (bits 4..5 its
                                 shape: 0 = 4-step slots x 3, 1 = 2-step x 5, 2 = 2-step x 4),
                                 bit 3 = 8-slot register ring (else 4).
-                                Streaming: bit 0 = persistent one-row kernel, bits 1..2 = chunks
-                                per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
+                                Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
+                                bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
 } qgemv_plan_info;
 
 typedef struct qgemv_handle qgemv_handle;

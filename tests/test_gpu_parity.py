@@ -214,7 +214,8 @@ def test_multi_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act
             Ya, pa = gu.run_gpu(prob, M, flags=1 | ({1: 1, 2: 2}[cpw] << bqw.FLAG_STREAM_CPW_SHIFT)
                                 | (nwg << bqw.FLAG_STREAM_NWG_SHIFT))
             assert pa["variant"] & 1 and pa["rows_per_pass"] >= M and pa["cols_per_wave"] == cpw, pa
-            assert nwg == 0 or pa["waves_per_wg"] == 4 * nwg, pa
+            cap = 8 if cpw == 2 else (12 if (fmt == "u4" and bs == 16 and M > 2) else 16)
+            assert nwg == 0 or pa["waves_per_wg"] == min(4 * nwg, cap), pa
             assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, nwg, pa)
 
 
