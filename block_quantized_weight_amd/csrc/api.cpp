@@ -45,7 +45,7 @@ uint32_t read_env_flags() {
     const char *ks = getenv("QGEMV_FORCE_KSPLIT");
     if (ks && *ks) {
         long v = strtol(ks, nullptr, 10);
-        if (v > 0 && v <= 8) f |= ((uint32_t)v << QGEMV_FLAG_KSPLIT_SHIFT);
+        if (v == 1 || v == 2 || v == 4 || v == 8) f |= ((uint32_t)v << QGEMV_FLAG_KSPLIT_SHIFT);
     }
     if (env_true("QGEMV_NO_MFMA")) f |= QGEMV_FLAG_NO_MFMA;
     return f;

@@ -43,7 +43,7 @@ int validate_desc(const qgemv_desc *d) {
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
     const uint32_t ks = (d->flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
-    if (ks > 8) return QGEMV_E_ARG;
+    if (ks > 8 || (ks & (ks - 1))) return QGEMV_E_ARG;  // 1, 2, 4 or 8: whole tiles per 8-wave workgroup
     if (((d->flags & QGEMV_FLAG_STREAM_NWG_MASK) >> QGEMV_FLAG_STREAM_NWG_SHIFT) > 4) return QGEMV_E_ARG;
     if (((d->flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT) > 2) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_STAGE_A_OFF) && (d->flags & QGEMV_FLAG_STAGE_A_ON)) return QGEMV_E_ARG;

@@ -85,8 +85,8 @@ enum qgemv_family {
 };
 
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
- * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1..8 waves
- * share the K range of a column tile). Bits 12..14: waves per workgroup of the
+ * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1, 2, 4 or
+ * 8 waves share the K range of a column tile). Bits 12..14: waves per workgroup of the
  * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
  * automatic; capped at 8 with two columns per wave and at 12 for four rows of 4-bit
  * codes in 16-wide blocks, the most those fit without spilling registers). Bit 15:

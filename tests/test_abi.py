@@ -56,7 +56,7 @@ def _sel(**kw):
     (dict(block_size=48), 3), (dict(block_size=8), 3), (dict(fmt="nvfp4", block_size=32), 3),
     (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
     (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
-    (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=1 << 15), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
+    (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=3 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=1 << 15), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
     (dict(cu_count=0), 7),
 ])
 def test_select_rejects_invalid_arguments(kw, status):
