@@ -61,6 +61,7 @@ class Desc(ctypes.Structure):
         ("zero_points", ctypes.c_void_p),
         ("tensor_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("bias", ctypes.c_void_p),
     ]
 
 
@@ -117,10 +118,10 @@ def _ptr(x: Any) -> Optional[int]:
 
 
 def make_desc(fmt: str, act: str, N: int, K: int, block_size: int, W: Any, scales: Any,
-              zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0) -> Desc:
+              zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0, bias: Any = None) -> Desc:
     return Desc(ctypes.sizeof(Desc), FORMATS.get(fmt, 0) if isinstance(fmt, str) else int(fmt),
                 ACT_DTYPES.get(act, 0) if isinstance(act, str) else int(act), int(block_size), int(N), int(K),
-                _ptr(W), _ptr(scales), _ptr(zero_points), float(tensor_scale), int(flags))
+                _ptr(W), _ptr(scales), _ptr(zero_points), float(tensor_scale), int(flags), _ptr(bias))
 
 
 def _plan_dict(p: PlanInfo) -> Dict[str, Any]:
@@ -130,9 +131,10 @@ def _plan_dict(p: PlanInfo) -> Dict[str, Any]:
 
 
 def select(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count: int = 256,
-           flags: int = 0, W: Any = 0x1000, scales: Any = 0x1000, zero_points: Any = None) -> Dict[str, Any]:
+           flags: int = 0, W: Any = 0x1000, scales: Any = 0x1000, zero_points: Any = None,
+           bias: Any = None) -> Dict[str, Any]:
     """Pure host dispatcher query (no GPU): the launch for M rows at cu_count CUs."""
-    d = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, 1.0, flags)
+    d = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, 1.0, flags, bias)
     out = PlanInfo()
     rc = lib().qgemv_select(ctypes.byref(d), int(M), int(cu_count), ctypes.byref(out))
     if rc != QGEMV_OK:
@@ -143,16 +145,17 @@ def select(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count
 class QGemv:
     """A quantized weight resident on the GPU, ready to multiply activations.
 
-    W, scales and zero_points are device buffers (torch tensors or raw device
-    pointers) in the layouts documented in include/qgemv.h; they must stay alive
-    as long as this object.
+    W, scales, zero_points and the optional bias ([N], activation dtype) are device
+    buffers (torch tensors or raw device pointers) in the layouts documented in
+    include/qgemv.h; they must stay alive as long as this object.
     """
 
     def __init__(self, fmt: str, act: str, N: int, K: int, block_size: int, W: Any, scales: Any,
-                 zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0, device: int = -1):
+                 zero_points: Any = None, tensor_scale: float = 1.0, flags: int = 0, device: int = -1,
+                 bias: Any = None):
         self.fmt, self.act, self.N, self.K, self.block_size = fmt, act, int(N), int(K), int(block_size)
-        self._keep = (W, scales, zero_points)
-        self._desc = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, tensor_scale, flags)
+        self._keep = (W, scales, zero_points, bias)
+        self._desc = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, tensor_scale, flags, bias)
         h = ctypes.c_void_p()
         rc = lib().qgemv_create(ctypes.byref(h), ctypes.byref(self._desc), int(device))
         if rc != QGEMV_OK:
@@ -207,6 +210,8 @@ def upload(problem, device: str = "cuda:0", flags: int = 0) -> "tuple[QGemv, dic
     t["zp"] = None if problem.zp is None else dev(problem.zp)
     tdt = torch.float16 if problem.act == "f16" else torch.bfloat16
     t["A"] = dev(problem.A.view(np.int16)).view(tdt)
+    bias = getattr(problem, "bias", None)
+    t["bias"] = None if bias is None else dev(bias.view(np.int16)).view(tdt)
     q = QGemv(problem.fmt, problem.act, problem.N, problem.K, problem.bs, t["W"], t["scales"], t["zp"],
-              problem.tensor_scale, flags)
+              problem.tensor_scale, flags, bias=t["bias"])
     return q, t

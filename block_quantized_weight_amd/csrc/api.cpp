@@ -70,6 +70,7 @@ void fill_args(const qgemv_handle *h, const void *A, void *Y, int M, qgemv::KArg
     a->M = M;
     a->ksplit = 1;
     a->tscale = (d.format == QGEMV_FMT_NVFP4) ? d.tensor_scale : 1.0f;
+    a->bias = d.bias;
 }
 
 void to_info(const qgemv::LaunchCfg &c, qgemv_plan_info *o) {

@@ -490,7 +490,7 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
             for (int r = 0; r < 4; ++r) tot[r] = sum_groups(acc[rg][r]);
             const float v = (g == 0) ? tot[0] : (g == 1) ? tot[1] : (g == 2) ? tot[2] : tot[3];
             const int row = 4 * rg + g;
-            if (n < a.N && row < a.M) store_out<ACT>(a.Y, (int64_t)row * a.N + n, v * a.tscale);
+            if (n < a.N && row < a.M) store_out<ACT>(a.Y, (int64_t)row * a.N + n, add_bias<ACT>(a.bias, n, v * a.tscale));
         }
     }
 }

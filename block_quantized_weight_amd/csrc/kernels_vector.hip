@@ -117,7 +117,8 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const float s = wave_sum(acc[i][m]) * a.tscale;
-                if (lane == 0 && nbase + i < a.N && rlive[m]) store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, s);
+                if (lane == 0 && nbase + i < a.N && rlive[m])
+                    store_out<ACT>(a.Y, (int64_t)(m0 + m) * a.N + nbase + i, add_bias<ACT>(a.bias, nbase + i, s));
             }
         }
     }
@@ -343,7 +344,7 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                 for (int m = 0; m < MT; ++m) {
                     if (MT == 1 || m < a.M) {
                         const float v = wave_sum(acc[i][m]) * a.tscale;
-                        if (lane == 0 && n < a.N) store_out<ACT>(a.Y, (int64_t)m * a.N + n, v);
+                        if (lane == 0 && n < a.N) store_out<ACT>(a.Y, (int64_t)m * a.N + n, add_bias<ACT>(a.bias, n, v));
                     }
                     acc[i][m] = 0.0f;
                 }
@@ -438,7 +439,7 @@ __global__ void __launch_bounds__(256) k_generic(KArgs a) {
         for (int m = 0; m < 16; ++m) {
             if (m < a.M) {
                 const float s = wave_sum(acc[m]) * a.tscale;
-                if (lane == 0) store_out<ACT>(a.Y, (int64_t)m * a.N + n, s);
+                if (lane == 0) store_out<ACT>(a.Y, (int64_t)m * a.N + n, add_bias<ACT>(a.bias, n, s));
             }
         }
     }

@@ -24,6 +24,7 @@ struct KArgs {
     int32_t M;
     int32_t ksplit;          // waves sharing one column tile's K range
     float tscale;            // nvfp4 tensor scale (1 otherwise)
+    const void *bias;        // [N] bias in the activation dtype, or nullptr
 };
 
 struct LaunchCfg {

@@ -101,6 +101,17 @@ __device__ __forceinline__ void store_out(void *Y, int64_t idx, float v) {
     }
 }
 
+// v + bias[n] in fp32 (the bias in the activation dtype), or v as it is without a
+// bias: added once, after every scale, right before the rounding to the output type.
+// The bias pointer is uniform, so the test is a scalar branch.
+template <int ACT>
+__device__ __forceinline__ float add_bias(const void *bias, int64_t n, float v) {
+    if (!bias) return v;
+    const uint16_t bits = ((const uint16_t *)bias)[n];
+    if constexpr (ACT == ACT_F16) return v + (float)__builtin_bit_cast(_Float16, bits);
+    else return v + __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+
 // Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 and is
 // returned to every lane through readlane. Fixed order: the result depends only on
 // the 64 inputs.

@@ -31,6 +31,7 @@ int validate_desc(const qgemv_desc *d) {
     if (d->act_dtype != QGEMV_ACT_F16 && d->act_dtype != QGEMV_ACT_BF16) return QGEMV_E_FORMAT;
     if (!d->W || !d->scales) return QGEMV_E_NULL;
     if ((d->format == QGEMV_FMT_FP8 || d->format == QGEMV_FMT_NVFP4) && d->zero_points) return QGEMV_E_FORMAT;
+    if ((uintptr_t)d->bias % 2) return QGEMV_E_ARG;  // read as 16-bit values
     if (d->N < 1 || d->K < 1) return QGEMV_E_SHAPE;
     if (!valid_block(d->format, d->block_size)) return QGEMV_E_BLOCK;
     if (d->K % d->block_size) return QGEMV_E_SHAPE;

@@ -49,7 +49,8 @@ class Problem:
       fp8   W [N, K] uint8 E4M3 codes; scales [N, K/bs] float32; no zp
       nvfp4 W [N, K/2] uint8 packed E2M1, low nibble = lower k;
             scales [N, K/16] uint8 E4M3 codes; tensor_scale float32; no zp
-    A is [M_max, K] activation bits (uint16) of dtype ``act`` (f16 or bf16).
+    A is [M_max, K] activation bits (uint16) of dtype ``act`` (f16 or bf16); the
+    optional bias is [N] bits of the same dtype, added to every row of Y.
     """
 
     name: str
@@ -65,6 +66,7 @@ class Problem:
     A: np.ndarray
     ms: Tuple[int, ...] = (1,)
     seed: int = 0
+    bias: Optional[np.ndarray] = None  # [N] activation bits (uint16), or None
 
     @property
     def m_max(self) -> int:
@@ -154,8 +156,12 @@ def make_problem(
     fp8_scale_exp: Tuple[float, float] = (-8.0, -4.0),
     tensor_scale: float = 0.01,
     with_zp: bool = True,
+    with_bias: bool = False,
+    bias_sigma: float = 0.5,
 ) -> Problem:
-    """Draw one problem: A, then codes, then zero points, then scales."""
+    """Draw one problem: A, then codes, then zero points, then scales, then (when
+    asked) the bias, N(0, bias_sigma) rounded to the activation dtype. The bias is
+    drawn last so the other arrays do not depend on whether it is drawn."""
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
     if fmt == "nvfp4" and bs != 16:
@@ -193,10 +199,12 @@ def make_problem(
         idx = rng.integers(0, NVFP4_SCALE_CODES.size, size=(N, nblk))
         scales = NVFP4_SCALE_CODES[idx]
         ts = float(np.float32(tensor_scale))
+    bias = activation_bits(rng.standard_normal(N) * bias_sigma, act).reshape(N) if with_bias else None
     return Problem(
         name=name, fmt=fmt, act=act, N=N, K=K, bs=bs, W=np.ascontiguousarray(W),
         scales=np.ascontiguousarray(scales), zp=None if zp is None else np.ascontiguousarray(zp),
         tensor_scale=ts, A=np.ascontiguousarray(A), ms=tuple(ms), seed=seed,
+        bias=None if bias is None else np.ascontiguousarray(bias),
     )
 
 

@@ -1,9 +1,9 @@
 /*
  * qgemv — block-scaled small-M decode GEMV for AMD Instinct MI355X (gfx950)
  *
- *     Y[M, N] = A[M, K] . dequant(W)[N, K]^T,   1 <= M <= 16,
+ *     Y[M, N] = A[M, K] . dequant(W)[N, K]^T (+ bias[N]),   1 <= M <= 16,
  *
- * with A and Y in fp16 or bf16 and fp32 accumulation. The weight W is quantized
+ * with A, Y and the optional bias in fp16 or bf16 and fp32 accumulation. The weight W is quantized
  * in blocks along K in one of four formats:
  *
  *   QGEMV_FMT_U4     4-bit unsigned codes, fp16 scale and 4-bit zero point per
@@ -29,6 +29,13 @@
  * A NULL zero-point pointer means the midpoint 2^(bits-1). FP8 and NVFP4 take no
  * zero points.
  *
+ * Optional bias: one value per output column, in the activation dtype, added in
+ * fp32 to the product of every row before the single rounding to the output type
+ * (after the NVFP4 tensor scale, which belongs to dequant(W)). The pages' tests
+ * cover such a bias ("[CUDA] Block-scaled MatMul decode GEMV: tensor cores, packed
+ * FP4 decode and M-tiling", reviewed-changes table; "[CUDA] Pin FP8 GEMV residency
+ * for grids just past two blocks per SM", review thread). NULL means none.
+ *
  * All pointers passed to qgemv_create and qgemv_run are DEVICE pointers, owned by
  * the caller. The handle keeps the weight pointers (not copies) and the caller
  * keeps them alive until qgemv_destroy. The library allocates no device memory.
@@ -46,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QGEMV_ABI_VERSION 1
+#define QGEMV_ABI_VERSION 2
 #define QGEMV_MAX_M 16
 
 /* Weight formats. */
@@ -138,6 +145,8 @@ typedef struct qgemv_desc {
     const void *zero_points; /* device: zero points, or NULL */
     float tensor_scale;    /* NVFP4 tensor scale (multiplies); ignored otherwise */
     uint32_t flags;        /* QGEMV_FLAG_* */
+    const void *bias;      /* device: [N] bias in the activation dtype, or NULL; kept by
+                              the handle like the weight pointers (ABI version 2) */
 } qgemv_desc;
 
 /* What qgemv_plan / qgemv_select report about a launch. */

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are the only users. The product path never imports
 this package, and this package imports nothing from the product.
 
-The C file computes Y = A . dequant(W)^T and S = sum |a*w| in float64 with plain
-loops; see its header for the pages it follows. This module only marshals
+The C file computes Y = A . dequant(W)^T (+ an optional per-column bias) and
+S = sum |a*w| in float64 with plain loops; see its header for the pages it follows. This module only marshals
 numpy arrays into it, builds it with gcc when the shared object is missing, and
 states the acceptance bound the GPU results are held to.
 """
@@ -56,6 +56,7 @@ class _Problem(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("zp", ctypes.c_void_p),
         ("tensor_scale", ctypes.c_double),
+        ("bias", ctypes.c_void_p),
     ]
 
 
@@ -91,10 +92,13 @@ class _Bound:
         self.W = np.ascontiguousarray(prob.W)
         self.scales = np.ascontiguousarray(prob.scales)
         self.zp = None if prob.zp is None else np.ascontiguousarray(prob.zp)
+        bias = getattr(prob, "bias", None)
+        self.bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
         self.s = _Problem(
             FORMAT_CODES[prob.fmt], ACT_CODES[prob.act], int(prob.bs), 0, int(prob.N), int(prob.K),
             self.W.ctypes.data, self.scales.ctypes.data,
             None if self.zp is None else self.zp.ctypes.data, float(prob.tensor_scale),
+            None if self.bias is None else self.bias.ctypes.data,
         )
 
 

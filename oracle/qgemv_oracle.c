@@ -29,6 +29,14 @@
  * nibbles are packed low nibble first, for weights and for 4-bit zero points; the
  * 4-bit zero-point row of a column holds ceil(blocks/2) bytes; a missing zero
  * point means 2^(bits-1); the NVFP4 tensor scale multiplies.
+ *
+ * Optional bias ("[CUDA] Block-scaled MatMul decode GEMV: ...", reviewed-changes
+ * table: the FP8 and FP4 tests cover a bias; "[CUDA] Pin FP8 GEMV residency for
+ * grids just past two blocks per SM", review thread: the tests cover an optional
+ * bias): one value per output column in the activation dtype, added to the product
+ * of every row, Y[m, n] = sum_k A[m, k] * dequant(W)[n, k] + bias[n] (the tensor
+ * scale is part of dequant(W) and does not touch the bias). S stays the sum of
+ * |a*w|: the bias is added once, exactly, in float64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,6 +62,7 @@ typedef struct {
     const void *scales;
     const uint8_t *zp; /* NULL allowed for u4/u8 */
     double tensor_scale;
+    const uint16_t *bias; /* NULL, or [N] activation-dtype bits added to every row */
 } orc_problem;
 
 /* ---------------------------------------------------------------------------------
@@ -181,6 +190,12 @@ static double dequant_element(const orc_problem *p, int64_t n, int64_t k) {
     }
 }
 
+/* The bias of column n in float64 (0 without a bias). */
+static double bias_value(const orc_problem *p, int64_t n) {
+    if (!p->bias) return 0.0;
+    return p->act_dtype == ORC_F16 ? half_bits_to_double(p->bias[n]) : bf16_bits_to_double(p->bias[n]);
+}
+
 static int check_problem(const orc_problem *p, int M) {
     if (!p || !p->W || !p->scales) return 1;
     if (p->N < 1 || p->K < 1 || M < 1) return 2;
@@ -238,7 +253,7 @@ int oracle_gemv(const orc_problem *p, const uint16_t *A, int M, double *Y, doubl
                     y += t;
                     s += fabs(t);
                 }
-                Y[(int64_t)m * p->N + n] = y;
+                Y[(int64_t)m * p->N + n] = y + bias_value(p, n);
                 S[(int64_t)m * p->N + n] = s;
             }
         }
@@ -270,7 +285,7 @@ int oracle_gemv_points(const orc_problem *p, const uint16_t *A, int M, int64_t n
             y += t;
             s += fabs(t);
         }
-        Y[i] = y;
+        Y[i] = y + bias_value(p, ns[i]);
         S[i] = s;
     }
     return 0;

@@ -32,10 +32,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert bqw.lib().qgemv_abi_version() == 1
-    # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields
-    assert ctypes.sizeof(bqw.Desc) == 64
+    assert bqw.lib().qgemv_abi_version() == 2
+    # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields; the
+    # bias pointer (version 2) follows the flags
+    assert ctypes.sizeof(bqw.Desc) == 72
     assert bqw.Desc.N.offset == 16 and bqw.Desc.W.offset == 32 and bqw.Desc.flags.offset == 60
+    assert bqw.Desc.bias.offset == 64
 
 
 def test_status_strings():
@@ -57,7 +59,7 @@ def _sel(**kw):
     (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
     (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
     (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=3 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=1 << 15), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
-    (dict(cu_count=0), 7),
+    (dict(cu_count=0), 7), (dict(bias=0x2001), 7),
 ])
 def test_select_rejects_invalid_arguments(kw, status):
     with pytest.raises(bqw.QGemvError) as e:

@@ -261,6 +261,61 @@ def test_integer_special_case_is_exact(fmt, act):
         assert np.array_equal(Y, want), fam
 
 
+@pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u8", "f16", 128), ("fp8", "f16", 128),
+                                         ("nvfp4", "bf16", 16), ("u4", "f16", 16)])
+def test_bias_epilogue_every_family(fmt, act, bs):
+    """Optional bias (one value per column, added after every scale): every family and
+    M meet the oracle bound on ragged N; row i of an M-row call equals the same row of
+    the 16-row call bit for bit within a family; and the persistent streaming kernel
+    keeps the classic kernel's bits with the bias too."""
+    prob = synth.make_problem(fmt, act, 1169, 2048, bs, 16, seed=37, with_bias=True,
+                              zp_range=(0, 15) if fmt == "u4" else (96, 160),
+                              scale_sigma=0.02 if fmt == "u4" else 0.004)
+    assert prob.bias is not None
+    gu.say(f"[bias] {fmt}/{act} bs{bs}")
+    fams = ["auto", "stream", "stream_classic", "generic"]
+    if mfma_supports(fmt, act):
+        fams += ["mfma_nolds", "mfma_lds", "mfma_ring"]
+    for fam in fams:
+        Y16, p16 = gu.run_gpu(prob, 16, flags=FAMILY_FLAG[fam])
+        ok, ratio, _, _ = gu.check_full(prob, 16, Y16, strict=False)
+        assert ok, (fam, ratio, p16)
+        for M in (1, 3, 5):
+            A = np.ascontiguousarray(prob.A[16 - M:])
+            Ym, pm = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam], A=A)
+            ok, ratio, _, _ = gu.check_full(prob, M, Ym, A=A, strict=False)
+            assert ok, (fam, M, ratio, pm)
+            if fam not in ("auto", "stream") and pm["family"] == p16["family"] and pm["ksplit"] == p16["ksplit"]:
+                assert np.array_equal(Ym.view(np.int64), Y16[16 - M:].view(np.int64)), (fam, M)
+    Yc, _ = gu.run_gpu(prob, 1, flags=FAMILY_FLAG["stream_classic"])
+    Ys, ps = gu.run_gpu(prob, 1, flags=FAMILY_FLAG["stream"])
+    assert ps["variant"] & 1 and np.array_equal(Ys.view(np.int64), Yc.view(np.int64))
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_integer_case_with_bias_is_exact(act):
+    """Integer codes with scale 1 and zero point 0, small integer activations and an
+    integer bias: every output is an integer the output type holds, so each family
+    must return it exactly."""
+    rng = np.random.default_rng(5)
+    M, N, K, bs = 5, 300, 512, 32
+    nblk = K // bs
+    a_int = rng.integers(-2, 3, size=(M, K))
+    q = rng.integers(0, 4, size=(N, K)).astype(np.uint8)
+    b_int = rng.integers(-64, 65, size=N)
+    prob = synth.Problem(name="int_bias", fmt="u4", act=act, N=N, K=K, bs=bs,
+                         W=synth.pack_nibbles(q).reshape(N, nblk, bs // 2),
+                         scales=np.full((N, nblk), 0x3C00, dtype=np.uint16),
+                         zp=synth.pack_nibbles(np.zeros((N, nblk), np.uint8)), tensor_scale=1.0,
+                         A=synth.activation_bits(a_int.astype(np.float64), act),
+                         bias=synth.activation_bits(b_int.astype(np.float64), act))
+    exact = (a_int @ q.astype(np.int64).T + b_int[None, :]).astype(np.float64)
+    assert np.abs(exact).max() <= 256  # exact in bf16 as well
+    for fam in ("stream", "stream_classic", "generic", "mfma_nolds", "mfma_lds", "mfma_ring"):
+        Y, _ = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam])
+        assert np.array_equal(Y, exact), fam
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4", "u4", "u8"])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_one_hot_probes_decode_every_code_exactly(fmt, act):

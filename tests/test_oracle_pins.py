@@ -373,3 +373,50 @@ def test_workload_data_is_not_vacuous(name):
     A2[:, :bs] = 0
     Y2, _ = oracle.gemv(p2, A=A2)
     assert not oracle.within_tolerance(Y2, Y, S)[0]
+
+
+@pytest.mark.parametrize("fmt,act,bs,with_zp", [("u4", "f16", 32, True), ("u8", "bf16", 16, True),
+                                                ("fp8", "bf16", 16, None), ("nvfp4", "bf16", 16, None),
+                                                ("nvfp4", "f16", 16, None)])
+def test_brute_force_with_bias(fmt, act, bs, with_zp):
+    """Optional bias: y[m, n] = sum_k a*w + bias[n] exactly (one value per output
+    column, the same for every row, outside the NVFP4 tensor scale), S unchanged.
+    Distinct rows and columns catch a bias indexed by the row, and NVFP4's tensor
+    scale (not 1) catches a bias scaled with the product."""
+    rng = np.random.default_rng(hash(("bias", fmt, act, bs)) % 2**32)
+    act_frac = _f16_fraction if act == "f16" else _bf16_fraction
+    for M, N, nblk in ((2, 3, 2), (3, 5, 1)):
+        K = nblk * bs
+        prob, L = _logical_problem(fmt, act, M, N, K, bs, rng, with_zp=bool(with_zp))
+        bias_bits = synth.activation_bits(rng.standard_normal(N) * 4.0, act).reshape(N)
+        prob_b = synth.Problem(**{**prob.__dict__, "bias": bias_bits})
+        Y, S = oracle.gemv(prob_b)
+        Y0, S0 = oracle.gemv(prob)
+        Ye, Se = _exact_result(fmt, act, M, N, K, bs, L)
+        assert np.array_equal(S, S0)
+        for m in range(M):
+            for n in range(N):
+                ye = float(Ye[m][n] + act_frac(bias_bits[n]))
+                assert abs(Y[m, n] - ye) <= 1e-12 * (float(Se[m][n]) + abs(ye)) + 1e-300, (m, n, Y[m, n], ye)
+        ys, ss = oracle.gemv_points(prob_b, [M - 1, 0], [N - 1, 0])
+        assert np.array_equal(ys, [Y[M - 1, N - 1], Y[0, 0]]) and np.array_equal(ss, [S[M - 1, N - 1], S[0, 0]])
+
+
+def test_integer_special_case_with_bias_is_exact():
+    """Integer codes, scale 1, zero point 0, integer activations and an integer bias:
+    Y = A_int @ Q^T + bias exactly."""
+    rng = np.random.default_rng(12)
+    M, N, K, bs = 3, 7, 64, 32
+    a_int = rng.integers(-8, 9, size=(M, K))
+    q = rng.integers(0, 16, size=(N, K))
+    b_int = rng.integers(-256, 257, size=N)  # integers of magnitude <= 256 are exact in bf16
+    nblk = K // bs
+    prob = synth.Problem(
+        name="int_bias", fmt="u4", act="bf16", N=N, K=K, bs=bs,
+        W=synth.pack_nibbles(q.astype(np.uint8)).reshape(N, nblk, bs // 2),
+        scales=np.full((N, nblk), 0x3C00, dtype=np.uint16),
+        zp=synth.pack_nibbles(np.zeros((N, nblk), dtype=np.uint8)), tensor_scale=1.0,
+        A=synth.round_to_bf16_bits(a_int.astype(np.float64)),
+        bias=synth.round_to_bf16_bits(b_int.astype(np.float64)))
+    Y, _ = oracle.gemv(prob)
+    assert np.array_equal(Y, (a_int @ q.T + b_int[None, :]).astype(np.float64))
