@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
     p.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm; not the metric)")
+    p.add_argument("--bias", action="store_true", help="add the optional per-column bias (fused epilogue)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain copy kernel of this many MiB before the warmup (counter calibration)")
     p.add_argument("--trace-summary", metavar="DIR", default=None)
@@ -222,7 +223,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    prob = synth.workload(args.workload)
+    prob = synth.workload(args.workload, with_bias=args.bias)
     M = args.m if args.m is not None else prob.ms[0]
     wbytes = prob.weight_bytes()
     copies = 1 if args.warm else max(2, int(math.ceil(COLD_BYTES / wbytes)))
@@ -236,13 +237,15 @@ def main():
     Z0 = None if prob.zp is None else dev_t(prob.zp)
     tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
     A = dev_t(prob.A[:M].view(np.int16)).view(tdt).contiguous()
+    bias = None if prob.bias is None else dev_t(prob.bias.view(np.int16)).view(tdt)
     Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
     slots = []
     for i in range(copies):
         W = W0 if i == 0 else W0.clone()
         S = S0 if i == 0 else S0.clone()
         Z = Z0 if (i == 0 or Z0 is None) else Z0.clone()
-        q = bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, W, S, Z, prob.tensor_scale, args.flags)
+        q = bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, W, S, Z, prob.tensor_scale, args.flags,
+                      bias=bias)
         slots.append((q, W, S, Z))
     plan = slots[0][0].plan(M)
     stream = torch.cuda.current_stream()
@@ -294,7 +297,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
                    "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
-                   "plan": plan, "flags": args.flags, "seed": spec["seed"]},
+                   "plan": plan, "flags": args.flags, "seed": spec["seed"], "bias": bool(args.bias)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": lookup_traffic(args.workload, M, args.flags)},
         "cpu_baseline": cpu,

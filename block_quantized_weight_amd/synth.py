@@ -233,11 +233,12 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, *, n_override: Optional[int] = None) -> Problem:
+def workload(name: str, *, n_override: Optional[int] = None, with_bias: bool = False) -> Problem:
     """Generate a named workload. ``n_override`` keeps the seed and the draw order
-    but changes N (used to make small slices with the same distributions)."""
+    but changes N (used to make small slices with the same distributions);
+    ``with_bias`` also draws a per-column bias, after everything else."""
     spec = dict(WORKLOADS[name])
     ms = spec.pop("ms")
     N = spec.pop("N") if n_override is None else (spec.pop("N"), n_override)[1]
     return make_problem(spec.pop("fmt"), spec.pop("act"), N, spec.pop("K"), spec.pop("bs"),
-                        max(ms), spec.pop("seed"), name=name, ms=ms, **spec)
+                        max(ms), spec.pop("seed"), name=name, ms=ms, with_bias=with_bias, **spec)
