@@ -40,7 +40,6 @@ DEFAULT_WORKLOAD = "u8_m1_k4096_n4096"
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
-CSRC = os.path.join(ROOT, "block_quantized_weight_amd", "csrc")
 
 
 def parse():
@@ -66,16 +65,36 @@ def parse():
 # rocprofv3 databases (rocpd SQLite) -> short text summaries
 
 
+def _elf_section(path, name):
+    """Bytes of section `name` of a 64-bit little-endian ELF file (plain header walk)."""
+    import struct
+
+    with open(path, "rb") as fh:
+        data = fh.read()
+    if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
+        raise ValueError(f"{path}: not a 64-bit little-endian ELF file")
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def sh(i):
+        name_off, _, _, _, off, size = struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize)
+        return name_off, off, size
+
+    _, str_off, _ = sh(shstrndx)
+    for i in range(shnum):
+        name_off, off, size = sh(i)
+        end = data.index(b"\0", str_off + name_off)
+        if data[str_off + name_off:end].decode() == name:
+            return data[off:off + size]
+    raise ValueError(f"{path}: no section {name}")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources and the dispatcher: a traffic figure is valid only for
-    the kernels it was measured on."""
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Hash of the built library's device code (its `.hip_fatbin` section: every
+    gfx950 kernel, nothing of the host side): a traffic figure is valid only for the
+    kernels it was measured on, and stays valid across host-only changes."""
+    lib = os.path.join(ROOT, "block_quantized_weight_amd", "libqgemv.so")
+    return hashlib.sha256(_elf_section(lib, ".hip_fatbin")).hexdigest()[:16]
 
 
 def _dbs(d):

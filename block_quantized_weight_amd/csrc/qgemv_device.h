@@ -149,24 +149,6 @@ __device__ __forceinline__ ZSel zsel(const void *zp, uint32_t midpoint) {
     return ZSel{keep, ~keep & midpoint};
 }
 
-// The same wait for a count known only at run time (uniform); counts above 31 wait
-// for everything.
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-    switch (n) {
-#define QGEMV_WAIT_CASE(k) \
-    case k: wait_vmcnt<k>(); break;
-        QGEMV_WAIT_CASE(1) QGEMV_WAIT_CASE(2) QGEMV_WAIT_CASE(3) QGEMV_WAIT_CASE(4) QGEMV_WAIT_CASE(5)
-        QGEMV_WAIT_CASE(6) QGEMV_WAIT_CASE(7) QGEMV_WAIT_CASE(8) QGEMV_WAIT_CASE(9) QGEMV_WAIT_CASE(10)
-        QGEMV_WAIT_CASE(11) QGEMV_WAIT_CASE(12) QGEMV_WAIT_CASE(13) QGEMV_WAIT_CASE(14) QGEMV_WAIT_CASE(15)
-        QGEMV_WAIT_CASE(16) QGEMV_WAIT_CASE(17) QGEMV_WAIT_CASE(18) QGEMV_WAIT_CASE(19) QGEMV_WAIT_CASE(20)
-        QGEMV_WAIT_CASE(21) QGEMV_WAIT_CASE(22) QGEMV_WAIT_CASE(23) QGEMV_WAIT_CASE(24) QGEMV_WAIT_CASE(25)
-        QGEMV_WAIT_CASE(26) QGEMV_WAIT_CASE(27) QGEMV_WAIT_CASE(28) QGEMV_WAIT_CASE(29) QGEMV_WAIT_CASE(30)
-        QGEMV_WAIT_CASE(31)
-#undef QGEMV_WAIT_CASE
-    default: wait_vmcnt<0>(); break;
-    }
-}
-
 // Wait until at most min(left, K) groups of OPS loads remain in flight (uniform
 // left >= 0): a compile-time count in each branch.
 template <int K, int OPS>
