@@ -10,7 +10,7 @@ Prints one JSON line. `value` is achieved GB/s = weight bytes (codes + block sca
 zero points) per call / average time per call. The roofline object reports the same
 bytes against the 8 TB/s HBM peak; its `traffic` is the HBM bytes per launch that two
 rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) measured for this workload, read from
-the summaries under profiles/ and only while the kernel sources still hash to what
+the summaries under profiles/ and only while the built kernels still hash to what
 was profiled (null otherwise). `cpu_baseline` times the CPU oracle on a bounded sample
 of the same workload on this host.
 
