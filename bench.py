@@ -174,7 +174,7 @@ def traffic_record(fetch_dir, write_dir, args):
 
 def lookup_traffic(workload, M, flags):
     """HBM bytes per launch from a committed counter summary, or None when there is
-    none for this workload or the kernel sources changed since it was taken."""
+    none for this workload or the built kernels changed since it was taken."""
     want = kernel_source_hash()
     for f in sorted(glob.glob(os.path.join(PROFILES, "*.md")) + glob.glob(os.path.join(PROFILES, "*.txt"))):
         with open(f) as fh:
