@@ -619,7 +619,8 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
 // (tiles gw, gw + nwaves, ...) over the whole of K. Codes and block metadata travel
 // global -> LDS by DMA (global_load_lds) in slots of SS K steps (CS = 4 * SS chunks
 // of each of the 16 columns), R slots per wave and R - 1 in flight, so the prefetch
-// depth costs no VGPRs and the waits are exact load counts.
+// depth costs no VGPRs and the waits are exact load counts. The launcher takes SS = 4
+// and R = 2: the next slot loads while the current one computes.
 //  - Coalescing: one code DMA instruction moves 64 / CS whole columns' CS chunks
 //    (CS * 16 contiguous bytes each, whole cache lines), not 16 columns' 64-byte
 //    pieces. Which lane fetches which chunk is permuted (chunk j of column n lands
@@ -985,18 +986,12 @@ hipError_t go_dma_rs(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// DMA ring shape from variant bits 4..5: 0 -> 4-step slots x 3, 1 -> 2-step slots x 5,
-// 2 -> 2-step slots x 4; one or two row groups only
+// DMA ring: 4-step slots, double-buffered; one or two row groups only
 template <int FMT, int ACT, int RG, int H, bool ZPP>
 hipError_t go_dma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.waves_per_wg != 8 || cfg.ksplit != 1) return hipErrorInvalidValue;
     if constexpr (RG <= 2) {
-        switch ((cfg.variant >> 4) & 3) {
-        case 0: return go_dma_rs<FMT, ACT, RG, H, ZPP, 3, 4>(cfg, a, s);
-        case 1: return go_dma_rs<FMT, ACT, RG, H, ZPP, 5, 2>(cfg, a, s);
-        case 2: return go_dma_rs<FMT, ACT, RG, H, ZPP, 4, 2>(cfg, a, s);
-        default: return hipErrorInvalidValue;
-        }
+        return go_dma_rs<FMT, ACT, RG, H, ZPP, 2, 4>(cfg, a, s);
     } else {
         return hipErrorInvalidValue;
     }

@@ -79,38 +79,30 @@ static bool mfma_shape_ok(const qgemv_desc *d) {
     return true;
 }
 
-// DMA-ring shape for the matrix family: 0 = 4-step slots x 3, 1 = 2-step slots x 5,
-// 2 = 2-step slots x 4 (the first that fits in LDS next to abytes of staged
-// activations), or -1 when the ring cannot take the problem: the scale (and zero-point)
-// rows must be whole dwords on 4-byte aligned arrays, a slot must hold whole blocks,
-// and a 4-bit slot at least two, so its zero points fill whole bytes. lds_out gets
-// the LDS bytes.
-static int dma_ring_shape(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t *lds_out) {
-    const int kpc = k_per_chunk(d->format);
+// Whether the matrix family's DMA ring takes the problem, and its LDS bytes next to
+// abytes of staged activations. The ring is double-buffered with 4-step slots (16
+// chunks of each of a tile's 16 columns per slot). Measured on MI355X, this beat every
+// deeper ring (4-step x 3, 2-step x 4..7) on every workload that had the LDS for those:
+// the per-slot costs (the wait, the refill's DMA issue) weigh more than depth. It is
+// also the smallest of them in LDS. The scale (and zero-point) rows must be whole dwords
+// on 4-byte aligned arrays. A slot of 64 chunks per column holds whole blocks for
+// every block size the formats take.
+static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t *lds_out) {
     const int64_t nblk = d->K / d->block_size;
     const int sb = d->format == QGEMV_FMT_FP8 ? 4 : (d->format == QGEMV_FMT_NVFP4 ? 1 : 2);
-    if ((nblk * sb) % 4 || (uintptr_t)d->scales % 4) return -1;
+    if ((nblk * sb) % 4 || (uintptr_t)d->scales % 4) return false;
     if (zpp) {
         const int64_t zrow = d->format == QGEMV_FMT_U4 ? (nblk + 1) / 2 : nblk;
-        if (zrow % 4 || (uintptr_t)d->zero_points % 4) return -1;
+        if (zrow % 4 || (uintptr_t)d->zero_points % 4) return false;
     }
-    // (steps per slot, slots); shallower rings measured slower than the register ring
-    static const int shapes[3][2] = {{4, 3}, {2, 5}, {2, 4}};
-    for (int i = 0; i < 3; ++i) {
-        const int ss = shapes[i][0], r = shapes[i][1];
-        if (4 * ss * kpc < d->block_size) continue;  // a slot holds whole blocks
-        if (d->format == QGEMV_FMT_U4 && (4 * ss * kpc) / d->block_size < 2) continue;
-        const int codeb = ss == 4 ? 4 * 1024 : 2 * 1152;
-        const bool wide_meta = d->format == QGEMV_FMT_FP8 || (d->format == QGEMV_FMT_U4 && d->block_size == 16);
-        const int nsd = wide_meta ? (ss == 4 ? 4 : 2) : (ss == 4 ? 2 : 1);
-        const int64_t slot = codeb + 256 * nsd + (zpp ? 256 : 0);
-        const int64_t lds = abytes + 8 * r * slot;
-        if (lds <= kLdsBytes) {
-            *lds_out = (int32_t)lds;
-            return i;
-        }
-    }
-    return -1;
+    // slot: 4 KiB of codes, the scale window (4 DMAs of 256 B where 16-wide blocks or
+    // FP8 need them, else 2), the zero-point window (256 B); 8 waves x 2 slots
+    const bool wide_meta = d->format == QGEMV_FMT_FP8 || (d->format == QGEMV_FMT_U4 && d->block_size == 16);
+    const int64_t slot = 4 * 1024 + 256 * (wide_meta ? 4 : 2) + (zpp ? 256 : 0);
+    const int64_t lds = abytes + 8 * 2 * slot;
+    if (lds > kLdsBytes) return false;
+    *lds_out = (int32_t)lds;
+    return true;
 }
 
 // Waves that share one 16-column tile's K range. Chosen from N and K only so that
@@ -300,13 +292,13 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
         // fits in LDS next to the staged activations.
         const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
-        const int ring_shape = dma_ring_shape(d, abytes16, zpp, &c.lds_bytes);
-        bool ring = c.ksplit == 1 && rg <= 2 && ring_shape >= 0 && groups > cu_count;
-        if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && rg <= 2 && ring_shape >= 0;
+        const bool ring_fits = dma_ring_fits(d, abytes16, zpp, &c.lds_bytes);
+        bool ring = c.ksplit == 1 && rg <= 2 && ring_fits && groups > cu_count;
+        if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && rg <= 2 && ring_fits;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {
             c.waves_per_wg = 8;
-            c.variant = 2 | (ring_shape << 4);
+            c.variant = 2;
             const int64_t wgs = (tiles + 7) / 8;
             c.grid = wgs < cu_count ? wgs : cu_count;
             *out = c;

@@ -160,9 +160,8 @@ typedef struct qgemv_plan_info {
     int64_t grid;            /* workgroups launched */
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
     int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
-                                LDS, bit 1 = weights through the LDS DMA ring (bits 4..5 its
-                                shape: 0 = 4-step slots x 3, 1 = 2-step x 5, 2 = 2-step x 4),
-                                bit 3 = 8-slot register ring (else 4).
+                                LDS, bit 1 = weights through the LDS DMA ring (4-step slots,
+                                double-buffered), bit 3 = 8-slot register ring (else 4).
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
 } qgemv_plan_info;
