@@ -1,7 +1,9 @@
 """Benchmark of the block-scaled small-M decode GEMV on one MI355X.
 
-One step = one qgemv_run call (dispatch + kernel) over one batch of synthetic input:
-Y[M, N] = A[M, K] . dequant(W)^T. The weights are cold: the timed loop rotates
+One step = one qgemv_run_ws call (dispatch + kernel) over one batch of synthetic
+input: Y[M, N] = A[M, K] . dequant(W)^T, with a workspace allocated and zeroed once
+before the timed region (plans that split K across workgroups use it, others ignore
+it; --no-workspace times qgemv_run instead). The weights are cold: the timed loop rotates
 through enough copies of the weight (>= 1 GiB together, several times the 256 MB
 last-level cache) that every call streams its weight from HBM. Inputs are resident in
 HBM before the timed region starts.
@@ -54,6 +56,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
     p.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm; not the metric)")
     p.add_argument("--bias", action="store_true", help="add the optional per-column bias (fused epilogue)")
+    p.add_argument("--no-workspace", action="store_true",
+                   help="time qgemv_run (no workspace: K is never split across workgroups)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain copy kernel of this many MiB before the warmup (counter calibration)")
     p.add_argument("--trace-summary", metavar="DIR", default=None)
@@ -154,8 +158,8 @@ def traffic_record(fetch_dir, write_dir, args):
 
     true_bytes = args.calib_copy_mib * (1 << 20)
     M = args.m if args.m is not None else synth.WORKLOADS[args.workload]["ms"][0]
-    rec = {"workload": args.workload, "M": M, "flags": args.flags, "src_hash": kernel_source_hash(),
-           "calib_bytes": true_bytes}
+    rec = {"workload": args.workload, "M": M, "flags": args.flags, "ws": not args.no_workspace,
+           "src_hash": kernel_source_hash(), "calib_bytes": true_bytes}
     for key, d, ctr in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         cm = counter_means(d)
         q = [(k, v[ctr]) for k, v in cm.items() if _is_qgemv(k) and ctr in v]
@@ -172,9 +176,10 @@ def traffic_record(fetch_dir, write_dir, args):
     print("traffic_record: " + json.dumps(rec, sort_keys=True))
 
 
-def lookup_traffic(workload, M, flags):
+def lookup_traffic(workload, M, flags, ws=True):
     """HBM bytes per launch from a committed counter summary, or None when there is
-    none for this workload or the built kernels changed since it was taken."""
+    none for this workload and entry point or the built kernels changed since it was
+    taken."""
     want = kernel_source_hash()
     for f in sorted(glob.glob(os.path.join(PROFILES, "*.md")) + glob.glob(os.path.join(PROFILES, "*.txt"))):
         with open(f) as fh:
@@ -185,8 +190,8 @@ def lookup_traffic(workload, M, flags):
                     rec = json.loads(line[len("traffic_record: "):])
                 except ValueError:
                     continue
-                if (rec.get("workload"), rec.get("M"), rec.get("flags"), rec.get("src_hash")) == \
-                        (workload, M, flags, want):
+                if (rec.get("workload"), rec.get("M"), rec.get("flags"), rec.get("ws", False), rec.get("src_hash")) == \
+                        (workload, M, flags, ws, want):
                     return rec["traffic_bytes"]
     return None
 
@@ -266,7 +271,10 @@ def main():
         q = bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, W, S, Z, prob.tensor_scale, args.flags,
                       bias=bias)
         slots.append((q, W, S, Z))
-    plan = slots[0][0].plan(M)
+    use_ws = not args.no_workspace
+    plan = slots[0][0].plan(M, with_workspace=use_ws)
+    # one workspace for every rotation slot (their plans are the same), zeroed once
+    ws = torch.zeros(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device=dev) if use_ws else None
     stream = torch.cuda.current_stream()
     if args.calib_copy_mib > 0:
         # one plain copy kernel of known size, for scaling counter readings
@@ -279,7 +287,7 @@ def main():
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        slots[i % copies][0].run(A, Y, M, stream)
+        slots[i % copies][0].run(A, Y, M, stream, workspace=ws)
     torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -287,7 +295,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        slots[i % copies][0].run(A, Y, M, stream)
+        slots[i % copies][0].run(A, Y, M, stream, workspace=ws)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -316,9 +324,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
                    "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
-                   "plan": plan, "flags": args.flags, "seed": spec["seed"], "bias": bool(args.bias)},
+                   "plan": plan, "flags": args.flags, "seed": spec["seed"], "bias": bool(args.bias),
+                   "entry": "qgemv_run_ws" if use_ws else "qgemv_run"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": lookup_traffic(args.workload, M, args.flags)},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": lookup_traffic(args.workload, M, args.flags, use_ws)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
     }

@@ -22,7 +22,9 @@ FAMILIES = {"auto": 0, "stream": 1, "mfma": 2, "generic": 3}
 FAMILY_NAMES = {v: k for k, v in FAMILIES.items()}
 
 QGEMV_OK = 0
+QGEMV_E_WORKSPACE = 9
 FLAG_FAMILY_MASK = 0x0000000F
+FLAG_KPARTS_SHIFT = 4
 FLAG_KSPLIT_SHIFT = 8
 FLAG_STREAM_NWG_SHIFT = 12
 FLAG_NO_MFMA = 0x00010000
@@ -76,6 +78,9 @@ class PlanInfo(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("lds_bytes", ctypes.c_int32),
         ("variant", ctypes.c_int32),
+        ("kparts", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -92,9 +97,14 @@ def lib() -> ctypes.CDLL:
             L.qgemv_create.restype = ctypes.c_int
             L.qgemv_run.argtypes = [vp, vp, vp, ctypes.c_int, vp]
             L.qgemv_run.restype = ctypes.c_int
-            L.qgemv_plan.argtypes = [vp, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+            L.qgemv_run_ws.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
+            L.qgemv_run_ws.restype = ctypes.c_int
+            L.qgemv_workspace_size.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+            L.qgemv_workspace_size.restype = ctypes.c_int
+            L.qgemv_plan.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanInfo)]
             L.qgemv_plan.restype = ctypes.c_int
-            L.qgemv_select.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+            L.qgemv_select.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(PlanInfo)]
             L.qgemv_select.restype = ctypes.c_int
             L.qgemv_destroy.argtypes = [vp]
             L.qgemv_destroy.restype = None
@@ -127,16 +137,18 @@ def make_desc(fmt: str, act: str, N: int, K: int, block_size: int, W: Any, scale
 def _plan_dict(p: PlanInfo) -> Dict[str, Any]:
     return {"family": FAMILY_NAMES.get(p.family, p.family), "rows_per_pass": p.rows_per_pass,
             "passes": p.passes, "cols_per_wave": p.cols_per_wave, "ksplit": p.ksplit,
-            "waves_per_wg": p.waves_per_wg, "grid": p.grid, "lds_bytes": p.lds_bytes, "variant": p.variant}
+            "waves_per_wg": p.waves_per_wg, "grid": p.grid, "lds_bytes": p.lds_bytes, "variant": p.variant,
+            "kparts": p.kparts, "workspace_bytes": p.workspace_bytes}
 
 
 def select(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count: int = 256,
            flags: int = 0, W: Any = 0x1000, scales: Any = 0x1000, zero_points: Any = None,
-           bias: Any = None) -> Dict[str, Any]:
-    """Pure host dispatcher query (no GPU): the launch for M rows at cu_count CUs."""
+           bias: Any = None, with_workspace: bool = False) -> Dict[str, Any]:
+    """Pure host dispatcher query (no GPU): the launch for M rows at cu_count CUs, as
+    qgemv_run makes it, or as qgemv_run_ws does with_workspace."""
     d = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, 1.0, flags, bias)
     out = PlanInfo()
-    rc = lib().qgemv_select(ctypes.byref(d), int(M), int(cu_count), ctypes.byref(out))
+    rc = lib().qgemv_select(ctypes.byref(d), int(M), int(cu_count), int(bool(with_workspace)), ctypes.byref(out))
     if rc != QGEMV_OK:
         raise QGemvError(rc, "qgemv_select")
     return _plan_dict(out)
@@ -162,9 +174,12 @@ class QGemv:
             raise QGemvError(rc, "qgemv_create")
         self._h = h
 
-    def run(self, A: Any, Y: Any, M: Optional[int] = None, stream: Any = None) -> None:
+    def run(self, A: Any, Y: Any, M: Optional[int] = None, stream: Any = None, workspace: Any = None,
+            workspace_bytes: Optional[int] = None) -> None:
         """Enqueue Y[M, N] = A[M, K] . dequant(W)^T on `stream` (torch stream, raw
-        hipStream_t int, or None for torch's current stream)."""
+        hipStream_t int, or None for torch's current stream). With a workspace (a
+        device buffer zeroed once before its first use, see workspace_size) the call
+        goes through qgemv_run_ws, which may split K across workgroups."""
         if M is None:
             M = int(A.shape[0])
         if stream is None:
@@ -172,13 +187,29 @@ class QGemv:
             stream = torch.cuda.current_stream().cuda_stream
         elif not isinstance(stream, int):
             stream = stream.cuda_stream
-        rc = lib().qgemv_run(self._h, _ptr(A), _ptr(Y), int(M), ctypes.c_void_p(stream))
+        if workspace is None and workspace_bytes is None:
+            rc = lib().qgemv_run(self._h, _ptr(A), _ptr(Y), int(M), ctypes.c_void_p(stream))
+            where = "qgemv_run"
+        else:
+            if workspace_bytes is None:
+                workspace_bytes = int(workspace.numel() * workspace.element_size())
+            rc = lib().qgemv_run_ws(self._h, _ptr(A), _ptr(Y), int(M), _ptr(workspace), int(workspace_bytes),
+                                    ctypes.c_void_p(stream))
+            where = "qgemv_run_ws"
         if rc != QGEMV_OK:
-            raise QGemvError(rc, "qgemv_run")
+            raise QGemvError(rc, where)
 
-    def plan(self, M: int) -> Dict[str, Any]:
+    def workspace_size(self, M: int = MAX_M) -> int:
+        """Bytes of workspace qgemv_run_ws needs for M rows (0: none)."""
+        out = ctypes.c_size_t()
+        rc = lib().qgemv_workspace_size(self._h, int(M), ctypes.byref(out))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_workspace_size")
+        return int(out.value)
+
+    def plan(self, M: int, with_workspace: bool = False) -> Dict[str, Any]:
         out = PlanInfo()
-        rc = lib().qgemv_plan(self._h, int(M), ctypes.byref(out))
+        rc = lib().qgemv_plan(self._h, int(M), int(bool(with_workspace)), ctypes.byref(out))
         if rc != QGEMV_OK:
             raise QGemvError(rc, "qgemv_plan")
         return _plan_dict(out)

@@ -71,6 +71,9 @@ void fill_args(const qgemv_handle *h, const void *A, void *Y, int M, qgemv::KArg
     a->ksplit = 1;
     a->tscale = (d.format == QGEMV_FMT_NVFP4) ? d.tensor_scale : 1.0f;
     a->bias = d.bias;
+    a->kparts = 1;
+    a->part = nullptr;
+    a->cnt = nullptr;
 }
 
 void to_info(const qgemv::LaunchCfg &c, qgemv_plan_info *o) {
@@ -83,6 +86,38 @@ void to_info(const qgemv::LaunchCfg &c, qgemv_plan_info *o) {
     o->grid = c.grid;
     o->lds_bytes = c.lds_bytes;
     o->variant = c.variant;
+    o->kparts = c.kparts;
+    o->reserved = 0;
+    o->workspace_bytes = c.ws_bytes;
+}
+
+// Shared body of qgemv_run and qgemv_run_ws: plan (with or without a workspace),
+// check the workspace the plan needs, and enqueue the launch.
+int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
+             void *hip_stream) {
+    if (!h || !A || !Y) return QGEMV_E_NULL;
+    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
+    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
+    qgemv::LaunchCfg c;
+    int rc = qgemv::select_plan(&h->d, M, h->cu_count, fast, h->env_flags, with_ws, &c);
+    if (rc) return rc;
+    qgemv::KArgs a;
+    fill_args(h, A, Y, M, &a);
+    a.ksplit = c.ksplit;
+    if (c.kparts > 1) {
+        if (!ws || (uintptr_t)ws % 256 || ws_bytes < (size_t)c.ws_bytes) return QGEMV_E_WORKSPACE;
+        a.kparts = c.kparts;
+        a.cnt = (uint32_t *)ws;
+        a.part = (float *)((unsigned char *)ws + c.ws_counters);
+    }
+    hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e;
+    switch (c.family) {
+    case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(c, a, s); break;
+    case QGEMV_FAMILY_MFMA: e = qgemv::launch_mfma(c, a, s); break;
+    default: e = qgemv::launch_generic(c, a, s); break;
+    }
+    return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
 }
 
 }  // namespace
@@ -102,6 +137,7 @@ const char *qgemv_status_str(int s) {
     case QGEMV_E_LAUNCH: return "kernel launch failed";
     case QGEMV_E_ARG: return "invalid argument";
     case QGEMV_E_ALLOC: return "host allocation failed";
+    case QGEMV_E_WORKSPACE: return "the plan needs a workspace: none, or too small or misaligned a one, was given";
     default: return "unknown status";
     }
 }
@@ -127,42 +163,41 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
     return QGEMV_OK;
 }
 
-int qgemv_plan(const qgemv_handle *h, int M, qgemv_plan_info *out) {
+int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info *out) {
     if (!h || !out) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, &c);
+    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, with_workspace != 0, &c);
     if (rc) return rc;
     to_info(c, out);
     return QGEMV_OK;
 }
 
-int qgemv_select(const qgemv_desc *d, int M, int cu_count, qgemv_plan_info *out) {
+int qgemv_select(const qgemv_desc *d, int M, int cu_count, int with_workspace, qgemv_plan_info *out) {
     if (!out) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(d, M, cu_count, d ? qgemv::pointers_fast_ok(d, nullptr, nullptr) : false, 0u, &c);
+    int rc = qgemv::select_plan(d, M, cu_count, d ? qgemv::pointers_fast_ok(d, nullptr, nullptr) : false, 0u,
+                                with_workspace != 0, &c);
     if (rc) return rc;
     to_info(c, out);
     return QGEMV_OK;
 }
 
 int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream) {
-    if (!h || !A || !Y) return QGEMV_E_NULL;
-    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
-    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
+    return run_plan(h, A, Y, M, false, nullptr, 0, hip_stream);
+}
+
+int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *workspace, size_t workspace_bytes,
+                 void *hip_stream) {
+    return run_plan(h, A, Y, M, true, workspace, workspace_bytes, hip_stream);
+}
+
+int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes) {
+    if (!h || !bytes) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, M, h->cu_count, fast, h->env_flags, &c);
+    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, true, &c);
     if (rc) return rc;
-    qgemv::KArgs a;
-    fill_args(h, A, Y, M, &a);
-    a.ksplit = c.ksplit;
-    hipStream_t s = (hipStream_t)hip_stream;
-    hipError_t e;
-    switch (c.family) {
-    case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(c, a, s); break;
-    case QGEMV_FAMILY_MFMA: e = qgemv::launch_mfma(c, a, s); break;
-    default: e = qgemv::launch_generic(c, a, s); break;
-    }
-    return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
+    *bytes = (size_t)c.ws_bytes;
+    return QGEMV_OK;
 }
 
 void qgemv_destroy(qgemv_handle *h) { delete h; }

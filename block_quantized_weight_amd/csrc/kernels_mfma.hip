@@ -250,16 +250,17 @@ __device__ __forceinline__ size_t staged_rows_bytes(const KArgs &a, int astride)
 }
 
 template <int FMT, int RG, int H>
-__device__ __forceinline__ size_t sums_bytes(const KArgs &a) {
-    return MfFmt<FMT>::ZP ? (size_t)a.nchunks * RG * H * 16 : 0;
+__device__ __forceinline__ size_t sums_bytes(size_t nch) {
+    return MfFmt<FMT>::ZP ? nch * RG * H * 16 : 0;
 }
 
 // One wave owns the 16 columns of a tile for one K slice. A workgroup of nw waves
 // holds nw / ksplit tiles; the ksplit waves of a tile take K steps t = kslice,
 // kslice + ksplit, ... and reduce in LDS in wave order.
 // One K step of one wave: the chunk c = 4t + g of each of the 16 columns (already in
-// w, with its raw block metadata m), multiplied by every row group of A. Shared by
-// both kernels below so that they compute bit-identical results.
+// w, with its raw block metadata m), multiplied by every row group of A. Staged
+// activations (and their sums) start at chunk cbase of the row. Shared by both
+// kernels below so that they compute bit-identical results.
 // A operands of one K step for every row group, loaded from global memory (used ahead
 // of time by the register-ring kernel when the activations are not staged in LDS).
 template <int FMT, int RG>
@@ -306,8 +307,8 @@ __device__ __forceinline__ void chunk_sums(const op4 (&av)[MfFmt<FMT>::MF], f4 (
 template <int FMT, int ACT, int RG, int H, bool LDSA>
 __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const MetaRaw<H> &m, int c, int ar,
                                           bool a_live_grp, const uint16_t *sA, const uint16_t *sZero,
-                                          const f4 *sSum, int astride, const AOps<FMT, RG> &areg, bool valid,
-                                          f4 acc[RG]) {
+                                          const f4 *sSum, int astride, int cbase, const AOps<FMT, RG> &areg,
+                                          bool valid, f4 acc[RG]) {
     using F = MfFmt<FMT>;
     // with one row group the B operands are decoded right before their MFMA; with
     // more they are decoded once and shared by the groups
@@ -325,7 +326,7 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
     // leaves them as they are, with one select per step instead of one per element.
     const uint32_t v0 = valid ? m.v[0] : 0u;
     const int zsh = (FMT == FMT_U4 && H == 1) ? u4_zshift(a, c) : 0;
-    const uint32_t kbase = (uint32_t)c * F::KPC;
+    const uint32_t kbase = (uint32_t)(c - cbase) * F::KPC;  // within the staged K range
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const int row = 4 * rg + ar;
@@ -342,7 +343,7 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             for (int j = 0; j < F::MF; ++j) avs[j] = *(const op4 *)(abase + 8 * j);
             if constexpr (F::ZP) {
 #pragma unroll
-                for (int h = 0; h < H; ++h) sa[h] = sSum[((size_t)c * RG + rg) * H + h];
+                for (int h = 0; h < H; ++h) sa[h] = sSum[((size_t)(c - cbase) * RG + rg) * H + h];
             }
         } else {
             const op4 z = {0u, 0u, 0u, 0u};
@@ -374,12 +375,12 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
 }
 
 // Fill the per-chunk activation-sum table (formats with zero points) from the staged
-// rows: the waves of the workgroup take K steps in turn and run chunk_sums on the
-// same A operands mfma_step reads; lane (0, g) of each lane group stores its chunk's
-// entry. The caller synchronizes the workgroup before and after.
+// rows: the waves of the workgroup take the nsteps staged K steps in turn and run
+// chunk_sums on the same A operands mfma_step reads; lane (0, g) of each lane group
+// stores its chunk's entry. The caller synchronizes the workgroup before and after.
 template <int FMT, int ACT, int RG, int H>
 __device__ __forceinline__ void stage_sums(const KArgs &a, const uint16_t *sA, const uint16_t *sZero, int astride,
-                                           f4 *sSum) {
+                                           f4 *sSum, int nsteps) {
     using F = MfFmt<FMT>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwv = (int)(blockDim.x >> 6);
@@ -387,7 +388,6 @@ __device__ __forceinline__ void stage_sums(const KArgs &a, const uint16_t *sA, c
     const int g = lane >> 4;
     const int ar = lane & 3;
     const bool a_live_grp = ((lane & 15) >> 2) == g;
-    const int nsteps = (int)(a.nchunks >> 2);
     for (int t = wave; t < nsteps; t += nwv) {
         const int c = 4 * t + g;
 #pragma unroll
@@ -416,16 +416,17 @@ __device__ __forceinline__ void pin_accumulators(f4 acc[RG]) {
     for (int r = 0; r < RG; ++r) asm volatile("" : "+v"(acc[r])::"memory");
 }
 
-// Stage the M activation rows into LDS once per workgroup, permuted into the MFMA
-// slot order (row stride K + kAPad elements). Each thread handles 16-byte pieces
-// it, it + blockDim, ... in batches of SB whose loads are all issued before the first
-// store, so the staging costs about one load latency per batch, not one per piece.
+// Stage k = k0 .. k0 + klen - 1 of the M activation rows into LDS once per
+// workgroup, permuted into the MFMA slot order (row stride astride elements). Each
+// thread handles 16-byte pieces it, it + blockDim, ... in batches of SB whose loads
+// are all issued before the first store, so the staging costs about one load latency
+// per batch, not one per piece.
 template <int FMT, int SB = 8>
-__device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astride) {
+__device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astride, int k0, int klen) {
     using F = MfFmt<FMT>;
-    const uint16_t *A16 = (const uint16_t *)a.A;
+    const uint16_t *A16 = (const uint16_t *)a.A + k0;
     const int K = (int)a.K;
-    const int k8n = K >> 3;
+    const int k8n = klen >> 3;
     const int items = a.M * k8n;
     const int last = items - 1;
     for (int base = threadIdx.x; base < items; base += SB * (int)blockDim.x) {
@@ -460,9 +461,30 @@ __device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astrid
 
 // K-split reduction over the ksplit waves of a tile (fixed wave order), then the sum
 // over the four lane groups and the store of rows 4*rg + g.
-template <int ACT, int RG>
+//
+// With K parts (XWG and a.kparts > 1; every wave of the workgroup calls this at the
+// same point, for tile group tg, of which this workgroup holds part `part`), the
+// K-part split across workgroups of "[CUDA] MatMul: add an opt-in split-K GEMV"
+// (Cross-block reduction; review: cache-safe publication, one counter contract with
+// an explicitly atomic reset):
+//  1. publish: each row's fp32 partial goes to the workspace ([kparts, M, N]) by
+//     agent-scope atomic stores (coherent for every compute unit), each wave waits
+//     until its stores have completed, then a workgroup barrier;
+//  2. count: one thread adds 1 to the tile group's counter with an agent-scope
+//     release RMW (the one cache write-back of the workgroup); the workgroup that
+//     brings it to kparts is the last: that thread takes the agent-scope acquire
+//     fence, resets the counter with an atomic store and tells the waves through
+//     LDS (a barrier orders their loads after the acquire);
+//  3. reduce: the last workgroup's waves load the kparts partials with agent-scope
+//     atomic loads and add them in part order
+//     0, 1, ..., so the result does not depend on which workgroup finished last,
+//     then store zeros over the partials they read. A completed run thus leaves the
+//     whole workspace as it found it, all zero, whatever handle or M used it before.
+// No workgroup waits for another: the last to arrive does the work.
+template <int ACT, int RG, bool XWG = true>
 __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *sR, int wave, int lane, int ks,
-                                            int kslice, int g, bool tile_ok, int64_t n) {
+                                            int kslice, int g, bool tile_ok, int64_t n, int part = 0,
+                                            int64_t tg = 0, uint32_t *sFlag = nullptr) {
     if (ks > 1) {
         float *mine = sR + (size_t)wave * (RG * 4 * 64);
 #pragma unroll
@@ -482,6 +504,11 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
         }
         __syncthreads();
     }
+    const bool xwg = XWG && a.kparts > 1;
+    // partial tiles [kparts, M, N]: 32-bit offsets (the dispatcher keeps
+    // kparts * M * N below 2^31)
+    const uint32_t pstride = (uint32_t)a.M * (uint32_t)a.N;
+    uint32_t *part_u = (uint32_t *)a.part;
     if (kslice == 0 && tile_ok) {
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
@@ -490,17 +517,79 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
             for (int r = 0; r < 4; ++r) tot[r] = sum_groups(acc[rg][r]);
             const float v = (g == 0) ? tot[0] : (g == 1) ? tot[1] : (g == 2) ? tot[2] : tot[3];
             const int row = 4 * rg + g;
-            if (n < a.N && row < a.M) store_out<ACT>(a.Y, (int64_t)row * a.N + n, add_bias<ACT>(a.bias, n, v * a.tscale));
+            if (n < a.N && row < a.M) {
+                if (!xwg)
+                    store_out<ACT>(a.Y, (int64_t)row * a.N + n, add_bias<ACT>(a.bias, n, v * a.tscale));
+                else
+                    __hip_atomic_store(part_u + ((uint32_t)part * pstride + (uint32_t)row * (uint32_t)a.N + (uint32_t)n),
+                                       __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
+    if (!xwg) return;
+    // every wave's partial stores complete before the barrier; one release per
+    // workgroup, on the counter
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(a.cnt + tg, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        const bool last = done == (uint32_t)a.kparts;
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(a.cnt + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *sFlag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (*sFlag) {  // uniform over the workgroup
+        if (kslice == 0 && tile_ok) {
+            const uint32_t kpm1 = (uint32_t)a.kparts - 1u;
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const int row = 4 * rg + g;
+                if (n < a.N && row < a.M) {
+                    // all eight loads issue unconditionally (parts past kparts - 1 re-read
+                    // the last), then the first kparts are added in part order
+                    const uint32_t base = (uint32_t)row * (uint32_t)a.N + (uint32_t)n;
+                    uint32_t pv[8];
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const uint32_t pp = (uint32_t)p < kpm1 ? (uint32_t)p : kpm1;
+                        pv[p] = __hip_atomic_load(part_u + (base + pp * pstride), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    float v = __uint_as_float(pv[0]);
+#pragma unroll
+                    for (int p = 1; p < 8; ++p) {
+                        const float w = v + __uint_as_float(pv[p]);
+                        v = (uint32_t)p <= kpm1 ? w : v;
+                    }
+                    store_out<ACT>(a.Y, (int64_t)row * a.N + n, add_bias<ACT>(a.bias, n, v * a.tscale));
+                    // each lane clears what it read (after its loads, same addresses)
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const uint32_t pp = (uint32_t)p < kpm1 ? (uint32_t)p : kpm1;
+                        __hip_atomic_store(part_u + (base + pp * pstride), 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // the flag is written again at the next tile group
 }
 
 // Register-ring kernel. A workgroup of 8 waves holds 8 / ksplit tiles of ksplit waves
-// each and walks tile groups g = blockIdx.x, + gridDim.x, ...; within a tile, wave
-// kslice takes K steps t = kslice, kslice + ksplit, ... Every wave runs the same
-// S = ceil(ceil(steps / ksplit) / P) * P slots per tile (a slot past the last step, or
-// of a tile past N, computes on a clamped valid address and its accumulator update is
-// discarded), so all waves reach the K-split barriers of finish_tile together. The
+// each. Without K parts (KP false) it walks tile groups blockIdx.x, + gridDim.x, ...
+// over all of K. With K parts (KP, a.kparts > 1; the grid is one workgroup per tile
+// group and part), workgroup b takes tile group b / kparts and part b mod kparts of
+// its K steps (a contiguous range, parts as even as whole steps allow), and the
+// cross-workgroup finish runs once, after the ring has drained. Within a tile,
+// wave kslice takes the part's K steps t = kslice, kslice + ksplit, ... Every wave
+// of a workgroup runs the same S = ceil(ceil(part steps / ksplit) / P) * P slots per
+// tile (a slot past the last step, or of a tile past N, computes on a clamped valid
+// address and its accumulator update is discarded), so all waves reach the barriers
+// of finish_tile together. The
 // (tile, slot) sequence is one pipeline: a register ring of P slots holds the codes and
 // raw metadata of the next P - 1 slots in flight, across tile boundaries. Activations
 // are either staged once per workgroup in LDS (LDSA) or, when they are not, fetched
@@ -513,7 +602,7 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
 // flight.
 // Register budget: four waves per SIMD (<= 128 VGPRs) for one row group, two waves
 // per SIMD (<= 256) beyond.
-template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
+template <int FMT, int ACT, int RG, int H, bool LDSA, int P, bool KP>
 __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     constexpr int NW = 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -526,21 +615,32 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     const int g = lane >> 4;
     const int ar = lane & 3;
     const bool a_live_grp = ((lane & 15) >> 2) == g;
-    const int nsteps = (int)(a.nchunks >> 2);
+    // K part of this workgroup: steps pbeg .. pbeg + nsteps - 1 (nsteps >= 1, as the
+    // dispatcher takes at most one part per step); the tile-group walk of the part
+    const uint32_t kp = KP ? (uint32_t)a.kparts : 1u;
+    const uint32_t part = blockIdx.x % kp;
+    const int64_t gx = blockIdx.x / kp;
+    const int64_t gdim = gridDim.x / kp;
+    const uint32_t steps_all = (uint32_t)(a.nchunks >> 2);
+    const int pbeg = (int)(steps_all * part / kp);
+    const int nsteps = (int)(steps_all * (part + 1) / kp) - pbeg;
+    const int smax = (int)((steps_all + kp - 1) / kp);  // the longest part: the LDS layout
+    const int cbase = 4 * pbeg;
     const int S = ((nsteps + ks - 1) / ks + P - 1) / P * P;
-    const int astride = (int)a.K + kAPad;
+    const int astride = smax * 4 * MfFmt<FMT>::KPC + kAPad;
     const int64_t ntiles = (a.N + 15) >> 4;
     const int64_t ngroups = (ntiles + tpw - 1) / tpw;
     // LDS: [zero block | staged rows | activation sums] when staged, then the K-split
-    // reduction area
+    // reduction area, then (with K parts) the last-workgroup flag
     uint16_t *sZero = (uint16_t *)smem;
     uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
-    f4 *sSum = (f4 *)(smem + kZeroBytes + (LDSA ? staged_rows_bytes(a, astride) : 0));
-    float *sR = (float *)(LDSA ? smem + kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>(a)
-                               : smem);
+    const size_t rows_b = LDSA ? staged_rows_bytes(a, astride) : 0;
+    f4 *sSum = (f4 *)(smem + kZeroBytes + rows_b);
+    float *sR = (float *)(LDSA ? smem + kZeroBytes + rows_b + sums_bytes<FMT, RG, H>((size_t)4 * smax) : smem);
+    uint32_t *sFlag = (uint32_t *)((unsigned char *)sR + (ks > 1 ? NW * RG * 4 * 64 * 4 : 0));
 
     // issue cursor: tile group, slot within the tile, and the column the lane loads
-    int64_t itg = blockIdx.x;
+    int64_t itg = gx;
     int is = 0;
     auto icol = [&]() {
         const int64_t n = (itg * tpw + slot) * 16 + (lane & 15);
@@ -552,13 +652,13 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     AOps<FMT, RG> ab[LDSA ? 1 : P];  // activations in the ring when they are not staged
     auto issue = [&](int p) {
         const int t0 = kslice + is * ks;
-        const int c = 4 * (t0 < nsteps ? t0 : nsteps - 1) + g;
+        const int c = 4 * (pbeg + (t0 < nsteps ? t0 : nsteps - 1)) + g;
         wb[p] = load16_stream(col.w + (uint32_t)c * 16u);
         mb[p] = load_meta_raw<FMT, H>(a, col, c);
         if constexpr (!LDSA) load_a_ops<FMT, RG>(a, c, ar, ab[p]);
         if (++is == S) {
             is = 0;
-            itg += gridDim.x;
+            itg += gdim;
             col = icol();
         }
     };
@@ -567,10 +667,10 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
 
     if constexpr (LDSA) {
         if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
-        stage_a<FMT>(a, sA, astride);
+        stage_a<FMT>(a, sA, astride, cbase * MfFmt<FMT>::KPC, nsteps * 4 * MfFmt<FMT>::KPC);
         __syncthreads();
         if constexpr (MfFmt<FMT>::ZP) {
-            stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum);
+            stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum, nsteps);
             __syncthreads();
         }
     }
@@ -578,10 +678,10 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     // One ring turn = P slots. Every turn but the last consumes and refills each slot;
     // the last turn only drains the ring, so nothing is fetched past the wave's work.
     // Tile boundaries fall on turn boundaries (S is a multiple of P).
-    const int64_t G = blockIdx.x < ngroups ? (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+    const int64_t G = KP ? (gx < ngroups ? 1 : 0) : (gx < ngroups ? (ngroups - gx + gdim - 1) / gdim : 0);
     const int64_t turns = G * (S / P);
     const int tpt = S / P;  // turns per tile
-    int64_t tg = blockIdx.x;
+    int64_t tg = gx;
     int tt = 0;  // turn within the tile
     f4 acc[RG];
 #pragma unroll
@@ -593,8 +693,8 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         for (int p = 0; p < P; ++p) {
             const int t = kslice + (tt * P + p) * ks;
             const int tc = t < nsteps ? t : nsteps - 1;
-            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * tc + g, ar, a_live_grp, sA, sZero, sSum,
-                                             astride, ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
+            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * (pbeg + tc) + g, ar, a_live_grp, sA, sZero,
+                                             sSum, astride, cbase, ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
             if (refill) {
                 // the slot's accumulation completes here (nothing of it may sink below
                 // the refill), then the refill reuses the slot's registers
@@ -603,16 +703,26 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
                 issue(p);
             }
         }
-        if (++tt == tpt) {
-            finish_tile<ACT, RG>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15));
+        if constexpr (!KP) {
+            if (++tt == tpt) {
+                finish_tile<ACT, RG, false>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15));
 #pragma unroll
-            for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
-            tt = 0;
-            tg += gridDim.x;
+                for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
+                tt = 0;
+                tg += gdim;
+            }
+        } else {
+            ++tt;
         }
     };
     for (int64_t i = 0; i + 1 < turns; ++i) turn(true);
     if (turns > 0) turn(false);
+    if constexpr (KP) {
+        // one tile group per workgroup: its finish, with nothing left in flight
+        const int64_t tile = gx * tpw + slot;
+        finish_tile<ACT, RG, true>(a, acc, sR, wave, lane, ks, kslice, g, tile < ntiles, tile * 16 + (lane & 15),
+                                   (int)part, gx, sFlag);
+    }
 }
 
 // DMA-ring kernel for wide N without a K split. Each wave owns 16-column tiles
@@ -667,7 +777,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     const int64_t gw = (int64_t)blockIdx.x * NW + wave;
     const int64_t mytiles = gw < ntiles ? (ntiles - gw + nw - 1) / nw : 0;
     const int64_t total = mytiles * nslots;
-    const size_t abytes = kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>(a);
+    const size_t abytes = kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>((size_t)a.nchunks);
     uint16_t *sZero = (uint16_t *)smem;
     uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
     f4 *sSum = (f4 *)(smem + kZeroBytes + staged_rows_bytes(a, astride));
@@ -779,10 +889,10 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         if (r < total) issue();
-    stage_a<FMT, 4>(a, sA, astride);
+    stage_a<FMT, 4>(a, sA, astride, 0, (int)a.K);
     __syncthreads();
     if constexpr (F::ZP) {
-        stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum);
+        stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum, nch >> 2);
         __syncthreads();
     }
 
@@ -923,7 +1033,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
         }
         cring = nring;
         if (++csl == nslots) {
-            finish_tile<ACT, RG>(a, acc, nullptr, wave, lane, 1, 0, g, true, ctile * 16 + n);
+            finish_tile<ACT, RG, false>(a, acc, nullptr, wave, lane, 1, 0, g, true, ctile * 16 + n);
 #pragma unroll
             for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
             csl = 0;
@@ -936,7 +1046,7 @@ namespace {
 
 template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
 hipError_t go_p(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    auto kern = k_mfma<FMT, ACT, RG, H, LDSA, P>;
+    auto kern = a.kparts > 1 ? k_mfma<FMT, ACT, RG, H, LDSA, P, true> : k_mfma<FMT, ACT, RG, H, LDSA, P, false>;
     if (cfg.lds_bytes > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
         if (e != hipSuccess) return e;

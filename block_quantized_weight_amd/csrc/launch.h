@@ -25,6 +25,12 @@ struct KArgs {
     int32_t ksplit;          // waves sharing one column tile's K range
     float tscale;            // nvfp4 tensor scale (1 otherwise)
     const void *bias;        // [N] bias in the activation dtype, or nullptr
+    // K parts split across workgroups (MFMA register ring only): 1 = none; else the
+    // fp32 partial tiles [kparts, M, N] and one completion counter per tile group,
+    // both in the caller's workspace
+    int32_t kparts;
+    float *part;
+    uint32_t *cnt;
 };
 
 struct LaunchCfg {
@@ -39,6 +45,9 @@ struct LaunchCfg {
     int64_t grid;
     int lds_bytes;
     int variant;
+    int kparts;               // K parts split across workgroups (1 = none)
+    int64_t ws_counters;      // workspace bytes of completion counters (256-byte multiple)
+    int64_t ws_bytes;         // workspace bytes in all (0 without K parts)
 };
 
 hipError_t launch_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);

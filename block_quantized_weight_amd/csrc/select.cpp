@@ -35,7 +35,7 @@ int validate_desc(const qgemv_desc *d) {
     if (d->N < 1 || d->K < 1) return QGEMV_E_SHAPE;
     if (!valid_block(d->format, d->block_size)) return QGEMV_E_BLOCK;
     if (d->K % d->block_size) return QGEMV_E_SHAPE;
-    const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA |
+    const uint32_t known = QGEMV_FLAG_FAMILY_MASK | QGEMV_FLAG_KPARTS_MASK | QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_NO_MFMA |
                            QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
                            QGEMV_FLAG_RING_ON | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
                            QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK |
@@ -45,6 +45,7 @@ int validate_desc(const qgemv_desc *d) {
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
     const uint32_t ks = (d->flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     if (ks > 8 || (ks & (ks - 1))) return QGEMV_E_ARG;  // 1, 2, 4 or 8: whole tiles per 8-wave workgroup
+    if (((d->flags & QGEMV_FLAG_KPARTS_MASK) >> QGEMV_FLAG_KPARTS_SHIFT) > 4) return QGEMV_E_ARG;  // 1..8 parts
     if (((d->flags & QGEMV_FLAG_STREAM_NWG_MASK) >> QGEMV_FLAG_STREAM_NWG_SHIFT) > 4) return QGEMV_E_ARG;
     if (((d->flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT) > 2) return QGEMV_E_ARG;
     if ((d->flags & QGEMV_FLAG_STAGE_A_OFF) && (d->flags & QGEMV_FLAG_STAGE_A_ON)) return QGEMV_E_ARG;
@@ -121,8 +122,33 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
         while (ks < 8 && tiles * ks < 4LL * cu_count && 2 * ks <= steps) ks *= 2;
     }
     if (ks > 8) ks = 8;
-    if (ks > steps) ks = (int)steps;
-    return ks < 1 ? 1 : ks;
+    while (ks > 1 && ks > steps) ks /= 2;  // a power of two: whole tiles per workgroup
+    return ks;
+}
+
+// K parts split across workgroups (qgemv_run_ws only): when the tile groups leave
+// compute units without a workgroup, the most parts (a power of two, at most 8) that
+// keep every workgroup in the first round, one per CU, and at least two K steps per
+// wave in every part. A grid past one round loses: a second workgroup on some CUs
+// costs more than the parts bring (measured on MI355X at M = 8: FP8 5120 x 6144, 160
+// tile groups, 19.5 us unsplit, 30.0 us in 2 parts; FP8 1024 x 16384, 64 tile groups,
+// 46.6 -> 16.0 us in 4 parts; 4-bit 512 x 8192, 32 groups, 18.4 -> 13.4 us in 4; 8-bit
+// 4096 x 4096, 128 groups, 20.3 -> 18.2 us in 2). From (format, N, K, block size,
+// flags, CU count) only, never M. A forced count is taken as given, up to one part
+// per K step.
+static int mfma_kparts(const qgemv_desc *d, int cu_count, uint32_t flags, int ks, int64_t groups) {
+    const int64_t steps = d->K / (4 * k_per_chunk(d->format));
+    const uint32_t forced = (flags & QGEMV_FLAG_KPARTS_MASK) >> QGEMV_FLAG_KPARTS_SHIFT;
+    int kp = 1;
+    if (forced) {
+        kp = 1 << (forced - 1);
+    } else {
+        while (kp < 8 && groups * (2 * kp) <= cu_count && steps >= 2LL * ks * (2 * kp)) kp *= 2;
+    }
+    while (kp > 1 && kp > steps) kp /= 2;
+    // the kernel indexes the partial tiles [kp, M <= 16, N] with 32-bit offsets
+    while (kp > 1 && (int64_t)kp * QGEMV_MAX_M * d->N >= (1LL << 31)) kp /= 2;
+    return kp;
 }
 
 // Persistent streaming kernel for M <= 4 rows in one pass (2 or 4 rows per pass for
@@ -230,7 +256,8 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
     return byte_codes || small;
 }
 
-int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t extra_flags, LaunchCfg *out) {
+int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t extra_flags, bool with_ws,
+                LaunchCfg *out) {
     int rc = validate_desc(d);
     if (rc) return rc;
     if (!out) return QGEMV_E_NULL;
@@ -245,6 +272,9 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
     c.waves_per_wg = 4;
     c.lds_bytes = 0;
     c.variant = 0;
+    c.kparts = 1;
+    c.ws_counters = 0;
+    c.ws_bytes = 0;
 
     const int forced = (int)(flags & QGEMV_FLAG_FAMILY_MASK);
     const bool stream_ok = fast_ok && stream_shape_ok(d);
@@ -280,21 +310,25 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t tiles = (d->N + 15) / 16;
         const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
         const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
-        // staged activations: a 64-byte zero block, the rows (stride K + 8 elements), and
-        // for formats with zero points one 16-byte activation-sum entry per chunk, row
-        // group and scale block of the chunk
-        const int64_t lds_a = (int64_t)M * (d->K + 8) * 2;
+        const int64_t steps = d->K / (4 * k_per_chunk(d->format));
+        const int kp = with_ws ? mfma_kparts(d, cu_count, flags, c.ksplit, groups) : 1;
+        const int64_t smax = (steps + kp - 1) / kp;  // K steps of the longest part
+        // staged activations: a 64-byte zero block, the rows of the longest K part
+        // (stride its k + 8 elements), and for formats with zero points one 16-byte
+        // activation-sum entry per chunk, row group and scale block of the chunk
+        const int64_t kpart = smax * 4 * k_per_chunk(d->format);
+        const int64_t lds_a = (int64_t)M * (kpart + 8) * 2;
         const bool zp_fmt = d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8;
         const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
-        const int64_t lds_sums = zp_fmt ? (d->K / k_per_chunk(d->format)) * rg * hh * 16 : 0;
+        const int64_t lds_sums = zp_fmt ? 4 * smax * rg * hh * 16 : 0;
         const int64_t abytes16 = 64 + ((lds_a + 15) & ~15LL) + lds_sums;
         // DMA ring (no K split, one or two row groups, metadata rows in whole dwords):
         // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
         // fits in LDS next to the staged activations.
         const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
         const bool ring_fits = dma_ring_fits(d, abytes16, zpp, &c.lds_bytes);
-        bool ring = c.ksplit == 1 && rg <= 2 && ring_fits && groups > cu_count;
-        if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && rg <= 2 && ring_fits;
+        bool ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits && groups > cu_count;
+        if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {
             c.waves_per_wg = 8;
@@ -308,8 +342,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // Stage the activations in LDS when they fit and every wave has enough K steps
         // per tile (8 or more) to amortize the copy; with fewer, the activations travel
         // with the codes in the register ring instead.
-        const int64_t steps = d->K / (4 * k_per_chunk(d->format));
-        const int64_t spw = (steps + c.ksplit - 1) / c.ksplit;
+        const int64_t spw = (smax + c.ksplit - 1) / c.ksplit;
         bool stage = abytes16 + lds_red <= kLdsBytes && spw >= 8;
         if (flags & QGEMV_FLAG_STAGE_A_ON) stage = abytes16 + lds_red <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
@@ -318,15 +351,25 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const uint32_t fdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
         const bool deep8 = fdep ? fdep == 2 : (spw % 8 == 0 || spw >= 32);
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
-        c.lds_bytes = (int)(lds_red + (stage ? abytes16 : 0));
-        int64_t grid = groups;
-        if (stage) {
+        // with K parts, 16 bytes more for the last-workgroup flag
+        c.lds_bytes = (int)(lds_red + (stage ? abytes16 : 0) + (kp > 1 ? 16 : 0));
+        // without K parts, a persistent grid of at most what fits at once; with them,
+        // exactly one workgroup per tile group and part
+        int64_t grid = groups * kp;
+        if (stage && kp == 1) {
             int64_t per_cu = c.lds_bytes > 0 ? kLdsBytes / c.lds_bytes : 8;
             if (per_cu > 32 / nw) per_cu = 32 / nw;
             if (per_cu < 1) per_cu = 1;
             if (grid > per_cu * cu_count) grid = per_cu * cu_count;
         }
         c.grid = grid;
+        c.kparts = kp;
+        if (kp > 1) {
+            // workspace: one 32-bit completion counter per tile group (rounded up to
+            // 256 bytes), then the fp32 partial tiles [kp, M, N]
+            c.ws_counters = (groups * 4 + 255) / 256 * 256;
+            c.ws_bytes = c.ws_counters + ((int64_t)kp * M * d->N * 4 + 255) / 256 * 256;
+        }
     } else if (family == QGEMV_FAMILY_GENERIC) {
         c.rows_per_pass = M;
         c.passes = 1;

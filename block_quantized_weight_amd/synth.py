@@ -230,6 +230,9 @@ WORKLOADS = {
     # small-N split-K corner
     "u4_m8_k2048_n1024": dict(fmt="u4", act="f16", N=1024, K=2048, bs=32, ms=(8,), seed=40,
                               zp_range=(0, 15), scale_sigma=0.02),
+    # a tall-K shape in the same corner (N <= 1024, large K), where the K range is also
+    # split across workgroups (FP8 codes and scales drawn as for the FP8 projection)
+    "fp8_m8_k16384_n1024": dict(fmt="fp8", act="f16", N=1024, K=16384, bs=128, ms=(8,), seed=41),
 }
 
 

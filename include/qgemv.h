@@ -36,9 +36,11 @@
  * FP4 decode and M-tiling", reviewed-changes table; "[CUDA] Pin FP8 GEMV residency
  * for grids just past two blocks per SM", review thread). NULL means none.
  *
- * All pointers passed to qgemv_create and qgemv_run are DEVICE pointers, owned by
- * the caller. The handle keeps the weight pointers (not copies) and the caller
- * keeps them alive until qgemv_destroy. The library allocates no device memory.
+ * All pointers passed to qgemv_create, qgemv_run and qgemv_run_ws are DEVICE
+ * pointers, owned by the caller. The handle keeps the weight pointers (not copies)
+ * and the caller keeps them alive until qgemv_destroy. The library allocates no
+ * device memory: the one kernel that needs scratch memory (the K split across
+ * workgroups of qgemv_run_ws) takes it from the caller.
  *
  * Every call returns QGEMV_OK (0) or a positive status; nothing aborts, prints or
  * throws across this interface. Arguments are validated before anything is
@@ -47,13 +49,14 @@
 #ifndef QGEMV_H_
 #define QGEMV_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define QGEMV_ABI_VERSION 2
+#define QGEMV_ABI_VERSION 3
 #define QGEMV_MAX_M 16
 
 /* Weight formats. */
@@ -80,7 +83,9 @@ enum qgemv_status {
     QGEMV_E_DEVICE = 5,   /* no usable device, or the device is not gfx950 */
     QGEMV_E_LAUNCH = 6,   /* the kernel launch reported an error */
     QGEMV_E_ARG = 7,      /* other invalid argument (struct size, flags, plan request) */
-    QGEMV_E_ALLOC = 8     /* host memory for the handle could not be allocated */
+    QGEMV_E_ALLOC = 8,    /* host memory for the handle could not be allocated */
+    QGEMV_E_WORKSPACE = 9 /* qgemv_run_ws: the plan needs a workspace and none, or too small
+                             or misaligned a one, was given */
 };
 
 /* Kernel families (qgemv_plan_info.family; also usable in QGEMV_FLAG_FORCE). */
@@ -92,6 +97,9 @@ enum qgemv_family {
 };
 
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
+ * Bits 4..6: forced number of K parts split across workgroups by qgemv_run_ws (v ->
+ * 2^(v-1): 1, 2, 4 or 8 parts, at most one per K step of the MFMA family; 0 =
+ * automatic). Bit 7: reserved (0).
  * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1, 2, 4 or
  * 8 waves share the K range of a column tile). Bits 12..14: waves per workgroup of the
  * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
@@ -109,9 +117,12 @@ enum qgemv_family {
  * at M = 1 as well. Bits 29..30: MFMA register-ring depth (1 -> 4 slots, 2 -> 8;
  * 0 = automatic). Bit 31: 16-wave workgroups for the one-row streaming kernel with one
  * column per wave (also chosen automatically when the columns fill 8 to 16 waves per
- * CU and neither bits 21..22 nor 25..27 are set). None of these changes a result's bits except the family choice and
- * the K split; they exist for A/B comparisons and tuning. */
+ * CU and neither bits 21..22 nor 25..27 are set). None of these changes a result's
+ * bits except the family choice, the K split and the K parts; they exist for A/B
+ * comparisons and tuning. */
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
+#define QGEMV_FLAG_KPARTS_SHIFT 4
+#define QGEMV_FLAG_KPARTS_MASK 0x00000070u
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
 #define QGEMV_FLAG_KSPLIT_MASK 0x00000F00u
 #define QGEMV_FLAG_STREAM_NWG_SHIFT 12
@@ -164,6 +175,10 @@ typedef struct qgemv_plan_info {
                                 double-buffered), bit 3 = 8-slot register ring (else 4).
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
+    int32_t kparts;          /* K parts split across workgroups (1 = none; only qgemv_run_ws
+                                splits, ABI version 3) */
+    int32_t reserved;        /* 0 */
+    int64_t workspace_bytes; /* device workspace this launch needs (0 without K parts) */
 } qgemv_plan_info;
 
 typedef struct qgemv_handle qgemv_handle;
@@ -182,14 +197,46 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device);
  * handle's device current. */
 int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream);
 
-/* The launch qgemv_run would make for M rows (pointers as given at create; A and Y
- * assumed 16-byte aligned). */
-int qgemv_plan(const qgemv_handle *h, int M, qgemv_plan_info *out);
+/* The same product, where the K range may also be split across workgroups: for N so
+ * small that the column tiles, even with the K split inside a workgroup, leave
+ * compute units idle, each of `kparts` workgroups takes one contiguous part of the
+ * K steps of a tile group, writes its fp32 partial tile to the workspace, and the
+ * last of them to finish (counted by an atomic counter per tile group) adds the
+ * partials in fixed part order and writes Y. This follows the pages' opt-in split-K
+ * GEMV with its global workspace, completion counters and last-block reduction in
+ * fixed slice order ("[CUDA] MatMul: add an opt-in split-K GEMV", Kernel and
+ * dispatch; review threads on the workspace's visibility), here for the quantized
+ * formats. The order of the fp32 sums depends on (format, N, K, block size, flags)
+ * and the device's compute-unit count, never on M, so rows stay bit-identical
+ * whatever tile carries them; the bits can differ from qgemv_run's where qgemv_run
+ * does not split (within the same error bound).
+ *
+ * workspace: device memory of at least qgemv_workspace_size(h, M) bytes, 256-byte
+ * aligned, owned by the caller: completion counters, then fp32 partial tiles. Zero
+ * the whole workspace once before its first use (hipMemset). Every run that
+ * completes leaves all of it zero again (the last workgroup of a tile group resets
+ * its counter with an atomic store and clears the partials it read), so later runs
+ * need no clearing and one workspace can serve any handle and any M in turn. Runs
+ * that overlap in time (on different streams) must not share a workspace. A plan
+ * without K parts ignores the workspace (it may then be NULL). Returns
+ * QGEMV_E_WORKSPACE when the plan needs a workspace and none, or too small or
+ * misaligned a one, is given. */
+int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *workspace,
+                 size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of workspace qgemv_run_ws needs for M rows (0 when its plan has no K parts).
+ * Sized at M = QGEMV_MAX_M, a workspace serves every M. */
+int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes);
+
+/* The launch qgemv_run (with_workspace = 0) or qgemv_run_ws (with_workspace != 0)
+ * would make for M rows (pointers as given at create; A and Y assumed 16-byte
+ * aligned). */
+int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info *out);
 
 /* Pure host selector, no device needed: the plan for d at M rows on a device with
- * cu_count compute units, assuming 16-byte aligned pointers. Used to test the
- * dispatcher at fixed CU counts. */
-int qgemv_select(const qgemv_desc *d, int M, int cu_count, qgemv_plan_info *out);
+ * cu_count compute units, assuming 16-byte aligned pointers; with_workspace as for
+ * qgemv_plan. Used to test the dispatcher at fixed CU counts. */
+int qgemv_select(const qgemv_desc *d, int M, int cu_count, int with_workspace, qgemv_plan_info *out);
 
 /* Release the handle (NULL is ignored). Does not touch the caller's buffers. */
 void qgemv_destroy(qgemv_handle *h);

@@ -25,10 +25,19 @@ def say(msg: str):
     sys.stdout.flush()
 
 
+def new_workspace(q: bqw.QGemv, M: int = bqw.MAX_M) -> torch.Tensor:
+    """A zeroed workspace for q's qgemv_run_ws (at least 256 bytes; torch's device
+    allocations are 256-byte aligned)."""
+    n = max(q.workspace_size(M), 256)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+
 def run_gpu(prob: synth.Problem, M: int, flags: int = 0, A: Optional[np.ndarray] = None,
-            a_offset_elems: int = 0, repeat: int = 1):
-    """Run Y = A[:M] . dequant(W)^T on cuda:0; returns (Y as float64 [M, N], plan)."""
+            a_offset_elems: int = 0, repeat: int = 1, ws: bool = False):
+    """Run Y = A[:M] . dequant(W)^T on cuda:0 through qgemv_run (or qgemv_run_ws with
+    a fresh zeroed workspace when ws); returns (Y as float64 [M, N], plan)."""
     q, t = bqw.upload(prob, flags=flags)
+    wsbuf = new_workspace(q, M) if ws else None
     tdt = t["A"].dtype
     if A is not None:
         t["A"] = torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).cuda().view(tdt)
@@ -40,10 +49,13 @@ def run_gpu(prob: synth.Problem, M: int, flags: int = 0, A: Optional[np.ndarray]
     outs = []
     for _ in range(repeat):
         Y = torch.full((M, prob.N), float("nan"), dtype=tdt, device="cuda")
-        q.run(Am, Y, M=M)
+        q.run(Am, Y, M=M, workspace=wsbuf)
         torch.cuda.synchronize()
         outs.append(Y.float().cpu().numpy().astype(np.float64))
-    plan = q.plan(M)
+    plan = q.plan(M, with_workspace=ws)
+    if ws:
+        # every completed run leaves the whole workspace zero
+        plan["ws_zero"] = bool((wsbuf == 0).all().item())
     q.close()
     return (outs if repeat > 1 else outs[0]), plan
 

@@ -23,8 +23,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert {"qgemv_create", "qgemv_run", "qgemv_plan", "qgemv_select", "qgemv_destroy",
-            "qgemv_status_str", "qgemv_abi_version"} <= names
+    assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_workspace_size", "qgemv_plan", "qgemv_select",
+            "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version"} <= names
     L = bqw.lib()
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -32,17 +32,22 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert bqw.lib().qgemv_abi_version() == 2
+    assert bqw.lib().qgemv_abi_version() == 3
     # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields; the
     # bias pointer (version 2) follows the flags
     assert ctypes.sizeof(bqw.Desc) == 72
     assert bqw.Desc.N.offset == 16 and bqw.Desc.W.offset == 32 and bqw.Desc.flags.offset == 60
     assert bqw.Desc.bias.offset == 64
+    # the plan report gains the K parts and the workspace size (version 3)
+    assert ctypes.sizeof(bqw.PlanInfo) == 56
+    assert bqw.PlanInfo.grid.offset == 24 and bqw.PlanInfo.variant.offset == 36
+    assert bqw.PlanInfo.kparts.offset == 40 and bqw.PlanInfo.workspace_bytes.offset == 48
 
 
 def test_status_strings():
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert bqw.status_str(s)
+    assert "workspace" in bqw.status_str(9)
     assert bqw.status_str(0) == "ok"
     assert "unknown" in bqw.status_str(99)
 
@@ -59,7 +64,7 @@ def _sel(**kw):
     (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
     (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
     (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=3 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=1 << 15), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
-    (dict(cu_count=0), 7), (dict(bias=0x2001), 7),
+    (dict(cu_count=0), 7), (dict(bias=0x2001), 7), (dict(flags=5 << 4), 7), (dict(flags=7 << 4), 7),
 ])
 def test_select_rejects_invalid_arguments(kw, status):
     with pytest.raises(bqw.QGemvError) as e:
@@ -69,13 +74,18 @@ def test_select_rejects_invalid_arguments(kw, status):
 
 def test_null_pointers_are_rejected_before_anything_else():
     L = bqw.lib()
-    assert L.qgemv_select(None, 1, 256, None) == 1
+    assert L.qgemv_select(None, 1, 256, 0, None) == 1
     out = bqw.PlanInfo()
-    assert L.qgemv_select(None, 1, 256, ctypes.byref(out)) == 1
+    assert L.qgemv_select(None, 1, 256, 0, ctypes.byref(out)) == 1
+    assert L.qgemv_select(None, 1, 256, 1, ctypes.byref(out)) == 1
     assert L.qgemv_create(None, None, 0) == 1
     h = ctypes.c_void_p()
     assert L.qgemv_create(ctypes.byref(h), None, 0) == 1
     assert L.qgemv_run(None, None, None, 1, None) == 1
+    assert L.qgemv_run_ws(None, None, None, 1, None, 0, None) == 1
+    size = ctypes.c_size_t()
+    assert L.qgemv_workspace_size(None, 1, ctypes.byref(size)) == 1
+    assert L.qgemv_plan(None, 1, 0, ctypes.byref(out)) == 1
     L.qgemv_destroy(None)  # ignored
 
 
@@ -107,12 +117,13 @@ def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
     for fmt, act, N, K, bs in [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128),
                                ("nvfp4", "bf16", 248320, 2048, 16), ("u8", "f16", 4096, 4096, 128),
                                ("u4", "f16", 1024, 2048, 32)]:
-        plans = [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=m) for m in range(1, 17)]
-        for key in ("ksplit",):
-            fams = {}
-            for p in plans:
-                fams.setdefault(p["family"], set()).add(p[key])
-            assert all(len(v) == 1 for v in fams.values()), (fmt, key, fams)
+        for ws in (False, True):
+            plans = [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=m, with_workspace=ws) for m in range(1, 17)]
+            for key in ("ksplit", "kparts"):
+                fams = {}
+                for p in plans:
+                    fams.setdefault(p["family"], set()).add(p[key])
+                assert all(len(v) == 1 for v in fams.values()), (fmt, ws, key, fams)
 
 
 def test_select_covers_the_machine():
@@ -123,3 +134,51 @@ def test_select_covers_the_machine():
         for M in (1, 4, 8):
             p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)
             assert p["grid"] * p["waves_per_wg"] >= 256 * 4 or p["grid"] * p["cols_per_wave"] * p["waves_per_wg"] >= N
+
+
+def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
+    """qgemv_run_ws splits K across workgroups only where the tile groups leave CUs
+    idle, with the most parts that keep the grid within one workgroup per CU; qgemv_run
+    never splits."""
+    # FP8 1024 x 16384: 64 tiles, K split 8 -> 64 tile groups -> 4 parts (256 workgroups)
+    for M in (5, 8, 16):
+        kw = dict(fmt="fp8", act="f16", N=1024, K=16384, block_size=128, M=M)
+        p0, p1 = _sel(**kw), _sel(**kw, with_workspace=True)
+        assert p0["kparts"] == 1 and p0["workspace_bytes"] == 0
+        assert p1["family"] == "mfma" and p1["ksplit"] == p0["ksplit"] == 8
+        assert p1["kparts"] == 4 and p1["grid"] == 64 * 4 and not (p1["variant"] & 2)
+        # 64 counters (256 bytes), then the [4, M, N] fp32 partials
+        assert p1["workspace_bytes"] == 256 + (4 * M * 1024 * 4 + 255) // 256 * 256
+    # 8-bit 4096 x 4096 at M = 8: 256 tiles, K split 4, 128 tile groups -> 2 parts
+    p = _sel(fmt="u8", act="f16", N=4096, K=4096, block_size=128, M=8, with_workspace=True)
+    assert p["family"] == "mfma" and p["ksplit"] == 4 and p["kparts"] == 2 and p["grid"] == 256
+    # FP8 5120 x 6144: 160 tile groups; 2 parts would need a second round: none
+    p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=8, with_workspace=True)
+    assert p["kparts"] == 1 and p["workspace_bytes"] == 0
+    # parts keep two K steps per wave: 4-bit 1024 x 2048 (16 steps, K split 8) takes none
+    p = _sel(fmt="u4", act="f16", N=1024, K=2048, block_size=32, M=8, with_workspace=True)
+    assert p["ksplit"] == 8 and p["kparts"] == 1
+    # wide N fills the machine with tile groups: no parts, no workspace
+    for M in (2, 8, 16):
+        p = _sel(M=M, with_workspace=True)
+        assert p["kparts"] == 1 and p["workspace_bytes"] == 0, p
+    # the streaming family never splits
+    p = _sel(fmt="fp8", act="f16", N=1024, K=16384, block_size=128, M=1, with_workspace=True)
+    assert p["family"] == "stream" and p["kparts"] == 1
+
+
+def test_forced_k_parts_and_k_split_are_clamped():
+    # 4 K steps (fp8, K = 256): 8 forced parts become 4, one step each
+    p = _sel(fmt="fp8", act="f16", N=100, K=256, block_size=128, M=8, flags=2 | (4 << 4), with_workspace=True)
+    assert p["kparts"] == 4 and p["grid"] % 4 == 0
+    # forced parts on a wide N: exactly one workgroup per tile group and part, no ring
+    p = _sel(M=4, flags=2 | (2 << 4), with_workspace=True)
+    groups = (151936 // 16 + (8 // p["ksplit"]) - 1) // (8 // p["ksplit"])
+    assert p["kparts"] == 2 and p["grid"] == 2 * groups and not (p["variant"] & 2)
+    # the partial tiles are indexed with 32-bit offsets: kparts * 16 * N < 2^31
+    p = _sel(N=1 << 24, M=1, flags=2 | (4 << 4), with_workspace=True)
+    assert p["kparts"] == 4
+    # a forced K split beyond the K steps falls to a power of two (whole tiles per
+    # 8-wave workgroup): 3 steps of 4-bit codes (K = 384), forced 8 -> 2
+    p = _sel(N=100, K=384, M=8, flags=2 | (8 << 8))
+    assert p["ksplit"] == 2

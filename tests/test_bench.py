@@ -48,12 +48,16 @@ def test_trace_durations_and_counter_means(tmp_path):
 
 
 def test_traffic_lookup_is_gated_on_the_source_hash(tmp_path, monkeypatch):
-    rec = {"workload": "w", "M": 4, "flags": 0, "src_hash": bench.kernel_source_hash(), "traffic_bytes": 1234}
+    rec = {"workload": "w", "M": 4, "flags": 0, "ws": True, "src_hash": bench.kernel_source_hash(),
+           "traffic_bytes": 1234}
     stale = dict(rec, src_hash="0" * 16, traffic_bytes=99)
+    plain = dict(rec, ws=False, traffic_bytes=777)
     (tmp_path / "k_w.md").write_text("# summary\n\ntraffic_record: " + json.dumps(stale) + "\n"
-                                     "traffic_record: " + json.dumps(rec) + "\n")
+                                     "traffic_record: " + json.dumps(rec) + "\n"
+                                     "traffic_record: " + json.dumps(plain) + "\n")
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.lookup_traffic("w", 4, 0) == 1234
+    assert bench.lookup_traffic("w", 4, 0, ws=False) == 777
     assert bench.lookup_traffic("w", 8, 0) is None
     (tmp_path / "k_w.md").write_text("traffic_record: " + json.dumps(stale) + "\n")
     assert bench.lookup_traffic("w", 4, 0) is None

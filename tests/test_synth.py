@@ -62,6 +62,7 @@ def test_full_size_byte_counts():
         "u4_m1_k512_n256": 75_776, "u8_m1_k4096_n4096": 17_170_432, "fp8_k6144_n5120": 32_440_320,
         "nvfp4_m4_k2048_n2048": 2_359_300, "nvfp4_m4_k2048_n248320": 286_064_644,
         "u4_k4096_n151936": 359_784_448, "u4_m8_k2048_n1024": 1_212_416,
+        "fp8_m8_k16384_n1024": 17_301_504,
     }
     for name, spec in synth.WORKLOADS.items():
         assert wb(spec["fmt"], spec["N"], spec["K"], spec["bs"]) == want[name]
