@@ -416,6 +416,32 @@ __device__ __forceinline__ void pin_accumulators(f4 acc[RG]) {
     for (int r = 0; r < RG; ++r) asm volatile("" : "+v"(acc[r])::"memory");
 }
 
+// The register ring loads codes in a coalesced lane order: lane l reads chunk
+// 4t + (l & 3) of the tile's column l >> 2, so four neighbouring lanes read 64
+// contiguous bytes of one column (in the MFMA order, lane n + 16g holding column n's
+// chunk 4t + g, neighbouring lanes sit in different columns and every lane's load
+// becomes its own cache and translation request). This moves a loaded chunk to its
+// MFMA lane: lane m takes the chunk of load lane 4 (m & 15) + (m >> 4), one
+// ds_bpermute per dword (a lane crossbar, no memory traffic).
+__device__ __forceinline__ u4v to_mfma_lanes(const u4v &v, int src_byte) {
+    u4v o;
+    o.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.x);
+    o.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.y);
+    o.z = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.z);
+    o.w = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.w);
+    return o;
+}
+
+// The same move for a chunk's raw block metadata (the zero-point word only for the
+// formats that have zero points).
+template <int FMT, int H>
+__device__ __forceinline__ MetaRaw<H> meta_to_mfma_lanes(const MetaRaw<H> &m, int src_byte) {
+    MetaRaw<H> o;
+    o.v[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)m.v[0]);
+    o.v[1] = MfFmt<FMT>::ZP ? (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)m.v[1]) : 0u;
+    return o;
+}
+
 // Stage k = k0 .. k0 + klen - 1 of the M activation rows into LDS once per
 // workgroup, permuted into the MFMA slot order (row stride astride elements). Each
 // thread handles 16-byte pieces it, it + blockDim, ... in batches of SB whose loads
@@ -640,21 +666,25 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     uint32_t *sFlag = (uint32_t *)((unsigned char *)sR + (ks > 1 ? NW * RG * 4 * 64 * 4 : 0));
 
     // issue cursor: tile group, slot within the tile, and the column the lane loads
+    // codes and block metadata of, in the coalesced order of to_mfma_lanes (column
+    // lane >> 2, chunk 4t + (lane & 3) of the step)
     int64_t itg = gx;
     int is = 0;
     auto icol = [&]() {
-        const int64_t n = (itg * tpw + slot) * 16 + (lane & 15);
+        const int64_t n = (itg * tpw + slot) * 16 + (lane >> 2);
         return mf_col<FMT>(a, n < a.N ? n : a.N - 1);
     };
+    const int perm_src = ((lane & 15) * 4 + (lane >> 4)) * 4;  // ds_bpermute source byte
     MfCol col = icol();
     u4v wb[P];
     MetaRaw<H> mb[P];
     AOps<FMT, RG> ab[LDSA ? 1 : P];  // activations in the ring when they are not staged
     auto issue = [&](int p) {
         const int t0 = kslice + is * ks;
-        const int c = 4 * (pbeg + (t0 < nsteps ? t0 : nsteps - 1)) + g;
-        wb[p] = load16_stream(col.w + (uint32_t)c * 16u);
-        mb[p] = load_meta_raw<FMT, H>(a, col, c);
+        const int c4 = 4 * (pbeg + (t0 < nsteps ? t0 : nsteps - 1));
+        const int c = c4 + g;
+        wb[p] = load16_stream(col.w + (uint32_t)(c4 + (lane & 3)) * 16u);
+        mb[p] = load_meta_raw<FMT, H>(a, col, c4 + (lane & 3));
         if constexpr (!LDSA) load_a_ops<FMT, RG>(a, c, ar, ab[p]);
         if (++is == S) {
             is = 0;
@@ -693,8 +723,10 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         for (int p = 0; p < P; ++p) {
             const int t = kslice + (tt * P + p) * ks;
             const int tc = t < nsteps ? t : nsteps - 1;
-            mfma_step<FMT, ACT, RG, H, LDSA>(a, wb[p], mb[p], 4 * (pbeg + tc) + g, ar, a_live_grp, sA, sZero,
-                                             sSum, astride, cbase, ab[LDSA ? 0 : p], tile_ok && t < nsteps, acc);
+            mfma_step<FMT, ACT, RG, H, LDSA>(a, to_mfma_lanes(wb[p], perm_src), meta_to_mfma_lanes<FMT, H>(mb[p], perm_src),
+                                             4 * (pbeg + tc) + g, ar,
+                                             a_live_grp, sA, sZero, sSum, astride, cbase, ab[LDSA ? 0 : p],
+                                             tile_ok && t < nsteps, acc);
             if (refill) {
                 // the slot's accumulation completes here (nothing of it may sink below
                 // the refill), then the refill reuses the slot's registers
