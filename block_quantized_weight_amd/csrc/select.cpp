@@ -126,24 +126,27 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     return ks;
 }
 
-// K parts split across workgroups (qgemv_run_ws only): when the tile groups leave
-// compute units without a workgroup, the most parts (a power of two, at most 8) that
-// keep every workgroup in the first round, one per CU, and at least two K steps per
-// wave in every part. A grid past one round loses: a second workgroup on some CUs
-// costs more than the parts bring (measured on MI355X at M = 8: FP8 5120 x 6144, 160
-// tile groups, 19.5 us unsplit, 30.0 us in 2 parts; FP8 1024 x 16384, 64 tile groups,
-// 46.6 -> 16.0 us in 4 parts; 4-bit 512 x 8192, 32 groups, 18.4 -> 13.4 us in 4; 8-bit
-// 4096 x 4096, 128 groups, 20.3 -> 18.2 us in 2). From (format, N, K, block size,
-// flags, CU count) only, never M. A forced count is taken as given, up to one part
-// per K step.
+// K parts split across workgroups (qgemv_run_ws only), from (format, N, K, block
+// size, flags, CU count), never M. A part count that pushes the grid past one
+// workgroup per CU always loses. Within that, measured on MI355X at M = 8 (unsplit ->
+// best split): where the tile groups fill at most a quarter of the CUs, parts pay
+// (FP8 1024 x 16384, 64 groups: 36.1 -> 15.1 us in 4; 4-bit 512 x 8192, 32 groups:
+// 15.8 -> 12.7 us in 4), so the most parts that keep two K steps per wave; where they
+// fill up to half, 2 parts pay only with long parts, whose activations then fit the
+// LDS (FP8 2048 x 16384: 36.4 -> 19.9 us; FP8 4096 x 8192: 19.1 -> 18.1 us; but
+// 4-bit 2048 x 8192, 8 steps per wave and part: 16.5 -> 18.6 us; 8-bit 4096 x 4096:
+// 15.4 -> 16.0 us), so only with 16 K steps or more per wave and part. A forced count
+// is taken as given, up to one part per K step.
 static int mfma_kparts(const qgemv_desc *d, int cu_count, uint32_t flags, int ks, int64_t groups) {
     const int64_t steps = d->K / (4 * k_per_chunk(d->format));
     const uint32_t forced = (flags & QGEMV_FLAG_KPARTS_MASK) >> QGEMV_FLAG_KPARTS_SHIFT;
     int kp = 1;
     if (forced) {
         kp = 1 << (forced - 1);
-    } else {
+    } else if (groups * 4 <= cu_count) {
         while (kp < 8 && groups * (2 * kp) <= cu_count && steps >= 2LL * ks * (2 * kp)) kp *= 2;
+    } else if (groups * 2 <= cu_count && steps >= 16LL * ks * 2) {
+        kp = 2;
     }
     while (kp > 1 && kp > steps) kp /= 2;
     // the kernel indexes the partial tiles [kp, M <= 16, N] with 32-bit offsets
@@ -346,10 +349,12 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         bool stage = abytes16 + lds_red <= kLdsBytes && spw >= 8;
         if (flags & QGEMV_FLAG_STAGE_A_ON) stage = abytes16 + lds_red <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
-        // register-ring depth: 8 slots when a wave's steps per tile are a multiple of 8
-        // or many (no idle padded slots to speak of), else 4; or forced
+        // register-ring depth: 4 slots unless forced. With the loads coalesced, 8 slots
+        // measured no faster anywhere and slower on the staged FP8 and 8-bit rings (FP8
+        // 5120 x 6144 M = 8: 16.6 us with 4, 17.4 with 8; 8-bit 4096 x 4096 M = 8: 15.5
+        // / 16.2 us; 4-bit lm_head M = 12 and 16: equal)
         const uint32_t fdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
-        const bool deep8 = fdep ? fdep == 2 : (spw % 8 == 0 || spw >= 32);
+        const bool deep8 = fdep == 2;
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
         // with K parts, 16 bytes more for the last-workgroup flag
         c.lds_bytes = (int)(lds_red + (stage ? abytes16 : 0) + (kp > 1 ? 16 : 0));

@@ -149,9 +149,18 @@ def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
         assert p1["kparts"] == 4 and p1["grid"] == 64 * 4 and not (p1["variant"] & 2)
         # 64 counters (256 bytes), then the [4, M, N] fp32 partials
         assert p1["workspace_bytes"] == 256 + (4 * M * 1024 * 4 + 255) // 256 * 256
-    # 8-bit 4096 x 4096 at M = 8: 256 tiles, K split 4, 128 tile groups -> 2 parts
+    # 128 tile groups (half the CUs): 2 parts only with 16 K steps or more per wave and
+    # part. FP8 2048 x 16384 (256 steps, K split 8): 2 parts; 8-bit 4096 x 4096 (64
+    # steps, K split 4) and 4-bit 2048 x 8192 (64 steps, K split 8): none
+    p = _sel(fmt="fp8", act="f16", N=2048, K=16384, block_size=128, M=8, with_workspace=True)
+    assert p["ksplit"] == 8 and p["kparts"] == 2 and p["grid"] == 256
     p = _sel(fmt="u8", act="f16", N=4096, K=4096, block_size=128, M=8, with_workspace=True)
-    assert p["family"] == "mfma" and p["ksplit"] == 4 and p["kparts"] == 2 and p["grid"] == 256
+    assert p["family"] == "mfma" and p["ksplit"] == 4 and p["kparts"] == 1
+    p = _sel(fmt="u4", act="bf16", N=2048, K=8192, block_size=32, M=8, with_workspace=True)
+    assert p["ksplit"] == 8 and p["kparts"] == 1
+    # 32 tile groups: 4-bit 512 x 8192 -> 4 parts (8 would leave one K step per wave)
+    p = _sel(fmt="u4", act="bf16", N=512, K=8192, block_size=32, M=8, with_workspace=True)
+    assert p["ksplit"] == 8 and p["kparts"] == 4
     # FP8 5120 x 6144: 160 tile groups; 2 parts would need a second round: none
     p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=8, with_workspace=True)
     assert p["kparts"] == 1 and p["workspace_bytes"] == 0

@@ -59,12 +59,12 @@ def test_fp8_projection_with_forced_k_parts():
 
 
 def test_u8_projection_with_k_parts_and_bias():
-    """The 8-bit 4096 x 4096 weight of the M = 1 workload at M = 8 (two K parts), with
-    the fused bias added by the last workgroup."""
+    """The 8-bit 4096 x 4096 weight of the M = 1 workload at M = 8 in two forced K
+    parts, with the fused bias added by the last workgroup."""
     prob = synth.make_problem("u8", "f16", 4096, 4096, 128, 8, seed=1, zp_range=(96, 160), scale_sigma=0.004,
                               with_bias=True)
     gu.say("[kparts] u8 4096x4096 M=8 bias")
-    Y, plan = gu.run_gpu(prob, 8, ws=True)
+    Y, plan = gu.run_gpu(prob, 8, flags=2 | kp_flags(2), ws=True)
     assert plan["kparts"] == 2 and plan["ws_zero"], plan
     ok, ratio, _, _ = gu.check_full(prob, 8, Y)
     assert ok, ratio
