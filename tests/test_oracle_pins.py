@@ -11,6 +11,7 @@
 """
 
 import os
+import zlib
 from fractions import Fraction
 
 import numpy as np
@@ -178,6 +179,11 @@ def test_nibble_packing_matches_golden_fixture():
 # brute force with exact rationals on tiny shapes
 
 
+def _seed(*key):
+    """A seed that is the same in every process (Python's str hash is salted)."""
+    return zlib.crc32(repr(key).encode())
+
+
 def _f16_fraction(bits):
     return Fraction(float(np.uint16(bits).view(np.float16)))
 
@@ -260,7 +266,7 @@ CASES = [
 
 @pytest.mark.parametrize("fmt,act,bs,with_zp", CASES)
 def test_brute_force_exact_rationals(fmt, act, bs, with_zp):
-    rng = np.random.default_rng(hash((fmt, act, bs, with_zp)) % 2**32)
+    rng = np.random.default_rng(_seed(fmt, act, bs, with_zp))
     for M, N, nblk in ((1, 1, 1), (2, 3, 3), (3, 5, 2)):
         K = nblk * bs
         prob, L = _logical_problem(fmt, act, M, N, K, bs, rng, with_zp=bool(with_zp))
@@ -271,6 +277,43 @@ def test_brute_force_exact_rationals(fmt, act, bs, with_zp):
                 ye, se = float(Ye[m][n]), float(Se[m][n])
                 assert abs(Y[m, n] - ye) <= 1e-12 * se + 1e-300, (m, n, Y[m, n], ye)
                 assert abs(S[m, n] - se) <= 1e-12 * se + 1e-300
+
+
+def _dequant_matrix(fmt, bs, L):
+    """W as an fp64 [N, K] matrix from the unpacked arrays: library decoders for the
+    scales and E4M3 codes (numpy float16, torch float8_e4m3fn), E2M1 from the pinned
+    table, and no packed byte at all."""
+    if fmt in ("u4", "u8"):
+        s = L["s_bits"].astype(np.uint16).view(np.float16).astype(np.float64)
+        return np.repeat(s, bs, axis=1) * (L["q"].astype(np.float64) - np.repeat(L["z"], bs, axis=1))
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if fmt == "fp8":
+        return np.repeat(L["s"].astype(np.float64), bs, axis=1) * e4[L["q"]]
+    e2, _ = oracle.tables()
+    return L["ts"] * np.repeat(e4[L["sc"]], 16, axis=1) * np.asarray(e2)[L["q"]]
+
+
+@pytest.mark.parametrize("fmt,act,bs,with_zp", CASES)
+def test_numpy_dequant_matmul_agrees_on_larger_shapes(fmt, act, bs, with_zp):
+    """A second implementation, numpy's: dequantize the unpacked arrays to fp64 and
+    multiply with A @ W.T. On shapes past the brute force (odd block counts, so the
+    4-bit zero-point rows end in half a byte; several rows; N not a multiple of
+    anything) it checks the oracle's unpacking and indexing of the packed bytes."""
+    rng = np.random.default_rng(_seed("numpy", fmt, act, bs, with_zp))
+    for M, N, nblk in ((5, 37, 7), (1, 64, 33)):
+        K = nblk * bs
+        prob, L = _logical_problem(fmt, act, M, N, K, bs, rng, with_zp=bool(with_zp))
+        Y, S = oracle.gemv(prob)
+        a = L["a_bits"].astype(np.uint16)
+        if act == "f16":
+            A = a.view(np.float16).astype(np.float64)
+        else:
+            A = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+        W = _dequant_matrix(fmt, bs, L)
+        Yn = A @ W.T
+        Sn = np.abs(A) @ np.abs(W).T
+        assert np.all(np.abs(Y - Yn) <= 1e-12 * Sn + 1e-300), (fmt, M, N, K)
+        assert np.allclose(S, Sn, rtol=1e-12, atol=0.0)
 
 
 def test_integer_special_case_is_exact():
@@ -383,7 +426,7 @@ def test_brute_force_with_bias(fmt, act, bs, with_zp):
     column, the same for every row, outside the NVFP4 tensor scale), S unchanged.
     Distinct rows and columns catch a bias indexed by the row, and NVFP4's tensor
     scale (not 1) catches a bias scaled with the product."""
-    rng = np.random.default_rng(hash(("bias", fmt, act, bs)) % 2**32)
+    rng = np.random.default_rng(_seed("bias", fmt, act, bs))
     act_frac = _f16_fraction if act == "f16" else _bf16_fraction
     for M, N, nblk in ((2, 3, 2), (3, 5, 1)):
         K = nblk * bs
