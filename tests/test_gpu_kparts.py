@@ -171,3 +171,39 @@ def test_workspace_is_checked_before_launch():
     ok, ratio, _, _ = gu.check_full(prob, 8, Y.float().cpu().numpy().astype(np.float64))
     assert ok, ratio
     q.close()
+
+
+def test_k_parts_replay_in_a_captured_graph():
+    """qgemv_run_ws needs no memset (every run leaves the workspace zero), so it can be
+    captured in a graph. Four replays, with eager work on the stream between them, must
+    each give the eager result bit for bit and leave the workspace zero."""
+    prob = synth.workload("fp8_m8_k16384_n1024")
+    q, t = bqw.upload(prob)
+    assert q.plan(8, with_workspace=True)["kparts"] == 4
+    A = t["A"][:8].contiguous()
+    ws = torch.zeros(q.workspace_size(8), dtype=torch.uint8, device="cuda")
+    Y = torch.zeros((8, prob.N), dtype=A.dtype, device="cuda")
+    q.run(A, Y, M=8, workspace=ws)
+    torch.cuda.synchronize()
+    Y_eager = Y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q.run(A, Y, M=8, workspace=ws)  # a run on the capture's side of the allocator first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.run(A, Y, M=8, workspace=ws)
+    x = torch.randn(256, 256, device="cuda")
+    for _ in range(4):
+        Y.fill_(float("nan"))
+        x = (x @ x.T).tanh()  # eager work between the replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y_eager.view(torch.int16))
+        assert bool((ws == 0).all().item())
+    ok, ratio, _, _ = gu.check_full(prob, 8, Y.float().cpu().numpy().astype(np.float64))
+    assert ok, ratio
+    del g
+    q.close()
