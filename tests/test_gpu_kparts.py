@@ -207,3 +207,31 @@ def test_k_parts_replay_in_a_captured_graph():
     assert ok, ratio
     del g
     q.close()
+
+
+def test_one_handle_on_two_streams_with_their_own_workspaces():
+    """The handle is immutable, so runs on two streams may overlap as long as each has
+    its own workspace: both streams' outputs equal the serial result bit for bit, and
+    both workspaces end zero."""
+    prob = synth.workload("fp8_m8_k16384_n1024")
+    q, t = bqw.upload(prob)
+    A = t["A"][:8].contiguous()
+    need = q.workspace_size(8)
+    ref = torch.zeros((8, prob.N), dtype=A.dtype, device="cuda")
+    q.run(A, ref, M=8, workspace=torch.zeros(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.zeros(need, dtype=torch.uint8, device="cuda") for _ in streams]
+    outs = [[torch.full((8, prob.N), float("nan"), dtype=A.dtype, device="cuda") for _ in range(10)] for _ in streams]
+    torch.cuda.synchronize()
+    for i in range(10):
+        for s, ws, ys in zip(streams, wss, outs):
+            with torch.cuda.stream(s):
+                q.run(A, ys[i], M=8, workspace=ws)
+    torch.cuda.synchronize()
+    for ys in outs:
+        for y in ys:
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    for ws in wss:
+        assert bool((ws == 0).all().item())
+    q.close()
