@@ -34,7 +34,7 @@
  * (after the NVFP4 tensor scale, which belongs to dequant(W)). The pages' tests
  * cover such a bias ("[CUDA] Block-scaled MatMul decode GEMV: tensor cores, packed
  * FP4 decode and M-tiling", reviewed-changes table; "[CUDA] Pin FP8 GEMV residency
- * for grids just past two blocks per SM", review thread). NULL means none.
+ * for grids just past two blocks per SM", a timeline note on its tests). NULL means none.
  *
  * All pointers passed to qgemv_create, qgemv_run and qgemv_run_ws are DEVICE
  * pointers, owned by the caller. The handle keeps the weight pointers (not copies)

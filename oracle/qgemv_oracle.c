@@ -32,7 +32,7 @@
  *
  * Optional bias ("[CUDA] Block-scaled MatMul decode GEMV: ...", reviewed-changes
  * table: the FP8 and FP4 tests cover a bias; "[CUDA] Pin FP8 GEMV residency for
- * grids just past two blocks per SM", review thread: the tests cover an optional
+ * grids just past two blocks per SM", a timeline note: the tests cover an optional
  * bias): one value per output column in the activation dtype, added to the product
  * of every row, Y[m, n] = sum_k A[m, k] * dequant(W)[n, k] + bias[n] (the tensor
  * scale is part of dequant(W) and does not touch the bias). S stays the sum of
