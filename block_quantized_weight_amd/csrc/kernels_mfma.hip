@@ -507,11 +507,15 @@ __device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astrid
 //     then store zeros over the partials they read. A completed run thus leaves the
 //     whole workspace as it found it, all zero, whatever handle or M used it before.
 // No workgroup waits for another: the last to arrive does the work.
+//
+// red_alias: the reduction area sR overlays the staged activations, so every wave
+// waits at a barrier until all have finished their K steps before writing to it.
 template <int ACT, int RG, bool XWG = true>
 __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *sR, int wave, int lane, int ks,
                                             int kslice, int g, bool tile_ok, int64_t n, int part = 0,
-                                            int64_t tg = 0, uint32_t *sFlag = nullptr) {
+                                            int64_t tg = 0, uint32_t *sFlag = nullptr, bool red_alias = false) {
     if (ks > 1) {
+        if (red_alias) __syncthreads();
         float *mine = sR + (size_t)wave * (RG * 4 * 64);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
@@ -657,13 +661,18 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     const int64_t ntiles = (a.N + 15) >> 4;
     const int64_t ngroups = (ntiles + tpw - 1) / tpw;
     // LDS: [zero block | staged rows | activation sums] when staged, then the K-split
-    // reduction area, then (with K parts) the last-workgroup flag
+    // reduction area, then (with K parts) the last-workgroup flag. When the workgroup
+    // holds a single tile group (always with K parts), the staged activations are dead
+    // once its K steps are done, and the reduction area overlays them from byte 0.
     uint16_t *sZero = (uint16_t *)smem;
     uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
     const size_t rows_b = LDSA ? staged_rows_bytes(a, astride) : 0;
     f4 *sSum = (f4 *)(smem + kZeroBytes + rows_b);
-    float *sR = (float *)(LDSA ? smem + kZeroBytes + rows_b + sums_bytes<FMT, RG, H>((size_t)4 * smax) : smem);
-    uint32_t *sFlag = (uint32_t *)((unsigned char *)sR + (ks > 1 ? NW * RG * 4 * 64 * 4 : 0));
+    const size_t abytes = LDSA ? kZeroBytes + rows_b + sums_bytes<FMT, RG, H>((size_t)4 * smax) : 0;
+    const size_t red_b = ks > 1 ? (size_t)NW * RG * 4 * 64 * 4 : 0;
+    const bool red_alias = LDSA && ks > 1 && (KP || gdim >= ngroups);
+    float *sR = (float *)(red_alias ? smem : smem + abytes);
+    uint32_t *sFlag = (uint32_t *)(smem + (red_alias ? (abytes > red_b ? abytes : red_b) : abytes + red_b));
 
     // issue cursor: tile group, slot within the tile, and the column the lane loads
     // codes and block metadata of, in the coalesced order of to_mfma_lanes (column
@@ -737,7 +746,8 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         }
         if constexpr (!KP) {
             if (++tt == tpt) {
-                finish_tile<ACT, RG, false>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15));
+                finish_tile<ACT, RG, false>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15), 0,
+                                            0, nullptr, red_alias);
 #pragma unroll
                 for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
                 tt = 0;
@@ -753,7 +763,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         // one tile group per workgroup: its finish, with nothing left in flight
         const int64_t tile = gx * tpw + slot;
         finish_tile<ACT, RG, true>(a, acc, sR, wave, lane, ks, kslice, g, tile < ntiles, tile * 16 + (lane & 15),
-                                   (int)part, gx, sFlag);
+                                   (int)part, gx, sFlag, red_alias);
     }
 }
 

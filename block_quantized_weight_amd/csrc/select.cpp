@@ -107,10 +107,21 @@ static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t
 }
 
 // Waves that share one 16-column tile's K range. Chosen from N and K only so that
-// the summation order of a row never depends on M: enough waves to fill the
-// machine (about four per CU: the split's LDS reduction and the per-workgroup
-// activation copy cost more than further waves bring), at least two K steps of four
-// chunks per wave, and at most 8, the waves of one workgroup.
+// the summation order of a row never depends on M. A workgroup holds 8 / ksplit tiles
+// of ksplit waves, so the split sets both the number of workgroups and the K steps
+// each wave walks. While the workgroups do not fill the CUs, the split taken is the
+// one with the least work on the busiest CU, (workgroups per CU, rounded up) x (K
+// steps per wave), ties to the smaller split (a finer one adds LDS reduction for
+// nothing); a grid that already fills them is not split further. A split that leaves a wave fewer than 8
+// K steps is taken only while the tiles are so few (tiles x ksplit < 4 per CU) that
+// the machine is mostly idle: it leaves too few steps to amortize staging the
+// activations. Measured on MI355X at M = 8, the old rule (about four waves per CU)
+// -> this one: 8-bit 16384 x 4096 37.7 -> 26.0 us (split 1 -> 2), FP8 8192 x 4096
+// 18.4 -> 14.0 (2 -> 4), 4-bit 8192 x 4096 16.8 -> 13.5 (2 -> 4), 8-bit 4096 x 4096
+// 15.4 -> 14.4 (4 -> 8); a finer split than this rule's measured slower on FP8
+// 5120 x 6144 (16.7 us at 4, 19.3 at 8), NVFP4 and 4-bit 4096 x 4096 (10.1 / 12.5 us
+// at 4, 12.9 / 13.8 at 8) and 4-bit 12288 x 4096 (17.3 us at 2, 19.1 at 4). At least
+// two K steps per wave, and at most 8, the waves of one workgroup.
 static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     const uint32_t forced = (flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     const int64_t tiles = (d->N + 15) / 16;
@@ -119,7 +130,12 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     if (forced) {
         ks = (int)forced;
     } else {
-        while (ks < 8 && tiles * ks < 4LL * cu_count && 2 * ks <= steps) ks *= 2;
+        auto groups = [&](int k) { return (tiles + 8 / k - 1) / (8 / k); };
+        auto cost = [&](int k) { return (groups(k) + cu_count - 1) / cu_count * ((steps + k - 1) / k); };
+        for (int k = 2; k <= 8 && 2 * k <= steps && groups(ks) < cu_count; k *= 2) {
+            const bool allowed = steps >= 8LL * k || tiles * ks < 4LL * cu_count;
+            if (allowed && cost(k) < cost(ks)) ks = k;
+        }
     }
     if (ks > 8) ks = 8;
     while (ks > 1 && ks > steps) ks /= 2;  // a power of two: whole tiles per workgroup
@@ -241,13 +257,27 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     return true;
 }
 
-// Where the persistent streaming kernel with 2 or 4 rows per pass beats the matrix
-// family (measured on MI355X): at M = 2..4 for 8-bit integer and FP8 codes, and for
-// 4-bit codes while the weight is small enough (under 64 MB) that the call is
-// latency-bound rather than bandwidth-bound. Wide 4-bit weights take the matrix
-// family's DMA ring from M = 2 (4-bit lm_head, M = 2: 90 us against 101 us).
+// Where the streaming family beats the matrix family (measured on MI355X):
+//  - M = 2..4 (the persistent kernel, 2 or 4 rows in one pass): for 8-bit integer
+//    and FP8 codes, and for 4-bit codes while the weight is small enough (under
+//    64 MB) that the call is latency-bound rather than bandwidth-bound. Wide 4-bit
+//    weights take the matrix family's DMA ring from M = 2 (4-bit lm_head, M = 2:
+//    90 us against 101 us).
+//  - M = 5..16 (the multi-pass kernel, 4 rows a pass, the weight re-read from L2):
+//    for small weights, N x K <= 4 Mi elements with K <= 4096, where the matrix
+//    family has too few tiles to fill the CUs. Matrix -> streaming at M = 8: 4-bit
+//    1024 x 2048 9.4 -> 7.1 us (M = 16: 15.2 -> 10.7), 4-bit 2048 x 2048 10.0 -> 9.3,
+//    FP8 1024 x 4096 9.7 -> 9.3, 8-bit 1024 x 4096 12.4 -> 10.6, 8-bit 2048 x 2048
+//    10.2 -> 9.2, NVFP4 2048 x 2048 8.8 -> 8.2. Past it the matrix family wins (4-bit
+//    1536 x 4096: 13.4 against 13.9 us; 4-bit 2048 x 4096: 13.4 against 14.3; FP8
+//    2048 x 4096: 10.0 against 11.3), and so it does on longer columns (4-bit
+//    512 x 8192: 15.8 against 16.7 us, 12.5 with K parts; FP8 512 x 8192: 13.3
+//    against 16.7), whose single wave per column walks too many steps. The same holds
+//    with a workspace: K parts on these shapes measured slower than the streaming
+//    kernel (FP8 1024 x 4096: 13.3 us).
 static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
-    if (!stream_ok || M > 4 || M < 2) return false;
+    if (!stream_ok || M < 2) return false;
+    if (M > 4) return d->K <= 4096 && (int64_t)d->N * d->K <= 4LL * 1024 * 1024;
     const int kpc = k_per_chunk(d->format);
     const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
@@ -346,8 +376,19 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // per tile (8 or more) to amortize the copy; with fewer, the activations travel
         // with the codes in the register ring instead.
         const int64_t spw = (smax + c.ksplit - 1) / c.ksplit;
-        bool stage = abytes16 + lds_red <= kLdsBytes && spw >= 8;
-        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = abytes16 + lds_red <= kLdsBytes;
+        // When every workgroup holds a single tile group (always with K parts; without,
+        // when one round of them fits at once), the K-split reduction area overlays the
+        // staged activations, which are dead by then; else it follows them. (FP8
+        // 8192 x 4096 at M = 16: 131 KB of staged rows and 32 KB of reduction area fit
+        // only overlaid.)
+        const int64_t flag_b = kp > 1 ? 16 : 0;
+        const int64_t lds_ovl = (abytes16 > lds_red ? abytes16 : lds_red) + flag_b;
+        int64_t pc_ovl = kLdsBytes / lds_ovl;
+        if (pc_ovl > 32 / nw) pc_ovl = 32 / nw;
+        const bool overlay = c.ksplit > 1 && (kp > 1 || groups <= pc_ovl * cu_count);
+        const int64_t lds_staged = overlay ? lds_ovl : abytes16 + lds_red + flag_b;
+        bool stage = lds_staged <= kLdsBytes && spw >= 8;
+        if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_staged <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;
         // register-ring depth: 4 slots unless forced. With the loads coalesced, 8 slots
         // measured no faster anywhere and slower on the staged FP8 and 8-bit rings (FP8
@@ -357,7 +398,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const bool deep8 = fdep == 2;
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
         // with K parts, 16 bytes more for the last-workgroup flag
-        c.lds_bytes = (int)(lds_red + (stage ? abytes16 : 0) + (kp > 1 ? 16 : 0));
+        c.lds_bytes = (int)(stage ? lds_staged : lds_red + flag_b);
         // without K parts, a persistent grid of at most what fits at once; with them,
         // exactly one workgroup per tile group and part
         int64_t grid = groups * kp;

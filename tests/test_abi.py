@@ -150,22 +150,24 @@ def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
         # 64 counters (256 bytes), then the [4, M, N] fp32 partials
         assert p1["workspace_bytes"] == 256 + (4 * M * 1024 * 4 + 255) // 256 * 256
     # 128 tile groups (half the CUs): 2 parts only with 16 K steps or more per wave and
-    # part. FP8 2048 x 16384 (256 steps, K split 8): 2 parts; 8-bit 4096 x 4096 (64
-    # steps, K split 4) and 4-bit 2048 x 8192 (64 steps, K split 8): none
+    # part. FP8 2048 x 16384 (256 steps, K split 8): 2 parts; 4-bit 2048 x 8192 (64
+    # steps, K split 8): none
     p = _sel(fmt="fp8", act="f16", N=2048, K=16384, block_size=128, M=8, with_workspace=True)
     assert p["ksplit"] == 8 and p["kparts"] == 2 and p["grid"] == 256
-    p = _sel(fmt="u8", act="f16", N=4096, K=4096, block_size=128, M=8, with_workspace=True)
-    assert p["family"] == "mfma" and p["ksplit"] == 4 and p["kparts"] == 1
     p = _sel(fmt="u4", act="bf16", N=2048, K=8192, block_size=32, M=8, with_workspace=True)
     assert p["ksplit"] == 8 and p["kparts"] == 1
+    # 8-bit 4096 x 4096 (64 steps, K split 8): 256 tile groups fill the CUs: none
+    p = _sel(fmt="u8", act="f16", N=4096, K=4096, block_size=128, M=8, with_workspace=True)
+    assert p["family"] == "mfma" and p["ksplit"] == 8 and p["kparts"] == 1
     # 32 tile groups: 4-bit 512 x 8192 -> 4 parts (8 would leave one K step per wave)
     p = _sel(fmt="u4", act="bf16", N=512, K=8192, block_size=32, M=8, with_workspace=True)
     assert p["ksplit"] == 8 and p["kparts"] == 4
     # FP8 5120 x 6144: 160 tile groups; 2 parts would need a second round: none
     p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=8, with_workspace=True)
     assert p["kparts"] == 1 and p["workspace_bytes"] == 0
-    # parts keep two K steps per wave: 4-bit 1024 x 2048 (16 steps, K split 8) takes none
-    p = _sel(fmt="u4", act="f16", N=1024, K=2048, block_size=32, M=8, with_workspace=True)
+    # parts keep two K steps per wave: 4-bit 1024 x 2048 (16 steps, K split 8) in the
+    # matrix family takes none
+    p = _sel(fmt="u4", act="f16", N=1024, K=2048, block_size=32, M=8, flags=2, with_workspace=True)
     assert p["ksplit"] == 8 and p["kparts"] == 1
     # wide N fills the machine with tile groups: no parts, no workspace
     for M in (2, 8, 16):
@@ -174,6 +176,77 @@ def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
     # the streaming family never splits
     p = _sel(fmt="fp8", act="f16", N=1024, K=16384, block_size=128, M=1, with_workspace=True)
     assert p["family"] == "stream" and p["kparts"] == 1
+
+
+def test_k_split_takes_the_least_work_on_the_busiest_cu():
+    """While the workgroups do not fill the CUs, the K split minimizes (workgroups per
+    CU, rounded up) x (K steps per wave), ties to the smaller split; fewer than 8
+    steps per wave only while the tiles are fewer than 4 per CU."""
+    def ks(fmt, N, K, bs=128, act="f16"):
+        return _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=8, flags=2)["ksplit"]
+    # 1024 tiles, 64 steps: split 1 -> 128 workgroups x 64 steps; 2 -> 256 x 32; 4 ->
+    # 512 (two per CU) x 16 = the same work as 2: the smaller split
+    assert ks("u8", 16384, 4096) == 2
+    # 512 tiles, 64 steps: 4 -> 256 x 16 beats 2 -> 128 x 32; 8 ties 4
+    assert ks("fp8", 8192, 4096) == 4
+    # 4-bit 8192 x 4096 (32 steps): 4 (8 steps per wave); 8 would leave 4 steps
+    assert ks("u4", 8192, 4096, 32, "bf16") == 4
+    # 4-bit 4096 x 4096: 4, not 8 (8 would leave 4 steps per wave, with 256 tiles)
+    assert ks("u4", 4096, 4096, 32, "bf16") == 4
+    assert ks("nvfp4", 4096, 4096, 16, "bf16") == 4
+    # 320 tiles, 96 steps: 4 -> 160 x 24 ties 8 -> 320 (two rounds) x 12: 4
+    assert ks("fp8", 5120, 6144) == 4
+    # 768 tiles, 32 steps: 2 -> 192 x 16 ties 4 -> 384 x 8
+    assert ks("u4", 12288, 4096, 32, "bf16") == 2
+    # few tiles: the finest split that keeps two K steps per wave
+    assert ks("u4", 1024, 2048, 32) == 8
+    assert ks("fp8", 1024, 2048) == 8
+    # wide N: no split (the lm_head's unsplit tile groups already fill the CUs)
+    assert ks("u4", 151936, 4096, 32, "bf16") == 1
+    assert ks("nvfp4", 248320, 2048, 16, "bf16") == 1
+
+
+def test_small_weights_take_the_streaming_family_at_every_m():
+    """Up to N x K = 4 Mi elements with K <= 4096, the streaming family serves every M
+    (the multi-pass kernel from M = 5), with or without a workspace; past either
+    bound, M >= 5 takes the matrix family."""
+    for fmt, act, N, K, bs in (("u4", "f16", 1024, 2048, 32), ("u4", "f16", 2048, 2048, 32),
+                               ("fp8", "f16", 1024, 4096, 128), ("u8", "f16", 2048, 2048, 128),
+                               ("nvfp4", "bf16", 2048, 2048, 16)):
+        for M in (5, 8, 12, 16):
+            for ws in (False, True):
+                p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=ws)
+                assert p["family"] == "stream" and p["kparts"] == 1, (fmt, N, K, M, ws, p)
+                assert p["rows_per_pass"] == 4 and p["passes"] == (M + 3) // 4
+    for fmt, act, N, K, bs in (("u4", "f16", 1536, 4096, 32), ("fp8", "f16", 2048, 4096, 128),
+                               ("u4", "f16", 512, 8192, 32), ("fp8", "f16", 512, 8192, 128)):
+        for M in (5, 8, 16):
+            assert _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)["family"] == "mfma"
+
+
+def test_reduction_area_overlays_the_staged_rows_when_one_round_fits():
+    """With one tile group per workgroup the K-split reduction area overlays the staged
+    activations (LDS = the larger of the two); a persistent grid that walks several
+    tile groups keeps them side by side."""
+    # FP8 8192 x 4096, M = 16: 256 tile groups (K split 4) on 256 CUs; staged rows
+    # 64 + 16 x (4096 + 8) x 2 bytes, reduction 8 waves x 4 row groups x 4 x 64 x 4
+    p = _sel(fmt="fp8", act="f16", N=8192, K=4096, block_size=128, M=16)
+    rows, red = 64 + 16 * 4104 * 2, 8 * 4 * 4 * 64 * 4
+    assert rows + red > 160 * 1024
+    assert p["family"] == "mfma" and p["ksplit"] == 4 and p["variant"] & 1 and p["grid"] == 256
+    assert p["lds_bytes"] == max(rows, red)
+    # with K parts (forced 2, one workgroup per tile group and part): overlaid, plus
+    # the 16-byte flag; the longest part's rows are staged
+    p = _sel(fmt="fp8", act="f16", N=8192, K=4096, block_size=128, M=16, flags=2 | (2 << 4), with_workspace=True)
+    assert p["kparts"] == 2 and p["variant"] & 1
+    assert p["lds_bytes"] == max(64 + 16 * 2056 * 2, red) + 16
+    # a forced split 2 on the 4-bit lm_head at M = 8: 2374 tile groups, more than fit
+    # at once, so the grid persists and the layout stays side by side
+    p = _sel(M=8, flags=2 | (2 << 8))
+    rows = 64 + 8 * (4096 + 8) * 2 + 4 * 32 * 2 * 16  # rows and activation sums
+    assert p["ksplit"] == 2 and p["variant"] & 1 and not (p["variant"] & 2)
+    assert p["lds_bytes"] == rows + 8 * 2 * 4 * 64 * 4
+    assert p["grid"] == 256 * (160 * 1024 // p["lds_bytes"])
 
 
 def test_forced_k_parts_and_k_split_are_clamped():

@@ -227,6 +227,37 @@ def test_repeated_runs_are_bitwise_equal(name, M):
         assert np.array_equal(o, outs[0]), plan
 
 
+@pytest.mark.parametrize("fmt,act,bs", [("fp8", "f16", 128), ("u8", "f16", 128), ("u4", "bf16", 32)])
+def test_reduction_area_overlaid_on_the_staged_rows(fmt, act, bs):
+    """M = 16, K = 4096: the staged rows and the K-split reduction area fit in LDS only
+    overlaid (one tile group per workgroup). Within the bound against the oracle, and
+    bit for bit equal to the unstaged run, at a ragged N."""
+    M, N, K = 16, 1000, 4096
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=11)
+    base = 2 | (4 << 8) | bqw.FLAG_RING_OFF
+    gu.say(f"[overlay] {fmt}/{act} bs={bs} N={N} K={K} M={M}")
+    Y, plan = gu.run_gpu(prob, M, flags=base | bqw.FLAG_STAGE_A_ON)
+    assert plan["ksplit"] == 4 and plan["variant"] & 1, plan
+    red = 8 * 4 * 4 * 64 * 4
+    assert plan["lds_bytes"] + red > 160 * 1024 >= plan["lds_bytes"], plan
+    Yu, pu = gu.run_gpu(prob, M, flags=base | bqw.FLAG_STAGE_A_OFF)
+    assert not (pu["variant"] & 1)
+    assert np.array_equal(Y.view(np.int64), Yu.view(np.int64))
+    ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
+    assert ok, ratio
+
+
+def test_sixteen_rows_full_size_with_the_overlaid_reduction_area():
+    """FP8 8192 x 4096 at M = 16 under the automatic plan (K split 4, staged rows with
+    the reduction area overlaid), on sampled outputs against the oracle."""
+    prob = synth.make_problem("fp8", "f16", 8192, 4096, 128, 16, seed=12)
+    gu.say("[overlay] fp8 8192 x 4096 M=16 auto")
+    Y, plan = gu.run_gpu(prob, 16)
+    assert plan["family"] == "mfma" and plan["ksplit"] == 4 and plan["variant"] & 1, plan
+    ok, ratio = gu.check_points(prob, 16, Y)
+    assert ok, ratio
+
+
 @pytest.mark.parametrize("stage", [False, True])
 @pytest.mark.parametrize("ks", [1, 2, 4, 8])
 def test_forced_k_split_is_correct(ks, stage):
