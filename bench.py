@@ -50,7 +50,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--m", type=int, default=None, help="rows of A (default: the workload's first M)")
+    p.add_argument("--shape", default=None, metavar="FMT:ACT:N:K:BS",
+                   help="time an arbitrary shape instead of a named workload (e.g. fp8:f16:8192:4096:128), "
+                        "drawn by synth.make_problem with its default value distributions")
+    p.add_argument("--seed", type=int, default=7, help="seed for --shape")
+    p.add_argument("--m", type=int, default=None, help="rows of A (default: the workload's first M; 1 for --shape)")
     p.add_argument("--flags", type=int, default=0, help="qgemv_desc.flags (force a family, K split)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
@@ -247,8 +251,18 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    prob = synth.workload(args.workload, with_bias=args.bias)
-    M = args.m if args.m is not None else prob.ms[0]
+    if args.shape:
+        fmt, act, n_s, k_s, bs_s = args.shape.split(":")
+        M = args.m if args.m is not None else 1
+        prob = synth.make_problem(fmt, act, int(n_s), int(k_s), int(bs_s), M, args.seed, name="shape",
+                                  ms=(M,), with_bias=args.bias)
+        workload = f"shape_{fmt}_{act}_n{n_s}_k{k_s}_bs{bs_s}"
+        seed = args.seed
+    else:
+        prob = synth.workload(args.workload, with_bias=args.bias)
+        M = args.m if args.m is not None else prob.ms[0]
+        workload = args.workload
+        seed = synth.WORKLOADS[args.workload]["seed"]
     wbytes = prob.weight_bytes()
     copies = 1 if args.warm else max(2, int(math.ceil(COLD_BYTES / wbytes)))
 
@@ -307,7 +321,6 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(prob, M, args.cpu_seconds)
 
-    spec = synth.WORKLOADS[args.workload]
     out = {
         "metric": "achieved HBM GB/s (weight bytes / kernel time), cold weights",
         "value": round(gbs, 2),
@@ -322,13 +335,13 @@ def main():
         "vs_baseline": None,
         "dtype": f"{prob.fmt} x {prob.act} -> f32 acc",
         "data": "synthetic",
-        "config": {"workload": args.workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
+        "config": {"workload": workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
                    "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
-                   "plan": plan, "flags": args.flags, "seed": spec["seed"], "bias": bool(args.bias),
+                   "plan": plan, "flags": args.flags, "seed": seed, "bias": bool(args.bias),
                    "entry": "qgemv_run_ws" if use_ws else "qgemv_run"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": lookup_traffic(args.workload, M, args.flags, use_ws)},
+                     "traffic": None if args.shape else lookup_traffic(args.workload, M, args.flags, use_ws)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
     }
