@@ -143,7 +143,7 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
 }
 
 // K parts split across workgroups (qgemv_run_ws only), from (format, N, K, block
-// size, flags, CU count), never M. A part count that pushes the grid past one
+// size, flags, CU count), not M (select_plan adds the one case that depends on M). A part count that pushes the grid past one
 // workgroup per CU always loses. Within that, measured on MI355X at M = 8 (unsplit ->
 // best split): where the tile groups fill at most a quarter of the CUs, parts pay
 // (FP8 1024 x 16384, 64 groups: 36.1 -> 15.1 us in 4; 4-bit 512 x 8192, 32 groups:
@@ -344,17 +344,50 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t groups = (tiles + (nw / c.ksplit) - 1) / (nw / c.ksplit);
         const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
         const int64_t steps = d->K / (4 * k_per_chunk(d->format));
-        const int kp = with_ws ? mfma_kparts(d, cu_count, flags, c.ksplit, groups) : 1;
-        const int64_t smax = (steps + kp - 1) / kp;  // K steps of the longest part
-        // staged activations: a 64-byte zero block, the rows of the longest K part
-        // (stride its k + 8 elements), and for formats with zero points one 16-byte
-        // activation-sum entry per chunk, row group and scale block of the chunk
-        const int64_t kpart = smax * 4 * k_per_chunk(d->format);
-        const int64_t lds_a = (int64_t)M * (kpart + 8) * 2;
+        // Staged layout for kpv K parts: a 64-byte zero block, the rows of the longest
+        // K part (stride its k + 8 elements), and for formats with zero points one
+        // 16-byte activation-sum entry per chunk, row group and scale block of the
+        // chunk (abytes); then the K-split reduction area, which overlays the staged
+        // activations when every workgroup holds a single tile group (always with K
+        // parts; without, when one round of them fits at once), as they are dead by
+        // then, and else follows them (FP8 8192 x 4096 at M = 16: 131 KB of staged rows
+        // and 32 KB of reduction area fit only overlaid); then, with K parts, the
+        // 16-byte last-workgroup flag (lds).
         const bool zp_fmt = d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8;
         const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
-        const int64_t lds_sums = zp_fmt ? 4 * smax * rg * hh * 16 : 0;
-        const int64_t abytes16 = 64 + ((lds_a + 15) & ~15LL) + lds_sums;
+        struct Staged { int64_t abytes, lds; };
+        auto staged = [&](int kpv) {
+            const int64_t sm = (steps + kpv - 1) / kpv;
+            const int64_t la = (int64_t)M * (sm * 4 * k_per_chunk(d->format) + 8) * 2;
+            const int64_t ab = 64 + ((la + 15) & ~15LL) + (zp_fmt ? 4 * sm * rg * hh * 16 : 0);
+            const int64_t fb = kpv > 1 ? 16 : 0;
+            const int64_t ovl = (ab > lds_red ? ab : lds_red) + fb;
+            int64_t pc = kLdsBytes / ovl;
+            if (pc > 32 / nw) pc = 32 / nw;
+            const bool overlay = c.ksplit > 1 && (kpv > 1 || groups <= pc * cu_count);
+            return Staged{ab, overlay ? ovl : ab + lds_red + fb};
+        };
+        int kp = with_ws ? mfma_kparts(d, cu_count, flags, c.ksplit, groups) : 1;
+        // With a workspace, where the unsplit plan's activations do not fit in LDS at
+        // this M, 2 parts: twice the workgroups, each staging half the K range where that
+        // fits. The one choice of the K parts that depends on M. Taken where the tile
+        // groups fill at most half the CUs, or all of them while each wave of the unsplit
+        // plan walks 24 K steps or more (the activations it would carry in the ring cost
+        // in proportion). Measured on MI355X, unsplit -> 2 parts: FP8 2048 x 8192 M = 16
+        // 36.9 -> 22.1 us; 8-bit 2048 x 8192 M = 16 37.8 -> 26.8; 4-bit 2048 x 16384
+        // M = 8 37.1 -> 22.3, M = 16 (unstaged either way) 66.6 -> 44.0; FP8 5120 x 6144
+        // M = 16 (160 groups, 24 steps per wave) 49.2 -> 35.1; 4-bit 16384 x 8192 M = 16
+        // (256 groups, 32 steps) 123.2 -> 61.7; but 8-bit 4096 x 8192 M = 16 (256
+        // groups, 16 steps) 39.5 -> 51.5. Where the rows fit, 2 parts lose (FP8
+        // 2048 x 8192 M = 8: 13.8 -> 16.4 us).
+        const int64_t spw1 = (steps + c.ksplit - 1) / c.ksplit;
+        if (with_ws && kp == 1 && !(flags & QGEMV_FLAG_KPARTS_MASK) &&
+            (groups * 2 <= cu_count || (groups <= cu_count && spw1 >= 24)) && steps >= 4LL * c.ksplit &&
+            staged(1).lds > kLdsBytes && 2LL * QGEMV_MAX_M * d->N < (1LL << 31))
+            kp = 2;
+        const int64_t smax = (steps + kp - 1) / kp;  // K steps of the longest part
+        const Staged st = staged(kp);
+        const int64_t abytes16 = st.abytes;
         // DMA ring (no K split, one or two row groups, metadata rows in whole dwords):
         // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
         // fits in LDS next to the staged activations.
@@ -376,17 +409,8 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // per tile (8 or more) to amortize the copy; with fewer, the activations travel
         // with the codes in the register ring instead.
         const int64_t spw = (smax + c.ksplit - 1) / c.ksplit;
-        // When every workgroup holds a single tile group (always with K parts; without,
-        // when one round of them fits at once), the K-split reduction area overlays the
-        // staged activations, which are dead by then; else it follows them. (FP8
-        // 8192 x 4096 at M = 16: 131 KB of staged rows and 32 KB of reduction area fit
-        // only overlaid.)
         const int64_t flag_b = kp > 1 ? 16 : 0;
-        const int64_t lds_ovl = (abytes16 > lds_red ? abytes16 : lds_red) + flag_b;
-        int64_t pc_ovl = kLdsBytes / lds_ovl;
-        if (pc_ovl > 32 / nw) pc_ovl = 32 / nw;
-        const bool overlay = c.ksplit > 1 && (kp > 1 || groups <= pc_ovl * cu_count);
-        const int64_t lds_staged = overlay ? lds_ovl : abytes16 + lds_red + flag_b;
+        const int64_t lds_staged = st.lds;
         bool stage = lds_staged <= kLdsBytes && spw >= 8;
         if (flags & QGEMV_FLAG_STAGE_A_ON) stage = lds_staged <= kLdsBytes;
         if (flags & QGEMV_FLAG_STAGE_A_OFF) stage = false;

@@ -207,9 +207,12 @@ int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_st
  * fixed slice order ("[CUDA] MatMul: add an opt-in split-K GEMV", Kernel and
  * dispatch; review threads on the workspace's visibility), here for the quantized
  * formats. The order of the fp32 sums depends on (format, N, K, block size, flags)
- * and the device's compute-unit count, never on M, so rows stay bit-identical
- * whatever tile carries them; the bits can differ from qgemv_run's where qgemv_run
- * does not split (within the same error bound).
+ * and the device's compute-unit count, and on M in one case only: where the tile
+ * groups fill at most half the compute units and the activation rows of an unsplit
+ * plan do not fit in LDS at this M, the K range is cut in 2 parts. Rows stay
+ * bit-identical whatever tile carries them within a call, and across M when the
+ * part count is forced through the flags; the bits can differ from qgemv_run's where
+ * qgemv_run does not split (within the same error bound).
  *
  * workspace: device memory of at least qgemv_workspace_size(h, M) bytes, 256-byte
  * aligned, owned by the caller: completion counters, then fp32 partial tiles. Zero

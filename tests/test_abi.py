@@ -110,7 +110,9 @@ def test_select_families_and_fallback():
 
 
 def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
-    """The K split orders each row's fp32 sums, so it may depend on N and K only. (The
+    """The K split orders each row's fp32 sums, so it may depend on N and K only; so do
+    the K parts on these shapes while their unsplit activation rows fit in LDS (up to
+    M = 12 here; FP8 5120 x 6144 takes 2 parts at M = 16, see the test below). (The
     matrix family's variants, register ring, LDS-staged activations or LDS DMA ring,
     feed identical MFMA operands in the same order; the GPU tests check that they
     agree bit for bit.)"""
@@ -119,9 +121,9 @@ def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
                                ("u4", "f16", 1024, 2048, 32)]:
         for ws in (False, True):
             plans = [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=m, with_workspace=ws) for m in range(1, 17)]
-            for key in ("ksplit", "kparts"):
+            for key, upto in (("ksplit", 16), ("kparts", 12)):
                 fams = {}
-                for p in plans:
+                for p in plans[:upto]:
                     fams.setdefault(p["family"], set()).add(p[key])
                 assert all(len(v) == 1 for v in fams.values()), (fmt, ws, key, fams)
 
@@ -247,6 +249,37 @@ def test_reduction_area_overlays_the_staged_rows_when_one_round_fits():
     assert p["ksplit"] == 2 and p["variant"] & 1 and not (p["variant"] & 2)
     assert p["lds_bytes"] == rows + 8 * 2 * 4 * 64 * 4
     assert p["grid"] == 256 * (160 * 1024 // p["lds_bytes"])
+
+
+def test_two_k_parts_where_the_unsplit_rows_do_not_fit_in_lds():
+    """With a workspace, where the unsplit plan's activation rows do not fit in LDS at
+    this M, 2 K parts (the one choice of the K parts that depends on M): where the tile
+    groups fill at most half the CUs, or all of them with 24 K steps or more per
+    unsplit wave; never without a workspace, never when the part count is forced, and
+    not where the rows fit."""
+    kw = dict(fmt="fp8", act="f16", N=2048, K=8192, block_size=128)
+    # 128 tile groups; M = 8: 8 x (8192 + 8) x 2 bytes of rows fit (staged, 1 part);
+    # M = 12 and 16 do not: 2 parts, each staging half the K range
+    for M, kp in ((5, 1), (8, 1), (12, 2), (16, 2)):
+        p = _sel(**kw, M=M, with_workspace=True)
+        assert p["kparts"] == kp and p["variant"] & 1, (M, p)
+        assert _sel(**kw, M=M)["kparts"] == 1
+    p = _sel(**kw, M=16, with_workspace=True)
+    assert p["grid"] == 256 and p["workspace_bytes"] == 512 + 2 * 16 * 2048 * 4
+    # a forced part count is taken as given
+    assert _sel(**kw, M=16, flags=2 | (1 << 4), with_workspace=True)["kparts"] == 1
+    # 4-bit 2048 x 16384: the rows do not fit from M = 5 on; at M = 12 and 16 not even
+    # half of them do, and the 2 parts run with the activations in the ring
+    for M, staged in ((5, True), (8, True), (12, False), (16, False)):
+        p = _sel(fmt="u4", act="bf16", N=2048, K=16384, block_size=32, M=M, with_workspace=True)
+        assert p["kparts"] == 2 and bool(p["variant"] & 1) == staged, (M, p)
+    # past half the CUs, only while each unsplit wave walks 24 K steps or more: FP8
+    # 5120 x 6144 (160 tile groups, 96 steps, split 4: 24 per wave) at M = 16; not at
+    # M = 12, where the rows fit
+    kw = dict(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, with_workspace=True)
+    assert _sel(**kw, M=16)["kparts"] == 2 and _sel(**kw, M=12)["kparts"] == 1
+    # 8-bit 4096 x 8192 (256 tile groups, 128 steps, split 8: 16 per wave): never
+    assert _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=True)["kparts"] == 1
 
 
 def test_forced_k_parts_and_k_split_are_clamped():

@@ -4,8 +4,8 @@ adding them in part order ("[CUDA] MatMul: add an opt-in split-K GEMV", Cross-bl
 reduction).
 
 Same bar as the other parity tests (|y - y_ref| <= 1e-3 * sum|a*w| + 1e-3 against the
-oracle). In addition: rows are bit-identical whatever tile carries them (the parts
-depend on N and K only), the staged and unstaged activation paths agree bit for bit,
+oracle). In addition: rows are bit-identical whatever tile carries them (with the part
+count forced, across M too), the staged and unstaged activation paths agree bit for bit,
 repeated runs are bitwise equal, one workspace serves several handles in turn, and
 every completed run leaves the whole workspace zero.
 """
@@ -46,6 +46,26 @@ def test_tall_k_fp8_with_automatic_k_parts(M):
     ok, ratio, _, _ = gu.check_full(prob, M, Y)
     gu.say(f"   max err/tol={ratio:.3e}")
     assert ok, ratio
+
+
+@pytest.mark.parametrize("fmt,act,N,K,bs,M,staged", [("fp8", "f16", 2048, 8192, 128, 16, True),
+                                                      ("u4", "bf16", 2048, 16384, 32, 8, True),
+                                                      ("u4", "bf16", 2048, 16384, 32, 12, False),
+                                                      ("fp8", "f16", 5120, 6144, 128, 16, True)])
+def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K, bs, M, staged):
+    """Where the unsplit plan's activation rows do not fit in LDS at this M (128 tile
+    groups; or 160 with 24 K steps per unsplit wave), the automatic plan takes 2 parts;
+    sampled outputs against the oracle, and bit for bit the run with 2 parts forced."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=26)
+    gu.say(f"[kparts] {fmt} {N}x{K} M={M} automatic 2 parts")
+    Y, plan = gu.run_gpu(prob, M, ws=True)
+    assert plan["family"] == "mfma" and plan["kparts"] == 2 and bool(plan["variant"] & 1) == staged, plan
+    assert plan["ws_zero"]
+    ok, ratio = gu.check_points(prob, M, Y)
+    assert ok, ratio
+    Yf, pf = gu.run_gpu(prob, M, flags=2 | kp_flags(2), ws=True)
+    assert pf["kparts"] == 2 and pf["ksplit"] == plan["ksplit"]
+    assert np.array_equal(Y.view(np.int64), Yf.view(np.int64))
 
 
 def test_fp8_projection_with_forced_k_parts():
