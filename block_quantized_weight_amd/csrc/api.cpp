@@ -114,7 +114,18 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
     hipError_t e;
     switch (c.family) {
     case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(c, a, s); break;
-    case QGEMV_FAMILY_MFMA: e = qgemv::launch_mfma(c, a, s); break;
+    case QGEMV_FAMILY_MFMA:
+        // row passes: rows_per_pass rows of A and Y per launch, in order, on the stream
+        e = hipSuccess;
+        for (int p = 0; p < c.passes && e == hipSuccess; ++p) {
+            const int r0 = p * c.rows_per_pass;
+            qgemv::KArgs ap = a;
+            ap.A = (const unsigned char *)A + (size_t)r0 * (size_t)h->d.K * 2;
+            ap.Y = (unsigned char *)Y + (size_t)r0 * (size_t)h->d.N * 2;
+            ap.M = (M - r0) < c.rows_per_pass ? (M - r0) : c.rows_per_pass;
+            e = qgemv::launch_mfma(c, ap, s);
+        }
+        break;
     default: e = qgemv::launch_generic(c, a, s); break;
     }
     return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;

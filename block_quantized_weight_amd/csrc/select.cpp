@@ -381,10 +381,28 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // groups, 16 steps) 39.5 -> 51.5. Where the rows fit, 2 parts lose (FP8
         // 2048 x 8192 M = 8: 13.8 -> 16.4 us).
         const int64_t spw1 = (steps + c.ksplit - 1) / c.ksplit;
-        if (with_ws && kp == 1 && !(flags & QGEMV_FLAG_KPARTS_MASK) &&
-            (groups * 2 <= cu_count || (groups <= cu_count && spw1 >= 24)) && steps >= 4LL * c.ksplit &&
-            staged(1).lds > kLdsBytes && 2LL * QGEMV_MAX_M * d->N < (1LL << 31))
+        const bool rows_too_big = (groups * 2 <= cu_count || (groups <= cu_count && spw1 >= 24)) &&
+                                  staged(1).lds > kLdsBytes;
+        if (with_ws && kp == 1 && !(flags & QGEMV_FLAG_KPARTS_MASK) && rows_too_big && steps >= 4LL * c.ksplit &&
+            2LL * QGEMV_MAX_M * d->N < (1LL << 31))
             kp = 2;
+        // Otherwise (no workspace, or a forced single part), the same case with more
+        // than 8 rows runs as passes of 8 rows, one launch each on the caller's stream,
+        // when 8 rows stage: every row's arithmetic is that of the single launch (the
+        // K split does not depend on M, and staged and unstaged activations give the
+        // same bits), the weight is read once per pass. Measured on MI355X, one launch
+        // -> two passes: FP8 5120 x 6144 M = 16 49.2 -> 32.5 us; FP8 2048 x 8192 M = 16
+        // 36.9 -> 27.3, M = 12 28.9 -> 24.5; 4-bit 16384 x 8192 M = 16 122.3 -> 65.0,
+        // M = 12 95.3 -> 60.1.
+        if (kp == 1 && rows_too_big && M > 8 && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON))) {
+            LaunchCfg half;
+            if (select_plan(d, 8, cu_count, fast_ok, extra_flags, with_ws, &half) == QGEMV_OK &&
+                half.family == QGEMV_FAMILY_MFMA && (half.variant & 1) && half.kparts == 1 && !(half.variant & 2)) {
+                half.passes = (M + 7) / 8;
+                *out = half;
+                return QGEMV_OK;
+            }
+        }
         const int64_t smax = (steps + kp - 1) / kp;  // K steps of the longest part
         const Staged st = staged(kp);
         const int64_t abytes16 = st.abytes;

@@ -164,7 +164,8 @@ typedef struct qgemv_desc {
 typedef struct qgemv_plan_info {
     int32_t family;          /* enum qgemv_family actually used */
     int32_t rows_per_pass;   /* rows of A carried by one pass over the weight */
-    int32_t passes;          /* passes over the weight for this M */
+    int32_t passes;          /* passes over the weight for this M (the matrix family's
+                                passes are one launch each, in order, on the stream) */
     int32_t cols_per_wave;   /* output columns one wave owns at a time */
     int32_t ksplit;          /* waves of a workgroup sharing one column tile's K */
     int32_t waves_per_wg;    /* waves per workgroup */

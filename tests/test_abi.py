@@ -282,6 +282,35 @@ def test_two_k_parts_where_the_unsplit_rows_do_not_fit_in_lds():
     assert _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=True)["kparts"] == 1
 
 
+def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
+    """Without K parts, the case where 2 parts would be taken with a workspace runs
+    more than 8 rows as passes of 8 (one launch each), each staging its rows; a forced
+    staging choice keeps one launch."""
+    kw = dict(fmt="fp8", act="f16", N=2048, K=8192, block_size=128)
+    for M, passes in ((8, 1), (9, 1), (12, 2), (13, 2), (16, 2)):
+        p = _sel(**kw, M=M)
+        assert p["passes"] == passes and p["variant"] & 1, (M, p)
+        if passes > 1:
+            assert p["rows_per_pass"] == 8 and p["kparts"] == 1 and p == _sel(**kw, M=8) | {"passes": passes}
+    # with a workspace: 2 K parts in one launch instead
+    p = _sel(**kw, M=16, with_workspace=True)
+    assert p["passes"] == 1 and p["kparts"] == 2
+    # a forced part count of 1 with a workspace: passes again
+    assert _sel(**kw, M=16, flags=1 << 4, with_workspace=True)["passes"] == 2
+    # forced staging off: one unstaged launch
+    p = _sel(**kw, M=16, flags=bqw.FLAG_STAGE_A_OFF)
+    assert p["passes"] == 1 and p["rows_per_pass"] == 16 and not (p["variant"] & 1)
+    # FP8 5120 x 6144 at M = 16 (160 tile groups, 24 K steps per wave): passes
+    p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=16)
+    assert p["passes"] == 2 and p["grid"] == 160
+    # 8-bit 4096 x 8192 (16 K steps per wave): one launch, unstaged
+    p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16)
+    assert p["passes"] == 1 and not (p["variant"] & 1)
+    # 4-bit 2048 x 16384: 8 rows do not fit either: one launch
+    p = _sel(fmt="u4", act="bf16", N=2048, K=16384, block_size=32, M=16)
+    assert p["passes"] == 1
+
+
 def test_forced_k_parts_and_k_split_are_clamped():
     # 4 K steps (fp8, K = 256): 8 forced parts become 4, one step each
     p = _sel(fmt="fp8", act="f16", N=100, K=256, block_size=128, M=8, flags=2 | (4 << 4), with_workspace=True)

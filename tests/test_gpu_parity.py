@@ -258,6 +258,25 @@ def test_sixteen_rows_full_size_with_the_overlaid_reduction_area():
     assert ok, ratio
 
 
+@pytest.mark.parametrize("fmt,act,N,K,bs,M", [("fp8", "f16", 2000, 8192, 128, 13), ("fp8", "f16", 2048, 8192, 128, 16),
+                                              ("u8", "f16", 1900, 8192, 128, 12)])
+def test_row_passes_match_one_unstaged_launch(fmt, act, N, K, bs, M):
+    """Where M > 8 rows do not fit in LDS and there are no K parts, the plan runs passes
+    of 8 rows (the last one shorter), one launch each. Every row comes out bit for bit
+    as in one launch with the activations in the register ring, and within the bound
+    against the oracle."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=27)
+    gu.say(f"[passes] {fmt}/{act} N={N} K={K} M={M}")
+    Y, plan = gu.run_gpu(prob, M)
+    assert plan["family"] == "mfma" and plan["passes"] == 2 and plan["rows_per_pass"] == 8, plan
+    assert plan["variant"] & 1
+    Yu, pu = gu.run_gpu(prob, M, flags=bqw.FLAG_STAGE_A_OFF)
+    assert pu["passes"] == 1 and not (pu["variant"] & 1) and pu["ksplit"] == plan["ksplit"], pu
+    assert np.array_equal(Y.view(np.int64), Yu.view(np.int64))
+    ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
+    assert ok, ratio
+
+
 @pytest.mark.parametrize("stage", [False, True])
 @pytest.mark.parametrize("ks", [1, 2, 4, 8])
 def test_forced_k_split_is_correct(ks, stage):
