@@ -311,6 +311,18 @@ def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
     assert p["passes"] == 1
 
 
+def test_a_workspace_sized_for_sixteen_rows_serves_every_m():
+    """The K parts may depend on M (2 parts where the rows do not fit), yet the
+    workspace a plan needs never exceeds the one at M = 16."""
+    for fmt, act, N, K, bs in [("fp8", "f16", 2048, 8192, 128), ("u4", "bf16", 2048, 16384, 32),
+                               ("fp8", "f16", 5120, 6144, 128), ("fp8", "f16", 1024, 16384, 128),
+                               ("u4", "bf16", 512, 8192, 32), ("u4", "bf16", 16384, 8192, 32)]:
+        full = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=16, with_workspace=True)["workspace_bytes"]
+        for M in range(1, 17):
+            p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=True)
+            assert p["workspace_bytes"] <= full, (fmt, N, K, M, p, full)
+
+
 def test_forced_k_parts_and_k_split_are_clamped():
     # 4 K steps (fp8, K = 256): 8 forced parts become 4, one step each
     p = _sel(fmt="fp8", act="f16", N=100, K=256, block_size=128, M=8, flags=2 | (4 << 4), with_workspace=True)

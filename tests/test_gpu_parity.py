@@ -258,15 +258,17 @@ def test_sixteen_rows_full_size_with_the_overlaid_reduction_area():
     assert ok, ratio
 
 
-@pytest.mark.parametrize("fmt,act,N,K,bs,M", [("fp8", "f16", 2000, 8192, 128, 13), ("fp8", "f16", 2048, 8192, 128, 16),
-                                              ("u8", "f16", 1900, 8192, 128, 12)])
-def test_row_passes_match_one_unstaged_launch(fmt, act, N, K, bs, M):
+@pytest.mark.parametrize("fmt,act,N,K,bs,M,bias", [("fp8", "f16", 2000, 8192, 128, 13, False),
+                                                   ("fp8", "f16", 2048, 8192, 128, 16, False),
+                                                   ("u8", "f16", 1900, 8192, 128, 12, False),
+                                                   ("fp8", "f16", 2000, 8192, 128, 16, True)])
+def test_row_passes_match_one_unstaged_launch(fmt, act, N, K, bs, M, bias):
     """Where M > 8 rows do not fit in LDS and there are no K parts, the plan runs passes
     of 8 rows (the last one shorter), one launch each. Every row comes out bit for bit
     as in one launch with the activations in the register ring, and within the bound
     against the oracle."""
-    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=27)
-    gu.say(f"[passes] {fmt}/{act} N={N} K={K} M={M}")
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=27, with_bias=bias)
+    gu.say(f"[passes] {fmt}/{act} N={N} K={K} M={M} bias={bias}")
     Y, plan = gu.run_gpu(prob, M)
     assert plan["family"] == "mfma" and plan["passes"] == 2 and plan["rows_per_pass"] == 8, plan
     assert plan["variant"] & 1
