@@ -38,7 +38,8 @@ FLAG_STREAM_WPC_SHIFT = 25
 FLAG_STREAM_CLASSIC = 0x10000000
 FLAG_MFMA_DEPTH_SHIFT = 29
 FLAG_STREAM_WIDE_WG = 0x80000000
-MAX_M = 16
+MAX_M = 16  # rows one plan carries
+MAX_ROWS = 65536  # rows one call accepts (more than MAX_M run as chunks of MAX_M)
 
 _lock = threading.Lock()
 _lib = None

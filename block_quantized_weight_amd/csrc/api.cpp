@@ -91,18 +91,48 @@ void to_info(const qgemv::LaunchCfg &c, qgemv_plan_info *o) {
     o->workspace_bytes = c.ws_bytes;
 }
 
-// Shared body of qgemv_run and qgemv_run_ws: plan (with or without a workspace),
-// check the workspace the plan needs, and enqueue the launch.
+// Enqueue the launch(es) of plan c for rows of A and Y (at most the plan's M).
+hipError_t launch_rows(const qgemv::LaunchCfg &c, const qgemv::KArgs &a0, const void *A, void *Y, int rows,
+                       const qgemv_desc &d, hipStream_t s) {
+    qgemv::KArgs a = a0;
+    a.A = A;
+    a.Y = Y;
+    a.M = rows;
+    switch (c.family) {
+    case QGEMV_FAMILY_STREAM: return qgemv::launch_stream(c, a, s);
+    case QGEMV_FAMILY_MFMA: {
+        // row passes: rows_per_pass rows of A and Y per launch, in order, on the stream
+        hipError_t e = hipSuccess;
+        for (int r0 = 0; r0 < rows && e == hipSuccess; r0 += c.rows_per_pass) {
+            qgemv::KArgs ap = a;
+            ap.A = (const unsigned char *)A + (size_t)r0 * (size_t)d.K * 2;
+            ap.Y = (unsigned char *)Y + (size_t)r0 * (size_t)d.N * 2;
+            ap.M = (rows - r0) < c.rows_per_pass ? (rows - r0) : c.rows_per_pass;
+            e = qgemv::launch_mfma(c, ap, s);
+        }
+        return e;
+    }
+    default: return qgemv::launch_generic(c, a, s);
+    }
+}
+
+// Shared body of qgemv_run and qgemv_run_ws: plan (with or without a workspace) for
+// min(M, 16) rows, check the workspace the plan needs, and enqueue the launches.
+// More than 16 rows run as chunks of 16 (the last one shorter), one after another on
+// the stream, each with the 16-row plan: a row's arithmetic does not depend on the
+// chunk that carries it, and the workspace, all zero again after each chunk, serves
+// every chunk in turn.
 int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
              void *hip_stream) {
     if (!h || !A || !Y) return QGEMV_E_NULL;
-    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
+    if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
+    const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
     const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, M, h->cu_count, fast, h->env_flags, with_ws, &c);
+    int rc = qgemv::select_plan(&h->d, Mp, h->cu_count, fast, h->env_flags, with_ws, &c);
     if (rc) return rc;
     qgemv::KArgs a;
-    fill_args(h, A, Y, M, &a);
+    fill_args(h, A, Y, Mp, &a);
     a.ksplit = c.ksplit;
     if (c.kparts > 1) {
         if (!ws || (uintptr_t)ws % 256 || ws_bytes < (size_t)c.ws_bytes) return QGEMV_E_WORKSPACE;
@@ -111,24 +141,27 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
         a.part = (float *)((unsigned char *)ws + c.ws_counters);
     }
     hipStream_t s = (hipStream_t)hip_stream;
-    hipError_t e;
-    switch (c.family) {
-    case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(c, a, s); break;
-    case QGEMV_FAMILY_MFMA:
-        // row passes: rows_per_pass rows of A and Y per launch, in order, on the stream
-        e = hipSuccess;
-        for (int p = 0; p < c.passes && e == hipSuccess; ++p) {
-            const int r0 = p * c.rows_per_pass;
-            qgemv::KArgs ap = a;
-            ap.A = (const unsigned char *)A + (size_t)r0 * (size_t)h->d.K * 2;
-            ap.Y = (unsigned char *)Y + (size_t)r0 * (size_t)h->d.N * 2;
-            ap.M = (M - r0) < c.rows_per_pass ? (M - r0) : c.rows_per_pass;
-            e = qgemv::launch_mfma(c, ap, s);
-        }
-        break;
-    default: e = qgemv::launch_generic(c, a, s); break;
+    hipError_t e = hipSuccess;
+    for (int r0 = 0; r0 < M && e == hipSuccess; r0 += Mp) {
+        const int rows = (M - r0) < Mp ? (M - r0) : Mp;
+        e = launch_rows(c, a, (const unsigned char *)A + (size_t)r0 * (size_t)h->d.K * 2,
+                        (unsigned char *)Y + (size_t)r0 * (size_t)h->d.N * 2, rows, h->d, s);
     }
     return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
+}
+
+// The plan of M rows as reported: the 16-row plan, its passes counted over all the
+// chunks of 16 rows.
+int plan_rows(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t env_flags, bool with_ws,
+              qgemv::LaunchCfg *c) {
+    int rc = qgemv::validate_desc(d);
+    if (rc) return rc;
+    if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
+    const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
+    rc = qgemv::select_plan(d, Mp, cu_count, fast_ok, env_flags, with_ws, c);
+    if (rc) return rc;
+    c->passes *= (M + Mp - 1) / Mp;
+    return QGEMV_OK;
 }
 
 }  // namespace
@@ -141,7 +174,7 @@ const char *qgemv_status_str(int s) {
     switch (s) {
     case QGEMV_OK: return "ok";
     case QGEMV_E_NULL: return "a required pointer is NULL";
-    case QGEMV_E_SHAPE: return "invalid shape (M outside [1,16], N or K < 1, or K not a multiple of the block size)";
+    case QGEMV_E_SHAPE: return "invalid shape (M outside [1,65536], N or K < 1, or K not a multiple of the block size)";
     case QGEMV_E_BLOCK: return "block size not supported for this format";
     case QGEMV_E_FORMAT: return "unknown format or activation dtype, or zero points given for FP8/NVFP4";
     case QGEMV_E_DEVICE: return "no usable gfx950 device";
@@ -177,7 +210,7 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
 int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info *out) {
     if (!h || !out) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, with_workspace != 0, &c);
+    int rc = plan_rows(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, with_workspace != 0, &c);
     if (rc) return rc;
     to_info(c, out);
     return QGEMV_OK;
@@ -185,9 +218,9 @@ int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info
 
 int qgemv_select(const qgemv_desc *d, int M, int cu_count, int with_workspace, qgemv_plan_info *out) {
     if (!out) return QGEMV_E_NULL;
+    if (!d) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(d, M, cu_count, d ? qgemv::pointers_fast_ok(d, nullptr, nullptr) : false, 0u,
-                                with_workspace != 0, &c);
+    int rc = plan_rows(d, M, cu_count, qgemv::pointers_fast_ok(d, nullptr, nullptr), 0u, with_workspace != 0, &c);
     if (rc) return rc;
     to_info(c, out);
     return QGEMV_OK;
@@ -205,7 +238,7 @@ int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *wor
 int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes) {
     if (!h || !bytes) return QGEMV_E_NULL;
     qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, true, &c);
+    int rc = plan_rows(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, true, &c);
     if (rc) return rc;
     *bytes = (size_t)c.ws_bytes;
     return QGEMV_OK;

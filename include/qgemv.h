@@ -1,7 +1,8 @@
 /*
  * qgemv — block-scaled small-M decode GEMV for AMD Instinct MI355X (gfx950)
  *
- *     Y[M, N] = A[M, K] . dequant(W)[N, K]^T (+ bias[N]),   1 <= M <= 16,
+ *     Y[M, N] = A[M, K] . dequant(W)[N, K]^T (+ bias[N]),   1 <= M <= 16 (up to
+ *     QGEMV_MAX_ROWS rows run as chunks of 16),
  *
  * with A, Y and the optional bias in fp16 or bf16 and fp32 accumulation. The weight W is quantized
  * in blocks along K in one of four formats:
@@ -56,8 +57,11 @@
 extern "C" {
 #endif
 
-#define QGEMV_ABI_VERSION 3
+#define QGEMV_ABI_VERSION 4
+/* Rows one plan carries; a call with more runs them as chunks of this many. */
 #define QGEMV_MAX_M 16
+/* Rows one call accepts. */
+#define QGEMV_MAX_ROWS 65536
 
 /* Weight formats. */
 enum qgemv_format {
@@ -77,7 +81,7 @@ enum qgemv_act_dtype {
 enum qgemv_status {
     QGEMV_OK = 0,
     QGEMV_E_NULL = 1,     /* a required pointer is NULL */
-    QGEMV_E_SHAPE = 2,    /* M outside [1, 16], N < 1, K < 1 or K % block_size != 0 */
+    QGEMV_E_SHAPE = 2,    /* M outside [1, QGEMV_MAX_ROWS], N < 1, K < 1 or K % block_size != 0 */
     QGEMV_E_BLOCK = 3,    /* block size not supported for the format */
     QGEMV_E_FORMAT = 4,   /* unknown format / dtype, or zero points given for FP8/NVFP4 */
     QGEMV_E_DEVICE = 5,   /* no usable device, or the device is not gfx950 */
@@ -195,7 +199,15 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device);
  * pointers in the handle's activation dtype. Asynchronous: no host sync, no
  * allocation, no environment read. Safe to call concurrently on different streams
  * (the handle is immutable after create). The call must be made with the
- * handle's device current. */
+ * handle's device current.
+ *
+ * The kernels are built for M <= QGEMV_MAX_M (16) rows, the decode regime of the
+ * pages. More rows, up to QGEMV_MAX_ROWS, run as chunks of 16 rows (the last one
+ * shorter), one after another on the stream, each with the plan for 16 rows: each
+ * chunk reads the whole weight again, so this serves short prefills rather than
+ * replacing a GEMM. A row's bits do not depend on the chunk that carries it. (The
+ * pages' batched small-M kernel falls back to another path past its M limit; "[CUDA]
+ * Batched small-M GEMV for MatMulNBits (4-bit/8-bit)", Description.) */
 int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream);
 
 /* The same product, where the K range may also be split across workgroups: for N so

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert bqw.lib().qgemv_abi_version() == 3
+    assert bqw.lib().qgemv_abi_version() == 4
     # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields; the
     # bias pointer (version 2) follows the flags
     assert ctypes.sizeof(bqw.Desc) == 72
@@ -59,7 +59,7 @@ def _sel(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(M=0), 2), (dict(M=17), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=4010), 2),
+    (dict(M=0), 2), (dict(M=65537), 2), (dict(M=-1), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=4010), 2),
     (dict(block_size=48), 3), (dict(block_size=8), 3), (dict(fmt="nvfp4", block_size=32), 3),
     (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
     (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
@@ -321,6 +321,21 @@ def test_a_workspace_sized_for_sixteen_rows_serves_every_m():
         for M in range(1, 17):
             p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=True)
             assert p["workspace_bytes"] <= full, (fmt, N, K, M, p, full)
+
+
+def test_more_than_sixteen_rows_take_the_sixteen_row_plan_in_chunks():
+    """M > 16 (up to 65536) runs as chunks of 16 rows with the plan for 16 rows; the
+    reported passes count every chunk's passes, and the workspace is that of 16 rows."""
+    shapes = [dict(), dict(fmt="fp8", act="f16", N=5120, K=6144, block_size=128),
+              dict(fmt="u4", act="f16", N=1024, K=2048, block_size=32),
+              dict(fmt="fp8", act="f16", N=1024, K=16384, block_size=128)]
+    for kw in shapes:
+        for ws in (False, True):
+            p16 = _sel(**kw, M=16, with_workspace=ws)
+            for M, chunks in ((17, 2), (32, 2), (33, 3), (100, 7), (65536, 4096)):
+                p = _sel(**kw, M=M, with_workspace=ws)
+                assert p == p16 | {"passes": p16["passes"] * chunks}, (kw, M, ws, p, p16)
+    assert bqw.MAX_ROWS == 65536
 
 
 def test_forced_k_parts_and_k_split_are_clamped():

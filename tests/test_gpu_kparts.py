@@ -68,6 +68,22 @@ def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K,
     assert np.array_equal(Y.view(np.int64), Yf.view(np.int64))
 
 
+def test_more_than_sixteen_rows_share_the_workspace_chunk_by_chunk():
+    """M = 20 with K parts (FP8 1024 x 16384, 4 parts): chunks of 16 and 4 rows run
+    through the same workspace in turn, which ends all zero; outputs against the
+    oracle, and rows 16..19 bit for bit a 4-row call held to the matrix family (on its
+    own, 4 rows of 1-byte codes take the streaming family)."""
+    prob = synth.make_problem("fp8", "f16", 1024, 16384, 128, 20, seed=29)
+    gu.say("[kparts] fp8 1024x16384 M=20 in chunks")
+    Y, plan = gu.run_gpu(prob, 20, ws=True)
+    assert plan["kparts"] == 4 and plan["ws_zero"], plan
+    ok, ratio, _, _ = gu.check_full(prob, 20, Y)
+    assert ok, ratio
+    Y4, p4 = gu.run_gpu(prob, 4, flags=2, ws=True, A=prob.A[16:20])
+    assert p4["kparts"] == 4 and p4["ksplit"] == plan["ksplit"]
+    assert np.array_equal(Y[16:20].view(np.int64), Y4.view(np.int64))
+
+
 def test_fp8_projection_with_forced_k_parts():
     """The FP8 5120 x 6144 workload at M = 8 in two forced parts (the automatic plan
     keeps it whole)."""

@@ -279,6 +279,27 @@ def test_row_passes_match_one_unstaged_launch(fmt, act, N, K, bs, M, bias):
     assert ok, ratio
 
 
+@pytest.mark.parametrize("fmt,act,N,K,bs,flags,family", [("u4", "f16", 1000, 2048, 32, 0, "stream"),
+                                                         ("fp8", "f16", 777, 4096, 128, 2, "mfma"),
+                                                         ("u4", "bf16", 3000, 4096, 32, 0, "mfma"),
+                                                         ("nvfp4", "bf16", 640, 1024, 16, 1, "stream"),
+                                                         ("u8", "f16", 500, 1024, 128, 3, "generic")])
+def test_more_than_sixteen_rows_run_as_chunks(fmt, act, N, K, bs, flags, family):
+    """M = 37 runs as chunks of 16, 16 and 5 rows with the 16-row plan: every output
+    within the bound against the oracle, and the middle chunk bit for bit the 16-row
+    call on those rows."""
+    M = 37
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=28)
+    gu.say(f"[chunks] {fmt}/{act} N={N} K={K} M={M} flags={flags:#x}")
+    Y, plan = gu.run_gpu(prob, M, flags=flags)
+    assert plan["family"] == family, plan
+    ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
+    assert ok, ratio
+    Y16, p16 = gu.run_gpu(prob, 16, flags=flags, A=prob.A[16:32])
+    assert plan["passes"] == 3 * p16["passes"], (plan, p16)
+    assert np.array_equal(Y[16:32].view(np.int64), Y16.view(np.int64))
+
+
 @pytest.mark.parametrize("stage", [False, True])
 @pytest.mark.parametrize("ks", [1, 2, 4, 8])
 def test_forced_k_split_is_correct(ks, stage):
@@ -425,7 +446,8 @@ def test_run_rejects_bad_arguments():
     prob = synth.workload("u4_m1_k512_n256")
     q, t = bqw.upload(prob)
     Y = torch.empty((16, prob.N), dtype=t["A"].dtype, device="cuda")
-    for M in (0, 17, -1):
+    # rejected before any launch (17 rows and more are valid: chunks of 16)
+    for M in (0, bqw.MAX_ROWS + 1, -1):
         with pytest.raises(bqw.QGemvError) as e:
             q.run(t["A"], Y, M=M)
         assert e.value.status == 2
