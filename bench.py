@@ -238,7 +238,7 @@ def main():
         traffic_record(*args.traffic_record, args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the weight would be split by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the weight would be split by "
               "output columns, one shard per GPU, with no communication in the product). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
