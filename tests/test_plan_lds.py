@@ -1,0 +1,73 @@
+"""The dispatcher's launch sizes against the register-ring kernel's own LDS layout.
+
+The matrix family's register-ring kernel (k_mfma) lays out its LDS from its arguments:
+a 64-byte zero block, the staged rows of the longest K part (row stride: that part's k
+plus 8 elements, 2 bytes each, rounded up to 16 bytes), for formats with zero points
+one 16-byte activation-sum entry per chunk, row group and scale block, then the K-split
+reduction area (8 waves x row groups x 4 x 64 fp32), which overlays the staged rows from
+byte 0 when the workgroup holds a single tile group (always with K parts), and, with K
+parts, a 4-byte completion flag after both. The host must launch with at least that
+much. This recomputes the kernel's layout for every automatic plan over a grid of
+shapes, every M, with and without a workspace, and checks it against the plan, with
+the plan's other invariants.
+"""
+
+import pytest
+
+import block_quantized_weight_amd as bqw
+
+KPC = {"u4": 32, "nvfp4": 32, "u8": 16, "fp8": 16}
+LDS = 160 * 1024
+
+SHAPES = [  # fmt, act, N, K, bs
+    ("u4", "bf16", 151936, 4096, 32), ("u4", "f16", 1024, 2048, 32), ("u4", "bf16", 4096, 4096, 32),
+    ("u4", "bf16", 16384, 8192, 32), ("u4", "bf16", 2048, 16384, 32), ("u4", "f16", 512, 8192, 32),
+    ("u4", "f16", 777, 896, 16), ("u4", "bf16", 3000, 4096, 128), ("u8", "f16", 4096, 4096, 128),
+    ("u8", "f16", 4096, 8192, 128), ("u8", "f16", 2048, 8192, 128), ("u8", "f16", 1900, 8192, 64),
+    ("fp8", "f16", 5120, 6144, 128), ("fp8", "f16", 8192, 4096, 128), ("fp8", "f16", 1024, 16384, 128),
+    ("fp8", "bf16", 2048, 8192, 128), ("fp8", "f16", 100, 256, 128), ("nvfp4", "bf16", 248320, 2048, 16),
+    ("nvfp4", "bf16", 2048, 4096, 16), ("nvfp4", "f16", 999, 3104, 16),
+]
+
+
+def kernel_lds(fmt, N, K, bs, rows, plan):
+    """Bytes the register-ring kernel addresses for a pass of `rows` rows."""
+    ks, kp = plan["ksplit"], plan["kparts"]
+    rg = (rows + 3) // 4
+    h = 2 if fmt == "nvfp4" or (fmt == "u4" and bs == 16) else 1
+    steps = K // (4 * KPC[fmt])
+    smax = (steps + kp - 1) // kp
+    staged = bool(plan["variant"] & 1)
+    tiles = (N + 15) // 16
+    ngroups = (tiles + 8 // ks - 1) // (8 // ks)
+    red = 8 * rg * 4 * 64 * 4 if ks > 1 else 0
+    abytes = 0
+    if staged:
+        astride = smax * 4 * KPC[fmt] + 8
+        rows_b = (rows * astride * 2 + 15) // 16 * 16
+        sums = 4 * smax * rg * h * 16 if fmt in ("u4", "u8") else 0
+        abytes = 64 + rows_b + sums
+    overlay = staged and ks > 1 and (kp > 1 or plan["grid"] // kp >= ngroups)
+    end = max(abytes, red) if overlay else abytes + red
+    return end + (4 if kp > 1 else 0)
+
+
+@pytest.mark.parametrize("fmt,act,N,K,bs", SHAPES)
+def test_every_register_ring_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs):
+    for M in (1, 2, 3, 4, 5, 8, 9, 12, 13, 16, 20, 37):
+        for ws in (False, True):
+            p = bqw.select(fmt, act, N, K, bs, M, with_workspace=ws)
+            assert 1 <= p["grid"] and 0 <= p["lds_bytes"] <= LDS, (M, ws, p)
+            rows = min(M, 16)
+            # passes of rows_per_pass rows cover every row of each 16-row chunk
+            chunks = (M + 15) // 16
+            per_chunk = p["passes"] // chunks
+            assert p["passes"] % chunks == 0 and p["rows_per_pass"] * per_chunk >= rows, (M, p)
+            if p["kparts"] > 1:
+                assert p["family"] == "mfma" and ws and p["grid"] % p["kparts"] == 0
+                assert p["kparts"] * 16 * N < 1 << 31
+                assert p["workspace_bytes"] >= p["kparts"] * min(M, 16) * N * 4
+            if p["family"] != "mfma" or p["variant"] & 2:
+                continue  # the streaming kernels and the DMA ring size their own layouts
+            need = kernel_lds(fmt, N, K, bs, min(p["rows_per_pass"], rows), p)
+            assert need <= p["lds_bytes"], (fmt, N, K, bs, M, ws, p, need)
