@@ -1,15 +1,16 @@
-"""The dispatcher's launch sizes against the register-ring kernel's own LDS layout.
+"""The dispatcher's launch sizes against the matrix-family kernels' own LDS layouts.
 
-The matrix family's register-ring kernel (k_mfma) lays out its LDS from its arguments:
+The register-ring kernel (k_mfma) lays out its LDS from its arguments:
 a 64-byte zero block, the staged rows of the longest K part (row stride: that part's k
 plus 8 elements, 2 bytes each, rounded up to 16 bytes), for formats with zero points
 one 16-byte activation-sum entry per chunk, row group and scale block, then the K-split
 reduction area (8 waves x row groups x 4 x 64 fp32), which overlays the staged rows from
 byte 0 when the workgroup holds a single tile group (always with K parts), and, with K
-parts, a 4-byte completion flag after both. The host must launch with at least that
-much. This recomputes the kernel's layout for every automatic plan over a grid of
-shapes, every M, with and without a workspace, and checks it against the plan, with
-the plan's other invariants.
+parts, a 4-byte completion flag after both. The DMA-ring kernel (k_mfma_dma) stages
+all of K the same way and follows it with two slots per wave. The host must launch
+with at least that much. This recomputes the kernels' layouts for every automatic
+plan over a grid of shapes, every M, with and without a workspace and zero points,
+and checks them against the plan, with the plan's other invariants.
 """
 
 import pytest
@@ -30,11 +31,21 @@ SHAPES = [  # fmt, act, N, K, bs
 ]
 
 
-def kernel_lds(fmt, N, K, bs, rows, plan):
-    """Bytes the register-ring kernel addresses for a pass of `rows` rows."""
+def kernel_lds(fmt, N, K, bs, rows, plan, zpp=False):
+    """Bytes the matrix-family kernel addresses for a pass of `rows` rows."""
     ks, kp = plan["ksplit"], plan["kparts"]
     rg = (rows + 3) // 4
     h = 2 if fmt == "nvfp4" or (fmt == "u4" and bs == 16) else 1
+    if plan["variant"] & 2:
+        # DMA ring: all of K staged, then 8 waves x 2 slots of 4 K steps: 4 KiB of codes,
+        # the scale windows (4 DMAs of 256 bytes for FP8 and 16-wide 4-bit blocks, else
+        # 2) and the zero-point window when there are zero points
+        nch = K // KPC[fmt]
+        rows_b = (rows * (K + 8) * 2 + 15) // 16 * 16
+        sums = nch * rg * h * 16 if fmt in ("u4", "u8") else 0
+        nsd = 4 if (fmt == "fp8" or (fmt == "u4" and h == 2)) else 2
+        slot = 4096 + 256 * nsd + (256 if zpp else 0)
+        return 64 + rows_b + sums + 8 * 2 * slot
     steps = K // (4 * KPC[fmt])
     smax = (steps + kp - 1) // kp
     staged = bool(plan["variant"] & 1)
@@ -52,11 +63,14 @@ def kernel_lds(fmt, N, K, bs, rows, plan):
     return end + (4 if kp > 1 else 0)
 
 
+@pytest.mark.parametrize("zp", [False, True])
 @pytest.mark.parametrize("fmt,act,N,K,bs", SHAPES)
-def test_every_register_ring_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs):
+def test_every_matrix_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs, zp):
+    if zp and fmt not in ("u4", "u8"):
+        pytest.skip("zero points are for the integer codes")
     for M in (1, 2, 3, 4, 5, 8, 9, 12, 13, 16, 20, 37):
         for ws in (False, True):
-            p = bqw.select(fmt, act, N, K, bs, M, with_workspace=ws)
+            p = bqw.select(fmt, act, N, K, bs, M, with_workspace=ws, zero_points=0x2000 if zp else None)
             assert 1 <= p["grid"] and 0 <= p["lds_bytes"] <= LDS, (M, ws, p)
             rows = min(M, 16)
             # passes of rows_per_pass rows cover every row of each 16-row chunk
@@ -67,7 +81,7 @@ def test_every_register_ring_plan_holds_the_kernels_lds_layout(fmt, act, N, K, b
                 assert p["family"] == "mfma" and ws and p["grid"] % p["kparts"] == 0
                 assert p["kparts"] * 16 * N < 1 << 31
                 assert p["workspace_bytes"] >= p["kparts"] * min(M, 16) * N * 4
-            if p["family"] != "mfma" or p["variant"] & 2:
-                continue  # the streaming kernels and the DMA ring size their own layouts
-            need = kernel_lds(fmt, N, K, bs, min(p["rows_per_pass"], rows), p)
+            if p["family"] != "mfma":
+                continue  # the streaming kernels' staged rows are sized by the same formula
+            need = kernel_lds(fmt, N, K, bs, min(p["rows_per_pass"], rows), p, zpp=zp)
             assert need <= p["lds_bytes"], (fmt, N, K, bs, M, ws, p, need)
