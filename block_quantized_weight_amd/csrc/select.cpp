@@ -262,7 +262,15 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 //    and FP8 codes, and for 4-bit codes while the weight is small enough (under
 //    64 MB) that the call is latency-bound rather than bandwidth-bound. Wide 4-bit
 //    weights take the matrix family's DMA ring from M = 2 (4-bit lm_head, M = 2:
-//    90 us against 101 us).
+//    90 us against 101 us). At M = 3..4, where the matrix family's tile groups fill
+//    the CUs, it wins for 4-bit codes and, from 64 MB of codes, for 1-byte ones
+//    (streaming -> matrix at M = 4: 4-bit 16384 x 4096 22.9 -> 15.9 us, 4-bit
+//    8192 x 4096 12.5 -> 10.9 (M = 3: 11.2 -> 10.3), NVFP4 8192 x 4096 12.7 -> 9.1,
+//    8-bit 16384 x 4096 28.4 -> 22.6, FP8 16384 x 4096 25.0 -> 19.5), but not for
+//    smaller 1-byte weights (8-bit 8192 x 4096: 14.5 against 14.0-14.6 us at M = 4,
+//    12.2 against 14.4 at M = 3; 8-bit 4096 x 4096: 9.8 against 11.5), nor with fewer
+//    tile groups (FP8 5120 x 6144, 160: 11.9 against 14.2; 4-bit 4096 x 4096, 128:
+//    9.0 against 10.1), nor at M = 2 (FP8 8192 x 4096: 9.9 against 12.7).
 //  - M = 5..16 (the multi-pass kernel, 4 rows a pass, the weight re-read from L2):
 //    for small weights, N x K <= 4 Mi elements with K <= 4096, where the matrix
 //    family has too few tiles to fill the CUs. Matrix -> streaming at M = 8: 4-bit
@@ -275,9 +283,17 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 //    against 16.7), whose single wave per column walks too many steps. The same holds
 //    with a workspace: K parts on these shapes measured slower than the streaming
 //    kernel (FP8 1024 x 4096: 13.3 us).
-static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok) {
+static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_count, uint32_t flags) {
     if (!stream_ok || M < 2) return false;
     if (M > 4) return d->K <= 4096 && (int64_t)d->N * d->K <= 4LL * 1024 * 1024;
+    if (M >= 3) {
+        // four rows per pass: the matrix family wins once its tile groups fill the CUs,
+        // for 1-byte codes only from 64 MB of codes on
+        const int ks = mfma_ksplit(d, cu_count, flags);
+        const int64_t groups = ((d->N + 15) / 16 + 8 / ks - 1) / (8 / ks);
+        const bool bytes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
+        if (groups >= cu_count && (!bytes || (int64_t)d->N * d->K >= 64LL * 1024 * 1024)) return false;
+    }
     const int kpc = k_per_chunk(d->format);
     const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
@@ -321,7 +337,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
     } else if (forced == QGEMV_FAMILY_MFMA) {
         if (!(fast_ok && mfma_shape_ok(d))) return QGEMV_E_ARG;
         family = QGEMV_FAMILY_MFMA;
-    } else if (mfma_ok && M >= 2 && !stream_rows_win(d, M, stream_ok)) {
+    } else if (mfma_ok && M >= 2 && !stream_rows_win(d, M, stream_ok, cu_count, flags)) {
         family = QGEMV_FAMILY_MFMA;
     } else if (stream_ok) {
         family = QGEMV_FAMILY_STREAM;

@@ -208,6 +208,21 @@ def test_k_split_takes_the_least_work_on_the_busiest_cu():
     assert ks("nvfp4", 248320, 2048, 16, "bf16") == 1
 
 
+def test_three_and_four_rows_take_the_matrix_family_where_its_tile_groups_fill_the_cus():
+    """M = 3..4: the matrix family where its tile groups fill the 256 CUs, for 1-byte
+    codes only from 64 MB of codes; M = 2 stays with the streaming kernel below the
+    4-bit 64 MB rule."""
+    def fams(fmt, act, N, K, bs):
+        return [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)["family"] for M in (2, 3, 4)]
+    assert fams("u4", "bf16", 8192, 4096, 32) == ["stream", "mfma", "mfma"]  # 256 tile groups (split 4)
+    assert fams("nvfp4", "bf16", 8192, 4096, 16) == ["stream", "mfma", "mfma"]
+    assert fams("u8", "f16", 16384, 4096, 128) == ["stream", "mfma", "mfma"]  # 64 MiB of codes
+    assert fams("fp8", "f16", 16384, 4096, 128) == ["stream", "mfma", "mfma"]
+    assert fams("u8", "f16", 8192, 4096, 128) == ["stream"] * 3  # 32 MiB
+    assert fams("u4", "bf16", 4096, 4096, 32) == ["stream"] * 3  # 128 tile groups
+    assert fams("fp8", "f16", 5120, 6144, 128) == ["stream"] * 3  # 160 tile groups
+
+
 def test_small_weights_take_the_streaming_family_at_every_m():
     """Up to N x K = 4 Mi elements with K <= 4096, the streaming family serves every M
     (the multi-pass kernel from M = 5), with or without a workspace; past either
