@@ -270,7 +270,10 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 //    smaller 1-byte weights (8-bit 8192 x 4096: 14.5 against 14.0-14.6 us at M = 4,
 //    12.2 against 14.4 at M = 3; 8-bit 4096 x 4096: 9.8 against 11.5), nor with fewer
 //    tile groups (FP8 5120 x 6144, 160: 11.9 against 14.2; 4-bit 4096 x 4096, 128:
-//    9.0 against 10.1), nor at M = 2 (FP8 8192 x 4096: 9.9 against 12.7).
+//    9.0 against 10.1), nor at M = 2, where two rows leave the streaming kernel
+//    ahead (FP8 8192 x 4096: 9.9 against 12.7 us; 4-bit 8192 x 4096: 9.2 against
+//    10.2; 8-bit 16384 x 4096: 16.7 against 21.8; only 4-bit 16384 x 4096 is close,
+//    16.3 against 15.4). 8-bit 16384 x 4096 at M = 3: 25.2 -> 22.1 us.
 //  - M = 5..16 (the multi-pass kernel, 4 rows a pass, the weight re-read from L2):
 //    for small weights, N x K <= 4 Mi elements with K <= 4096, where the matrix
 //    family has too few tiles to fill the CUs. Matrix -> streaming at M = 8: 4-bit
