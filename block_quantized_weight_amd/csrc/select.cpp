@@ -460,6 +460,18 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
         // with K parts, 16 bytes more for the last-workgroup flag
         c.lds_bytes = (int)(stage ? lds_staged : lds_red + flag_b);
+        // Without K parts, where the rows do not fit in LDS, not even 8 at a time (no row
+        // passes above), so the activations would travel in the register ring, and the
+        // tile groups fill at most a quarter of the CUs: from M = 6 the streaming family
+        // is faster (matrix -> streaming, no workspace: FP8 1024 x 16384 M = 8 36.1 ->
+        // 29.7 us, M = 16 66.1 -> 56.0, M = 6 29.4 -> 28.2; 8-bit 1024 x 16384 M = 8
+        // 38.8 -> 33.1; 4-bit 1024 x 16384 M = 8 36.6 -> 30.9; FP8 512 x 16384 M = 8
+        // 36.0 -> 28.8; at M = 5 the two are even, 26.0 against 26.8). With more tile
+        // groups the matrix family stays ahead (4-bit 2048 x 16384, 128 groups: M = 8
+        // 37.1 against 43.5 us, M = 16 66.7 against 81.2).
+        if (forced == 0 && kp == 1 && !stage && groups * 4 <= cu_count && staged(1).lds > kLdsBytes && M >= 6 &&
+            stream_ok && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON)))
+            return select_plan(d, M, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_STREAM, with_ws, out);
         // without K parts, a persistent grid of at most what fits at once; with them,
         // exactly one workgroup per tile group and part
         int64_t grid = groups * kp;

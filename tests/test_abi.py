@@ -147,7 +147,10 @@ def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
         kw = dict(fmt="fp8", act="f16", N=1024, K=16384, block_size=128, M=M)
         p0, p1 = _sel(**kw), _sel(**kw, with_workspace=True)
         assert p0["kparts"] == 1 and p0["workspace_bytes"] == 0
-        assert p1["family"] == "mfma" and p1["ksplit"] == p0["ksplit"] == 8
+        # without a workspace, from M = 6 the rows (K = 16384) fit in LDS not even 8 at
+        # a time: the streaming family; the matrix family keeps the same K split
+        assert p0["family"] == ("mfma" if M == 5 else "stream"), p0
+        assert p1["family"] == "mfma" and p1["ksplit"] == _sel(**kw, flags=2)["ksplit"] == 8
         assert p1["kparts"] == 4 and p1["grid"] == 64 * 4 and not (p1["variant"] & 2)
         # 64 counters (256 bytes), then the [4, M, N] fp32 partials
         assert p1["workspace_bytes"] == 256 + (4 * M * 1024 * 4 + 255) // 256 * 256
@@ -321,9 +324,15 @@ def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
     # 8-bit 4096 x 8192 (16 K steps per wave): one launch, unstaged
     p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16)
     assert p["passes"] == 1 and not (p["variant"] & 1)
-    # 4-bit 2048 x 16384: 8 rows do not fit either: one launch
-    p = _sel(fmt="u4", act="bf16", N=2048, K=16384, block_size=32, M=16)
-    assert p["passes"] == 1
+    # 4-bit 2048 x 16384: 8 rows do not fit either: one unstaged matrix launch (128 tile
+    # groups: the streaming fallback is for a quarter of the CUs or fewer)
+    kw = dict(fmt="u4", act="bf16", N=2048, K=16384, block_size=32)
+    for M in (6, 16):
+        p = _sel(**kw, M=M)
+        assert p["family"] == "mfma" and p["passes"] == 1 and not (p["variant"] & 1), p
+    # 4-bit 1024 x 16384 (64 tile groups): the streaming family from M = 6
+    kw = dict(fmt="u4", act="f16", N=1024, K=16384, block_size=32)
+    assert [_sel(**kw, M=M)["family"] for M in (5, 6, 16)] == ["mfma", "stream", "stream"]
 
 
 def test_a_workspace_sized_for_sixteen_rows_serves_every_m():
