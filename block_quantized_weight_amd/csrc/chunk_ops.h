@@ -6,17 +6,21 @@
 // 16 k, each with its own scale).
 //
 // Per half the codes are decoded exactly into fp16/bf16 pairs and multiplied into an
-// fp32 sum with v_dot2; the block scale then multiplies that sum, and for the integer
-// formats the zero point enters as -z * sum(a) over the same k:
-//     s * sum_k a_k (q_k - z) = s * (sum_k a_k q_k - z * sum_k a_k)
-// A decode may carry a constant offset Z0 in every code (q + Z0 is what it feeds to
-// v_dot2); the zero point then enters as z + Z0.
-// ("[CUDA] MatMulNBits 8-bit: wide fp16 M=1 kernel", Description: exact (q - zp),
-// scale applied once per chunk to an fp32 partial; "[CUDA] Block-scaled MatMul decode
-// GEMV", FP4 row-tiling paragraph: load, decode and scales shared by the rows).
+// fp32 sum with v_dot2; the block scale then multiplies that sum once:
+//     s * sum_k a_k (q_k - z)
+// For U8 (both activation types) and for U4 with fp16 activations the decode forms
+// (q - z) itself, exactly, so the sum holds only true products ("[CUDA] MatMulNBits
+// 8-bit: wide fp16 M=1 kernel", Description: (q - zp) exact, scale applied once per
+// chunk to an fp32 partial). U4 with bf16 activations decodes the bare codes q (no
+// offset) and takes the zero point as -z * sum(a) over the same k (ASUM): gfx950 has
+// no packed bf16 subtract, and the per-element route through fp32 would triple the
+// decode's instructions. The rounding of that difference then scales with z <= 15,
+// never with an offset added to the codes.
+// ("[CUDA] Block-scaled MatMul decode GEMV", FP4 row-tiling paragraph: load, decode
+// and scales shared by the rows).
 //
-// The activation side of a chunk (pairs in the decode's k order, and sum(a)) is
-// prepared once per row and reused by every column the wave owns.
+// The activation side of a chunk (pairs in the decode's k order, and sum(a) where
+// ASUM) is prepared once per row and reused by every column the wave owns.
 #pragma once
 
 #include "qgemv_device.h"
@@ -24,7 +28,7 @@
 namespace qgemv {
 
 // Activations of one chunk for one row: 16 dwords (32 values) at most, in the order
-// the format's decode pairs them, plus sum(a) per half.
+// the format's decode pairs them, plus sum(a) per half (ASUM formats only).
 struct ChunkAct {
     uint32_t p[16];
     float asum[2];
@@ -44,12 +48,14 @@ __device__ __forceinline__ float sum_pairs(const uint32_t *x, int count) {
 // ----------------------------------------------------------------------------------
 // U4, fp16 activations. Codes become fp16 subnormals: a nibble at bits 0..3 of a half
 // is q * 2^-24, a nibble at bits 4..7 is q * 2^-20 (kept in a second sum that weighs
-// 1/16 against the first when both return to units of 1).
+// 1/16 against the first when both return to units of 1). The zero point, placed the
+// same way, is subtracted from each pair with one packed fp16 op: (q - z) * 2^-24 and
+// (q - z) * 2^-20 are exact subnormals (|q - z| <= 15).
 template <int H>
 struct ChunkOps<FMT_U4, ACT_F16, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;  // activation dwords per chunk
-    static constexpr float Z0 = 0.0f;
+    static constexpr bool ASUM = false;
 
     // x: natural pairs (a0,a1),(a2,a3),...; weight dword d (k = 8d..8d+7) decodes to
     // pairs (k0,k4), (k2,k6) [low nibbles] and (k1,k5), (k3,k7) [high nibbles].
@@ -62,28 +68,26 @@ struct ChunkOps<FMT_U4, ACT_F16, H> {
             h.p[4 * d + 2] = perm(x2, x0, 0x07060302u);  // (a1, a5)
             h.p[4 * d + 3] = perm(x3, x1, 0x07060302u);  // (a3, a7)
         }
-        if constexpr (H == 2) {
-            h.asum[0] = sum_pairs<ACT_F16>(x, 8);
-            h.asum[1] = sum_pairs<ACT_F16>(x + 8, 8);
-        } else {
-            h.asum[0] = sum_pairs<ACT_F16>(x, 16);
-        }
     }
 
-    // decoded operand words of a chunk (exact), shared by every row of a tile
+    // decoded operand words of a chunk (exact q - z), shared by every row of a tile;
+    // z[h]: the integer zero point of half h
     static constexpr int NWD = 16;
-    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+    __device__ static void decode(const u4v &w, const uint32_t z[H], uint32_t wd[16]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
+            const int i = (H == 2) ? (d >> 1) : 0;
+            const uint32_t zl = z[i] | (z[i] << 16);  // (z, z) * 2^-24
+            const uint32_t zh = zl << 4;              // (z, z) * 2^-20
             const uint32_t wv = w[d], w8 = w[d] >> 8;
-            wd[4 * d + 0] = wv & 0x000F000Fu;
-            wd[4 * d + 1] = w8 & 0x000F000Fu;
-            wd[4 * d + 2] = wv & 0x00F000F0u;
-            wd[4 * d + 3] = w8 & 0x00F000F0u;
+            wd[4 * d + 0] = sub_h2(wv & 0x000F000Fu, zl);
+            wd[4 * d + 1] = sub_h2(w8 & 0x000F000Fu, zl);
+            wd[4 * d + 2] = sub_h2(wv & 0x00F000F0u, zh);
+            wd[4 * d + 3] = sub_h2(w8 & 0x00F000F0u, zh);
         }
     }
 
-    // sum_k a_k q_k per half
+    // sum_k a_k (q_k - z) per half
     __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[H]) {
         float lo[H], hi[H];
 #pragma unroll
@@ -101,24 +105,25 @@ struct ChunkOps<FMT_U4, ACT_F16, H> {
     }
 };
 
-// U4, bf16 activations. A nibble q placed in the low mantissa bits of bf16 0x4300
-// (= 128) reads as the exact integer 128 + q, so each dword of codes becomes four
-// bf16 pairs with one shift and one and-or each; the offset 128 joins the zero point.
+// U4, bf16 activations. The low and the high nibbles of a dword are split into
+// bytes (one and, one shift and one and), and the E4M3 converter turns two bytes
+// 0..15 into the exact bf16 integers q: dword d gives pairs (k0,k2), (k4,k6) from the
+// low nibbles and (k1,k3), (k5,k7) from the high ones. No offset is added to q; the
+// zero point enters as -z * sum(a) (ASUM).
 template <int H>
 struct ChunkOps<FMT_U4, ACT_BF16, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;
-    static constexpr float Z0 = 128.0f;
+    static constexpr bool ASUM = true;
 
-    // same pairing as the fp16 decode: (a0,a4), (a2,a6), (a1,a5), (a3,a7) per 8 k
     __device__ static void prep(const uint32_t x[16], ChunkAct &h) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t x0 = x[4 * d], x1 = x[4 * d + 1], x2 = x[4 * d + 2], x3 = x[4 * d + 3];
-            h.p[4 * d + 0] = perm(x2, x0, 0x05040100u);  // (a0, a4)
-            h.p[4 * d + 1] = perm(x3, x1, 0x05040100u);  // (a2, a6)
-            h.p[4 * d + 2] = perm(x2, x0, 0x07060302u);  // (a1, a5)
-            h.p[4 * d + 3] = perm(x3, x1, 0x07060302u);  // (a3, a7)
+            h.p[4 * d + 0] = perm(x1, x0, 0x05040100u);  // (a0, a2)
+            h.p[4 * d + 1] = perm(x3, x2, 0x05040100u);  // (a4, a6)
+            h.p[4 * d + 2] = perm(x1, x0, 0x07060302u);  // (a1, a3)
+            h.p[4 * d + 3] = perm(x3, x2, 0x07060302u);  // (a5, a7)
         }
         if constexpr (H == 2) {
             h.asum[0] = sum_pairs<ACT_BF16>(x, 8);
@@ -129,19 +134,18 @@ struct ChunkOps<FMT_U4, ACT_BF16, H> {
     }
 
     static constexpr int NWD = 16;
-    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
-        constexpr uint32_t MAGIC = 0x43004300u;
+    __device__ static void decode(const u4v &w, const uint32_t *, uint32_t wd[16]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t wv = w[d];
-            wd[4 * d + 0] = and_or(wv, 0x000F000Fu, MAGIC);
-            wd[4 * d + 1] = and_or(wv >> 8, 0x000F000Fu, MAGIC);
-            wd[4 * d + 2] = and_or(wv >> 4, 0x000F000Fu, MAGIC);
-            wd[4 * d + 3] = and_or(wv >> 12, 0x000F000Fu, MAGIC);
+            const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+            wd[4 * d + 0] = small_int_bf16_pair<false>(lo);
+            wd[4 * d + 1] = small_int_bf16_pair<true>(lo);
+            wd[4 * d + 2] = small_int_bf16_pair<false>(hi);
+            wd[4 * d + 3] = small_int_bf16_pair<true>(hi);
         }
     }
 
-    // sum_k a_k (128 + q_k) per half
+    // sum_k a_k q_k per half
     __device__ static void dotd(const uint32_t wd[16], const ChunkAct &h, float out[H]) {
         float s[H];
 #pragma unroll
@@ -158,25 +162,27 @@ struct ChunkOps<FMT_U4, ACT_BF16, H> {
 };
 
 // U8, fp16 activations: bytes become fp16 subnormals q * 2^-24 with one byte permute
-// per pair; pairs keep the natural k order.
+// per pair, and the zero point's pair (z, z) * 2^-24 is subtracted with one packed
+// fp16 op: (q - z) * 2^-24 is an exact subnormal (|q - z| <= 255). Pairs keep the
+// natural k order.
 template <int H>
 struct ChunkOps<FMT_U8, ACT_F16, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
-    static constexpr float Z0 = 0.0f;
+    static constexpr bool ASUM = false;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) h.p[i] = x[i];
-        h.asum[0] = sum_pairs<ACT_F16>(x, 8);
     }
 
     static constexpr int NWD = 8;
-    __device__ static void decode(const u4v &w, uint32_t wd[8]) {
+    __device__ static void decode(const u4v &w, const uint32_t z[H], uint32_t wd[8]) {
+        const uint32_t zz = z[0] | (z[0] << 16);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            wd[2 * d] = perm(0u, w[d], 0x0C010C00u);
-            wd[2 * d + 1] = perm(0u, w[d], 0x0C030C02u);
+            wd[2 * d] = sub_h2(perm(0u, w[d], 0x0C010C00u), zz);
+            wd[2 * d + 1] = sub_h2(perm(0u, w[d], 0x0C030C02u), zz);
         }
     }
 
@@ -188,28 +194,29 @@ struct ChunkOps<FMT_U8, ACT_F16, H> {
     }
 };
 
-// U8, bf16 activations: bytes widened to fp32 and multiplied in fp32.
+// U8, bf16 activations: each byte q becomes the exact fp32 value q - z, multiplied
+// with the widened activation in fp32.
 template <int H>
 struct ChunkOps<FMT_U8, ACT_BF16, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
-    static constexpr float Z0 = 0.0f;
+    static constexpr bool ASUM = false;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) h.p[i] = x[i];
-        h.asum[0] = sum_pairs<ACT_BF16>(x, 8);
     }
 
-    // decoded words: the 16 bytes as float bits
+    // decoded words: the 16 values q - z as float bits
     static constexpr int NWD = 16;
-    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+    __device__ static void decode(const u4v &w, const uint32_t z[H], uint32_t wd[16]) {
+        const float zf = (float)z[0];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            wd[4 * d + 0] = __builtin_bit_cast(uint32_t, (float)(w[d] & 0xFFu));
-            wd[4 * d + 1] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 8) & 0xFFu));
-            wd[4 * d + 2] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 16) & 0xFFu));
-            wd[4 * d + 3] = __builtin_bit_cast(uint32_t, (float)(w[d] >> 24));
+            wd[4 * d + 0] = __builtin_bit_cast(uint32_t, (float)(w[d] & 0xFFu) - zf);
+            wd[4 * d + 1] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 8) & 0xFFu) - zf);
+            wd[4 * d + 2] = __builtin_bit_cast(uint32_t, (float)((w[d] >> 16) & 0xFFu) - zf);
+            wd[4 * d + 3] = __builtin_bit_cast(uint32_t, (float)(w[d] >> 24) - zf);
         }
     }
 
@@ -235,7 +242,7 @@ template <int ACT, int H>
 struct ChunkOps<FMT_FP8, ACT, H> {
     static constexpr int KPC = 16;
     static constexpr int ND = 8;
-    static constexpr float Z0 = 0.0f;
+    static constexpr bool ASUM = false;
 
     __device__ static void prep(const uint32_t x[8], ChunkAct &h) {
 #pragma unroll
@@ -243,7 +250,7 @@ struct ChunkOps<FMT_FP8, ACT, H> {
     }
 
     static constexpr int NWD = 8;
-    __device__ static void decode(const u4v &w, uint32_t wd[8]) {
+    __device__ static void decode(const u4v &w, const uint32_t *, uint32_t wd[8]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             wd[2 * d] = fp8_pair<ACT, false>(w[d]);
@@ -264,7 +271,7 @@ template <int ACT, int H>
 struct ChunkOps<FMT_NVFP4, ACT, H> {
     static constexpr int KPC = 32;
     static constexpr int ND = 16;
-    static constexpr float Z0 = 0.0f;
+    static constexpr bool ASUM = false;
 
     __device__ static void prep(const uint32_t x[16], ChunkAct &h) {
 #pragma unroll
@@ -272,7 +279,7 @@ struct ChunkOps<FMT_NVFP4, ACT, H> {
     }
 
     static constexpr int NWD = 16;
-    __device__ static void decode(const u4v &w, uint32_t wd[16]) {
+    __device__ static void decode(const u4v &w, const uint32_t *, uint32_t wd[16]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             wd[4 * d + 0] = fp4_pair<ACT, 0>(w[d]);
@@ -299,11 +306,20 @@ struct ChunkOps<FMT_NVFP4, ACT, H> {
 // dot products in the format's fixed order. Splitting the two lets a tile of rows
 // share one decode without changing any row's arithmetic.
 template <int FMT, int ACT, int H>
-__device__ __forceinline__ void chunk_dot(const u4v &w, const ChunkAct &h, float out[H]) {
+__device__ __forceinline__ void chunk_dot(const u4v &w, const uint32_t z[H], const ChunkAct &h, float out[H]) {
     using Ops = ChunkOps<FMT, ACT, H>;
     uint32_t wd[Ops::NWD];
-    Ops::decode(w, wd);
+    Ops::decode(w, z, wd);
     Ops::dotd(wd, h, out);
+}
+
+// The block sum of half h in the accumulator: acc + s * (part - z * sum(a)) for the
+// ASUM format, acc + s * part for the others (whose part already holds q - z).
+template <bool ASUM>
+__device__ __forceinline__ float block_acc(float acc, float s, float part, uint32_t z, float asum) {
+    float v = part;
+    if constexpr (ASUM) v = __builtin_fmaf(-(float)z, asum, v);
+    return __builtin_fmaf(s, v, acc);
 }
 
 // ----------------------------------------------------------------------------------
@@ -367,40 +383,38 @@ __device__ __forceinline__ void meta_load_s(const KArgs &a, const ColPtrs &p, in
     }
 }
 
-// Scale and zero point (plus the decode's offset Z0) of each half of chunk c; zs is
-// zsel(a.zp, midpoint byte) (0x88 for U4, 128 for U8).
+// Scale and integer zero point of each half of chunk c; zs is zsel(a.zp, midpoint
+// byte) (0x88 for U4, 128 for U8), so a weight without zero points takes the midpoint.
 template <int FMT, int H>
-__device__ __forceinline__ void meta_decode_s(const KArgs &a, int c, const MetaS<H> &m, float z0, ZSel zs,
-                                              float sc[H], float zr[H]) {
+__device__ __forceinline__ void meta_decode_s(const KArgs &a, int c, const MetaS<H> &m, ZSel zs, float sc[H],
+                                              uint32_t zr[H]) {
     if constexpr (FMT == FMT_U4) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             const int b = chunk_block<FMT>(a, c, h);
             sc[h] = half_bits_to_float((uint16_t)m.s[h]);
             const uint32_t zb = (m.z[h] & zs.keep) | zs.fill;
-            const uint32_t z = (b & 1) ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu);
-            zr[h] = (float)z + z0;
+            zr[h] = (b & 1) ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu);
         }
     } else if constexpr (FMT == FMT_U8) {
         sc[0] = half_bits_to_float((uint16_t)m.s[0]);
-        zr[0] = (float)(((m.z[0] & zs.keep) | zs.fill) & 0xFFu) + z0;
+        zr[0] = ((m.z[0] & zs.keep) | zs.fill) & 0xFFu;
     } else if constexpr (FMT == FMT_FP8) {
         sc[0] = __builtin_bit_cast(float, m.s[0]);
-        zr[0] = 0.0f;
+        zr[0] = 0u;
     } else {
         sc[0] = e4m3_to_float(m.s[0] & 0xFFu);
         sc[1] = e4m3_to_float((m.s[0] >> 8) & 0xFFu);
-        zr[0] = zr[1] = 0.0f;
+        zr[0] = zr[1] = 0u;
     }
 }
 
-// Scale and zero point of each of the H halves of chunk c, loaded and decoded.
+// Scale and integer zero point of each of the H halves of chunk c, loaded and decoded.
 template <int FMT, int H>
-__device__ __forceinline__ void chunk_meta(const KArgs &a, const ColPtrs &p, int c, float z0, float sc[H],
-                                           float zr[H]) {
+__device__ __forceinline__ void chunk_meta(const KArgs &a, const ColPtrs &p, int c, float sc[H], uint32_t zr[H]) {
     MetaS<H> m;
     meta_load_s<FMT, H>(a, p, c, m);
-    meta_decode_s<FMT, H>(a, c, m, z0, zsel(a.zp, FMT == FMT_U4 ? 0x88u : 128u), sc, zr);
+    meta_decode_s<FMT, H>(a, c, m, zsel(a.zp, FMT == FMT_U4 ? 0x88u : 128u), sc, zr);
 }
 
 }  // namespace qgemv

@@ -16,9 +16,14 @@
 //    two scale blocks (the reason the pages fold the NVFP4 scale into the weight).
 //  - Rows of A travel in groups of four. M rows take ceil(M/4) groups, each with the
 //    same arithmetic, so a row's result never depends on M or on its group.
-//  - Zero points: codes enter the MFMA as M0 + q (an exact fp16/bf16 integer built
-//    with two bit operations) and sum(a) over the chunk comes from one more MFMA
-//    against a ones operand; the epilogue forms s * (D - (M0 + z) * sum(a)).
+//  - Zero points: with fp16 activations the codes enter the MFMA as the exact fp16
+//    integers q - z (1024 + q and 1024 + z built with bit operations, subtracted with
+//    one packed fp16 op), as the pages form (q - zp) exactly before the mma ("[CUDA]
+//    MatMulNBits 8-bit: wide fp16 M=1 kernel", Description). With bf16 activations,
+//    8-bit codes form q - z exactly in fp32 and round the pair to bf16 (exact); 4-bit
+//    codes enter as the bare bf16 integers q (E4M3 converter, no offset) and sum(a)
+//    over the chunk comes from one more MFMA against a ones operand, the epilogue
+//    forming s * (D - z * sum(a)) (gfx950 has no packed bf16 subtract).
 //  - K split: ksplit waves of a workgroup take strided K steps of the same column
 //    tile and reduce through LDS in fixed wave order ("[CUDA] Block-scaled MatMul
 //    decode GEMV", FP8 mma paragraph: KSplit warps per block reduce through shared
@@ -45,42 +50,69 @@ __device__ __forceinline__ f4 mfma(op4 a, op4 b, f4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
 
-// Integer offset carried by 4-bit codes in the MFMA: fp16 0x6400|q = 1024 + q,
-// bf16 0x4300|q = 128 + q.
-template <int ACT> struct U4Magic;
-template <> struct U4Magic<ACT_F16> { static constexpr uint32_t bits = 0x64006400u; static constexpr float off = 1024.0f; };
-template <> struct U4Magic<ACT_BF16> { static constexpr uint32_t bits = 0x43004300u; static constexpr float off = 128.0f; };
-
 // Per-format description of one 16-byte chunk in the MFMA family.
 //   MF   : MFMAs per chunk (8 k per lane each)
-//   EPI  : epilogues per chunk (one per scale block the chunk touches)
-//   PERM : activations need the U4 slot order [0,4,1,5,2,6,3,7] within each 8
 template <int FMT> struct MfFmt;
-template <> struct MfFmt<FMT_U4> { static constexpr int KPC = 32, MF = 4, PERM = 1, ZP = 1; };
-template <> struct MfFmt<FMT_U8> { static constexpr int KPC = 16, MF = 2, PERM = 0, ZP = 1; };
-template <> struct MfFmt<FMT_FP8> { static constexpr int KPC = 16, MF = 2, PERM = 0, ZP = 0; };
-template <> struct MfFmt<FMT_NVFP4> { static constexpr int KPC = 32, MF = 4, PERM = 0, ZP = 0; };
+template <> struct MfFmt<FMT_U4> { static constexpr int KPC = 32, MF = 4; };
+template <> struct MfFmt<FMT_U8> { static constexpr int KPC = 16, MF = 2; };
+template <> struct MfFmt<FMT_FP8> { static constexpr int KPC = 16, MF = 2; };
+template <> struct MfFmt<FMT_NVFP4> { static constexpr int KPC = 32, MF = 4; };
 
-// B operand (8 weight values) of MFMA j from the chunk's 4 code dwords.
+// Per (format, activation type):
+//   ASUM : the zero point enters as -z * sum(a) (4-bit codes on bf16); the other
+//          formats with zero points form q - z in the decode
+//   PERM : slot order of the 8 activations of one MFMA: 0 natural; 1 = [0,4,1,5,2,6,3,7]
+//          (4-bit codes on fp16); 2 = [0,2,4,6,1,3,5,7] (4-bit codes on bf16)
+template <int FMT, int ACT> struct MfAct {
+    static constexpr bool ASUM = FMT == FMT_U4 && ACT == ACT_BF16;
+    static constexpr int PERM = FMT == FMT_U4 ? (ACT == ACT_F16 ? 1 : 2) : 0;
+};
+
+// The zero-point operand of a chunk half the decode subtracts, from the integer z:
+// fp16 (1024 + z, 1024 + z) for codes on fp16, fp32 z for 8-bit codes on bf16.
+template <int FMT, int ACT>
+__device__ __forceinline__ uint32_t zero_word(uint32_t z) {
+    if constexpr (ACT == ACT_F16) return (0x6400u | z) * 0x00010001u;
+    else return __builtin_bit_cast(uint32_t, (float)z);
+}
+
+// B operand (8 weight values) of MFMA j from the chunk's 4 code dwords; zw: the
+// zero-point operand (zero_word) of the chunk half MFMA j lies in.
 template <int FMT, int ACT, int J>
-__device__ __forceinline__ op4 decode_b(const u4v &w) {
+__device__ __forceinline__ op4 decode_b(const u4v &w, uint32_t zw) {
     op4 r;
-    if constexpr (FMT == FMT_U4) {
-        // dword J holds k = 8J..8J+7: slots (k0,k4),(k1,k5),(k2,k6),(k3,k7)
+    if constexpr (FMT == FMT_U4 && ACT == ACT_F16) {
+        // dword J holds k = 8J..8J+7: slots (k0,k4),(k1,k5),(k2,k6),(k3,k7) as the
+        // fp16 integers 1024 + q, minus (1024 + z): exactly q - z
         const uint32_t x = w[J];
-        constexpr uint32_t M = U4Magic<ACT>::bits;
-        r.x = and_or(x, 0x000F000Fu, M);
-        r.y = and_or(x >> 4, 0x000F000Fu, M);
-        r.z = and_or(x >> 8, 0x000F000Fu, M);
-        r.w = and_or(x >> 12, 0x000F000Fu, M);
-    } else if constexpr (FMT == FMT_U8) {
-        // dwords 2J, 2J+1 hold k = 8J..8J+7 in natural order; (1024 + q) as fp16
+        r.x = sub_h2(and_or(x, 0x000F000Fu, 0x64006400u), zw);
+        r.y = sub_h2(and_or(x >> 4, 0x000F000Fu, 0x64006400u), zw);
+        r.z = sub_h2(and_or(x >> 8, 0x000F000Fu, 0x64006400u), zw);
+        r.w = sub_h2(and_or(x >> 12, 0x000F000Fu, 0x64006400u), zw);
+    } else if constexpr (FMT == FMT_U4) {
+        // bf16: the bare integers q from the E4M3 converter, slots (k0,k2),(k4,k6) from
+        // the low nibbles and (k1,k3),(k5,k7) from the high ones
+        const uint32_t lo = w[J] & 0x0F0F0F0Fu, hi = (w[J] >> 4) & 0x0F0F0F0Fu;
+        r.x = small_int_bf16_pair<false>(lo);
+        r.y = small_int_bf16_pair<true>(lo);
+        r.z = small_int_bf16_pair<false>(hi);
+        r.w = small_int_bf16_pair<true>(hi);
+    } else if constexpr (FMT == FMT_U8 && ACT == ACT_F16) {
+        // dwords 2J, 2J+1 hold k = 8J..8J+7 in natural order; (1024 + q) - (1024 + z)
         constexpr uint32_t MB = 0x64646464u;
         const uint32_t x0 = w[2 * J], x1 = w[2 * J + 1];
-        r.x = perm(MB, x0, 0x04010400u);
-        r.y = perm(MB, x0, 0x04030402u);
-        r.z = perm(MB, x1, 0x04010400u);
-        r.w = perm(MB, x1, 0x04030402u);
+        r.x = sub_h2(perm(MB, x0, 0x04010400u), zw);
+        r.y = sub_h2(perm(MB, x0, 0x04030402u), zw);
+        r.z = sub_h2(perm(MB, x1, 0x04010400u), zw);
+        r.w = sub_h2(perm(MB, x1, 0x04030402u), zw);
+    } else if constexpr (FMT == FMT_U8) {
+        // bf16: q - z formed in fp32 (exact), rounded to bf16 pairs (exact)
+        const float z = __builtin_bit_cast(float, zw);
+        const uint32_t x0 = w[2 * J], x1 = w[2 * J + 1];
+        r.x = u8_diff_bf16_pair<0>(x0, z);
+        r.y = u8_diff_bf16_pair<2>(x0, z);
+        r.z = u8_diff_bf16_pair<0>(x1, z);
+        r.w = u8_diff_bf16_pair<2>(x1, z);
     } else if constexpr (FMT == FMT_FP8) {
         const uint32_t x0 = w[2 * J], x1 = w[2 * J + 1];
         r.x = fp8_pair<ACT, false>(x0);
@@ -97,34 +129,48 @@ __device__ __forceinline__ op4 decode_b(const u4v &w) {
     return r;
 }
 
+// 8 activations (4 natural pairs) in the MFMA slot order PERM of MfAct.
+template <int PERM>
+__device__ __forceinline__ u4v slot_order(const u4v &v) {
+    u4v o;
+    if constexpr (PERM == 1) {
+        o.x = perm(v.z, v.x, 0x05040100u);  // (a0, a4)
+        o.y = perm(v.z, v.x, 0x07060302u);  // (a1, a5)
+        o.z = perm(v.w, v.y, 0x05040100u);  // (a2, a6)
+        o.w = perm(v.w, v.y, 0x07060302u);  // (a3, a7)
+    } else if constexpr (PERM == 2) {
+        o.x = perm(v.y, v.x, 0x05040100u);  // (a0, a2)
+        o.y = perm(v.w, v.z, 0x05040100u);  // (a4, a6)
+        o.z = perm(v.y, v.x, 0x07060302u);  // (a1, a3)
+        o.w = perm(v.w, v.z, 0x07060302u);  // (a5, a7)
+    } else {
+        o = v;
+    }
+    return o;
+}
+
 // A operand of MFMA j for row group rg: lane (i, gs) with i>>2 == gs holds row
 // 4*rg + (i&3) over the 8 k the weights of chunk 4t+gs use in MFMA j; zero elsewhere.
-template <int FMT>
+template <int FMT, int ACT>
 __device__ __forceinline__ op4 load_a(const uint16_t *arow, bool live, uint32_t k0) {
     op4 r = {0u, 0u, 0u, 0u};
     if (live) {
-        const u4v v = load16(arow + k0);
-        if constexpr (MfFmt<FMT>::PERM) {
-            r.x = perm(v.z, v.x, 0x05040100u);  // (a0, a4)
-            r.y = perm(v.z, v.x, 0x07060302u);  // (a1, a5)
-            r.z = perm(v.w, v.y, 0x05040100u);  // (a2, a6)
-            r.w = perm(v.w, v.y, 0x07060302u);  // (a3, a7)
-        } else {
-            r.x = v.x; r.y = v.y; r.z = v.z; r.w = v.w;
-        }
+        const u4v v = slot_order<MfAct<FMT, ACT>::PERM>(load16(arow + k0));
+        r.x = v.x; r.y = v.y; r.z = v.z; r.w = v.w;
     }
     return r;
 }
 
 // Block metadata of one chunk kept raw while it waits in the prefetch ring: the
 // loaded values as they are (nothing is computed from a load until the chunk is
-// consumed, so a prefetch never waits for its own data), decoded by meta_values.
+// consumed, so a prefetch never waits for its own data), decoded by meta_scale and
+// meta_zero.
 //   U4, one block per chunk : v0 = fp16 scale bits, v1 = the zero-point byte holding the block
 //   U4, two blocks per chunk: v0 = both fp16 scales, v1 = the zero-point byte of the pair
 //   U8                      : v0 = fp16 scale bits, v1 = zero-point byte
 //   FP8                     : v0 = fp32 scale bits
 //   NVFP4                   : v0 = the two E4M3 scale bytes
-// (without zero points v1 holds whatever the aliased address held; meta_values then
+// (without zero points v1 holds whatever the aliased address held; meta_zero then
 // uses the midpoint, 8 for U4 and 128 for U8)
 template <int H>
 struct MetaRaw {
@@ -178,32 +224,51 @@ __device__ __forceinline__ MetaRaw<H> load_meta_raw(const KArgs &a, const MfCol 
     return m;
 }
 
-// Scale and (M0 + zero point) of half h of a chunk from its raw metadata (v0, v1 as
-// MetaRaw holds them). zsh is the bit position of the chunk's zero-point nibble in v1
-// for 4-bit codes with one block per chunk (4 for an odd block index, else 0).
-template <int FMT, int ACT, int H>
-__device__ __forceinline__ void meta_values(const KArgs &a, uint32_t v0, uint32_t v1, int zsh, int h, float &s,
-                                            float &zoff) {
+// Scale of half h of a chunk from its raw metadata word v0 (as MetaRaw holds it).
+template <int FMT, int H>
+__device__ __forceinline__ float meta_scale(uint32_t v0, int h) {
+    if constexpr (FMT == FMT_U4) {
+        if constexpr (H == 1) return half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
+        else return half_bits_to_float((uint16_t)(h ? (v0 >> 16) : (v0 & 0xFFFFu)));
+    } else if constexpr (FMT == FMT_U8) {
+        return half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
+    } else if constexpr (FMT == FMT_FP8) {
+        return __builtin_bit_cast(float, v0);
+    } else {
+        return e4m3_to_float(h ? ((v0 >> 8) & 0xFFu) : (v0 & 0xFFu));
+    }
+}
+
+// Integer zero point of half h of a chunk from its raw zero-point word v1 (the
+// midpoint when the weight has none; 0 for the formats without). zsh is the bit
+// position of the chunk's zero-point nibble in v1 for 4-bit codes with one block per
+// chunk (4 for an odd block index, else 0).
+template <int FMT, int H>
+__device__ __forceinline__ uint32_t meta_zero(const KArgs &a, uint32_t v1, int zsh, int h) {
     if constexpr (FMT == FMT_U4) {
         const ZSel zs = zsel(a.zp, 0x88u);
         const uint32_t zb = (v1 & zs.keep) | zs.fill;
-        if constexpr (H == 1) {
-            s = half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
-            zoff = U4Magic<ACT>::off + (float)((zb >> zsh) & 0x0Fu);
-        } else {
-            s = half_bits_to_float((uint16_t)(h ? (v0 >> 16) : (v0 & 0xFFFFu)));
-            zoff = U4Magic<ACT>::off + (float)(h ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu));
-        }
+        if constexpr (H == 1) return (zb >> zsh) & 0x0Fu;
+        else return h ? ((zb >> 4) & 0x0Fu) : (zb & 0x0Fu);
     } else if constexpr (FMT == FMT_U8) {
         const ZSel zs = zsel(a.zp, 128u);
-        s = half_bits_to_float((uint16_t)(v0 & 0xFFFFu));
-        zoff = 1024.0f + (float)(((v1 & zs.keep) | zs.fill) & 0xFFu);
-    } else if constexpr (FMT == FMT_FP8) {
-        s = __builtin_bit_cast(float, v0);
-        zoff = 0.0f;
+        return ((v1 & zs.keep) | zs.fill) & 0xFFu;
     } else {
-        s = e4m3_to_float(h ? ((v0 >> 8) & 0xFFu) : (v0 & 0xFFu));
-        zoff = 0.0f;
+        return 0u;
+    }
+}
+
+// The B operands of every MFMA of a chunk, decoded with their half's zero point.
+template <int FMT, int ACT, int H>
+__device__ __forceinline__ void decode_chunk(const u4v &w, const uint32_t (&z)[H], op4 (&bv)[MfFmt<FMT>::MF]) {
+    // MFMAs 0 .. MF/2 - 1 lie in half 0, the rest in half H - 1
+    const uint32_t z0 = zero_word<FMT, ACT>(z[0]);
+    const uint32_t z1 = H == 2 ? zero_word<FMT, ACT>(z[H - 1]) : z0;
+    bv[0] = decode_b<FMT, ACT, 0>(w, z0);
+    bv[1] = decode_b<FMT, ACT, 1>(w, MfFmt<FMT>::MF == 4 ? z0 : z1);
+    if constexpr (MfFmt<FMT>::MF == 4) {
+        bv[2] = decode_b<FMT, ACT, 2>(w, z1);
+        bv[3] = decode_b<FMT, ACT, 3>(w, z1);
     }
 }
 
@@ -212,14 +277,15 @@ __device__ __forceinline__ int u4_zshift(const KArgs &a, int c) {
     return (((c << 5) >> a.bs_shift) & 1) << 2;
 }
 
-// One output group's epilogue: acc += s * (d - zoff * sa) (the zero-point term only
-// for formats with zero points). Shared by every matrix-family kernel.
-template <bool ZP>
-__device__ __forceinline__ void epilogue(const f4 &d, const f4 &sa, float sc, float zoff, f4 &acc) {
+// One output group's epilogue: acc += s * (d - z * sa) (the zero-point term only for
+// the ASUM format; the others hold q - z in d already). Shared by every
+// matrix-family kernel.
+template <bool ASUM>
+__device__ __forceinline__ void epilogue(const f4 &d, const f4 &sa, float sc, uint32_t z, f4 &acc) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float v = d[r];
-        if constexpr (ZP) v = __builtin_fmaf(-zoff, sa[r], v);
+        if constexpr (ASUM) v = __builtin_fmaf(-(float)z, sa[r], v);
         acc[r] = __builtin_fmaf(sc, v, acc[r]);
     }
 }
@@ -241,17 +307,17 @@ constexpr int kAPad = 8;
 
 // LDS layout of the kernels that stage the activations: a 64-byte zero block (the A
 // operand of lanes off the block diagonal, MF reads of 16 bytes), the staged rows,
-// then for formats with zero points the per-chunk activation sums (f4 entries indexed
-// (chunk * RG + row group) * H + half), then the kernel's own area.
+// then for the ASUM format (4-bit codes on bf16) the per-chunk activation sums (f4
+// entries indexed (chunk * RG + row group) * H + half), then the kernel's own area.
 constexpr int kZeroBytes = 64;
 
 __device__ __forceinline__ size_t staged_rows_bytes(const KArgs &a, int astride) {
     return ((size_t)a.M * astride * 2 + 15) & ~(size_t)15;
 }
 
-template <int FMT, int RG, int H>
+template <int FMT, int ACT, int RG, int H>
 __device__ __forceinline__ size_t sums_bytes(size_t nch) {
-    return MfFmt<FMT>::ZP ? nch * RG * H * 16 : 0;
+    return MfAct<FMT, ACT>::ASUM ? nch * RG * H * 16 : 0;
 }
 
 // One wave owns the 16 columns of a tile for one K slice. A workgroup of nw waves
@@ -271,7 +337,7 @@ struct AOps {
 // Every lane loads (rows past M read row M - 1); lanes off the block diagonal or past
 // M are zeroed when the operands are used (mfma_step), so the loads themselves are
 // unconditional.
-template <int FMT, int RG>
+template <int FMT, int ACT, int RG>
 __device__ __forceinline__ void load_a_ops(const KArgs &a, int c, int ar, AOps<FMT, RG> &o) {
     using F = MfFmt<FMT>;
     const uint16_t *A16 = (const uint16_t *)a.A;
@@ -281,7 +347,7 @@ __device__ __forceinline__ void load_a_ops(const KArgs &a, int c, int ar, AOps<F
         const int row = 4 * rg + ar;
         const uint16_t *arow = A16 + (int64_t)(row < a.M ? row : a.M - 1) * a.K;
 #pragma unroll
-        for (int j = 0; j < F::MF; ++j) o.v[rg][j] = load_a<FMT>(arow, true, kbase + 8 * j);
+        for (int j = 0; j < F::MF; ++j) o.v[rg][j] = load_a<FMT, ACT>(arow, true, kbase + 8 * j);
     }
 }
 
@@ -310,22 +376,19 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
                                           const f4 *sSum, int astride, int cbase, const AOps<FMT, RG> &areg,
                                           bool valid, f4 acc[RG]) {
     using F = MfFmt<FMT>;
-    // with one row group the B operands are decoded right before their MFMA; with
-    // more they are decoded once and shared by the groups
-    op4 bv[RG == 1 ? 1 : F::MF];
-    if constexpr (RG > 1) {
-        bv[0] = decode_b<FMT, ACT, 0>(w);
-        bv[1] = decode_b<FMT, ACT, 1>(w);
-        if constexpr (F::MF == 4) {
-            bv[2] = decode_b<FMT, ACT, 2>(w);
-            bv[3] = decode_b<FMT, ACT, 3>(w);
-        }
-    }
+    constexpr bool ASUM = MfAct<FMT, ACT>::ASUM;
     // A discarded step (past K, or a tile past N, both on clamped valid addresses)
     // gets a zero scale: it adds 0 * (a finite value) to the accumulators, which
     // leaves them as they are, with one select per step instead of one per element.
     const uint32_t v0 = valid ? m.v[0] : 0u;
     const int zsh = (FMT == FMT_U4 && H == 1) ? u4_zshift(a, c) : 0;
+    uint32_t zq[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) zq[h] = meta_zero<FMT, H>(a, m.v[1], zsh, h);
+    // with one row group the B operands are decoded right before their MFMA; with
+    // more they are decoded once and shared by the groups
+    op4 bv[F::MF];
+    if constexpr (RG > 1) decode_chunk<FMT, ACT, H>(w, zq, bv);
     const uint32_t kbase = (uint32_t)(c - cbase) * F::KPC;  // within the staged K range
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -341,7 +404,7 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             const uint16_t *abase = live ? sA + row * astride + kbase : sZero;
 #pragma unroll
             for (int j = 0; j < F::MF; ++j) avs[j] = *(const op4 *)(abase + 8 * j);
-            if constexpr (F::ZP) {
+            if constexpr (ASUM) {
 #pragma unroll
                 for (int h = 0; h < H; ++h) sa[h] = sSum[((size_t)(c - cbase) * RG + rg) * H + h];
             }
@@ -349,28 +412,25 @@ __device__ __forceinline__ void mfma_step(const KArgs &a, const u4v &w, const Me
             const op4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < F::MF; ++j) avs[j] = live ? areg.v[rg][j] : z;
-            if constexpr (F::ZP) chunk_sums<FMT, ACT, H>(avs, sa);
+            if constexpr (ASUM) chunk_sums<FMT, ACT, H>(avs, sa);
         }
 #pragma unroll
         for (int j = 0; j < F::MF; ++j) {
             const int h = (H == 2) ? (j / (F::MF / 2)) : 0;
             op4 b;
             if constexpr (RG == 1) {
-                if (j == 0) b = decode_b<FMT, ACT, 0>(w);
-                else if (j == 1) b = decode_b<FMT, ACT, 1>(w);
-                else if (j == 2) b = decode_b<FMT, ACT, (F::MF == 4 ? 2 : 0)>(w);
-                else b = decode_b<FMT, ACT, (F::MF == 4 ? 3 : 0)>(w);
+                const uint32_t zw = zero_word<FMT, ACT>(zq[h]);
+                if (j == 0) b = decode_b<FMT, ACT, 0>(w, zw);
+                else if (j == 1) b = decode_b<FMT, ACT, 1>(w, zw);
+                else if (j == 2) b = decode_b<FMT, ACT, (F::MF == 4 ? 2 : 0)>(w, zw);
+                else b = decode_b<FMT, ACT, (F::MF == 4 ? 3 : 0)>(w, zw);
             } else {
                 b = bv[j];
             }
             d[h] = mfma<ACT>(avs[j], b, d[h]);
         }
 #pragma unroll
-        for (int h = 0; h < H; ++h) {
-            float sc, zoff;
-            meta_values<FMT, ACT, H>(a, v0, m.v[1], zsh, h, sc, zoff);
-            epilogue<F::ZP>(d[h], sa[h], sc, zoff, acc[rg]);
-        }
+        for (int h = 0; h < H; ++h) epilogue<ASUM>(d[h], sa[h], meta_scale<FMT, H>(v0, h), zq[h], acc[rg]);
     }
 }
 
@@ -438,7 +498,7 @@ template <int FMT, int H>
 __device__ __forceinline__ MetaRaw<H> meta_to_mfma_lanes(const MetaRaw<H> &m, int src_byte) {
     MetaRaw<H> o;
     o.v[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)m.v[0]);
-    o.v[1] = MfFmt<FMT>::ZP ? (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)m.v[1]) : 0u;
+    o.v[1] = (FMT == FMT_U4 || FMT == FMT_U8) ? (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)m.v[1]) : 0u;
     return o;
 }
 
@@ -447,7 +507,7 @@ __device__ __forceinline__ MetaRaw<H> meta_to_mfma_lanes(const MetaRaw<H> &m, in
 // thread handles 16-byte pieces it, it + blockDim, ... in batches of SB whose loads
 // are all issued before the first store, so the staging costs about one load latency
 // per batch, not one per piece.
-template <int FMT, int SB = 8>
+template <int FMT, int ACT, int SB = 8>
 __device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astride, int k0, int klen) {
     using F = MfFmt<FMT>;
     const uint16_t *A16 = (const uint16_t *)a.A + k0;
@@ -470,16 +530,7 @@ __device__ __forceinline__ void stage_a(const KArgs &a, uint16_t *sA, int astrid
             if (it < items) {
                 const int m = it / k8n;
                 const int k8 = (it - m * k8n) << 3;
-                u4v o;
-                if constexpr (F::PERM) {
-                    o.x = perm(v[j].z, v[j].x, 0x05040100u);  // (a0, a4)
-                    o.y = perm(v[j].z, v[j].x, 0x07060302u);  // (a1, a5)
-                    o.z = perm(v[j].w, v[j].y, 0x05040100u);  // (a2, a6)
-                    o.w = perm(v[j].w, v[j].y, 0x07060302u);  // (a3, a7)
-                } else {
-                    o = v[j];
-                }
-                *(u4v *)(sA + m * astride + k8) = o;
+                *(u4v *)(sA + m * astride + k8) = slot_order<MfAct<FMT, ACT>::PERM>(v[j]);
             }
         }
     }
@@ -668,7 +719,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
     const size_t rows_b = LDSA ? staged_rows_bytes(a, astride) : 0;
     f4 *sSum = (f4 *)(smem + kZeroBytes + rows_b);
-    const size_t abytes = LDSA ? kZeroBytes + rows_b + sums_bytes<FMT, RG, H>((size_t)4 * smax) : 0;
+    const size_t abytes = LDSA ? kZeroBytes + rows_b + sums_bytes<FMT, ACT, RG, H>((size_t)4 * smax) : 0;
     const size_t red_b = ks > 1 ? (size_t)NW * RG * 4 * 64 * 4 : 0;
     const bool red_alias = LDSA && ks > 1 && (KP || gdim >= ngroups);
     float *sR = (float *)(red_alias ? smem : smem + abytes);
@@ -694,7 +745,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         const int c = c4 + g;
         wb[p] = load16_stream(col.w + (uint32_t)(c4 + (lane & 3)) * 16u);
         mb[p] = load_meta_raw<FMT, H>(a, col, c4 + (lane & 3));
-        if constexpr (!LDSA) load_a_ops<FMT, RG>(a, c, ar, ab[p]);
+        if constexpr (!LDSA) load_a_ops<FMT, ACT, RG>(a, c, ar, ab[p]);
         if (++is == S) {
             is = 0;
             itg += gdim;
@@ -706,9 +757,9 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
 
     if constexpr (LDSA) {
         if (threadIdx.x < kZeroBytes / 16) ((u4v *)sZero)[threadIdx.x] = u4v{0u, 0u, 0u, 0u};
-        stage_a<FMT>(a, sA, astride, cbase * MfFmt<FMT>::KPC, nsteps * 4 * MfFmt<FMT>::KPC);
+        stage_a<FMT, ACT>(a, sA, astride, cbase * MfFmt<FMT>::KPC, nsteps * 4 * MfFmt<FMT>::KPC);
         __syncthreads();
-        if constexpr (MfFmt<FMT>::ZP) {
+        if constexpr (MfAct<FMT, ACT>::ASUM) {
             stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum, nsteps);
             __syncthreads();
         }
@@ -819,7 +870,8 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     const int64_t gw = (int64_t)blockIdx.x * NW + wave;
     const int64_t mytiles = gw < ntiles ? (ntiles - gw + nw - 1) / nw : 0;
     const int64_t total = mytiles * nslots;
-    const size_t abytes = kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, RG, H>((size_t)a.nchunks);
+    constexpr bool ASUM = MfAct<FMT, ACT>::ASUM;
+    const size_t abytes = kZeroBytes + staged_rows_bytes(a, astride) + sums_bytes<FMT, ACT, RG, H>((size_t)a.nchunks);
     uint16_t *sZero = (uint16_t *)smem;
     uint16_t *sA = (uint16_t *)(smem + kZeroBytes);
     f4 *sSum = (f4 *)(smem + kZeroBytes + staged_rows_bytes(a, astride));
@@ -931,9 +983,9 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 #pragma unroll
     for (int r = 0; r < R - 1; ++r)
         if (r < total) issue();
-    stage_a<FMT, 4>(a, sA, astride, 0, (int)a.K);
+    stage_a<FMT, ACT, 4>(a, sA, astride, 0, (int)a.K);
     __syncthreads();
-    if constexpr (F::ZP) {
+    if constexpr (ASUM) {
         stage_sums<FMT, ACT, RG, H>(a, sA, sZero, astride, sSum, nch >> 2);
         __syncthreads();
     }
@@ -997,7 +1049,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) read_a(kc, rg, o.av[rg]);
         }
-        if constexpr (F::ZP) {
+        if constexpr (ASUM) {
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -1010,16 +1062,15 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
     for (int r = 0; r < RG; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](const In &o, int st, bool valid) {
         const uint32_t v0 = valid ? o.sv : 0u;
-        op4 bv[F::MF];
-        bv[0] = decode_b<FMT, ACT, 0>(o.w);
-        bv[1] = decode_b<FMT, ACT, 1>(o.w);
-        if constexpr (F::MF == 4) {
-            bv[2] = decode_b<FMT, ACT, 2>(o.w);
-            bv[3] = decode_b<FMT, ACT, 3>(o.w);
-        }
-        float sc[H], zo[H];
+        float sc[H];
+        uint32_t zq[H];
 #pragma unroll
-        for (int h = 0; h < H; ++h) meta_values<FMT, ACT, H>(a, v0, o.zv, zsh[st], h, sc[h], zo[h]);
+        for (int h = 0; h < H; ++h) {
+            sc[h] = meta_scale<FMT, H>(v0, h);
+            zq[h] = meta_zero<FMT, H>(a, o.zv, zsh[st], h);
+        }
+        op4 bv[F::MF];
+        decode_chunk<FMT, ACT, H>(o.w, zq, bv);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             f4 d[H];
@@ -1035,7 +1086,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 #pragma unroll
             for (int h = 0; h < H; ++h) {
                 const f4 z4 = {0.f, 0.f, 0.f, 0.f};
-                epilogue<F::ZP>(d[h], F::ZP ? o.sa[rg][h] : z4, sc[h], zo[h], acc[rg]);
+                epilogue<ASUM>(d[h], ASUM ? o.sa[rg][h] : z4, sc[h], zq[h], acc[rg]);
             }
         }
     };
@@ -1189,9 +1240,7 @@ hipError_t pick_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 hipError_t launch_mfma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     switch (cfg.fmt) {
     case FMT_U4: return pick_act<FMT_U4>(cfg, a, s);
-    case FMT_U8:
-        if (cfg.act != ACT_F16) return hipErrorInvalidValue;  // 8-bit codes plus an offset exceed bf16's integers
-        return pick_h<FMT_U8, ACT_F16>(cfg, a, s);
+    case FMT_U8: return pick_act<FMT_U8>(cfg, a, s);
     case FMT_FP8: return pick_act<FMT_FP8>(cfg, a, s);
     case FMT_NVFP4: return pick_act<FMT_NVFP4>(cfg, a, s);
     default: return hipErrorInvalidValue;

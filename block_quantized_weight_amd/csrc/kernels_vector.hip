@@ -25,7 +25,6 @@ namespace qgemv {
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
 __global__ void __launch_bounds__(256) k_stream(KArgs a) {
     using Ops = ChunkOps<FMT, ACT, H>;
-    constexpr bool ZP = (FMT == FMT_U4 || FMT == FMT_U8);
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t nbase = wave * CPW;
@@ -52,7 +51,8 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 
         for (int base = 0; base < nch; base += 64 * UNR) {
             u4v w[UNR][CPW];
-            float sc[UNR][CPW][H], zr[UNR][CPW][H];
+            float sc[UNR][CPW][H];
+            uint32_t zr[UNR][CPW][H];
             bool valid[UNR];
             // all weight loads of this round first, then the block metadata
 #pragma unroll
@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
                 const int c = base + 64 * u + lane;
                 if (valid[u]) {
 #pragma unroll
-                    for (int i = 0; i < CPW; ++i) chunk_meta<FMT, H>(a, cp[i], c, Ops::Z0, sc[u][i], zr[u][i]);
+                    for (int i = 0; i < CPW; ++i) chunk_meta<FMT, H>(a, cp[i], c, sc[u][i], zr[u][i]);
                 }
             }
 #pragma unroll
@@ -96,17 +96,15 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
                     uint32_t wd[Ops::NWD];
-                    Ops::decode(w[u][i], wd);  // once per chunk, shared by the rows
+                    Ops::decode(w[u][i], zr[u][i], wd);  // once per chunk, shared by the rows
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         float part[H];
                         Ops::dotd(wd, act[m], part);
 #pragma unroll
-                        for (int h = 0; h < H; ++h) {
-                            float v = part[h];
-                            if constexpr (ZP) v = __builtin_fmaf(-zr[u][i][h], act[m].asum[h], v);
-                            acc[i][m] = __builtin_fmaf(sc[u][i][h], v, acc[i][m]);
-                        }
+                        for (int h = 0; h < H; ++h)
+                            acc[i][m] = block_acc<Ops::ASUM>(acc[i][m], sc[u][i][h], part[h], zr[u][i][h],
+                                                             act[m].asum[h]);
                     }
                 }
             }
@@ -188,7 +186,7 @@ __device__ __forceinline__ void stage_rows(const KArgs &a, u4v *sP, float *sS, i
                 for (int q = 0; q < NQ; ++q)
                     sP[m * rowq + stage_index<NQ>(c, q)] =
                         u4v{act.p[4 * q], act.p[4 * q + 1], act.p[4 * q + 2], act.p[4 * q + 3]};
-                if constexpr (FMT == FMT_U4 || FMT == FMT_U8) {
+                if constexpr (Ops::ASUM) {
 #pragma unroll
                     for (int h = 0; h < H; ++h) sS[m * rows + c * H + h] = act.asum[h];
                 }
@@ -201,7 +199,6 @@ template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
 __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     using Ops = ChunkOps<FMT, ACT, H>;
     using B = SBatch<FMT, H, UNR, CPW>;
-    constexpr bool ZP = (FMT == FMT_U4 || FMT == FMT_U8);
     constexpr int NQ = Ops::ND / 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63;
@@ -274,32 +271,30 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                     const u4v v = sP[stage_index<NQ>(cc, q)];
                     act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
                 }
-                if constexpr (ZP) {
+                if constexpr (Ops::ASUM) {
 #pragma unroll
                     for (int h = 0; h < H; ++h) act.asum[h] = sS[cc * H + h];
                 }
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
-                    float sc[H], zr[H], part[H];
-                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc, zr);
-                    chunk_dot<FMT, ACT, H>(b.w[u][i], act, part);
+                    float sc[H], part[H];
+                    uint32_t zr[H];
+                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], zs, sc, zr);
+                    chunk_dot<FMT, ACT, H>(b.w[u][i], zr, act, part);
                     float t = acc[i][0];
 #pragma unroll
-                    for (int h = 0; h < H; ++h) {
-                        float v = part[h];
-                        if constexpr (ZP) v = __builtin_fmaf(-zr[h], act.asum[h], v);
-                        t = __builtin_fmaf(sc[h], v, t);
-                    }
+                    for (int h = 0; h < H; ++h) t = block_acc<Ops::ASUM>(t, sc[h], part[h], zr[h], act.asum[h]);
                     acc[i][0] = valid ? t : acc[i][0];
                 }
             } else {
                 // several rows: every column's codes are decoded once and shared
                 uint32_t wd[CPW][Ops::NWD];
-                float sc[CPW][H], zr[CPW][H];
+                float sc[CPW][H];
+                uint32_t zr[CPW][H];
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
-                    Ops::decode(b.w[u][i], wd[i]);
-                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], Ops::Z0, zs, sc[i], zr[i]);
+                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], zs, sc[i], zr[i]);
+                    Ops::decode(b.w[u][i], zr[i], wd[i]);
                 }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
@@ -310,7 +305,7 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                         const u4v v = sP[m * rowq + stage_index<NQ>(cc, q)];
                         act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
                     }
-                    if constexpr (ZP) {
+                    if constexpr (Ops::ASUM) {
 #pragma unroll
                         for (int h = 0; h < H; ++h) act.asum[h] = sS[m * rows + cc * H + h];
                     }
@@ -320,11 +315,7 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                         Ops::dotd(wd[i], act, part);
                         float t = acc[i][m];
 #pragma unroll
-                        for (int h = 0; h < H; ++h) {
-                            float v = part[h];
-                            if constexpr (ZP) v = __builtin_fmaf(-zr[i][h], act.asum[h], v);
-                            t = __builtin_fmaf(sc[i][h], v, t);
-                        }
+                        for (int h = 0; h < H; ++h) t = block_acc<Ops::ASUM>(t, sc[i][h], part[h], zr[i][h], act.asum[h]);
                         acc[i][m] = valid ? t : acc[i][m];
                     }
                 }

@@ -3,11 +3,17 @@
 // Decoders turn 16-byte chunks of packed codes into fp16/bf16 operand pairs that
 // feed v_dot2_f32_{f16,bf16} (vector family) or v_mfma_f32_16x16x32_{f16,bf16}
 // (matrix family). Every decode here is exact:
-//  - 4-/8-bit codes q become fp16 subnormals q*2^-24 (4-bit codes in the upper
-//    nibble of a half become q*2^-20), or bf16 integers q through the E4M3
+//  - With fp16 activations, 4-/8-bit codes q and the block's zero point z are both
+//    placed in fp16 bit patterns (subnormals q*2^-24, or the integers 1024 + q) and
+//    subtracted with one packed fp16 op, which forms (q - z) exactly ("[CUDA]
+//    MatMulNBits 8-bit: wide fp16 M=1 kernel", Description: (q - zp) formed exactly
+//    in fp16 before the multiply).
+//  - With bf16 activations gfx950 has no packed bf16 subtract. 8-bit codes form
+//    q - z exactly in fp32 and round the pair to bf16 (exact: |q - z| <= 255 needs 8
+//    significant bits). 4-bit codes become the bf16 integers q through the E4M3
 //    converter (codes 0..15 of E4M3 are exactly q*2^-9; the converter's power-of-two
-//    scale 2^9 restores q). The zero point is applied as z * sum(a) on the fp32
-//    block sum, so (q - zp) never needs a packed subtract.
+//    scale 2^9 restores q), and the zero point enters the fp32 block sum as
+//    z * sum(a), with no offset added to q.
 //  - E4M3 and E2M1 use the hardware converters, which decode OCP E4M3FN and
 //    E2M1 exactly (E4M3 to fp16/bf16 widening is lossless: "[CUDA] Block-scaled
 //    MatMul decode GEMV", FP8 mma paragraph).
@@ -84,6 +90,29 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
 template <bool WORD>
 __device__ __forceinline__ uint32_t small_int_bf16_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, WORD));
+}
+
+// Packed fp16 difference x - y of two fp16 pairs (one v_pk_add_f16 with negated
+// second operand); exact whenever the differences are representable, as they are for
+// the integer codes and zero points here.
+__device__ __forceinline__ uint32_t sub_h2(uint32_t x, uint32_t y) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) - __builtin_bit_cast(h2, y));
+}
+
+// bf16 pair (x, y) rounded from fp32 (v_cvt_pk_bf16_f32, nearest-even; exact for the
+// small integers it is given here).
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){x, y}, b2));
+}
+
+// bf16 pair (q[sel] - z, q[sel + 1] - z) from bytes sel, sel + 1 of w (8-bit codes):
+// formed in fp32, where the difference is exact, then packed.
+template <int SEL>
+__device__ __forceinline__ uint32_t u8_diff_bf16_pair(uint32_t w, float z) {
+    const float a = (float)((w >> (8 * SEL)) & 0xFFu) - z;
+    const float b = (float)((w >> (8 * SEL + 8)) & 0xFFu) - z;
+    return pack_bf16(a, b);
 }
 
 // (x & mask) | bits in one v_bitop3 (truth table 0xEA: bit i is the result for

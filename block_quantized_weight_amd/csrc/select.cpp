@@ -7,9 +7,15 @@
 // leaves a nearly empty tail ("[CUDA] Pin FP8 GEMV residency", Description). Here the
 // unit is the wave64 and the machine is cu_count compute units (256 on MI355X).
 //
-// Every parameter that changes per-row arithmetic (the family, the lanes that own a
-// column, the K split) is chosen from (format, N, K, block size, flags) only, never
-// from M, so a row's result does not depend on how many rows travel with it.
+// Within a kernel family, every parameter that changes per-row arithmetic (the lanes
+// that own a column, the K split) is chosen from (format, N, K, block size, flags and
+// the CU count) only, never from M, so a row's bits do not depend on how many rows
+// travel with it in that family. The family itself is chosen from M as well (the
+// streaming family at M = 1, the matrix family from M = 2 or 3 on wide weights, and
+// the fallbacks below), as are the K parts of qgemv_run_ws in one case; the families
+// sum in different fp32 orders, so a row's bits can change where M moves a shape
+// from one family to the other (both within the same bound). A caller who needs the
+// same bits for a row at every M forces one family (and the part count) in the flags.
 #include "select.h"
 
 #include <stdint.h>
@@ -71,13 +77,14 @@ static bool stream_shape_ok(const qgemv_desc *d) {
     return d->K % k_per_chunk(d->format) == 0;
 }
 
-// The matrix family walks K in steps of four 16-byte chunks per column, and takes
-// 8-bit codes only with fp16 activations (1024 + q is an exact fp16 integer; bf16
-// has no room for an offset 8-bit code).
-static bool mfma_shape_ok(const qgemv_desc *d) {
-    if (d->K % (4 * k_per_chunk(d->format))) return false;
-    if (d->format == QGEMV_FMT_U8 && d->act_dtype != QGEMV_ACT_F16) return false;
-    return true;
+// The matrix family walks K in steps of four 16-byte chunks per column.
+static bool mfma_shape_ok(const qgemv_desc *d) { return d->K % (4 * k_per_chunk(d->format)) == 0; }
+
+// Whether the kernels keep per-chunk activation sums (for the zero point's
+// -z * sum(a) term): 4-bit codes on bf16 activations only. Every other format with
+// zero points forms q - z in its decode.
+static bool needs_act_sums(const qgemv_desc *d) {
+    return d->format == QGEMV_FMT_U4 && d->act_dtype == QGEMV_ACT_BF16;
 }
 
 // Whether the matrix family's DMA ring takes the problem, and its LDS bytes next to
@@ -188,7 +195,7 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     const int64_t nch64 = (nch + 63) / 64 * 64;
     const int nd = kpc == 32 ? 16 : 8;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
-    const int64_t lds = mt * (nch64 * nd * 4 + nch64 * h * 4);
+    const int64_t lds = mt * (nch64 * nd * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0));
     if (lds > (mt > 1 ? 64 : 48) * 1024) return false;
     const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
     int unr = 0;
@@ -301,7 +308,7 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_c
     const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
     const int mt = M == 2 ? 2 : 4;
-    if (mt * (nch64 * (kpc == 32 ? 16 : 8) * 4 + nch64 * h * 4) > 64 * 1024) return false;
+    if (mt * (nch64 * (kpc == 32 ? 16 : 8) * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0)) > 64 * 1024) return false;
     const double wbytes = (double)d->N * d->K * (kpc == 32 ? 0.5 : 1.0);
     const bool small = wbytes < 64.0 * 1024 * 1024;
     const bool byte_codes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
@@ -364,15 +371,15 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         const int64_t lds_red = c.ksplit > 1 ? (int64_t)nw * rg * 4 * 64 * 4 : 0;
         const int64_t steps = d->K / (4 * k_per_chunk(d->format));
         // Staged layout for kpv K parts: a 64-byte zero block, the rows of the longest
-        // K part (stride its k + 8 elements), and for formats with zero points one
-        // 16-byte activation-sum entry per chunk, row group and scale block of the
-        // chunk (abytes); then the K-split reduction area, which overlays the staged
+        // K part (stride its k + 8 elements), and for 4-bit codes on bf16 (the zero
+        // point's sum(a) term) one 16-byte activation-sum entry per chunk, row group and
+        // scale block of the chunk (abytes); then the K-split reduction area, which overlays the staged
         // activations when every workgroup holds a single tile group (always with K
         // parts; without, when one round of them fits at once), as they are dead by
         // then, and else follows them (FP8 8192 x 4096 at M = 16: 131 KB of staged rows
         // and 32 KB of reduction area fit only overlaid); then, with K parts, the
         // 16-byte last-workgroup flag (lds).
-        const bool zp_fmt = d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8;
+        const bool zp_fmt = needs_act_sums(d);
         const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
         struct Staged { int64_t abytes, lds; };
         auto staged = [&](int kpv) {

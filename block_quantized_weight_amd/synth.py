@@ -208,6 +208,57 @@ def make_problem(
     )
 
 
+def make_zero_point_problem(
+    fmt: str,
+    act: str,
+    N: int,
+    K: int,
+    bs: int,
+    seed: int,
+    *,
+    frac: float = 1.0,
+    rows: Tuple[Tuple[float, float], ...] = ((16.0, 0.0), (64.0, 0.0), (1.0, 8192.0), (0.0, 8192.0)),
+    scale_sigma: Optional[float] = None,
+) -> Problem:
+    """A 4- or 8-bit problem whose codes equal their block's zero point in a fraction
+    ``frac`` of the (column, block) pairs (every pair for frac = 1): the weight those
+    blocks dequantize to is zero, so the outputs are sums over the other blocks only
+    (all zero for frac = 1), while the codes and zero points themselves span their
+    whole range. Row i of A is N(0, rows[i][0]) plus, when rows[i][1] is nonzero, one
+    entry of +-rows[i][1] at a random k (a single large activation). Drawn after
+    make_problem's own draws with the same generator: the block choice, then per row
+    the normal values, the spike position and its sign. Zero points are uniform over
+    the full code range (0..15 or 0..255); scales are |N(0,1)| * scale_sigma (by default
+    0.02 for 4-bit and 0.004 for 8-bit codes, as in the named workloads)."""
+    if fmt not in ("u4", "u8"):
+        raise ValueError("zero points exist for the 4- and 8-bit codes only")
+    if scale_sigma is None:
+        scale_sigma = 0.02 if fmt == "u4" else 0.004
+    zr = (0, 15) if fmt == "u4" else (0, 255)
+    base = make_problem(fmt, act, N, K, bs, 1, seed, name=f"zp_{fmt}_{act}", zp_range=zr,
+                        scale_sigma=scale_sigma)
+    rng = np.random.default_rng(seed + 7919)
+    nblk = K // bs
+    if fmt == "u4":
+        z = unpack_nibbles(base.zp, nblk)  # [N, nblk]
+        fill = (z | (z << 4)).astype(np.uint8)  # both nibbles of a byte hold z
+    else:
+        z = base.zp
+        fill = z.astype(np.uint8)
+    pick = rng.random((N, nblk)) < frac
+    W = base.W.copy()
+    W[pick] = fill[pick][:, None]
+    A = np.zeros((len(rows), K), dtype=np.float64)
+    for i, (sigma, spike) in enumerate(rows):
+        A[i] = rng.standard_normal(K) * sigma
+        if spike:
+            k = int(rng.integers(0, K))
+            A[i, k] = spike if rng.random() < 0.5 else -spike
+    Abits = activation_bits(A, act).reshape(len(rows), K)
+    return dataclasses.replace(base, W=np.ascontiguousarray(W), A=np.ascontiguousarray(Abits),
+                               ms=(len(rows),))
+
+
 # --------------------------------------------------------------------------------------
 # the named workloads
 

@@ -175,18 +175,22 @@ def tolerance(S: np.ndarray) -> np.ndarray:
     return TOL_REL * np.asarray(S, dtype=np.float64) + TOL_ABS
 
 
-# Half an ulp of the output type, relative: the final rounding of an fp32 result to
-# the output type may add this much of |y| on top of the accumulation error.
-OUTPUT_HALF_ULP = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# The output type's unit roundoff, relative, allowed on top of the bound for synthetic
+# edge cases whose |y| approaches S. Only bf16 needs it: rounding an fp32 result to
+# bf16 (8 significant bits) moves it by up to 2^-8 |y|, more than the 1e-3 * S term
+# when |y| is close to S. Rounding to fp16 (11 significant bits) moves it by at most
+# 2^-11 |y| <= 2^-11 S, about half of 1e-3 * S, so fp16 outputs are held to the bound
+# as it stands.
+OUTPUT_HALF_ULP = {"f16": 0.0, "bf16": 2.0 ** -8}
 
 
 def within_tolerance(y: np.ndarray, y_ref: np.ndarray, S: np.ndarray,
                      out_dtype: Optional[str] = None) -> Tuple[bool, float]:
     """(all outputs inside the bound, max(err / bound)).
 
-    The bound is REL * S + ABS. With ``out_dtype`` given, the output type's final
-    rounding (half an ulp of |y_ref|) is allowed on top; without it the bound is
-    applied to the rounded output as is (the named workloads are held to that)."""
+    The bound is REL * S + ABS. With ``out_dtype`` "bf16", the output type's final
+    rounding (2^-8 of |y_ref|) is allowed on top; fp16 outputs and calls
+    without ``out_dtype`` (the named workloads) are held to the bound as it stands."""
     y = np.asarray(y, dtype=np.float64)
     err = np.abs(y - y_ref)
     bound = tolerance(S)

@@ -61,7 +61,7 @@ def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K,
     Y, plan = gu.run_gpu(prob, M, ws=True)
     assert plan["family"] == "mfma" and plan["kparts"] == 2 and bool(plan["variant"] & 1) == staged, plan
     assert plan["ws_zero"]
-    ok, ratio = gu.check_points(prob, M, Y)
+    ok, ratio, _, _ = gu.check_full(prob, M, Y)
     assert ok, ratio
     Yf, pf = gu.run_gpu(prob, M, flags=2 | kp_flags(2), ws=True)
     assert pf["kparts"] == 2 and pf["ksplit"] == plan["ksplit"]

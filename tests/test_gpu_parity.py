@@ -1,8 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Bar: |y - y_ref| <= 1e-3 * sum|a*w| + 1e-3 per output (fp32 accumulation), checked
-element by element on every output for the small workloads and on sampled outputs
-(random points plus every row of the first and last 40 columns) at full size.
+element by element on every output of every named workload, the lm_head sizes included
+(the oracle runs on all host cores; its rows do not depend on M, so one 16-row product
+serves the whole M sweep).
 Integer-valued and one-hot cases must match bit for bit; rows must come out
 bit-identical whatever tile carries them; repeated runs must be bitwise equal.
 """
@@ -49,31 +50,69 @@ def test_named_workload_full_parity(name, M):
 
 @pytest.fixture(scope="module")
 def lm_head_u4():
-    return synth.workload("u4_k4096_n151936")
+    prob = synth.workload("u4_k4096_n151936")
+    gu.say("[oracle] u4 lm_head, 16 rows")
+    Yr, S = oracle.gemv(prob, M=16)
+    return prob, Yr, S
 
 
 @pytest.fixture(scope="module")
 def lm_head_nvfp4():
-    return synth.workload("nvfp4_m4_k2048_n248320")
+    prob = synth.workload("nvfp4_m4_k2048_n248320")
+    gu.say("[oracle] nvfp4 lm_head, 4 rows")
+    Yr, S = oracle.gemv(prob, M=4)
+    return prob, Yr, S
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
-def test_u4_lm_head_sampled_parity(lm_head_u4, M):
+def test_u4_lm_head_full_parity(lm_head_u4, M):
+    prob, Yr, S = lm_head_u4
     gu.say(f"[parity] u4 lm_head M={M}")
-    Y, plan = gu.run_gpu(lm_head_u4, M)
-    assert np.all(np.isfinite(Y))
-    ok, ratio = gu.check_points(lm_head_u4, M, Y, seed=M)
+    Y, plan = gu.run_gpu(prob, M)
+    ok, ratio = oracle.within_tolerance(Y, Yr[:M], S[:M])
     gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
     assert ok, (M, ratio, plan)
 
 
-def test_nvfp4_lm_head_sampled_parity(lm_head_nvfp4):
+def test_nvfp4_lm_head_full_parity(lm_head_nvfp4):
+    prob, Yr, S = lm_head_nvfp4
     gu.say("[parity] nvfp4 lm_head M=4")
-    Y, plan = gu.run_gpu(lm_head_nvfp4, 4)
-    assert np.all(np.isfinite(Y))
-    ok, ratio = gu.check_points(lm_head_nvfp4, 4, Y)
+    Y, plan = gu.run_gpu(prob, 4)
+    ok, ratio = oracle.within_tolerance(Y, Yr, S)
     gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
-    assert ok, ratio
+    assert ok, (ratio, plan)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [4, 8])
+def test_dma_ring_walks_several_rounds(act, M):
+    """A 4-bit weight of 40000 columns: 2500 tiles on 256 eight-wave workgroups, so every
+    wave of the DMA ring walks more than one tile; every output against the oracle."""
+    prob = synth.make_problem("u4", act, 40000, 1024, 32, M, seed=77)
+    gu.say(f"[parity] dma ring u4/{act} 40000x1024 M={M}")
+    Y, plan = gu.run_gpu(prob, M)
+    assert plan["family"] == "mfma" and plan["variant"] & 2, plan
+    assert (40000 + 15) // 16 > plan["grid"] * plan["waves_per_wg"], plan
+    ok, ratio, _, _ = gu.check_full(prob, M, Y)
+    gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
+    assert ok, (ratio, plan)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "u4"])
+@pytest.mark.parametrize("M,family", [(5, "mfma"), (6, "stream"), (16, "stream")])
+def test_tall_narrow_shapes_without_workspace(fmt, M, family):
+    """1024 x 16384 through qgemv_run: the activation rows do not fit in LDS, not even 8
+    at a time, and the tile groups fill a quarter of the CUs, so from M = 6 the
+    dispatcher takes the streaming family (M = 5 stays on the matrix cores, activations
+    in the register ring). Every output against the oracle."""
+    bs = 128 if fmt == "fp8" else 32
+    prob = synth.make_problem(fmt, "f16", 1024, 16384, bs, M, seed=91)
+    gu.say(f"[parity] tall {fmt} 1024x16384 M={M}")
+    Y, plan = gu.run_gpu(prob, M)
+    assert plan["family"] == family and plan["kparts"] == 1, plan
+    ok, ratio, _, _ = gu.check_full(prob, M, Y)
+    gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
+    assert ok, (ratio, plan)
 
 
 # ----------------------------------------------------------------------------------
@@ -95,15 +134,9 @@ def ring_eligible(prob, M):
     return M <= 8 and (nblk * sb) % 4 == 0 and zrow % 4 == 0
 
 
-def mfma_supports(fmt, act):
-    return not (fmt == "u8" and act == "bf16")
-
-
 @pytest.mark.parametrize("family", ["auto", "stream", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", FMT_CASES)
 def test_families_ragged_shapes(family, fmt, act, bs):
-    if family.startswith("mfma") and not mfma_supports(fmt, act):
-        pytest.skip("the matrix family takes 8-bit codes with fp16 activations only")
     for N, K, M in [(1, 256, 1), (17, 512, 3), (36, 1024, 5), (1169, 768, 16), (300, 4096, 2)]:
         if K % bs:
             continue
@@ -121,7 +154,7 @@ def test_families_ragged_shapes(family, fmt, act, bs):
         assert ok, (family, fmt, act, bs, N, K, M, ratio, plan)
 
 
-@pytest.mark.parametrize("fmt,act", [("u4", "f16"), ("u8", "f16"), ("u4", "bf16")])
+@pytest.mark.parametrize("fmt,act", [("u4", "f16"), ("u8", "f16"), ("u4", "bf16"), ("u8", "bf16")])
 def test_missing_zero_points_mean_midpoint(fmt, act):
     prob = synth.make_problem(fmt, act, 200, 512, 32, 4, seed=9, with_zp=False)
     assert prob.zp is None
@@ -136,7 +169,8 @@ def test_missing_zero_points_mean_midpoint(fmt, act):
 
 @pytest.mark.parametrize("family", ["stream", "stream_classic", "mfma_nolds", "mfma_lds", "mfma_ring", "generic"])
 @pytest.mark.parametrize("fmt,act,bs", [("u4", "bf16", 32), ("u4", "f16", 32), ("fp8", "f16", 128),
-                                         ("nvfp4", "bf16", 16), ("u8", "f16", 128), ("u4", "f16", 16)])
+                                         ("nvfp4", "bf16", 16), ("u8", "f16", 128), ("u4", "f16", 16),
+                                         ("u8", "bf16", 64)])
 def test_row_results_do_not_depend_on_the_tile(family, fmt, act, bs):
     """Row i of an M-row call equals the same row run alone, and in any other M. The
     two activation paths of the matrix family must also agree bit for bit."""
@@ -329,7 +363,7 @@ def test_integer_special_case_is_exact(fmt, act):
     exact = (a_int @ q.astype(np.int64).T).astype(np.float64)
     assert np.abs(exact).max() > 128  # large enough that bf16 must round some results
     want = oracle.decode_activation_bits(synth.activation_bits(exact, act), act)
-    for fam in ("stream", "generic") + (("mfma_nolds", "mfma_lds", "mfma_ring") if mfma_supports(fmt, act) else ()):
+    for fam in ("stream", "generic", "mfma_nolds", "mfma_lds", "mfma_ring"):
         Y, _ = gu.run_gpu(prob, M, flags=FAMILY_FLAG[fam])
         assert np.array_equal(Y, want), fam
 
@@ -346,9 +380,7 @@ def test_bias_epilogue_every_family(fmt, act, bs):
                               scale_sigma=0.02 if fmt == "u4" else 0.004)
     assert prob.bias is not None
     gu.say(f"[bias] {fmt}/{act} bs{bs}")
-    fams = ["auto", "stream", "stream_classic", "generic"]
-    if mfma_supports(fmt, act):
-        fams += ["mfma_nolds", "mfma_lds", "mfma_ring"]
+    fams = ["auto", "stream", "stream_classic", "generic", "mfma_nolds", "mfma_lds", "mfma_ring"]
     for fam in fams:
         Y16, p16 = gu.run_gpu(prob, 16, flags=FAMILY_FLAG[fam])
         ok, ratio, _, _ = gu.check_full(prob, 16, Y16, strict=False)
@@ -425,7 +457,7 @@ def test_one_hot_probes_decode_every_code_exactly(fmt, act):
                          tensor_scale=1.0, A=np.zeros((16, K), np.uint16))
     one = 0x3C00 if act == "f16" else 0x3F80
     deq = oracle.dequant_columns(base)  # [N, K] exact values
-    for fam in ("stream", "generic") + (("mfma_nolds", "mfma_lds", "mfma_ring") if mfma_supports(fmt, act) else ()):
+    for fam in ("stream", "generic", "mfma_nolds", "mfma_lds", "mfma_ring"):
         for k0 in range(0, K, 16):
             A = np.zeros((16, K), np.uint16)
             A[np.arange(16), k0 + np.arange(16)] = one

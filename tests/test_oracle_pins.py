@@ -463,3 +463,36 @@ def test_integer_special_case_with_bias_is_exact():
         bias=synth.round_to_bf16_bits(b_int.astype(np.float64)))
     Y, _ = oracle.gemv(prob)
     assert np.array_equal(Y, (a_int @ q.T + b_int[None, :]).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt,act,bs", [("u4", "f16", 32), ("u4", "bf16", 16), ("u8", "f16", 128),
+                                         ("u8", "bf16", 32)])
+def test_codes_at_their_zero_points_give_exact_zeros(fmt, act, bs):
+    """Blocks whose codes all equal their zero point dequantize to w = s * 0 = 0, so with
+    every block so, Y and S are exactly zero whatever the activations (large normal
+    values and single large spikes here); with 90% of the blocks so, Y equals the product
+    over the other blocks alone, computed by numpy from the unpacked codes and zero points
+    with those blocks removed (fp64, within 1e-12 of S)."""
+    prob = synth.make_zero_point_problem(fmt, act, 40, 1024, bs, seed=3)
+    Y, S = oracle.gemv(prob)
+    assert np.all(Y == 0.0) and np.all(S == 0.0)
+    prob = synth.make_zero_point_problem(fmt, act, 40, 1024, bs, seed=3, frac=0.9)
+    Y, S = oracle.gemv(prob)
+    nblk = 1024 // bs
+    if fmt == "u4":
+        q = synth.unpack_nibbles(prob.W.reshape(40, -1), 1024).astype(np.float64)
+        z = synth.unpack_nibbles(prob.zp, nblk).astype(np.float64)
+    else:
+        q = prob.W.reshape(40, 1024).astype(np.float64)
+        z = prob.zp.astype(np.float64)
+    s = prob.scales.view(np.float16).astype(np.float64)
+    live = ~np.all(q.reshape(40, nblk, bs) == z[:, :, None], axis=2)  # blocks not at their zero point
+    assert 0.03 < live.mean() < 0.2
+    W = (np.repeat(s * live, bs, axis=1)) * (q - np.repeat(z, bs, axis=1))
+    a = prob.A
+    A = (a.view(np.float16).astype(np.float64) if act == "f16"
+         else torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy())
+    Yn = A @ W.T
+    Sn = np.abs(A) @ np.abs(W).T
+    assert np.all(np.abs(Y - Yn) <= 1e-12 * Sn + 1e-300)
+    assert np.abs(Yn).max() > 1.0

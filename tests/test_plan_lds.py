@@ -2,8 +2,9 @@
 
 The register-ring kernel (k_mfma) lays out its LDS from its arguments:
 a 64-byte zero block, the staged rows of the longest K part (row stride: that part's k
-plus 8 elements, 2 bytes each, rounded up to 16 bytes), for formats with zero points
-one 16-byte activation-sum entry per chunk, row group and scale block, then the K-split
+plus 8 elements, 2 bytes each, rounded up to 16 bytes), for 4-bit codes on bf16
+activations one 16-byte activation-sum entry per chunk, row group and scale block (the
+other formats with zero points form q - z in the decode), then the K-split
 reduction area (8 waves x row groups x 4 x 64 fp32), which overlays the staged rows from
 byte 0 when the workgroup holds a single tile group (always with K parts), and, with K
 parts, a 4-byte completion flag after both. The DMA-ring kernel (k_mfma_dma) stages
@@ -25,13 +26,14 @@ SHAPES = [  # fmt, act, N, K, bs
     ("u4", "bf16", 16384, 8192, 32), ("u4", "bf16", 2048, 16384, 32), ("u4", "f16", 512, 8192, 32),
     ("u4", "f16", 777, 896, 16), ("u4", "bf16", 3000, 4096, 128), ("u8", "f16", 4096, 4096, 128),
     ("u8", "f16", 4096, 8192, 128), ("u8", "f16", 2048, 8192, 128), ("u8", "f16", 1900, 8192, 64),
+    ("u8", "bf16", 4096, 4096, 32), ("u8", "bf16", 151936, 2048, 128), ("u4", "f16", 151936, 4096, 32),
     ("fp8", "f16", 5120, 6144, 128), ("fp8", "f16", 8192, 4096, 128), ("fp8", "f16", 1024, 16384, 128),
     ("fp8", "bf16", 2048, 8192, 128), ("fp8", "f16", 100, 256, 128), ("nvfp4", "bf16", 248320, 2048, 16),
     ("nvfp4", "bf16", 2048, 4096, 16), ("nvfp4", "f16", 999, 3104, 16),
 ]
 
 
-def kernel_lds(fmt, N, K, bs, rows, plan, zpp=False):
+def kernel_lds(fmt, act, N, K, bs, rows, plan, zpp=False):
     """Bytes the matrix-family kernel addresses for a pass of `rows` rows."""
     ks, kp = plan["ksplit"], plan["kparts"]
     rg = (rows + 3) // 4
@@ -42,7 +44,7 @@ def kernel_lds(fmt, N, K, bs, rows, plan, zpp=False):
         # 2) and the zero-point window when there are zero points
         nch = K // KPC[fmt]
         rows_b = (rows * (K + 8) * 2 + 15) // 16 * 16
-        sums = nch * rg * h * 16 if fmt in ("u4", "u8") else 0
+        sums = nch * rg * h * 16 if (fmt, act) == ("u4", "bf16") else 0
         nsd = 4 if (fmt == "fp8" or (fmt == "u4" and h == 2)) else 2
         slot = 4096 + 256 * nsd + (256 if zpp else 0)
         return 64 + rows_b + sums + 8 * 2 * slot
@@ -56,7 +58,7 @@ def kernel_lds(fmt, N, K, bs, rows, plan, zpp=False):
     if staged:
         astride = smax * 4 * KPC[fmt] + 8
         rows_b = (rows * astride * 2 + 15) // 16 * 16
-        sums = 4 * smax * rg * h * 16 if fmt in ("u4", "u8") else 0
+        sums = 4 * smax * rg * h * 16 if (fmt, act) == ("u4", "bf16") else 0
         abytes = 64 + rows_b + sums
     overlay = staged and ks > 1 and (kp > 1 or plan["grid"] // kp >= ngroups)
     end = max(abytes, red) if overlay else abytes + red
@@ -83,5 +85,5 @@ def test_every_matrix_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs, zp):
                 assert p["workspace_bytes"] >= p["kparts"] * min(M, 16) * N * 4
             if p["family"] != "mfma":
                 continue  # the streaming kernels' staged rows are sized by the same formula
-            need = kernel_lds(fmt, N, K, bs, min(p["rows_per_pass"], rows), p, zpp=zp)
+            need = kernel_lds(fmt, act, N, K, bs, min(p["rows_per_pass"], rows), p, zpp=zp)
             assert need <= p["lds_bytes"], (fmt, N, K, bs, M, ws, p, need)
