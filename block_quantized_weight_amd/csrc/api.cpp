@@ -4,8 +4,10 @@
 // its environment switches once per instance, never per call ("[CUDA] Block-scaled
 // MatMul decode GEMV", review fixes; "[CUDA] MatMul: add an opt-in split-K GEMV",
 // Kernel and dispatch). The handle here does the same: qgemv_create captures the
-// compute-unit count and the environment overrides, and qgemv_run only validates the
-// per-call arguments, picks the launch and enqueues it.
+// compute-unit count and the environment overrides and plans every launch the handle
+// can make (each row count up to 16, with and without a workspace, with aligned and
+// misaligned activations), so qgemv_run only validates the per-call arguments, looks
+// its launch up and enqueues it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -23,6 +25,10 @@ struct qgemv_handle {
     int cu_count;
     uint32_t env_flags;
     bool weights_fast_ok;
+    // the launch of every (workspace, fast pointers, M - 1) case, and its status
+    qgemv::LaunchCfg plan[2][2][QGEMV_MAX_M];
+    int plan_rc[2][2][QGEMV_MAX_M];
+    qgemv::KArgs args;  // kernel arguments common to every call (M, A, Y set per call)
 };
 
 namespace {
@@ -116,23 +122,25 @@ hipError_t launch_rows(const qgemv::LaunchCfg &c, const qgemv::KArgs &a0, const 
     }
 }
 
-// Shared body of qgemv_run and qgemv_run_ws: plan (with or without a workspace) for
-// min(M, 16) rows, check the workspace the plan needs, and enqueue the launches.
-// More than 16 rows run as chunks of 16 (the last one shorter), one after another on
-// the stream, each with the 16-row plan: a row's arithmetic does not depend on the
-// chunk that carries it, and the workspace, all zero again after each chunk, serves
-// every chunk in turn.
+// Shared body of qgemv_run and qgemv_run_ws: the cached plan (with or without a
+// workspace) for min(M, 16) rows, the workspace check, and the launches. More than 16
+// rows run as chunks of 16 (the last one shorter), one after another on the stream,
+// each with the 16-row plan: a row's arithmetic does not depend on the chunk that
+// carries it, and the workspace, all zero again after each chunk, serves every chunk
+// in turn.
 int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
              void *hip_stream) {
     if (!h || !A || !Y) return QGEMV_E_NULL;
     if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
     const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
     const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
-    qgemv::LaunchCfg c;
-    int rc = qgemv::select_plan(&h->d, Mp, h->cu_count, fast, h->env_flags, with_ws, &c);
+    const int rc = h->plan_rc[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1];
     if (rc) return rc;
-    qgemv::KArgs a;
-    fill_args(h, A, Y, Mp, &a);
+    const qgemv::LaunchCfg &c = h->plan[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1];
+    qgemv::KArgs a = h->args;
+    a.A = A;
+    a.Y = Y;
+    a.M = Mp;
     a.ksplit = c.ksplit;
     if (c.kparts > 1) {
         if (!ws || (uintptr_t)ws % 256 || ws_bytes < (size_t)c.ws_bytes) return QGEMV_E_WORKSPACE;
@@ -203,6 +211,16 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
     h->cu_count = prop.multiProcessorCount;
     h->env_flags = read_env_flags();
     h->weights_fast_ok = qgemv::pointers_fast_ok(d, nullptr, nullptr);
+    for (int w = 0; w < 2; ++w)
+        for (int f = 0; f < 2; ++f)
+            for (int m = 1; m <= QGEMV_MAX_M; ++m) {
+                qgemv::LaunchCfg &c = h->plan[w][f][m - 1];
+                c = qgemv::LaunchCfg{};
+                h->plan_rc[w][f][m - 1] =
+                    qgemv::select_plan(d, m, h->cu_count, f && h->weights_fast_ok, h->env_flags, w != 0, &c);
+                c.device = dev;
+            }
+    fill_args(h, nullptr, nullptr, 1, &h->args);
     *out = h;
     return QGEMV_OK;
 }

@@ -1139,11 +1139,11 @@ namespace {
 
 template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
 hipError_t go_p(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    auto kern = a.kparts > 1 ? k_mfma<FMT, ACT, RG, H, LDSA, P, true> : k_mfma<FMT, ACT, RG, H, LDSA, P, false>;
-    if (cfg.lds_bytes > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
-        if (e != hipSuccess) return e;
-    }
+    const bool kp = a.kparts > 1;
+    auto kern = kp ? k_mfma<FMT, ACT, RG, H, LDSA, P, true> : k_mfma<FMT, ACT, RG, H, LDSA, P, false>;
+    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};  // per kernel: without / with K parts
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[kp ? 1 : 0]);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }
@@ -1181,10 +1181,9 @@ hipError_t go(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 template <int FMT, int ACT, int RG, int H, bool ZPP, int R, int SS>
 hipError_t go_dma_rs(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     auto kern = k_mfma_dma<FMT, ACT, RG, H, ZPP, R, SS>;
-    if (cfg.lds_bytes > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }

@@ -482,10 +482,9 @@ hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
 hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     auto kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG>;
-    if (cfg.lds_bytes > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(64 * NWG), (size_t)cfg.lds_bytes, s, a);
     return hipGetLastError();
 }

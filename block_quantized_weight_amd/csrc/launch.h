@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qgemv {
 
 // Arguments every kernel receives (by value).
@@ -34,6 +36,7 @@ struct KArgs {
 };
 
 struct LaunchCfg {
+    int device;         // device the launch goes to (set by the caller of a launcher)
     int fmt;            // Fmt
     int act;            // Act
     int family;         // qgemv_family
@@ -49,6 +52,22 @@ struct LaunchCfg {
     int64_t ws_counters;      // workspace bytes of completion counters (256-byte multiple)
     int64_t ws_bytes;         // workspace bytes in all (0 without K parts)
 };
+
+// Dynamic LDS of one gfx950 compute unit (bytes).
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+// Raise kern's dynamic-LDS limit to the whole CU once per device (bit d of `done`):
+// the limit is a property of the function on a device, so a launch that needs more
+// than the default 64 KB pays the call once, not per launch. `done` is a static of the
+// launcher instantiation that owns kern.
+inline hipError_t lds_limit_once(const void *kern, int device, int lds_bytes, std::atomic<uint64_t> &done) {
+    if (lds_bytes <= 65536) return hipSuccess;
+    const uint64_t bit = 1ull << (device & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 hipError_t launch_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
 hipError_t launch_generic(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);

@@ -191,7 +191,15 @@ typedef struct qgemv_handle qgemv_handle;
 /* Validate d, read the device's properties (device index, or -1 for the current
  * device), and return a handle in *out. The weight pointers are kept, not copied.
  * Environment overrides (QGEMV_FORCE_FAMILY, QGEMV_FORCE_KSPLIT, QGEMV_NO_MFMA) are
- * read here once, never per call. */
+ * read here once, never per call; a switch set to 0, false, off or no is off. Every
+ * launch the handle can make (M = 1..16, with and without a workspace, aligned or not)
+ * is planned here too, so a run only looks its plan up. The pages' review fixes ask for
+ * exactly this split: device properties passed to each instance instead of a
+ * process-wide cached SM count, and kill switches parsed as booleans ("[CUDA]
+ * Block-scaled MatMul decode GEMV: tensor cores, packed FP4 decode and M-tiling",
+ * review fixes). The handle is plain host memory (QGEMV_E_ALLOC if it cannot be
+ * allocated), owned by the caller until qgemv_destroy. Returns QGEMV_E_DEVICE for a
+ * device that is not gfx950 and the descriptor's own status for an invalid d. */
 int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device);
 
 /* Enqueue Y[M, N] = A[M, K] . dequant(W)^T on hip_stream (a hipStream_t; NULL = the
@@ -246,18 +254,32 @@ int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes);
 
 /* The launch qgemv_run (with_workspace = 0) or qgemv_run_ws (with_workspace != 0)
  * would make for M rows (pointers as given at create; A and Y assumed 16-byte
- * aligned). */
+ * aligned), written to *out (caller-owned): the kernel family, grid, K split, K parts
+ * and workspace. It makes the dispatcher's choice visible, as the pages' tests check
+ * which kernel a shape reaches and its fallback path ("[CUDA] MatMulNBits 8-bit: wide
+ * fp16 M=1 kernel for decode GEMVs", review: which test shapes reach the new path).
+ * Returns QGEMV_E_SHAPE for M outside [1, QGEMV_MAX_ROWS]. */
 int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info *out);
 
-/* Pure host selector, no device needed: the plan for d at M rows on a device with
- * cu_count compute units, assuming 16-byte aligned pointers; with_workspace as for
- * qgemv_plan. Used to test the dispatcher at fixed CU counts. */
+/* Pure host selector, no device needed and no HIP call made: the plan for d at M rows
+ * on a device with cu_count compute units, assuming 16-byte aligned pointers;
+ * with_workspace as for qgemv_plan; *out is caller-owned. The pages test their
+ * occupancy window the same way, as a pure predicate at a fixed SM count so that the
+ * expectations do not move with the test machine ("[CUDA] Pin FP8 GEMV residency for
+ * grids just past two blocks per SM", Tests). Returns QGEMV_E_ARG for cu_count < 1 and
+ * the descriptor's status for an invalid d. */
 int qgemv_select(const qgemv_desc *d, int M, int cu_count, int with_workspace, qgemv_plan_info *out);
 
-/* Release the handle (NULL is ignored). Does not touch the caller's buffers. */
+/* Release the handle (NULL is ignored). Does not touch the caller's buffers or wait
+ * for launches in flight: the caller keeps the weight buffers alive until the work it
+ * enqueued has finished. */
 void qgemv_destroy(qgemv_handle *h);
 
-/* Static English text for a status code. */
+/* Static English text for a status code (owned by the library, never freed). Every
+ * entry point reports failure as a status instead of aborting or printing, as the
+ * pages' launchers return an error status to the operator that then falls back
+ * ("[CUDA] MatMulNBits 8-bit: wide fp16 M=1 kernel for decode GEMVs", Description:
+ * the guarded dispatch and its fallback). */
 const char *qgemv_status_str(int status);
 
 /* ABI version of the loaded library (QGEMV_ABI_VERSION it was built with). */

@@ -23,8 +23,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_workspace_size", "qgemv_plan", "qgemv_select",
-            "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version"} <= names
+    assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_workspace_size", "qgemv_plan",
+            "qgemv_select", "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version"} <= names
     L = bqw.lib()
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -46,7 +46,7 @@ def test_abi_version_and_struct_layout():
 
 def test_status_strings():
     for s in range(0, 10):
-        assert bqw.status_str(s)
+        assert bqw.status_str(s) and bqw.status_str(s) != bqw.status_str(99)
     assert "workspace" in bqw.status_str(9)
     assert bqw.status_str(0) == "ok"
     assert "unknown" in bqw.status_str(99)
