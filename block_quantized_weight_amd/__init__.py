@@ -23,6 +23,8 @@ FAMILY_NAMES = {v: k for k, v in FAMILIES.items()}
 
 QGEMV_OK = 0
 QGEMV_E_WORKSPACE = 9
+QGEMV_E_SCRATCH = 10
+NOALLOC_SCRATCH_BYTES = 8 << 20  # QGEMV_NOALLOC_SCRATCH_BYTES
 FLAG_FAMILY_MASK = 0x0000000F
 FLAG_KPARTS_SHIFT = 4
 FLAG_KSPLIT_SHIFT = 8
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
             L.qgemv_run.restype = ctypes.c_int
             L.qgemv_run_ws.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
             L.qgemv_run_ws.restype = ctypes.c_int
+            L.qgemv_run_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, vp]
+            L.qgemv_run_noalloc.restype = ctypes.c_int
             L.qgemv_workspace_size.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
             L.qgemv_workspace_size.restype = ctypes.c_int
             L.qgemv_plan.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(PlanInfo)]
@@ -199,6 +203,21 @@ class QGemv:
             where = "qgemv_run_ws"
         if rc != QGEMV_OK:
             raise QGemvError(rc, where)
+
+    def run_noalloc(self, A: Any, Y: Any, M: Optional[int] = None, stream: Any = None) -> None:
+        """qgemv_run_noalloc: the qgemv_run_ws product with the library's own device
+        scratch array as the workspace; allocates nothing. Calls that overlap in time
+        on one device share that array and must be serialized by the caller."""
+        if M is None:
+            M = int(A.shape[0])
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        rc = lib().qgemv_run_noalloc(self._h, _ptr(A), _ptr(Y), int(M), ctypes.c_void_p(stream))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_run_noalloc")
 
     def workspace_size(self, M: int = MAX_M) -> int:
         """Bytes of workspace qgemv_run_ws needs for M rows (0: none)."""

@@ -29,7 +29,12 @@ struct qgemv_handle {
     qgemv::LaunchCfg plan[2][2][QGEMV_MAX_M];
     int plan_rc[2][2][QGEMV_MAX_M];
     qgemv::KArgs args;  // kernel arguments common to every call (M, A, Y set per call)
+    void *scratch;      // the device's scratch array (qgemv_run_noalloc), or nullptr
 };
+
+namespace qgemv {
+int scratch_address(int device, void **out);  // scratch.hip
+}
 
 namespace {
 
@@ -122,14 +127,15 @@ hipError_t launch_rows(const qgemv::LaunchCfg &c, const qgemv::KArgs &a0, const 
     }
 }
 
-// Shared body of qgemv_run and qgemv_run_ws: the cached plan (with or without a
-// workspace) for min(M, 16) rows, the workspace check, and the launches. More than 16
-// rows run as chunks of 16 (the last one shorter), one after another on the stream,
-// each with the 16-row plan: a row's arithmetic does not depend on the chunk that
-// carries it, and the workspace, all zero again after each chunk, serves every chunk
-// in turn.
+// Shared body of qgemv_run, qgemv_run_ws and qgemv_run_noalloc: the cached plan
+// (with or without a workspace) for min(M, 16) rows, the workspace check, and the
+// launches. More than 16 rows run as chunks of 16 (the last one shorter), one after
+// another on the stream, each with the 16-row plan: a row's arithmetic does not depend
+// on the chunk that carries it, and the workspace, all zero again after each chunk,
+// serves every chunk in turn. short_ws: the status for a workspace that is missing or
+// too small (QGEMV_E_SCRATCH when it is the library's own array).
 int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
-             void *hip_stream) {
+             void *hip_stream, int short_ws = QGEMV_E_WORKSPACE) {
     if (!h || !A || !Y) return QGEMV_E_NULL;
     if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
     const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
@@ -143,7 +149,7 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
     a.M = Mp;
     a.ksplit = c.ksplit;
     if (c.kparts > 1) {
-        if (!ws || (uintptr_t)ws % 256 || ws_bytes < (size_t)c.ws_bytes) return QGEMV_E_WORKSPACE;
+        if (!ws || (uintptr_t)ws % 256 || ws_bytes < (size_t)c.ws_bytes) return short_ws;
         a.kparts = c.kparts;
         a.cnt = (uint32_t *)ws;
         a.part = (float *)((unsigned char *)ws + c.ws_counters);
@@ -190,6 +196,9 @@ const char *qgemv_status_str(int s) {
     case QGEMV_E_ARG: return "invalid argument";
     case QGEMV_E_ALLOC: return "host allocation failed";
     case QGEMV_E_WORKSPACE: return "the plan needs a workspace: none, or too small or misaligned a one, was given";
+    case QGEMV_E_SCRATCH:
+        return "the plan needs more workspace than qgemv_run_noalloc's fixed scratch array "
+               "(QGEMV_NOALLOC_SCRATCH_BYTES) holds; use qgemv_run_ws with a larger workspace";
     default: return "unknown status";
     }
 }
@@ -221,6 +230,10 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
                 c.device = dev;
             }
     fill_args(h, nullptr, nullptr, 1, &h->args);
+    // the device's scratch array for qgemv_run_noalloc (set up with the first handle on
+    // the device); a failure here only disables that entry point
+    h->scratch = nullptr;
+    if (qgemv::scratch_address(dev, &h->scratch) != QGEMV_OK) h->scratch = nullptr;
     *out = h;
     return QGEMV_OK;
 }
@@ -251,6 +264,12 @@ int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_st
 int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *workspace, size_t workspace_bytes,
                  void *hip_stream) {
     return run_plan(h, A, Y, M, true, workspace, workspace_bytes, hip_stream);
+}
+
+int qgemv_run_noalloc(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream) {
+    if (!h) return QGEMV_E_NULL;
+    if (!h->scratch) return QGEMV_E_DEVICE;
+    return run_plan(h, A, Y, M, true, h->scratch, QGEMV_NOALLOC_SCRATCH_BYTES, hip_stream, QGEMV_E_SCRATCH);
 }
 
 int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes) {

@@ -37,11 +37,12 @@
  * FP4 decode and M-tiling", reviewed-changes table; "[CUDA] Pin FP8 GEMV residency
  * for grids just past two blocks per SM", a timeline note on its tests). NULL means none.
  *
- * All pointers passed to qgemv_create, qgemv_run and qgemv_run_ws are DEVICE
- * pointers, owned by the caller. The handle keeps the weight pointers (not copies)
- * and the caller keeps them alive until qgemv_destroy. The library allocates no
- * device memory: the one kernel that needs scratch memory (the K split across
- * workgroups of qgemv_run_ws) takes it from the caller.
+ * All pointers passed to qgemv_create, qgemv_run, qgemv_run_ws and qgemv_run_noalloc
+ * are DEVICE pointers, owned by the caller. The handle keeps the weight pointers (not
+ * copies) and the caller keeps them alive until qgemv_destroy. The library allocates
+ * no device memory: the one kernel that needs scratch memory (the K split across
+ * workgroups of qgemv_run_ws) takes it from the caller, or, through qgemv_run_noalloc,
+ * from a fixed device array the library holds.
  *
  * Every call returns QGEMV_OK (0) or a positive status; nothing aborts, prints or
  * throws across this interface. Arguments are validated before anything is
@@ -57,11 +58,14 @@
 extern "C" {
 #endif
 
-#define QGEMV_ABI_VERSION 4
+#define QGEMV_ABI_VERSION 5
 /* Rows one plan carries; a call with more runs them as chunks of this many. */
 #define QGEMV_MAX_M 16
 /* Rows one call accepts. */
 #define QGEMV_MAX_ROWS 65536
+/* Bytes of the library's own device scratch array that qgemv_run_noalloc uses in place
+ * of a workspace (one copy per device, held until the process ends). */
+#define QGEMV_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /* Weight formats. */
 enum qgemv_format {
@@ -88,8 +92,10 @@ enum qgemv_status {
     QGEMV_E_LAUNCH = 6,   /* the kernel launch reported an error */
     QGEMV_E_ARG = 7,      /* other invalid argument (struct size, flags, plan request) */
     QGEMV_E_ALLOC = 8,    /* host memory for the handle could not be allocated */
-    QGEMV_E_WORKSPACE = 9 /* qgemv_run_ws: the plan needs a workspace and none, or too small
-                             or misaligned a one, was given */
+    QGEMV_E_WORKSPACE = 9, /* qgemv_run_ws: the plan needs a workspace and none, or too small
+                              or misaligned a one, was given */
+    QGEMV_E_SCRATCH = 10   /* qgemv_run_noalloc: the plan needs more workspace than
+                              QGEMV_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Kernel families (qgemv_plan_info.family; also usable in QGEMV_FLAG_FORCE). */
@@ -247,6 +253,23 @@ int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_st
  * misaligned a one, is given. */
 int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *workspace,
                  size_t workspace_bytes, void *hip_stream);
+
+/* qgemv_run_ws without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc. The same plans and kernels as qgemv_run_ws,
+ * with the library's own device array of QGEMV_NOALLOC_SCRATCH_BYTES (8 MiB, one per
+ * device, set up and zeroed when the first handle for that device is created, held
+ * until the process ends) as the workspace; the result is bit-identical to
+ * qgemv_run_ws's. The call allocates nothing and frees nothing. Returns
+ * QGEMV_E_SCRATCH, before any launch, when the plan for M rows needs more workspace
+ * than the array holds (qgemv_workspace_size reports the need; automatic plans on a
+ * 256-CU device need at most 4 MiB), and QGEMV_E_DEVICE when the array could not be
+ * set up. Every completed call leaves the area it used zero again, which is how the
+ * next call finds its counters. All calls on one device share the one array: calls
+ * that overlap in time on one device (different streams, or threads) race on it and
+ * must be serialized by the caller. The other arguments and the threading contract
+ * are those of qgemv_run_ws. */
+int qgemv_run_noalloc(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_stream);
 
 /* Bytes of workspace qgemv_run_ws needs for M rows (0 when its plan has no K parts).
  * Sized at M = QGEMV_MAX_M, a workspace serves every M. */

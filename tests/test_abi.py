@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_workspace_size", "qgemv_plan",
+    assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_run_noalloc", "qgemv_workspace_size", "qgemv_plan",
             "qgemv_select", "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version"} <= names
     L = bqw.lib()
     for n in sorted(names):
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert bqw.lib().qgemv_abi_version() == 4
+    assert bqw.lib().qgemv_abi_version() == 5
     # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields; the
     # bias pointer (version 2) follows the flags
     assert ctypes.sizeof(bqw.Desc) == 72
@@ -45,9 +45,10 @@ def test_abi_version_and_struct_layout():
 
 
 def test_status_strings():
-    for s in range(0, 10):
+    for s in range(0, 11):
         assert bqw.status_str(s) and bqw.status_str(s) != bqw.status_str(99)
     assert "workspace" in bqw.status_str(9)
+    assert "scratch" in bqw.status_str(10)
     assert bqw.status_str(0) == "ok"
     assert "unknown" in bqw.status_str(99)
 

@@ -66,7 +66,7 @@ def _gfx950_objects(blob):
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
     objs = _gfx950_objects(_section(LIB, ".hip_fatbin"))
-    assert len(objs) == 2, "one gfx950 code object per HIP source expected"
+    assert len(objs) == 3, "one gfx950 code object per HIP source expected (two kernel files, the scratch array)"
     recs = {}
     for i, obj in enumerate(objs):
         path = tmp_path_factory.mktemp("co") / f"co{i}.o"
