@@ -3,18 +3,24 @@
 One step = one qgemv_run_ws call (dispatch + kernel) over one batch of synthetic
 input: Y[M, N] = A[M, K] . dequant(W)^T, with a workspace allocated and zeroed once
 before the timed region (plans that split K across workgroups use it, others ignore
-it; --no-workspace times qgemv_run instead). The weights are cold: the timed loop rotates
-through enough copies of the weight (>= 1 GiB together, several times the 256 MB
-last-level cache) that every call streams its weight from HBM. Inputs are resident in
-HBM before the timed region starts.
+it; --no-workspace times qgemv_run instead). The weights are cold: the timed loop
+rotates through R copies of the weight (R * weight bytes >= 1 GiB, four times the
+256 MB last-level cache; R <= 4096, copies held in one device buffer per array), and
+the rotation continues from the warmup, so every call streams a weight last touched
+at least 1 GiB of traffic earlier (310 MB for the 75 KB tiny case, still past the
+cache). Inputs are resident in HBM before the timed region starts.
 
-Prints one JSON line. `value` is achieved GB/s = weight bytes (codes + block scales +
-zero points) per call / average time per call. The roofline object reports the same
-bytes against the 8 TB/s HBM peak; its `traffic` is the HBM bytes per launch that two
-rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) measured for this workload, read from
-the summaries under profiles/ and only while the built kernels still hash to what
-was profiled (null otherwise). `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload on this host.
+The default workload is the 4-bit lm_head (K = 4096, N = 151936, bf16): `value` is its
+achieved GB/s at M = 1 = weight bytes (codes + block scales + zero points) per call /
+average time per call; the same line carries the M sweep 1, 2, 4, 8, 16 of that weight
+(us/call, GB/s, t(M)/t(1), plan) and the FP8 5120 x 6144 projection at M = 1, 4, 8.
+`roofline` reports the M = 1 figure against the 8 TB/s HBM peak and against a plain
+streaming read of the same bytes (the control kernel in libreadctl.so, timed with the
+same cold rotation); its `traffic` is the HBM bytes per launch that two rocprofv3
+counter runs (FETCH_SIZE, WRITE_SIZE) measured for this workload, read from the
+summaries under profiles/ and only while the built kernels still hash to what was
+profiled (null otherwise). `cpu_baseline` times the CPU oracle on a bounded sample of
+the same workload on this host, on all threads and on one.
 
 Profiling helpers (no GPU needed):
   --calib-copy-mib X      also run one plain copy kernel of X MiB (torch.neg on fp32)
@@ -38,10 +44,15 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "u8_m1_k4096_n4096"
+DEFAULT_WORKLOAD = "u4_k4096_n151936"
+# second workload of the default line: the FP8 projection at the metric's M = 1, 4, 8
+EXTRA_WORKLOADS = (("fp8_k6144_n5120", (1, 4, 8)),)
+METRIC = "achieved HBM GB/s (weight bytes/kernel time) and us/call at M=1,4,8"
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 1 << 30
+MAX_COPIES = 4096
 PROFILES = os.path.join(ROOT, "profiles")
+READ_CONTROL_LIB = os.path.join(ROOT, "block_quantized_weight_amd", "libreadctl.so")
 
 
 def parse():
@@ -54,7 +65,10 @@ def parse():
                    help="time an arbitrary shape instead of a named workload (e.g. fp8:f16:8192:4096:128), "
                         "drawn by synth.make_problem with its default value distributions")
     p.add_argument("--seed", type=int, default=7, help="seed for --shape")
-    p.add_argument("--m", type=int, default=None, help="rows of A (default: the workload's first M; 1 for --shape)")
+    p.add_argument("--m", type=int, default=None,
+                   help="rows of A (default: the workload's M sweep, the first M as the headline; 1 for --shape)")
+    p.add_argument("--no-extra", action="store_true", help="skip the FP8 projection's M = 1, 4, 8 lines")
+    p.add_argument("--no-read-control", action="store_true", help="skip the plain streaming read control")
     p.add_argument("--flags", type=int, default=0, help="qgemv_desc.flags (force a family, K split)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
@@ -200,33 +214,195 @@ def lookup_traffic(workload, M, flags, ws=True):
     return None
 
 
-def cpu_baseline(prob, M, target_s):
-    """Time the CPU oracle (as it stands) on a bounded column sample of the workload."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    import oracle
+
+def _sub_problem(prob, ncols):
     from block_quantized_weight_amd import synth
 
-    # pick a column count that takes roughly target_s, after a short calibration
-    ncal = min(prob.N, 256)
-    sub = synth.Problem(**{**prob.__dict__, "N": ncal, "W": prob.W[:ncal], "scales": prob.scales[:ncal],
-                           "zp": None if prob.zp is None else prob.zp[:ncal]})
+    return synth.Problem(**{**prob.__dict__, "N": ncols, "W": prob.W[:ncols], "scales": prob.scales[:ncols],
+                            "zp": None if prob.zp is None else prob.zp[:ncols],
+                            "bias": None if prob.bias is None else prob.bias[:ncols]})
+
+
+def _time_oracle(prob, M, target_s, nthreads):
+    """(GB/s of weight, columns, repetitions, seconds per pass) of the oracle on a column
+    sample sized to take about target_s."""
+    import oracle
+
+    ncal = min(prob.N, 256 if nthreads != 1 else 32)
     t0 = time.perf_counter()
-    oracle.gemv(sub, M=M)
+    oracle.gemv(_sub_problem(prob, ncal), M=M, nthreads=nthreads)
     dt = max(time.perf_counter() - t0, 1e-4)
     ncols = int(min(prob.N, max(ncal, ncal * target_s / dt)))
     reps = max(1, int(math.ceil(ncal * target_s / dt / max(ncols, 1))))
-    sub = synth.Problem(**{**prob.__dict__, "N": ncols, "W": prob.W[:ncols], "scales": prob.scales[:ncols],
-                           "zp": None if prob.zp is None else prob.zp[:ncols]})
+    sub = _sub_problem(prob, ncols)
     t0 = time.perf_counter()
     for _ in range(reps):
-        oracle.gemv(sub, M=M)
+        oracle.gemv(sub, M=M, nthreads=nthreads)
     el = (time.perf_counter() - t0) / reps
-    bytes_per_col = prob.weight_bytes() / prob.N
-    return {"value": round(bytes_per_col * ncols / el / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+    return prob.weight_bytes() / prob.N * ncols / el / 1e9, ncols, reps, el
+
+
+def cpu_baseline(prob, M, target_s):
+    """Time the CPU oracle (as it stands) on a bounded column sample of the workload: on
+    all host threads (the reported value) and on one thread."""
+    import oracle
+
+    nt = oracle.max_threads()
+    gbs, ncols, reps, el = _time_oracle(prob, M, target_s, nt)
+    gbs1, ncols1, reps1, el1 = _time_oracle(prob, M, max(target_s / 2, 0.05), 1)
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": nt, "kind": "oracle",
             "sample": f"{ncols} of {prob.N} columns x {reps} repetition(s), M={M}, fp64 plain loops, "
-                      f"{el * 1e3:.1f} ms per sample pass"}
+                      f"{el * 1e3:.1f} ms per sample pass",
+            "single_thread": {"value": round(gbs1, 6), "unit": "GB/s", "cores": 1,
+                              "sample": f"{ncols1} columns x {reps1} repetition(s), {el1 * 1e3:.1f} ms per pass"},
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
+
+
+class Rotation:
+    """R cold copies of a problem's weight arrays, each array's copies in one device
+    buffer, and one handle per copy (R * weight bytes >= COLD_BYTES, R <= MAX_COPIES)."""
+
+    def __init__(self, prob, flags, dev, warm=False):
+        import numpy as np
+        import torch
+
+        import block_quantized_weight_amd as bqw
+
+        wbytes = prob.weight_bytes()
+        self.copies = 1 if warm else int(min(MAX_COPIES, max(2, math.ceil(COLD_BYTES / wbytes))))
+        R = self.copies
+
+        def rep(a):
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            buf = torch.empty((R,) + tuple(t.shape), dtype=t.dtype, device=dev)
+            buf[0].copy_(t)
+            if R > 1:
+                buf[1:].copy_(t.unsqueeze(0).expand((R - 1,) + tuple(t.shape)))
+            return buf
+
+        self.W = rep(prob.W)
+        self.S = rep(prob.scales if prob.scales.dtype == np.float32 else prob.scales.view(np.uint8))
+        self.Z = None if prob.zp is None else rep(prob.zp)
+        tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
+        self.bias = None if prob.bias is None else \
+            torch.from_numpy(prob.bias.view(np.int16)).to(dev).view(tdt)
+        self.handles = [bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, self.W[i], self.S[i],
+                                  None if self.Z is None else self.Z[i], prob.tensor_scale, flags, bias=self.bias)
+                        for i in range(R)]
+
+    def close(self):
+        for q in self.handles:
+            q.close()
+
+
+def time_calls(rot, A, Y, M, stream, ws, warmup, steps):
+    """(ms per call from HIP events on the launch stream, wall seconds of the timed
+    loop). The rotation continues from the warmup into the timed loop."""
+    import torch
+
+    R = rot.copies
+    hs = rot.handles
+    for i in range(warmup):
+        hs[i % R].run(A, Y, M, stream, workspace=ws)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(warmup, warmup + steps):
+        hs[i % R].run(A, Y, M, stream, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+
+READ_CONTROL_SHAPES = ((2048, 4), (2048, 8), (4096, 4), (4096, 8), (8192, 4), (1024, 16), (2048, 16))
+
+
+def time_read_control(nbytes, dev, stream, warmup, steps):
+    """The plain streaming read of nbytes, cold like the GEMV (copies rotated, the
+    rotation continuing from the warmup), for each (workgroups, loads in flight per
+    lane) of READ_CONTROL_SHAPES: the fastest, as the control is a ceiling. Returns
+    (ms per read, GB/s, shape, {shape: GB/s})."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(READ_CONTROL_LIB):
+        raise SystemExit(f"{READ_CONTROL_LIB} is missing: build with block_quantized_weight_amd.build.build()")
+    L = ctypes.CDLL(READ_CONTROL_LIB)
+    L.read_control.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    L.read_control.restype = ctypes.c_int
+    nb = (nbytes + 15) // 16 * 16
+    R = int(min(MAX_COPIES, max(2, math.ceil(COLD_BYTES / nb))))
+    buf = torch.randint(0, 255, (R, nb), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    never = 0x9E3779B9  # the xor fold of random bytes lands here with probability 2^-32
+    best, table = None, {}
+    for blocks, unroll in READ_CONTROL_SHAPES:
+        def go(i):
+            rc = L.read_control(buf[i % R].data_ptr(), nb, blocks, unroll, never, sink.data_ptr(), stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"read control launch failed ({rc})")
+
+        for i in range(warmup):
+            go(i)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(warmup, warmup + steps):
+            go(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        gbs = nb / (ms * 1e-3) / 1e9
+        table[f"{blocks}x256 threads, {unroll} loads"] = round(gbs, 1)
+        if best is None or ms < best[0]:
+            best = (ms, gbs, (blocks, unroll))
+    del buf
+    return best[0], best[1], best[2], table
+
+
+def measure(prob, ms, args, dev, stream):
+    """Time the problem at every M in ms: {M: {...}} plus the rotation size."""
+    import torch
+
+    rot = Rotation(prob, args.flags, dev, warm=args.warm)
+    tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
+    import numpy as np
+
+    A_all = torch.from_numpy(prob.A.view(np.int16)).to(dev).view(tdt)
+    use_ws = not args.no_workspace
+    wbytes = prob.weight_bytes()
+    out = {}
+    ws = None
+    for M in ms:
+        plan = rot.handles[0].plan(M, with_workspace=use_ws)
+        if use_ws and (ws is None or ws.numel() < plan["workspace_bytes"]):
+            ws = torch.zeros(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
+        A = A_all[:M].contiguous()
+        Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
+        msc, wall = time_calls(rot, A, Y, M, stream, ws if use_ws else None, args.warmup, args.steps)
+        out[M] = {"us_per_call": round(msc * 1e3, 3), "gbs": round(wbytes / (msc * 1e-3) / 1e9, 2),
+                  "ms_per_step": msc, "wall_s": round(wall, 4), "plan": plan}
+    t1 = out[ms[0]]["us_per_call"]
+    for M in ms:
+        out[M]["t_over_t_first"] = round(out[M]["us_per_call"] / t1, 3)
+    copies = rot.copies
+    rot.close()
+    return out, copies
 
 
 def main():
@@ -243,14 +419,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import block_quantized_weight_amd as bqw
     from block_quantized_weight_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
     if args.shape:
         fmt, act, n_s, k_s, bs_s = args.shape.split(":")
         M = args.m if args.m is not None else 1
@@ -258,38 +433,12 @@ def main():
                                   ms=(M,), with_bias=args.bias)
         workload = f"shape_{fmt}_{act}_n{n_s}_k{k_s}_bs{bs_s}"
         seed = args.seed
+        ms = (M,)
     else:
         prob = synth.workload(args.workload, with_bias=args.bias)
-        M = args.m if args.m is not None else prob.ms[0]
+        ms = (args.m,) if args.m is not None else tuple(prob.ms)
         workload = args.workload
         seed = synth.WORKLOADS[args.workload]["seed"]
-    wbytes = prob.weight_bytes()
-    copies = 1 if args.warm else max(2, int(math.ceil(COLD_BYTES / wbytes)))
-
-    # device buffers: one copy of each input per rotation slot
-    def dev_t(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    W0 = dev_t(prob.W)
-    S0 = dev_t(prob.scales if prob.scales.dtype == np.float32 else prob.scales.view(np.uint8))
-    Z0 = None if prob.zp is None else dev_t(prob.zp)
-    tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
-    A = dev_t(prob.A[:M].view(np.int16)).view(tdt).contiguous()
-    bias = None if prob.bias is None else dev_t(prob.bias.view(np.int16)).view(tdt)
-    Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
-    slots = []
-    for i in range(copies):
-        W = W0 if i == 0 else W0.clone()
-        S = S0 if i == 0 else S0.clone()
-        Z = Z0 if (i == 0 or Z0 is None) else Z0.clone()
-        q = bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, W, S, Z, prob.tensor_scale, args.flags,
-                      bias=bias)
-        slots.append((q, W, S, Z))
-    use_ws = not args.no_workspace
-    plan = slots[0][0].plan(M, with_workspace=use_ws)
-    # one workspace for every rotation slot (their plans are the same), zeroed once
-    ws = torch.zeros(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device=dev) if use_ws else None
-    stream = torch.cuda.current_stream()
     if args.calib_copy_mib > 0:
         # one plain copy kernel of known size, for scaling counter readings
         csrc = torch.ones(args.calib_copy_mib * (1 << 18), dtype=torch.float32, device=dev)
@@ -298,38 +447,45 @@ def main():
         torch.neg(csrc, out=cdst)
         torch.cuda.synchronize()
         del csrc, cdst
-    torch.cuda.synchronize()
+    wbytes = prob.weight_bytes()
+    sweep, copies = measure(prob, ms, args, dev, stream)
+    M = ms[0]
+    head = sweep[M]
+    gbs = head["gbs"]
+    ms_per = head["ms_per_step"]
 
-    for i in range(args.warmup):
-        slots[i % copies][0].run(A, Y, M, stream, workspace=ws)
-    torch.cuda.synchronize()
+    extra = {}
+    if not args.no_extra and not args.shape and args.workload == DEFAULT_WORKLOAD and args.m is None:
+        for name, ems in EXTRA_WORKLOADS:
+            p2 = synth.workload(name)
+            res, c2 = measure(p2, ems, args, dev, stream)
+            extra[name] = {"weight_bytes": p2.weight_bytes(), "cold_copies": c2,
+                           "by_m": {str(m): {k: v for k, v in r.items() if k != "ms_per_step"}
+                                    for m, r in res.items()}}
+            del p2
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        slots[i % copies][0].run(A, Y, M, stream, workspace=ws)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per = ms_total / args.steps
-    gbs = wbytes / (ms_per * 1e-3) / 1e9
+    read = None
+    if not args.no_read_control:
+        rms, rgbs, shape, table = time_read_control(wbytes, dev, stream, args.warmup, args.steps)
+        read = {"bytes": wbytes, "us_per_read": round(rms * 1e3, 3), "gbs": round(rgbs, 2),
+                "kernel": f"k_read_control (libreadctl.so): 16-byte nontemporal loads, {shape[1]} in flight per "
+                          f"lane, {shape[0]} workgroups of 256 threads (fastest of the shapes tried)",
+                "shapes_gbs": table}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(prob, M, args.cpu_seconds)
 
+    use_ws = not args.no_workspace
     out = {
-        "metric": "achieved HBM GB/s (weight bytes / kernel time), cold weights",
-        "value": round(gbs, 2),
+        "metric": METRIC,
+        "value": gbs,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per, 6),
-        "us_per_call": round(ms_per * 1e3, 3),
+        "us_per_call": head["us_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -337,16 +493,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "format": prob.fmt, "act": prob.act, "M": M, "N": prob.N,
                    "K": prob.K, "block_size": prob.bs, "weight_bytes": wbytes, "cold_copies": copies,
-                   "plan": plan, "flags": args.flags, "seed": seed, "bias": bool(args.bias),
+                   "plan": head["plan"], "flags": args.flags, "seed": seed, "bias": bool(args.bias),
                    "entry": "qgemv_run_ws" if use_ws else "qgemv_run"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "m_sweep": {str(m): {k: v for k, v in r.items() if k != "ms_per_step"} for m, r in sweep.items()},
+        "extra_workloads": extra or None,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if args.shape else lookup_traffic(args.workload, M, args.flags, use_ws)},
+                     "traffic": None if args.shape else lookup_traffic(args.workload, M, args.flags, use_ws),
+                     "read_control_gbs": None if read is None else read["gbs"],
+                     "frac_of_read_control": None if read is None else round(gbs / read["gbs"], 4)},
+        "read_control": read,
         "cpu_baseline": cpu,
-        "wall_s": round(wall, 4),
+        "wall_s": head["wall_s"],
     }
-    for q, *_ in slots:
-        q.close()
     print(json.dumps(out), flush=True)
 
 

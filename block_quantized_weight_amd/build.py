@@ -50,19 +50,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link libqgemv.so next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+READ_CONTROL_SRC = "read_control.hip"
+READ_CONTROL_OUT = os.path.join(PKG, "libreadctl.so")
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link libqgemv.so next to this file, and the benchmark's
+    plain-read control (libreadctl.so, a separate library the GEMV never loads)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + [READ_CONTROL_SRC]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], READ_CONTROL_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", READ_CONTROL_OUT)
     return OUT
 
 

@@ -234,11 +234,12 @@ int oracle_gemv(const orc_problem *p, const uint16_t *A, int M, double *Y, doubl
     if (!A || !Y || !S) return 1;
     build_tables();
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    /* a thread count for this call only (the process-wide default stays as it is) */
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
     (void)nthreads;
 #endif
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
     {
         double *w = (double *)malloc((size_t)p->K * sizeof(double));
 #pragma omp for schedule(static)

@@ -71,6 +71,8 @@ def test_cpu_baseline_times_the_oracle_on_a_sample():
     assert out["kind"] == "oracle" and out["unit"] == "GB/s"
     assert out["value"] > 0 and out["cores"] >= 1
     assert "columns" in out["sample"]
+    assert out["single_thread"]["cores"] == 1 and out["single_thread"]["value"] > 0
+    assert out["cpu_model"]
 
 
 def test_committed_profiles_name_their_commands():
