@@ -326,7 +326,8 @@ def time_calls(rot, A, Y, M, stream, ws, warmup, steps):
     return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
 
 
-READ_CONTROL_SHAPES = ((2048, 4), (2048, 8), (4096, 4), (4096, 8), (8192, 4), (1024, 16), (2048, 16))
+READ_CONTROL_SHAPES = ((2048, 4), (4096, 4), (4096, 8), (8192, 4), (8192, 8), (16384, 4), (32768, 4),
+                       (2048, 16))
 
 
 def time_read_control(nbytes, dev, stream, warmup, steps):

@@ -27,8 +27,10 @@ QGEMV_E_SCRATCH = 10
 NOALLOC_SCRATCH_BYTES = 8 << 20  # QGEMV_NOALLOC_SCRATCH_BYTES
 FLAG_FAMILY_MASK = 0x0000000F
 FLAG_KPARTS_SHIFT = 4
+FLAG_STREAM_META_CHUNK = 0x00000080
 FLAG_KSPLIT_SHIFT = 8
 FLAG_STREAM_NWG_SHIFT = 12
+FLAG_NO_RESIDENCY_FIT = 0x00008000
 FLAG_NO_MFMA = 0x00010000
 FLAG_STAGE_A_OFF = 0x00020000
 FLAG_STAGE_A_ON = 0x00040000

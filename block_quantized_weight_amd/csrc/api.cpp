@@ -164,6 +164,48 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
     return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
 }
 
+// Persistent launches: every workgroup walks its share of the work, so the grid may
+// be anything up to the work units. (K-part and classic streaming launches need one
+// workgroup per unit.)
+bool persistent(const qgemv::LaunchCfg &c) {
+    if (c.family == QGEMV_FAMILY_MFMA) return c.kparts == 1;
+    if (c.family == QGEMV_FAMILY_STREAM) return (c.variant & 1) != 0;
+    return c.family == QGEMV_FAMILY_GENERIC;
+}
+
+// Keep a persistent grid within what stays resident at once. The dispatcher sizes
+// persistent grids from LDS and a wave budget per CU; the registers the compiler gave
+// the kernel can allow fewer workgroups per CU than that, and a grid past the resident
+// count leaves a second, partly empty round of workgroups that start only as the first
+// finish: the near-empty tail past a whole number of resident blocks per SM that the
+// pages fix by pinning the kernel's residency ("[CUDA] Pin FP8 GEMV residency for
+// grids just past two blocks per SM", Description). On gfx950 a register cap that
+// raises the residency makes the register-ring kernels spill, so the grid is cut to
+// the resident count instead, which the runtime reports for the kernel as compiled.
+void fit_residency(const qgemv_handle *h, qgemv::LaunchCfg *c, int m) {
+    if (!persistent(*c) || ((h->d.flags | h->env_flags) & QGEMV_FLAG_NO_RESIDENCY_FIT)) return;
+    qgemv::KernelRef ref{nullptr, 0, 0};
+    qgemv::LaunchCfg q = *c;
+    q.query = &ref;
+    qgemv::KArgs a = h->args;
+    a.M = (c->family == QGEMV_FAMILY_MFMA && m > c->rows_per_pass) ? c->rows_per_pass : m;
+    a.ksplit = c->ksplit;
+    a.kparts = c->kparts;
+    hipError_t e;
+    switch (c->family) {
+    case QGEMV_FAMILY_STREAM: e = qgemv::launch_stream(q, a, nullptr); break;
+    case QGEMV_FAMILY_MFMA: e = qgemv::launch_mfma(q, a, nullptr); break;
+    default: e = qgemv::launch_generic(q, a, nullptr); break;
+    }
+    if (e != hipSuccess || !ref.fn) return;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ref.fn, ref.threads, (size_t)ref.lds_bytes) != hipSuccess ||
+        per_cu < 1)
+        return;
+    const int64_t cap = (int64_t)per_cu * h->cu_count;
+    if (c->grid > cap) c->grid = cap;
+}
+
 // The plan of M rows as reported: the 16-row plan, its passes counted over all the
 // chunks of 16 rows.
 int plan_rows(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t env_flags, bool with_ws,
@@ -230,6 +272,10 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
                 c.device = dev;
             }
     fill_args(h, nullptr, nullptr, 1, &h->args);
+    for (int w = 0; w < 2; ++w)
+        for (int f = 0; f < 2; ++f)
+            for (int m = 1; m <= QGEMV_MAX_M; ++m)
+                if (!h->plan_rc[w][f][m - 1]) fit_residency(h, &h->plan[w][f][m - 1], m);
     // the device's scratch array for qgemv_run_noalloc (set up with the first handle on
     // the device); a failure here only disables that entry point
     h->scratch = nullptr;
@@ -240,9 +286,13 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device) {
 
 int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info *out) {
     if (!h || !out) return QGEMV_E_NULL;
-    qgemv::LaunchCfg c;
-    int rc = plan_rows(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, with_workspace != 0, &c);
+    if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
+    const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
+    const int w = with_workspace ? 1 : 0;
+    const int rc = h->plan_rc[w][1][Mp - 1];
     if (rc) return rc;
+    qgemv::LaunchCfg c = h->plan[w][1][Mp - 1];
+    c.passes *= (M + Mp - 1) / Mp;
     to_info(c, out);
     return QGEMV_OK;
 }

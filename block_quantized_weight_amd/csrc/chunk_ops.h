@@ -383,6 +383,49 @@ __device__ __forceinline__ void meta_load_s(const KArgs &a, const ColPtrs &p, in
     }
 }
 
+// 8-bit codes: the block metadata of one round of a column group (64 * UNR consecutive
+// chunks per column) loaded as ONE dword per lane per column instead of two small
+// loads per chunk: lane l holds dword l of the round's scale window and dword l of its
+// zero-point window (clamped to the row's last dword, so lanes past a short window
+// repeat it and nothing is read outside the row). A chunk's scale and zero-point bytes
+// are then taken from the lane that holds them with one ds_bpermute each (a lane
+// crossbar, no memory traffic): the very bytes meta_load_s reads. The host takes this
+// path where a round's windows fit in 64 dwords and the rows are whole dwords on
+// 4-byte aligned arrays.
+struct MetaW {
+    uint32_t s, z;
+};
+
+// Blocks of one round (UNR chunks of 16 k per lane), the dword its windows start at.
+template <int UNR>
+__device__ __forceinline__ int u8_round_blocks(const KArgs &a) {
+    return (64 * UNR * 16) >> a.bs_shift;
+}
+
+template <int UNR>
+__device__ __forceinline__ MetaW meta_window_load_u8(const KArgs &a, const ColPtrs &p, int round, int lane) {
+    const int bpr = u8_round_blocks<UNR>(a);
+    MetaW m;
+    const int sd0 = (round * bpr) >> 1, slast = (a.nblk >> 1) - 1;  // fp16 scales: 2 per dword
+    const int sd = sd0 + lane < slast ? sd0 + lane : slast;
+    m.s = ((const uint32_t *)p.s)[sd];
+    const int zd0 = (round * bpr) >> 2, zlast = (a.zstride >> 2) - 1;  // zero points: 4 per dword
+    const int zd = zd0 + lane < zlast ? zd0 + lane : zlast;
+    m.z = ((const uint32_t *)p.z)[zd];
+    return m;
+}
+
+// The raw metadata (what meta_load_s loads) of local chunk lc = 64 u + lane of the
+// round, from the round's window dwords.
+template <int UNR>
+__device__ __forceinline__ void meta_from_window_u8(const KArgs &a, const MetaW &w, int lc, MetaS<1> &m) {
+    const int lb = (lc * 16) >> a.bs_shift;  // the chunk's block within the round
+    const uint32_t sv = (uint32_t)__builtin_amdgcn_ds_bpermute((lb >> 1) << 2, (int)w.s);
+    const uint32_t zv = (uint32_t)__builtin_amdgcn_ds_bpermute((lb >> 2) << 2, (int)w.z);
+    m.s[0] = (sv >> ((lb & 1) << 4)) & 0xFFFFu;
+    m.z[0] = (zv >> ((lb & 3) << 3)) & 0xFFu;
+}
+
 // Scale and integer zero point of each half of chunk c; zs is zsel(a.zp, midpoint
 // byte) (0x88 for U4, 128 for U8), so a weight without zero points takes the midpoint.
 template <int FMT, int H>

@@ -1144,8 +1144,7 @@ hipError_t go_p(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};  // per kernel: without / with K parts
     hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[kp ? 1 : 0]);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
-    return hipGetLastError();
+    return launch_or_report(cfg, kern, 512, a, s);
 }
 
 // Ring depth when the activations travel in the ring too: as deep as the register
@@ -1184,8 +1183,7 @@ hipError_t go_dma_rs(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(512), (size_t)cfg.lds_bytes, s, a);
-    return hipGetLastError();
+    return launch_or_report(cfg, kern, 512, a, s);
 }
 
 // DMA ring: 4-step slots, double-buffered; one or two row groups only

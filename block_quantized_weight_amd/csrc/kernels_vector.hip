@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 template <int FMT, int H, int UNR, int CPW>
 struct SBatch {
     u4v w[UNR][CPW];
-    MetaS<H> m[UNR][CPW];
+    MetaS<H> m[UNR][CPW];  // per-chunk metadata loads
+    MetaW mw[CPW];         // or the round's metadata windows (WM, 8-bit codes)
 };
 
 // Index (in 16-byte pieces) of piece q of chunk c of a staged activation row.
@@ -195,7 +196,10 @@ __device__ __forceinline__ void stage_rows(const KArgs &a, u4v *sP, float *sS, i
     }
 }
 
-template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
+// WM (8-bit codes): the block metadata of a round comes as one window dword per lane
+// per column (meta_window_load_u8) instead of per-chunk loads; the values, and so the
+// results, are the same.
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG, bool WM>
 __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     using Ops = ChunkOps<FMT, ACT, H>;
     using B = SBatch<FMT, H, UNR, CPW>;
@@ -233,12 +237,17 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) b.w[u][i] = load16_stream(cp[i].w + (uint32_t)cc * 16u);
         }
+        if constexpr (WM) {
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int c = ir * (64 * UNR) + 64 * u + lane;
-            const int cc = c < nch ? c : nch - 1;
+            for (int i = 0; i < CPW; ++i) b.mw[i] = meta_window_load_u8<UNR>(a, cp[i], ir, lane);
+        } else {
 #pragma unroll
-            for (int i = 0; i < CPW; ++i) meta_load_s<FMT, H>(a, cp[i], cc, b.m[u][i]);
+            for (int u = 0; u < UNR; ++u) {
+                const int c = ir * (64 * UNR) + 64 * u + lane;
+                const int cc = c < nch ? c : nch - 1;
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) meta_load_s<FMT, H>(a, cp[i], cc, b.m[u][i]);
+            }
         }
         if (++ir == rounds) {
             ir = 0;
@@ -279,7 +288,10 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                 for (int i = 0; i < CPW; ++i) {
                     float sc[H], part[H];
                     uint32_t zr[H];
-                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], zs, sc, zr);
+                    MetaS<H> mu;
+                    if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
+                    else mu = b.m[u][i];
+                    meta_decode_s<FMT, H>(a, cc, mu, zs, sc, zr);
                     chunk_dot<FMT, ACT, H>(b.w[u][i], zr, act, part);
                     float t = acc[i][0];
 #pragma unroll
@@ -293,7 +305,10 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                 uint32_t zr[CPW][H];
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
-                    meta_decode_s<FMT, H>(a, cc, b.m[u][i], zs, sc[i], zr[i]);
+                    MetaS<H> mu;
+                    if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
+                    else mu = b.m[u][i];
+                    meta_decode_s<FMT, H>(a, cc, mu, zs, sc[i], zr[i]);
                     Ops::decode(b.w[u][i], zr[i], wd[i]);
                 }
 #pragma unroll
@@ -445,16 +460,13 @@ template <int FMT, int ACT, int MT, int CPW>
 hipError_t go_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     // two scale blocks per chunk: every NVFP4 chunk, and U4 chunks with 16-wide blocks
     if constexpr (FMT == FMT_NVFP4) {
-        hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+        return launch_or_report(cfg, k_stream<FMT, ACT, MT, CPW, 2, 2>, 256, a, s);
     } else if constexpr (FMT == FMT_U4) {
-        if (a.bs == 16)
-            hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 2>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 1>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+        if (a.bs == 16) return launch_or_report(cfg, k_stream<FMT, ACT, MT, CPW, 2, 2>, 256, a, s);
+        return launch_or_report(cfg, k_stream<FMT, ACT, MT, CPW, 2, 1>, 256, a, s);
     } else {
-        hipLaunchKernelGGL((k_stream<FMT, ACT, MT, CPW, 2, 1>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
+        return launch_or_report(cfg, k_stream<FMT, ACT, MT, CPW, 2, 1>, 256, a, s);
     }
-    return hipGetLastError();
 }
 
 template <int FMT, int ACT, int MT>
@@ -481,12 +493,18 @@ hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 // (2 -> 2, 3 -> 3, 0 -> 4).
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
 hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    auto kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG>;
-    static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set);
+    // variant bit 3: the round's metadata windows (8-bit codes)
+    constexpr bool can_wm = FMT == FMT_U8;
+    const bool wm = (cfg.variant >> 3) & 1;
+    if (wm && !can_wm) return hipErrorInvalidValue;
+    void (*kern)(KArgs) = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, false>;
+    if constexpr (can_wm) {
+        if (wm) kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, true>;
+    }
+    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[wm ? 1 : 0]);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(64 * NWG), (size_t)cfg.lds_bytes, s, a);
-    return hipGetLastError();
+    return launch_or_report(cfg, kern, 64 * NWG, a, s);
 }
 
 // Workgroups of 4 waves; of 16 for one row with one column per wave; of 4, 8, 12 or
@@ -579,11 +597,8 @@ hipError_t pick_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 
 template <int FMT>
 hipError_t generic_act(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    if (cfg.act == ACT_F16)
-        hipLaunchKernelGGL((k_generic<FMT, ACT_F16>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_generic<FMT, ACT_BF16>), dim3((unsigned)cfg.grid), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (cfg.act == ACT_F16) return launch_or_report(cfg, k_generic<FMT, ACT_F16>, 256, a, s);
+    return launch_or_report(cfg, k_generic<FMT, ACT_BF16>, 256, a, s);
 }
 
 }  // namespace

@@ -35,7 +35,17 @@ struct KArgs {
     uint32_t *cnt;
 };
 
+// The kernel a launcher would launch: reported instead of launching when a plan's
+// `query` points here (used to ask the runtime how many of its workgroups stay
+// resident on one CU).
+struct KernelRef {
+    const void *fn;
+    int threads;    // per workgroup
+    int lds_bytes;  // dynamic LDS per workgroup
+};
+
 struct LaunchCfg {
+    KernelRef *query;   // when set, the launcher fills *query and launches nothing
     int device;         // device the launch goes to (set by the caller of a launcher)
     int fmt;            // Fmt
     int act;            // Act
@@ -55,6 +65,18 @@ struct LaunchCfg {
 
 // Dynamic LDS of one gfx950 compute unit (bytes).
 constexpr int kMaxLdsBytes = 160 * 1024;
+
+// Report (query set) or launch kernel `kern` with the plan's grid, `threads` per
+// workgroup and the plan's dynamic LDS.
+template <typename Kern>
+inline hipError_t launch_or_report(const LaunchCfg &cfg, Kern kern, int threads, const KArgs &a, hipStream_t s) {
+    if (cfg.query) {
+        *cfg.query = KernelRef{(const void *)kern, threads, cfg.lds_bytes};
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)cfg.grid), dim3(threads), (size_t)cfg.lds_bytes, s, a);
+    return hipGetLastError();
+}
 
 // Raise kern's dynamic-LDS limit to the whole CU once per device (bit d of `done`):
 // the limit is a property of the function on a device, so a launch that needs more

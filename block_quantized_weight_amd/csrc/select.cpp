@@ -45,7 +45,8 @@ int validate_desc(const qgemv_desc *d) {
                            QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_RING_OFF |
                            QGEMV_FLAG_RING_ON | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
                            QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_MFMA_DEPTH_MASK |
-                           QGEMV_FLAG_STREAM_WIDE_WG | QGEMV_FLAG_STREAM_NWG_MASK;
+                           QGEMV_FLAG_STREAM_WIDE_WG | QGEMV_FLAG_STREAM_NWG_MASK | QGEMV_FLAG_NO_RESIDENCY_FIT |
+                           QGEMV_FLAG_STREAM_META_CHUNK;
     if (d->flags & ~known) return QGEMV_E_ARG;
     const uint32_t fam = d->flags & QGEMV_FLAG_FAMILY_MASK;
     if (fam > QGEMV_FAMILY_GENERIC) return QGEMV_E_ARG;
@@ -177,6 +178,24 @@ static int mfma_kparts(const qgemv_desc *d, int cu_count, uint32_t flags, int ks
     return kp;
 }
 
+// Whether the persistent streaming kernel takes a round's block metadata as one window
+// dword per lane per column (variant bit 3) with unr chunks per lane: 8-bit codes
+// only, where the round's scale and zero-point windows are whole dwords within 64 of
+// them and the rows are whole dwords on 4-byte aligned arrays (the loads never leave a
+// row). Measured on MI355X (A/B, one session): 8-bit 4096 x 4096 M = 1 6.20 -> 5.71 us;
+// for the other formats the per-chunk loads were as fast or faster (4-bit lm_head M = 1
+// 65.2 against 67.2 us, NVFP4 lm_head M = 1 70.6 against 71.7, FP8 5120 x 6144 M = 1
+// and 4 7.53 / 11.82 against 7.68 / 11.97), so they keep them.
+static bool stream_meta_window(const qgemv_desc *d, int unr) {
+    if (d->format != QGEMV_FMT_U8) return false;
+    const int64_t nblk = d->K / d->block_size;
+    const int64_t bpr = (64LL * unr * 16) / d->block_size;  // blocks per round
+    const int64_t zrow = nblk;
+    if (bpr * 2 > 256 || bpr % 4 || (nblk * 2) % 4 || (uintptr_t)d->scales % 4) return false;
+    if (zrow % 4 || (uintptr_t)d->zero_points % 4) return false;
+    return true;
+}
+
 // Persistent streaming kernel for M <= 4 rows in one pass (2 or 4 rows per pass for
 // M = 2 or 3..4): the activation rows (in the decode's pair order) and per-chunk sums
 // of them live in LDS; each wave walks column groups with the next batch of codes in
@@ -261,6 +280,7 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     c->grid = wgs < cap ? wgs : (cap > 0 ? cap : 1);
     c->lds_bytes = (int)lds;
     c->variant = 1 | ((unr & 3) << 1);
+    if (!(flags & QGEMV_FLAG_STREAM_META_CHUNK) && stream_meta_window(d, unr)) c->variant |= 8;
     return true;
 }
 

@@ -109,13 +109,15 @@ enum qgemv_family {
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
  * Bits 4..6: forced number of K parts split across workgroups by qgemv_run_ws (v ->
  * 2^(v-1): 1, 2, 4 or 8 parts, at most one per K step of the MFMA family; 0 =
- * automatic). Bit 7: reserved (0).
+ * automatic). Bit 7: the persistent streaming kernel loads 8-bit codes' block metadata
+ * per chunk, never as one window per round (for A/B comparisons).
  * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1, 2, 4 or
  * 8 waves share the K range of a column tile). Bits 12..14: waves per workgroup of the
  * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
  * automatic; capped at 8 with two columns per wave and at 12 for four rows of 4-bit
  * codes in 16-wide blocks, the most those fit without spilling registers). Bit 15:
- * reserved (0).
+ * keep persistent grids as the dispatcher sizes them, without the create-time cut to
+ * the workgroups the kernel's registers leave resident per CU (for A/B comparisons).
  * Bit 16: never pick the MFMA family.
  * Bits 17/18: MFMA family never / always stages the activations in LDS (when they
  * fit); neither set = automatic. Bits 19/20: MFMA family never / always (when
@@ -133,10 +135,12 @@ enum qgemv_family {
 #define QGEMV_FLAG_FAMILY_MASK 0x0000000Fu
 #define QGEMV_FLAG_KPARTS_SHIFT 4
 #define QGEMV_FLAG_KPARTS_MASK 0x00000070u
+#define QGEMV_FLAG_STREAM_META_CHUNK 0x00000080u
 #define QGEMV_FLAG_KSPLIT_SHIFT 8
 #define QGEMV_FLAG_KSPLIT_MASK 0x00000F00u
 #define QGEMV_FLAG_STREAM_NWG_SHIFT 12
 #define QGEMV_FLAG_STREAM_NWG_MASK 0x00007000u
+#define QGEMV_FLAG_NO_RESIDENCY_FIT 0x00008000u
 #define QGEMV_FLAG_NO_MFMA 0x00010000u
 #define QGEMV_FLAG_STAGE_A_OFF 0x00020000u
 #define QGEMV_FLAG_STAGE_A_ON 0x00040000u
@@ -179,13 +183,17 @@ typedef struct qgemv_plan_info {
     int32_t cols_per_wave;   /* output columns one wave owns at a time */
     int32_t ksplit;          /* waves of a workgroup sharing one column tile's K */
     int32_t waves_per_wg;    /* waves per workgroup */
-    int64_t grid;            /* workgroups launched */
+    int64_t grid;            /* workgroups launched (qgemv_plan: a persistent grid cut at create to
+                                the workgroups that stay resident at once; qgemv_select, which asks
+                                no device, reports the grid before that cut) */
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
     int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
                                 LDS, bit 1 = weights through the LDS DMA ring (4-step slots,
                                 double-buffered), bit 3 = 8-slot register ring (else 4).
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
-                                bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4) */
+                                bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4),
+                                bit 3 = block metadata loaded as one window per round (8-bit
+                                codes) */
     int32_t kparts;          /* K parts split across workgroups (1 = none; only qgemv_run_ws
                                 splits, ABI version 3) */
     int32_t reserved;        /* 0 */

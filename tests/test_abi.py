@@ -64,7 +64,7 @@ def _sel(**kw):
     (dict(block_size=48), 3), (dict(block_size=8), 3), (dict(fmt="nvfp4", block_size=32), 3),
     (dict(fmt="bogus"), 4), (dict(act="fp32"), 4), (dict(fmt="fp8", zero_points=0x2000), 4),
     (dict(fmt="nvfp4", block_size=16, zero_points=0x2000), 4),
-    (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=3 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=1 << 15), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
+    (dict(W=None), 1), (dict(scales=None), 1), (dict(flags=0x4), 7), (dict(flags=9 << 8), 7), (dict(flags=3 << 8), 7), (dict(flags=5 << 12), 7), (dict(flags=3 << 29), 7), (dict(flags=(1 << 19) | (1 << 20)), 7), (dict(flags=(1 << 17) | (1 << 18)), 7),
     (dict(cu_count=0), 7), (dict(bias=0x2001), 7), (dict(flags=5 << 4), 7), (dict(flags=7 << 4), 7),
 ])
 def test_select_rejects_invalid_arguments(kw, status):
@@ -378,3 +378,19 @@ def test_forced_k_parts_and_k_split_are_clamped():
     # 8-wave workgroup): 3 steps of 4-bit codes (K = 384), forced 8 -> 2
     p = _sel(N=100, K=384, M=8, flags=2 | (8 << 8))
     assert p["ksplit"] == 2
+
+
+def test_streaming_metadata_windows_where_they_fit():
+    """Variant bit 3 (one metadata window per round) is taken for 8-bit codes where a
+    round's scale and zero-point windows are whole dwords within 64 of them and the rows
+    are whole dwords; the other formats keep the per-chunk loads, as does an odd block
+    count, and flag bit 7 forces them."""
+    u8 = dict(fmt="u8", act="f16", N=4096, K=4096, block_size=128)
+    p = _sel(**u8)
+    assert p["family"] == "stream" and p["variant"] & 8
+    assert _sel(**dict(u8, block_size=32))["variant"] & 8
+    assert _sel(**dict(u8, M=3, N=900))["variant"] & 8                   # several rows per pass
+    assert not _sel(**dict(u8, K=128 * 33))["variant"] & 8               # 33 blocks: odd rows
+    assert not _sel(**dict(u8, flags=bqw.FLAG_STREAM_META_CHUNK))["variant"] & 8
+    assert not _sel()["variant"] & 8                                      # 4-bit lm_head
+    assert not _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128)["variant"] & 8

@@ -487,3 +487,24 @@ def test_run_rejects_bad_arguments():
         q.run(0, Y, M=1)
     assert e.value.status == 1
     q.close()
+
+
+@pytest.mark.parametrize("act,bs,K", [("f16", 16, 16 * 120), ("bf16", 32, 2048), ("f16", 32, 32 * 100),
+                                      ("f16", 128, 4096), ("bf16", 128, 128 * 44), ("f16", 256, 256 * 20)])
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("zp", [True, False])
+def test_metadata_windows_match_per_chunk_loads(act, bs, K, M, zp):
+    """8-bit codes: the persistent streaming kernel's round metadata windows (one dword
+    per lane per column, values handed out across lanes) give the same bits as the
+    per-chunk loads, including partial last rounds, ragged N and missing zero points
+    (the midpoint), and meet the oracle."""
+    prob = synth.make_problem("u8", act, 333, K, bs, M, seed=K + bs, zp_range=(96, 160), scale_sigma=0.004,
+                              with_zp=zp)
+    gu.say(f"[meta window] u8/{act} bs={bs} K={K} M={M} zp={zp}")
+    Yw, pw = gu.run_gpu(prob, M, flags=1)
+    Yc, pc = gu.run_gpu(prob, M, flags=1 | bqw.FLAG_STREAM_META_CHUNK)
+    assert pw["variant"] & 1 and pw["variant"] & 8, pw
+    assert pc["variant"] & 1 and not pc["variant"] & 8, pc
+    assert np.array_equal(Yw.view(np.int64), Yc.view(np.int64))
+    ok, ratio, _, _ = gu.check_full(prob, M, Yw, strict=False)
+    assert ok, ratio
