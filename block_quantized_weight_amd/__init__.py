@@ -42,6 +42,7 @@ FLAG_STREAM_WPC_SHIFT = 25
 FLAG_STREAM_CLASSIC = 0x10000000
 FLAG_MFMA_DEPTH_SHIFT = 29
 FLAG_STREAM_WIDE_WG = 0x80000000
+TUNE_MAX_CANDIDATES = 256  # QGEMV_TUNE_MAX_CANDIDATES
 MAX_M = 16  # rows one plan carries
 MAX_ROWS = 65536  # rows one call accepts (more than MAX_M run as chunks of MAX_M)
 
@@ -89,6 +90,17 @@ class PlanInfo(ctypes.Structure):
     ]
 
 
+class TuneInfo(ctypes.Structure):
+    _fields_ = [
+        ("candidates", ctypes.c_int32),
+        ("rounds", ctypes.c_int32),
+        ("chosen_flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_int32),
+        ("auto_us", ctypes.c_double),
+        ("chosen_us", ctypes.c_double),
+    ]
+
+
 def lib() -> ctypes.CDLL:
     """Load libqgemv.so (raises if it has not been built)."""
     global _lib
@@ -113,6 +125,13 @@ def lib() -> ctypes.CDLL:
             L.qgemv_select.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(PlanInfo)]
             L.qgemv_select.restype = ctypes.c_int
+            L.qgemv_tune_candidates.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_uint32), ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_int)]
+            L.qgemv_tune_candidates.restype = ctypes.c_int
+            L.qgemv_tune.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_int, vp, ctypes.POINTER(TuneInfo)]
+            L.qgemv_tune.restype = ctypes.c_int
             L.qgemv_destroy.argtypes = [vp]
             L.qgemv_destroy.restype = None
             L.qgemv_status_str.argtypes = [ctypes.c_int]
@@ -159,6 +178,28 @@ def select(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count
     if rc != QGEMV_OK:
         raise QGemvError(rc, "qgemv_select")
     return _plan_dict(out)
+
+
+def tune_candidates(fmt: str, act: str, N: int, K: int, block_size: int, M: int, cu_count: int = 256,
+                    flags: int = 0, W: Any = 0x1000, scales: Any = 0x1000, zero_points: Any = None,
+                    bias: Any = None, with_workspace: bool = False) -> "list[int]":
+    """Pure host query (no GPU): the flag sets qgemv_tune would time for M rows at
+    cu_count CUs (the first, 0, is the automatic plan)."""
+    d = make_desc(fmt, act, N, K, block_size, W, scales, zero_points, 1.0, flags, bias)
+    buf = (ctypes.c_uint32 * TUNE_MAX_CANDIDATES)()
+    n = ctypes.c_int()
+    rc = lib().qgemv_tune_candidates(ctypes.byref(d), int(M), int(cu_count), int(bool(with_workspace)), buf,
+                                     TUNE_MAX_CANDIDATES, ctypes.byref(n))
+    if rc != QGEMV_OK:
+        raise QGemvError(rc, "qgemv_tune_candidates")
+    return [int(buf[i]) for i in range(n.value)]
+
+
+def _stream_handle(stream: Any) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
 
 
 class QGemv:
@@ -220,6 +261,25 @@ class QGemv:
         rc = lib().qgemv_run_noalloc(self._h, _ptr(A), _ptr(Y), int(M), ctypes.c_void_p(stream))
         if rc != QGEMV_OK:
             raise QGemvError(rc, "qgemv_run_noalloc")
+
+    def tune(self, A: Any, Y: Any, M: Optional[int] = None, with_workspace: bool = False, workspace: Any = None,
+             workspace_bytes: Optional[int] = None, rounds: int = 0, reps: int = 0,
+             stream: Any = None) -> Dict[str, Any]:
+        """qgemv_tune: time the launches that give the automatic plan's bits for M rows
+        on these buffers and keep the fastest in the handle (for qgemv_run, or with a
+        workspace for qgemv_run_ws / qgemv_run_noalloc). Waits for its work."""
+        if M is None:
+            M = int(A.shape[0])
+        if workspace is not None and workspace_bytes is None:
+            workspace_bytes = int(workspace.numel() * workspace.element_size())
+        info = TuneInfo()
+        rc = lib().qgemv_tune(self._h, _ptr(A), _ptr(Y), int(M), int(bool(with_workspace)), _ptr(workspace),
+                              int(workspace_bytes or 0), int(rounds), int(reps),
+                              ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(info))
+        if rc != QGEMV_OK:
+            raise QGemvError(rc, "qgemv_tune")
+        return {"candidates": info.candidates, "rounds": info.rounds, "chosen_flags": info.chosen_flags,
+                "auto_us": info.auto_us, "chosen_us": info.chosen_us}
 
     def workspace_size(self, M: int = MAX_M) -> int:
         """Bytes of workspace qgemv_run_ws needs for M rows (0: none)."""

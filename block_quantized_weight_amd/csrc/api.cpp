@@ -13,7 +13,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
+#include <vector>
 
 #include "../../include/qgemv.h"
 #include "launch.h"
@@ -127,22 +129,15 @@ hipError_t launch_rows(const qgemv::LaunchCfg &c, const qgemv::KArgs &a0, const 
     }
 }
 
-// Shared body of qgemv_run, qgemv_run_ws and qgemv_run_noalloc: the cached plan
-// (with or without a workspace) for min(M, 16) rows, the workspace check, and the
-// launches. More than 16 rows run as chunks of 16 (the last one shorter), one after
-// another on the stream, each with the 16-row plan: a row's arithmetic does not depend
-// on the chunk that carries it, and the workspace, all zero again after each chunk,
-// serves every chunk in turn. short_ws: the status for a workspace that is missing or
-// too small (QGEMV_E_SCRATCH when it is the library's own array).
-int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
-             void *hip_stream, int short_ws = QGEMV_E_WORKSPACE) {
-    if (!h || !A || !Y) return QGEMV_E_NULL;
-    if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
+// Enqueue plan c (the plan of Mp = min(M, 16) rows) for M rows: the workspace check,
+// then the launches. More than 16 rows run as chunks of 16 (the last one shorter), one
+// after another on the stream, each with the 16-row plan: a row's arithmetic does not
+// depend on the chunk that carries it, and the workspace, all zero again after each
+// chunk, serves every chunk in turn. short_ws: the status for a workspace that is
+// missing or too small (QGEMV_E_SCRATCH when it is the library's own array).
+int enqueue(const qgemv_handle *h, const qgemv::LaunchCfg &c, const void *A, void *Y, int M, void *ws,
+            size_t ws_bytes, hipStream_t s, int short_ws) {
     const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
-    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
-    const int rc = h->plan_rc[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1];
-    if (rc) return rc;
-    const qgemv::LaunchCfg &c = h->plan[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1];
     qgemv::KArgs a = h->args;
     a.A = A;
     a.Y = Y;
@@ -154,7 +149,6 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
         a.cnt = (uint32_t *)ws;
         a.part = (float *)((unsigned char *)ws + c.ws_counters);
     }
-    hipStream_t s = (hipStream_t)hip_stream;
     hipError_t e = hipSuccess;
     for (int r0 = 0; r0 < M && e == hipSuccess; r0 += Mp) {
         const int rows = (M - r0) < Mp ? (M - r0) : Mp;
@@ -164,13 +158,18 @@ int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws,
     return e == hipSuccess ? QGEMV_OK : QGEMV_E_LAUNCH;
 }
 
-// Persistent launches: every workgroup walks its share of the work, so the grid may
-// be anything up to the work units. (K-part and classic streaming launches need one
-// workgroup per unit.)
-bool persistent(const qgemv::LaunchCfg &c) {
-    if (c.family == QGEMV_FAMILY_MFMA) return c.kparts == 1;
-    if (c.family == QGEMV_FAMILY_STREAM) return (c.variant & 1) != 0;
-    return c.family == QGEMV_FAMILY_GENERIC;
+// Shared body of qgemv_run, qgemv_run_ws and qgemv_run_noalloc: the cached plan (with
+// or without a workspace) for min(M, 16) rows, then enqueue.
+int run_plan(const qgemv_handle *h, const void *A, void *Y, int M, bool with_ws, void *ws, size_t ws_bytes,
+             void *hip_stream, int short_ws = QGEMV_E_WORKSPACE) {
+    if (!h || !A || !Y) return QGEMV_E_NULL;
+    if (M < 1 || M > QGEMV_MAX_ROWS) return QGEMV_E_SHAPE;
+    const int Mp = M < QGEMV_MAX_M ? M : QGEMV_MAX_M;
+    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
+    const int rc = h->plan_rc[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1];
+    if (rc) return rc;
+    return enqueue(h, h->plan[with_ws ? 1 : 0][fast ? 1 : 0][Mp - 1], A, Y, M, ws, ws_bytes,
+                   (hipStream_t)hip_stream, short_ws);
 }
 
 // Keep a persistent grid within what stays resident at once. The dispatcher sizes
@@ -182,8 +181,8 @@ bool persistent(const qgemv::LaunchCfg &c) {
 // grids just past two blocks per SM", Description). On gfx950 a register cap that
 // raises the residency makes the register-ring kernels spill, so the grid is cut to
 // the resident count instead, which the runtime reports for the kernel as compiled.
-void fit_residency(const qgemv_handle *h, qgemv::LaunchCfg *c, int m) {
-    if (!persistent(*c) || ((h->d.flags | h->env_flags) & QGEMV_FLAG_NO_RESIDENCY_FIT)) return;
+void fit_residency(const qgemv_handle *h, qgemv::LaunchCfg *c, int m, uint32_t extra_flags = 0) {
+    if (!qgemv::persistent(*c) || ((h->d.flags | h->env_flags | extra_flags) & QGEMV_FLAG_NO_RESIDENCY_FIT)) return;
     qgemv::KernelRef ref{nullptr, 0, 0};
     qgemv::LaunchCfg q = *c;
     q.query = &ref;
@@ -328,6 +327,107 @@ int qgemv_workspace_size(const qgemv_handle *h, int M, size_t *bytes) {
     int rc = plan_rows(&h->d, M, h->cu_count, h->weights_fast_ok, h->env_flags, true, &c);
     if (rc) return rc;
     *bytes = (size_t)c.ws_bytes;
+    return QGEMV_OK;
+}
+
+int qgemv_tune_candidates(const qgemv_desc *d, int M, int cu_count, int with_workspace, uint32_t *flags_out,
+                          int max, int *count) {
+    if (!d || !flags_out || !count) return QGEMV_E_NULL;
+    *count = 0;
+    int rc = qgemv::validate_desc(d);
+    if (rc) return rc;
+    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
+    if (cu_count < 1 || max < 1) return QGEMV_E_ARG;
+    return qgemv::tune_candidates(d, M, cu_count, qgemv::pointers_fast_ok(d, nullptr, nullptr), 0u,
+                                  with_workspace != 0, flags_out, max, count);
+}
+
+int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspace, void *workspace,
+               size_t workspace_bytes, int rounds, int reps, void *hip_stream, qgemv_tune_info *out) {
+    if (!h || !A || !Y) return QGEMV_E_NULL;
+    if (M < 1 || M > QGEMV_MAX_M) return QGEMV_E_SHAPE;
+    if (rounds < 0 || reps < 0) return QGEMV_E_ARG;
+    if (rounds == 0) rounds = 5;
+    if (reps == 0) reps = 10;
+    const int w = with_workspace ? 1 : 0;
+    const bool fast = h->weights_fast_ok && qgemv::pointers_fast_ok(&h->d, A, Y);
+    const int f = fast ? 1 : 0;
+    if (h->plan_rc[w][f][M - 1]) return h->plan_rc[w][f][M - 1];
+    // the launches: the automatic one first, then each other distinct one after the
+    // residency cut
+    uint32_t flags[QGEMV_TUNE_MAX_CANDIDATES];
+    int n = 0;
+    int rc = qgemv::tune_candidates(&h->d, M, h->cu_count, fast, h->env_flags, w != 0, flags,
+                                    QGEMV_TUNE_MAX_CANDIDATES, &n);
+    if (rc) return rc;
+    std::vector<qgemv::LaunchCfg> plans;
+    std::vector<uint32_t> kept_flags;
+    for (int i = 0; i < n; ++i) {
+        qgemv::LaunchCfg c{};
+        if (qgemv::select_plan(&h->d, M, h->cu_count, fast, h->env_flags | flags[i], w != 0, &c)) continue;
+        c.device = h->device;
+        fit_residency(h, &c, M, flags[i]);
+        bool dup = false;
+        for (const qgemv::LaunchCfg &k : plans) dup = dup || qgemv::same_launch(k, c);
+        if (dup) continue;
+        plans.push_back(c);
+        kept_flags.push_back(flags[i]);
+    }
+    const int nc = (int)plans.size();
+    if (nc == 0) return QGEMV_E_ARG;  // plans[0], with no extra flags, is the automatic launch
+    hipStream_t s = (hipStream_t)hip_stream;
+    std::vector<hipEvent_t> ev(2 * (size_t)nc, nullptr);
+    std::vector<double> us((size_t)nc * rounds, 0.0);
+    int status = QGEMV_OK;
+    for (size_t i = 0; i < ev.size() && status == QGEMV_OK; ++i)
+        if (hipEventCreate(&ev[i]) != hipSuccess) status = QGEMV_E_LAUNCH;
+    // one untimed call of each (first-launch costs), then the rounds
+    for (int i = 0; i < nc && status == QGEMV_OK; ++i)
+        status = enqueue(h, plans[i], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
+    for (int r = 0; r < rounds && status == QGEMV_OK; ++r) {
+        for (int i = 0; i < nc && status == QGEMV_OK; ++i) {
+            if (hipEventRecord(ev[2 * i], s) != hipSuccess) status = QGEMV_E_LAUNCH;
+            for (int k = 0; k < reps && status == QGEMV_OK; ++k)
+                status = enqueue(h, plans[i], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
+            if (status == QGEMV_OK && hipEventRecord(ev[2 * i + 1], s) != hipSuccess) status = QGEMV_E_LAUNCH;
+        }
+        if (status == QGEMV_OK && hipEventSynchronize(ev[2 * nc - 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
+        for (int i = 0; i < nc && status == QGEMV_OK; ++i) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
+            us[(size_t)i * rounds + r] = 1000.0 * (double)ms / reps;
+        }
+    }
+    int best = 0;
+    std::vector<double> med((size_t)nc, 0.0);
+    if (status == QGEMV_OK) {
+        for (int i = 0; i < nc; ++i) {
+            std::vector<double> v(us.begin() + (size_t)i * rounds, us.begin() + (size_t)(i + 1) * rounds);
+            std::sort(v.begin(), v.end());
+            med[i] = v[v.size() / 2];
+        }
+        for (int i = 1; i < nc; ++i)
+            if (med[i] < med[best]) best = i;
+        if (best != 0 && !(med[best] < 0.98 * med[0])) best = 0;  // keep the automatic launch within 2%
+        // Y ends with the kept launch's product; wait for it
+        status = enqueue(h, plans[best], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
+        if (status == QGEMV_OK && (hipEventRecord(ev[0], s) != hipSuccess || hipEventSynchronize(ev[0]) != hipSuccess))
+            status = QGEMV_E_LAUNCH;
+    } else {
+        hipStreamSynchronize(s);  // nothing of this call stays in flight on a failure
+    }
+    for (hipEvent_t e : ev)
+        if (e) hipEventDestroy(e);
+    if (status != QGEMV_OK) return status;
+    h->plan[w][f][M - 1] = plans[best];
+    if (out) {
+        out->candidates = nc;
+        out->rounds = rounds;
+        out->chosen_flags = kept_flags[best];
+        out->reserved = 0;
+        out->auto_us = med[0];
+        out->chosen_us = med[best];
+    }
     return QGEMV_OK;
 }
 

@@ -18,6 +18,8 @@
 // same bits for a row at every M forces one family (and the part count) in the flags.
 #include "select.h"
 
+#include <initializer_list>
+
 #include <stdint.h>
 
 namespace qgemv {
@@ -483,7 +485,10 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // 5120 x 6144 M = 8: 16.6 us with 4, 17.4 with 8; 8-bit 4096 x 4096 M = 8: 15.5
         // / 16.2 us; 4-bit lm_head M = 12 and 16: equal)
         const uint32_t fdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
-        const bool deep8 = fdep == 2;
+        // (8 slots only where the kernel takes them: staged rows, one or two row groups,
+        // one scale block per chunk, and not one row group of a 32-k chunk format)
+        const bool two_blocks = d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16);
+        const bool deep8 = fdep == 2 && stage && rg <= 2 && !two_blocks && !(k_per_chunk(d->format) == 32 && rg == 1);
         c.variant = (stage ? 1 : 0) | (deep8 ? 8 : 0);
         // with K parts, 16 bytes more for the last-workgroup flag
         c.lds_bytes = (int)(stage ? lds_staged : lds_red + flag_b);
@@ -535,6 +540,111 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         c.grid = (waves + c.waves_per_wg - 1) / c.waves_per_wg;
     }
     *out = c;
+    return QGEMV_OK;
+}
+
+bool persistent(const LaunchCfg &c) {
+    if (c.family == QGEMV_FAMILY_MFMA) return c.kparts == 1;
+    if (c.family == QGEMV_FAMILY_STREAM) return (c.variant & 1) != 0;
+    return c.family == QGEMV_FAMILY_GENERIC;
+}
+
+bool same_launch(const LaunchCfg &x, const LaunchCfg &y) {
+    return x.family == y.family && x.rows_per_pass == y.rows_per_pass && x.passes == y.passes &&
+           x.cols_per_wave == y.cols_per_wave && x.ksplit == y.ksplit && x.waves_per_wg == y.waves_per_wg &&
+           x.grid == y.grid && x.lds_bytes == y.lds_bytes && x.variant == y.variant && x.kparts == y.kparts &&
+           x.ws_bytes == y.ws_bytes;
+}
+
+// The online choice the pages' batched small-M review asks for in place of thresholds
+// tuned on one machine ("[CUDA] Batched small-M GEMV for MatMulNBits (4-bit/8-bit)",
+// review), limited here to the choices that leave every result bit unchanged: the
+// automatic plan's family, K split and K parts fix the order of the fp32 sums, and
+// within them the streaming family's columns per wave, batch depth, workgroup size and
+// grid, its classic or persistent kernel and its metadata loads, and the matrix
+// family's activation staging, weight ring (registers or LDS DMA) and ring depth only
+// move work between waves and change how it is fetched. Each dimension takes its
+// values in turn (0 = automatic) unless the descriptor's or the environment's flags
+// already fix it; the product is cut to the plans that keep family, K split and K
+// parts, and to one set of flags per distinct launch (the residency cut, made at
+// create, counts as part of the launch for persistent grids).
+int tune_candidates(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t env_flags, bool with_ws,
+                    uint32_t *out, int max, int *count) {
+    if (!count) return QGEMV_E_NULL;
+    *count = 0;
+    if (max < 1 || !out) return QGEMV_E_ARG;
+    LaunchCfg base;
+    int rc = select_plan(d, M, cu_count, fast_ok, env_flags, with_ws, &base);
+    if (rc) return rc;
+    const uint32_t fixed = d->flags | env_flags;
+    struct Dim {
+        uint32_t mask;
+        uint32_t vals[5];
+        int n;
+    };
+    Dim dims[8];
+    int nd = 0;
+    auto add = [&](uint32_t mask, std::initializer_list<uint32_t> v) {
+        if (fixed & mask) return;
+        Dim &x = dims[nd++];
+        x.mask = mask;
+        x.n = 0;
+        for (uint32_t e : v) x.vals[x.n++] = e;
+    };
+    if (base.family == QGEMV_FAMILY_STREAM) {
+        const bool one_row = M == 1;
+        // the classic kernel has none of the persistent kernel's shape choices: not
+        // offered where the flags fix one of them
+        add(QGEMV_FLAG_STREAM_CLASSIC | QGEMV_FLAG_STREAM_CPW_MASK | QGEMV_FLAG_STREAM_UNR_MASK |
+                QGEMV_FLAG_STREAM_WPC_MASK | QGEMV_FLAG_STREAM_WIDE_WG | QGEMV_FLAG_STREAM_NWG_MASK |
+                QGEMV_FLAG_STREAM_META_CHUNK,
+            {0u, QGEMV_FLAG_STREAM_CLASSIC});
+        add(QGEMV_FLAG_STREAM_CPW_MASK, {0u, 1u << QGEMV_FLAG_STREAM_CPW_SHIFT, 2u << QGEMV_FLAG_STREAM_CPW_SHIFT,
+                                         3u << QGEMV_FLAG_STREAM_CPW_SHIFT});
+        if (one_row) {
+            add(QGEMV_FLAG_STREAM_UNR_MASK, {0u, 1u << QGEMV_FLAG_STREAM_UNR_SHIFT, 2u << QGEMV_FLAG_STREAM_UNR_SHIFT,
+                                             3u << QGEMV_FLAG_STREAM_UNR_SHIFT});
+            add(QGEMV_FLAG_STREAM_WIDE_WG, {0u, QGEMV_FLAG_STREAM_WIDE_WG});
+        } else {
+            add(QGEMV_FLAG_STREAM_NWG_MASK, {0u, 1u << QGEMV_FLAG_STREAM_NWG_SHIFT, 2u << QGEMV_FLAG_STREAM_NWG_SHIFT,
+                                             3u << QGEMV_FLAG_STREAM_NWG_SHIFT, 4u << QGEMV_FLAG_STREAM_NWG_SHIFT});
+        }
+        add(QGEMV_FLAG_STREAM_WPC_MASK, {0u, 2u << QGEMV_FLAG_STREAM_WPC_SHIFT, 4u << QGEMV_FLAG_STREAM_WPC_SHIFT,
+                                         6u << QGEMV_FLAG_STREAM_WPC_SHIFT});
+        if (d->format == QGEMV_FMT_U8) add(QGEMV_FLAG_STREAM_META_CHUNK, {0u, QGEMV_FLAG_STREAM_META_CHUNK});
+    } else if (base.family == QGEMV_FAMILY_MFMA) {
+        add(QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON, {0u, QGEMV_FLAG_STAGE_A_OFF, QGEMV_FLAG_STAGE_A_ON});
+        add(QGEMV_FLAG_RING_OFF | QGEMV_FLAG_RING_ON, {0u, QGEMV_FLAG_RING_OFF, QGEMV_FLAG_RING_ON});
+        add(QGEMV_FLAG_MFMA_DEPTH_MASK, {0u, 1u << QGEMV_FLAG_MFMA_DEPTH_SHIFT, 2u << QGEMV_FLAG_MFMA_DEPTH_SHIFT});
+    }
+    add(QGEMV_FLAG_NO_RESIDENCY_FIT, {0u, QGEMV_FLAG_NO_RESIDENCY_FIT});
+    // the kept launches and the residency bit each was planned with
+    LaunchCfg kept[QGEMV_TUNE_MAX_CANDIDATES];
+    int n = 0;
+    int idx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (;;) {
+        uint32_t f = 0;
+        for (int i = 0; i < nd; ++i) f |= dims[i].vals[idx[i]];
+        LaunchCfg c;
+        if (select_plan(d, M, cu_count, fast_ok, env_flags | f, with_ws, &c) == QGEMV_OK && c.family == base.family &&
+            c.ksplit == base.ksplit && c.kparts == base.kparts) {
+            // the residency cut is part of the launch only for persistent grids
+            if (!persistent(c)) f &= ~QGEMV_FLAG_NO_RESIDENCY_FIT;
+            bool dup = false;
+            for (int j = 0; j < n && !dup; ++j)
+                dup = same_launch(kept[j], c) &&
+                      ((out[j] ^ f) & QGEMV_FLAG_NO_RESIDENCY_FIT) == 0;
+            if (!dup) {
+                if (n == max || n == QGEMV_TUNE_MAX_CANDIDATES) break;
+                kept[n] = c;
+                out[n++] = f;
+            }
+        }
+        int i = nd - 1;
+        while (i >= 0 && ++idx[i] == dims[i].n) idx[i--] = 0;
+        if (i < 0) break;
+    }
+    *count = n;
     return QGEMV_OK;
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define QGEMV_ABI_VERSION 5
+#define QGEMV_ABI_VERSION 6
 /* Rows one plan carries; a call with more runs them as chunks of this many. */
 #define QGEMV_MAX_M 16
 /* Rows one call accepts. */
@@ -66,6 +66,8 @@ extern "C" {
 /* Bytes of the library's own device scratch array that qgemv_run_noalloc uses in place
  * of a workspace (one copy per device, held until the process ends). */
 #define QGEMV_NOALLOC_SCRATCH_BYTES (8u << 20)
+/* Most launches qgemv_tune_candidates lists (and qgemv_tune times) for one M. */
+#define QGEMV_TUNE_MAX_CANDIDATES 256
 
 /* Weight formats. */
 enum qgemv_format {
@@ -189,7 +191,8 @@ typedef struct qgemv_plan_info {
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
     int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
                                 LDS, bit 1 = weights through the LDS DMA ring (4-step slots,
-                                double-buffered), bit 3 = 8-slot register ring (else 4).
+                                double-buffered), bit 3 = 8-slot register ring (else 4, or fewer
+                                where the registers do not allow 4).
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4),
                                 bit 3 = block metadata loaded as one window per round (8-bit
@@ -220,8 +223,8 @@ int qgemv_create(qgemv_handle **out, const qgemv_desc *d, int device);
  * default stream). A is [M, K] row-major and Y is [M, N] row-major, both device
  * pointers in the handle's activation dtype. Asynchronous: no host sync, no
  * allocation, no environment read. Safe to call concurrently on different streams
- * (the handle is immutable after create). The call must be made with the
- * handle's device current.
+ * (only qgemv_tune changes a handle after create, and it must not overlap any other
+ * call on it). The call must be made with the handle's device current.
  *
  * The kernels are built for M <= QGEMV_MAX_M (16) rows, the decode regime of the
  * pages. More rows, up to QGEMV_MAX_ROWS, run as chunks of 16 rows (the last one
@@ -245,8 +248,10 @@ int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_st
  * and the device's compute-unit count, and on M in one case only: where the tile
  * groups fill at most half the compute units and the activation rows of an unsplit
  * plan do not fit in LDS at this M, the K range is cut in 2 parts. Rows stay
- * bit-identical whatever tile carries them within a call, and across M when the
- * part count is forced through the flags; the bits can differ from qgemv_run's where
+ * bit-identical whatever tile carries them within a call. Across M they stay so only
+ * when the flags force both the kernel family (the automatic choice takes the
+ * streaming family at small M and the matrix family above it, and the two add in
+ * different orders) and the part count; the bits can differ from qgemv_run's where
  * qgemv_run does not split (within the same error bound).
  *
  * workspace: device memory of at least qgemv_workspace_size(h, M) bytes, 256-byte
@@ -300,6 +305,61 @@ int qgemv_plan(const qgemv_handle *h, int M, int with_workspace, qgemv_plan_info
  * grids just past two blocks per SM", Tests). Returns QGEMV_E_ARG for cu_count < 1 and
  * the descriptor's status for an invalid d. */
 int qgemv_select(const qgemv_desc *d, int M, int cu_count, int with_workspace, qgemv_plan_info *out);
+
+/* What qgemv_tune measured and kept. */
+typedef struct qgemv_tune_info {
+    int32_t candidates;     /* distinct launches timed (the automatic one included) */
+    int32_t rounds;         /* timing rounds; each times `reps` calls of every candidate */
+    uint32_t chosen_flags;  /* flag bits, over the descriptor's, that give the kept launch
+                               (0 = the automatic one); a handle created with them in
+                               qgemv_desc.flags plans the same launch for this M */
+    int32_t reserved;       /* 0 */
+    double auto_us;         /* median of the rounds' mean time per call, automatic launch */
+    double chosen_us;       /* the same for the kept launch */
+} qgemv_tune_info;
+
+/* Pure host list, no device needed and no HIP call made: the flag sets that qgemv_tune
+ * would time for d at M rows (1..QGEMV_MAX_M) on cu_count compute units (16-byte
+ * aligned pointers assumed; with_workspace as for qgemv_plan). flags_out[0] is 0, the
+ * automatic plan; each later entry, added to the descriptor's flags, gives a launch of
+ * its own with the automatic plan's kernel family, K split and K parts, hence the same
+ * order of every fp32 sum and the same result bits, only spread over waves and fetched
+ * differently (streaming: columns per wave, chunks per batch, waves per workgroup,
+ * grid, classic or persistent kernel, metadata loads; matrix family: activation
+ * staging, register or LDS DMA ring, ring depth; either: the create-time residency
+ * cut). Dimensions the descriptor's flags already fix are left as they are. Writes at
+ * most max entries and their number to *count. Returns QGEMV_E_SHAPE for M outside
+ * [1, QGEMV_MAX_M], QGEMV_E_ARG for cu_count < 1 or max < 1, and the descriptor's
+ * status for an invalid d. */
+int qgemv_tune_candidates(const qgemv_desc *d, int M, int cu_count, int with_workspace, uint32_t *flags_out,
+                          int max, int *count);
+
+/* Online choice of the launch for M rows (1..QGEMV_MAX_M), the per-shape profiling the
+ * pages' reviewers ask for instead of thresholds tuned on one machine ("[CUDA] Batched
+ * small-M GEMV for MatMulNBits (4-bit/8-bit)", review). Times every launch that
+ * qgemv_tune_candidates lists for this handle's device (after the create-time
+ * residency cut; launches that come out equal are timed once) on the caller's A, Y
+ * and workspace, `rounds` rounds of `reps` back-to-back calls each (0 for either: 5
+ * and 10), interleaved so that every candidate sees the same conditions, and keeps
+ * the launch with the least median time in the handle, for qgemv_run (with_workspace
+ * = 0) or qgemv_run_ws and qgemv_run_noalloc (with_workspace != 0), for the pointer
+ * alignment that A and Y have. The automatic launch is kept unless another is faster
+ * by more than 2%. Every launch listed gives the same bits, so results do not change;
+ * only the time does. Calls with more than 16 rows use the 16-row plan and so follow a
+ * tuning of M = 16.
+ *
+ * The timing sees the memory system as the calls leave it: a weight small enough to
+ * stay in the last-level cache is timed warm. A, Y, workspace and workspace_bytes are
+ * as for qgemv_run_ws (the workspace only when with_workspace != 0 and the plan has K
+ * parts); Y is written many times and holds the kept launch's product on return. The
+ * call waits for its own work on hip_stream (HIP events) and returns after it; it
+ * creates and destroys HIP events but allocates no device memory. It changes the
+ * handle: no other call on the same handle may overlap it. *out (may be NULL) receives
+ * what was measured. Returns QGEMV_E_SHAPE for M outside [1, QGEMV_MAX_M],
+ * QGEMV_E_WORKSPACE when the plan needs a workspace that is not given, QGEMV_E_LAUNCH
+ * when a launch or an event fails (the handle keeps the plan it had). */
+int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspace, void *workspace,
+               size_t workspace_bytes, int rounds, int reps, void *hip_stream, qgemv_tune_info *out);
 
 /* Release the handle (NULL is ignored). Does not touch the caller's buffers or wait
  * for launches in flight: the caller keeps the weight buffers alive until the work it

@@ -24,7 +24,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"qgemv_create", "qgemv_run", "qgemv_run_ws", "qgemv_run_noalloc", "qgemv_workspace_size", "qgemv_plan",
-            "qgemv_select", "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version"} <= names
+            "qgemv_select", "qgemv_destroy", "qgemv_status_str", "qgemv_abi_version", "qgemv_tune",
+            "qgemv_tune_candidates"} <= names
     L = bqw.lib()
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert bqw.lib().qgemv_abi_version() == 5
+    assert bqw.lib().qgemv_abi_version() == 6
     # the descriptor is 8-byte aligned with int64 N, K after four 32-bit fields; the
     # bias pointer (version 2) follows the flags
     assert ctypes.sizeof(bqw.Desc) == 72
@@ -42,6 +43,9 @@ def test_abi_version_and_struct_layout():
     assert ctypes.sizeof(bqw.PlanInfo) == 56
     assert bqw.PlanInfo.grid.offset == 24 and bqw.PlanInfo.variant.offset == 36
     assert bqw.PlanInfo.kparts.offset == 40 and bqw.PlanInfo.workspace_bytes.offset == 48
+    # the tuner's report (version 6)
+    assert ctypes.sizeof(bqw.TuneInfo) == 32
+    assert bqw.TuneInfo.chosen_flags.offset == 8 and bqw.TuneInfo.auto_us.offset == 16
 
 
 def test_status_strings():

@@ -1,0 +1,168 @@
+"""qgemv_tune on the GPU: the online per-shape choice of launch that the pages'
+batched small-M review asks for ("[CUDA] Batched small-M GEMV for MatMulNBits
+(4-bit/8-bit)", review: an online profiler in place of thresholds tuned on one
+machine), kept to launches that leave every result bit as the automatic plan makes it.
+
+Two checks. Every candidate the tuner may pick, run on its own through a handle created
+with its flags, gives the automatic plan's bits on named and ragged shapes (so any
+choice the timing makes is safe). And a tuned handle gives the untuned handle's bits
+through qgemv_run, qgemv_run_ws and qgemv_run_noalloc, also for more than 16 rows, its
+reported flags reproduce its plan, and the kept launch is never slower than the
+automatic one by its own measurement.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_amd as bqw
+from block_quantized_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+from tests import gpu_util as gu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _problem(spec, rows=16):
+    if isinstance(spec, str):
+        return synth.workload(spec)
+    fmt, act, N, K, bs = spec
+    return synth.make_problem(fmt, act, N, K, bs, rows, seed=41)
+
+
+def _handle(prob, t, flags=0):
+    return bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, t["W"], t["scales"], t["zp"],
+                     prob.tensor_scale, flags, bias=t["bias"])
+
+
+def _run(q, A, M, N, ws=None, noalloc=False):
+    Y = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+    if noalloc:
+        q.run_noalloc(A, Y, M=M)
+    else:
+        q.run(A, Y, M=M, workspace=ws)
+    torch.cuda.synchronize()
+    return Y
+
+
+def _same(x, y):
+    return torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+CU = None
+
+
+def _cu():
+    global CU
+    if CU is None:
+        CU = torch.cuda.get_device_properties(0).multi_processor_count
+    return CU
+
+
+EVERY = [("fp8_k6144_n5120", 1, False), ("fp8_k6144_n5120", 4, False), ("fp8_k6144_n5120", 8, False),
+         (("u8", "f16", 4096, 4096, 128), 1, False), (("u8", "bf16", 333, 128 * 37, 128), 3, False),
+         (("u4", "bf16", 1001, 4064, 32), 1, False), (("u4", "f16", 777, 896, 16), 2, False),
+         ("nvfp4_m4_k2048_n2048", 4, False), (("nvfp4", "bf16", 999, 3104, 16), 1, False),
+         ("u4_m8_k2048_n1024", 8, False), (("u4", "bf16", 8192, 4096, 32), 8, False),
+         (("u4", "bf16", 8192, 4096, 32), 16, False), (("fp8", "f16", 1024, 16384, 128), 8, True),
+         (("u8", "f16", 2048, 8192, 128), 13, False)]
+
+
+@pytest.mark.parametrize("spec,M,ws", EVERY)
+def test_every_candidate_gives_the_automatic_bits(spec, M, ws):
+    prob = _problem(spec)
+    gu.say(f"[tune-every] {spec} M={M} ws={ws}")
+    qa, t = bqw.upload(prob)
+    A = t["A"][:M].contiguous()
+    wsbuf = gu.new_workspace(qa, M) if ws else None
+    Ya = _run(qa, A, M, prob.N, wsbuf)
+    pa = qa.plan(M, with_workspace=ws)
+    cands = bqw.tune_candidates(prob.fmt, prob.act, prob.N, prob.K, prob.bs, M, cu_count=_cu(), W=t["W"],
+                                scales=t["scales"], zero_points=t["zp"], bias=t["bias"], with_workspace=ws)
+    assert cands[0] == 0
+    for f in cands[1:]:
+        q = _handle(prob, t, f)
+        p = q.plan(M, with_workspace=ws)
+        assert (p["family"], p["ksplit"], p["kparts"]) == (pa["family"], pa["ksplit"], pa["kparts"]), (hex(f), p)
+        Y = _run(q, A, M, prob.N, wsbuf)
+        assert _same(Y, Ya), (hex(f), p, pa)
+        q.close()
+    if ws:
+        assert bool((wsbuf == 0).all().item())
+    qa.close()
+
+
+TUNED = [("fp8_k6144_n5120", 1, False), ("fp8_k6144_n5120", 4, False), ("fp8_k6144_n5120", 8, False),
+         ("u4_k4096_n151936", 1, False), ("u4_k4096_n151936", 8, False), (("u4", "bf16", 1001, 4064, 32), 3, False),
+         (("fp8", "f16", 1024, 16384, 128), 8, True), (("u8", "f16", 4096, 4096, 128), 2, True)]
+
+
+@pytest.mark.parametrize("spec,M,ws", TUNED)
+def test_tuned_handle_keeps_the_bits(spec, M, ws):
+    prob = _problem(spec)
+    gu.say(f"[tune] {spec} M={M} ws={ws}")
+    qa, t = bqw.upload(prob)
+    qt = _handle(prob, t)
+    A = t["A"][:M].contiguous()
+    wsbuf = gu.new_workspace(qa, M) if ws else None
+    Ya = _run(qa, A, M, prob.N, wsbuf)
+    Yt = torch.full((M, prob.N), float("nan"), dtype=A.dtype, device="cuda")
+    info = qt.tune(A, Yt, M=M, with_workspace=ws, workspace=wsbuf, rounds=3, reps=4)
+    gu.say(f"   {info}")
+    assert _same(Yt, Ya)  # the tuning leaves the kept launch's product in Y
+    assert _same(_run(qt, A, M, prob.N, wsbuf), Ya)
+    if ws:
+        assert _same(_run(qt, A, M, prob.N, noalloc=True), Ya)
+        assert bool((wsbuf == 0).all().item())
+    n_listed = len(bqw.tune_candidates(prob.fmt, prob.act, prob.N, prob.K, prob.bs, M, cu_count=_cu(), W=t["W"],
+                                       scales=t["scales"], zero_points=t["zp"], bias=t["bias"], with_workspace=ws))
+    assert 1 <= info["candidates"] <= n_listed and info["rounds"] == 3
+    assert 0 < info["chosen_us"] <= info["auto_us"]
+    if info["chosen_flags"] == 0:
+        assert qt.plan(M, with_workspace=ws) == qa.plan(M, with_workspace=ws)
+    else:
+        assert info["chosen_us"] < 0.98 * info["auto_us"]
+    # the reported flags plan the same launch in a new handle
+    qf = _handle(prob, t, info["chosen_flags"])
+    assert qf.plan(M, with_workspace=ws) == qt.plan(M, with_workspace=ws)
+    # the other row counts keep their automatic plans
+    for m in (1, 2, 16):
+        if m != M:
+            assert qt.plan(m, with_workspace=ws) == qa.plan(m, with_workspace=ws)
+    for q in (qa, qt, qf):
+        q.close()
+
+
+def test_more_than_sixteen_rows_follow_the_sixteen_row_tuning():
+    prob = _problem(("u4", "bf16", 1001, 4064, 32), rows=20)
+    qa, t = bqw.upload(prob)
+    qt = _handle(prob, t)
+    A16 = t["A"][:16].contiguous()
+    Y16 = torch.empty((16, prob.N), dtype=A16.dtype, device="cuda")
+    info = qt.tune(A16, Y16, M=16, rounds=2, reps=2)
+    gu.say(f"[tune-20] {info}")
+    A = t["A"][:20].contiguous()
+    assert _same(_run(qt, A, 20, prob.N), _run(qa, A, 20, prob.N))
+    assert qt.plan(20)["passes"] == 2 * qt.plan(16)["passes"]
+    qa.close()
+    qt.close()
+
+
+def test_tune_rejects_bad_requests():
+    prob = _problem(("fp8", "f16", 1024, 16384, 128))
+    q, t = bqw.upload(prob)
+    A = t["A"][:8].contiguous()
+    Y = torch.empty((8, prob.N), dtype=A.dtype, device="cuda")
+    with pytest.raises(bqw.QGemvError) as e:
+        q.tune(A, Y, M=17)
+    assert e.value.status == 2
+    with pytest.raises(bqw.QGemvError) as e:
+        q.tune(A, Y, M=8, with_workspace=True)  # this plan has K parts and needs the workspace
+    assert e.value.status == bqw.QGEMV_E_WORKSPACE
+    assert q.plan(8, with_workspace=True)["kparts"] > 1
+    q.close()
