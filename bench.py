@@ -69,6 +69,8 @@ def parse():
                    help="rows of A (default: the workload's M sweep, the first M as the headline; 1 for --shape)")
     p.add_argument("--no-extra", action="store_true", help="skip the FP8 projection's M = 1, 4, 8 lines")
     p.add_argument("--no-read-control", action="store_true", help="skip the plain streaming read control")
+    p.add_argument("--no-tune", dest="tune", action="store_false",
+                   help="skip qgemv_tune (by default each M is also tuned and the kept launch timed cold)")
     p.add_argument("--flags", type=int, default=0, help="qgemv_desc.flags (force a family, K split)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
@@ -296,22 +298,31 @@ class Rotation:
         tdt = torch.float16 if prob.act == "f16" else torch.bfloat16
         self.bias = None if prob.bias is None else \
             torch.from_numpy(prob.bias.view(np.int16)).to(dev).view(tdt)
+        self.tensor_scale = prob.tensor_scale
         self.handles = [bqw.QGemv(prob.fmt, prob.act, prob.N, prob.K, prob.bs, self.W[i], self.S[i],
                                   None if self.Z is None else self.Z[i], prob.tensor_scale, flags, bias=self.bias)
                         for i in range(R)]
+
+    def handle_with(self, flags, i=0):
+        """A handle on weight copy i with other descriptor flags."""
+        import block_quantized_weight_amd as bqw
+
+        h0 = self.handles[0]
+        return bqw.QGemv(h0.fmt, h0.act, h0.N, h0.K, h0.block_size, self.W[i], self.S[i],
+                         None if self.Z is None else self.Z[i], self.tensor_scale, flags, bias=self.bias)
 
     def close(self):
         for q in self.handles:
             q.close()
 
 
-def time_calls(rot, A, Y, M, stream, ws, warmup, steps):
+def time_calls(hs, A, Y, M, stream, ws, warmup, steps):
     """(ms per call from HIP events on the launch stream, wall seconds of the timed
-    loop). The rotation continues from the warmup into the timed loop."""
+    loop), the calls rotating over the handles hs (one per weight copy). The rotation
+    continues from the warmup into the timed loop."""
     import torch
 
-    R = rot.copies
-    hs = rot.handles
+    R = len(hs)
     for i in range(warmup):
         hs[i % R].run(A, Y, M, stream, workspace=ws)
     torch.cuda.synchronize()
@@ -376,6 +387,27 @@ def time_read_control(nbytes, dev, stream, warmup, steps):
     return best[0], best[1], best[2], table
 
 
+def tuned_calls(rot, A, Y, M, stream, ws, args, wbytes, auto_ms):
+    """qgemv_tune on the first copy's handle (warm: it times one weight), then the kept
+    flags timed cold like the automatic plan, over the same copies."""
+    q = rot.handle_with(args.flags)
+    info = q.tune(A, Y, M=M, with_workspace=ws is not None, workspace=ws)
+    f = info["chosen_flags"]
+    res = {"flags": hex(f), "candidates": info["candidates"], "probe_auto_us": round(info["auto_us"], 3),
+           "probe_chosen_us": round(info["chosen_us"], 3), "plan": q.plan(M, with_workspace=ws is not None)}
+    if f == 0:
+        msc = auto_ms  # the automatic launch was kept: its cold time stands
+    else:
+        hs = [rot.handle_with(args.flags | f, i) for i in range(rot.copies)]
+        msc, _ = time_calls(hs, A, Y, M, stream, ws, args.warmup, args.steps)
+        for h in hs:
+            h.close()
+    q.close()
+    res["us_per_call"] = round(msc * 1e3, 3)
+    res["gbs"] = round(wbytes / (msc * 1e-3) / 1e9, 2)
+    return res
+
+
 def measure(prob, ms, args, dev, stream):
     """Time the problem at every M in ms: {M: {...}} plus the rotation size."""
     import torch
@@ -395,9 +427,11 @@ def measure(prob, ms, args, dev, stream):
             ws = torch.zeros(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
         A = A_all[:M].contiguous()
         Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
-        msc, wall = time_calls(rot, A, Y, M, stream, ws if use_ws else None, args.warmup, args.steps)
+        msc, wall = time_calls(rot.handles, A, Y, M, stream, ws if use_ws else None, args.warmup, args.steps)
         out[M] = {"us_per_call": round(msc * 1e3, 3), "gbs": round(wbytes / (msc * 1e-3) / 1e9, 2),
                   "ms_per_step": msc, "wall_s": round(wall, 4), "plan": plan}
+        if args.tune:
+            out[M]["tuned"] = tuned_calls(rot, A, Y, M, stream, ws if use_ws else None, args, wbytes, msc)
     t1 = out[ms[0]]["us_per_call"]
     for M in ms:
         out[M]["t_over_t_first"] = round(out[M]["us_per_call"] / t1, 3)

@@ -345,8 +345,9 @@ __device__ __forceinline__ ColPtrs col_ptrs(const KArgs &a, int64_t n) {
     return p;
 }
 
-// Raw block metadata of chunk c (scale bits and zero-point byte per half), loaded
-// ahead of use; decoded by meta_decode_s once the loads have landed.
+// Raw block metadata of chunk c, loaded ahead of use and decoded by meta_decode_s once
+// the loads have landed: per half, the scale bits and the zero-point byte (narrow
+// loads), or (DW) the aligned dwords that hold them.
 template <int H>
 struct MetaS {
     uint32_t s[H];
@@ -359,8 +360,35 @@ __device__ __forceinline__ int chunk_block(const KArgs &a, int c, int h) {
     else return (c << 4) >> a.bs_shift;
 }
 
-template <int FMT, int H>
+// DW: each field comes as the aligned dword that holds it (the host takes this where
+// the scale and zero-point rows are whole dwords on 4-byte aligned arrays, so no such
+// dword reaches past its row). What a dword load returns is what the decode takes: a
+// narrow load's value would need a zero-extension, which the compiler may place where
+// the loop hands the next batch's registers over (its latch), and the wait that puts
+// there for the batch just issued drains the prefetch.
+template <int FMT, int H, bool DW = false>
 __device__ __forceinline__ void meta_load_s(const KArgs &a, const ColPtrs &p, int c, MetaS<H> &m) {
+    if constexpr (DW && FMT != FMT_FP8) {
+        const uint32_t *S = (const uint32_t *)p.s;
+        const uint32_t *Z = (const uint32_t *)p.z;
+        if constexpr (FMT == FMT_U4) {
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const int b = chunk_block<FMT>(a, c, h);
+                m.s[h] = S[b >> 1];  // two fp16 scales per dword
+                m.z[h] = Z[b >> 3];  // eight 4-bit zero points per dword
+            }
+        } else if constexpr (FMT == FMT_U8) {
+            const int b = chunk_block<FMT>(a, c, 0);
+            m.s[0] = S[b >> 1];
+            m.z[0] = Z[b >> 2];  // four 8-bit zero points per dword
+        } else {
+            m.s[0] = S[c >> 1];  // the chunk's two E4M3 scale bytes: half c & 1 of the dword
+            m.z[0] = 0u;
+            if constexpr (H == 2) m.s[1] = 0u, m.z[1] = 0u;
+        }
+        return;
+    }
     if constexpr (FMT == FMT_U4) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {
@@ -428,9 +456,31 @@ __device__ __forceinline__ void meta_from_window_u8(const KArgs &a, const MetaW 
 
 // Scale and integer zero point of each half of chunk c; zs is zsel(a.zp, midpoint
 // byte) (0x88 for U4, 128 for U8), so a weight without zero points takes the midpoint.
-template <int FMT, int H>
+// With DW, zs.fill holds the midpoint in every field of a dword (0x88888888 for U4,
+// 0x80808080 for U8) and the fields are taken at their places in the loaded dwords.
+template <int FMT, int H, bool DW = false>
 __device__ __forceinline__ void meta_decode_s(const KArgs &a, int c, const MetaS<H> &m, ZSel zs, float sc[H],
                                               uint32_t zr[H]) {
+    if constexpr (DW && FMT != FMT_FP8) {
+        if constexpr (FMT == FMT_U4) {
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const int b = chunk_block<FMT>(a, c, h);
+                sc[h] = half_bits_to_float((uint16_t)(m.s[h] >> ((b & 1) << 4)));
+                zr[h] = (((m.z[h] & zs.keep) | zs.fill) >> ((b & 7) << 2)) & 0x0Fu;
+            }
+        } else if constexpr (FMT == FMT_U8) {
+            const int b = chunk_block<FMT>(a, c, 0);
+            sc[0] = half_bits_to_float((uint16_t)(m.s[0] >> ((b & 1) << 4)));
+            zr[0] = (((m.z[0] & zs.keep) | zs.fill) >> ((b & 3) << 3)) & 0xFFu;
+        } else {
+            const uint32_t s2 = m.s[0] >> ((c & 1) << 4);
+            sc[0] = e4m3_to_float(s2 & 0xFFu);
+            sc[1] = e4m3_to_float((s2 >> 8) & 0xFFu);
+            zr[0] = zr[1] = 0u;
+        }
+        return;
+    }
     if constexpr (FMT == FMT_U4) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {

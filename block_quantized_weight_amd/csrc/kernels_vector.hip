@@ -141,9 +141,20 @@ __global__ void __launch_bounds__(256) k_stream(KArgs a) {
 template <int FMT, int H, int UNR, int CPW>
 struct SBatch {
     u4v w[UNR][CPW];
-    MetaS<H> m[UNR][CPW];  // per-chunk metadata loads
-    MetaW mw[CPW];         // or the round's metadata windows (WM, 8-bit codes)
+    MetaS<H> m[UNR][CPW];  // per-chunk metadata loads (narrow, or the dwords that hold them)
+    MetaW mw[CPW];         // or the round's metadata windows (8-bit codes)
 };
+
+// Keep a chunk's metadata decode at its use: an empty asm that takes the loaded values
+// and hands them back, so the compiler cannot hoist the decode (a zero-point mask, a
+// shift) up to the refill of the other buffer, where it would wait for these loads
+// while that refill is being issued. It emits no instruction; the wait it implies is
+// the one the chunk's use needs anyway.
+template <int H>
+__device__ __forceinline__ void pin_meta(MetaS<H> &m) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) asm volatile("" : "+v"(m.s[h]), "+v"(m.z[h]));
+}
 
 // Index (in 16-byte pieces) of piece q of chunk c of a staged activation row.
 template <int NQ>
@@ -196,11 +207,12 @@ __device__ __forceinline__ void stage_rows(const KArgs &a, u4v *sP, float *sS, i
     }
 }
 
-// WM (8-bit codes): the block metadata of a round comes as one window dword per lane
-// per column (meta_window_load_u8) instead of per-chunk loads; the values, and so the
-// results, are the same.
-template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG, bool WM>
+// MD, how the block metadata is loaded (the values, and so the results, are the same):
+// 0 per chunk with narrow loads; 1 (8-bit codes) one window dword per lane per column
+// and round (meta_window_load_u8); 2 per chunk as the aligned dwords that hold it.
+template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG, int MD>
 __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
+    constexpr bool WM = MD == 1, DW = MD == 2;
     using Ops = ChunkOps<FMT, ACT, H>;
     using B = SBatch<FMT, H, UNR, CPW>;
     constexpr int NQ = Ops::ND / 4;
@@ -218,7 +230,7 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     const int rounds = (nch + 64 * UNR - 1) / (64 * UNR);
     const int mine = gw < ngroups ? (int)((ngroups - gw + nw - 1) / nw) : 0;
     const int total = mine * rounds;
-    const ZSel zs = zsel(a.zp, FMT == FMT_U4 ? 0x88u : 128u);
+    const ZSel zs = zsel(a.zp, FMT == FMT_U4 ? (DW ? 0x88888888u : 0x88u) : (DW ? 0x80808080u : 128u));
 
     // issue cursor (group, round)
     int64_t ig = gw;
@@ -246,7 +258,7 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                 const int c = ir * (64 * UNR) + 64 * u + lane;
                 const int cc = c < nch ? c : nch - 1;
 #pragma unroll
-                for (int i = 0; i < CPW; ++i) meta_load_s<FMT, H>(a, cp[i], cc, b.m[u][i]);
+                for (int i = 0; i < CPW; ++i) meta_load_s<FMT, H, DW>(a, cp[i], cc, b.m[u][i]);
             }
         }
         if (++ir == rounds) {
@@ -291,7 +303,8 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                     MetaS<H> mu;
                     if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
                     else mu = b.m[u][i];
-                    meta_decode_s<FMT, H>(a, cc, mu, zs, sc, zr);
+                    pin_meta(mu);
+                    meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc, zr);
                     chunk_dot<FMT, ACT, H>(b.w[u][i], zr, act, part);
                     float t = acc[i][0];
 #pragma unroll
@@ -308,7 +321,8 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                     MetaS<H> mu;
                     if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
                     else mu = b.m[u][i];
-                    meta_decode_s<FMT, H>(a, cc, mu, zs, sc[i], zr[i]);
+                    pin_meta(mu);
+                    meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc[i], zr[i]);
                     Ops::decode(b.w[u][i], zr[i], wd[i]);
                 }
 #pragma unroll
@@ -493,16 +507,21 @@ hipError_t pick_mt(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 // (2 -> 2, 3 -> 3, 0 -> 4).
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
 hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    // variant bit 3: the round's metadata windows (8-bit codes)
-    constexpr bool can_wm = FMT == FMT_U8;
-    const bool wm = (cfg.variant >> 3) & 1;
-    if (wm && !can_wm) return hipErrorInvalidValue;
-    void (*kern)(KArgs) = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, false>;
+    // variant bit 3: the round's metadata windows (8-bit codes); bit 4: metadata as
+    // the dwords that hold it (4-bit, 8-bit and NVFP4 codes; FP8 scales are dwords)
+    constexpr bool can_wm = FMT == FMT_U8, can_dw = FMT != FMT_FP8;
+    const bool wm = (cfg.variant >> 3) & 1, dw = (cfg.variant >> 4) & 1;
+    if ((wm && !can_wm) || (dw && !can_dw) || (wm && dw)) return hipErrorInvalidValue;
+    void (*kern)(KArgs) = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, 0>;
     if constexpr (can_wm) {
-        if (wm) kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, true>;
+        if (wm) kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, 1>;
     }
-    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};
-    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[wm ? 1 : 0]);
+    if constexpr (can_dw) {
+        if (dw) kern = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, 2>;
+    }
+    const int md = wm ? 1 : (dw ? 2 : 0);
+    static std::atomic<uint64_t> lds_set[3] = {{0}, {0}, {0}};
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[md]);
     if (e != hipSuccess) return e;
     return launch_or_report(cfg, kern, 64 * NWG, a, s);
 }

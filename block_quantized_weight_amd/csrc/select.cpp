@@ -198,6 +198,26 @@ static bool stream_meta_window(const qgemv_desc *d, int unr) {
     return true;
 }
 
+// Whether the persistent streaming kernel may load 4-bit, 8-bit and NVFP4 block
+// metadata as the aligned dwords that hold it: every scale and zero-point row is whole
+// dwords on a 4-byte aligned array, so no such dword reaches past its row. (FP8 scales
+// are dwords already.) Without zero points the zero-point loads read the scale row,
+// which is at least as long.
+static bool stream_meta_dword(const qgemv_desc *d) {
+    const int64_t nblk = d->K / d->block_size;
+    if ((uintptr_t)d->scales % 4) return false;
+    switch (d->format) {
+    case QGEMV_FMT_U4:
+        if ((nblk * 2) % 4) return false;
+        return !d->zero_points || (((nblk + 1) / 2) % 4 == 0 && (uintptr_t)d->zero_points % 4 == 0);
+    case QGEMV_FMT_U8:
+        if ((nblk * 2) % 4) return false;
+        return !d->zero_points || (nblk % 4 == 0 && (uintptr_t)d->zero_points % 4 == 0);
+    case QGEMV_FMT_NVFP4: return nblk % 4 == 0;  // one E4M3 byte per 16 k
+    default: return false;
+    }
+}
+
 // Persistent streaming kernel for M <= 4 rows in one pass (2 or 4 rows per pass for
 // M = 2 or 3..4): the activation rows (in the decode's pair order) and per-chunk sums
 // of them live in LDS; each wave walks column groups with the next batch of codes in
@@ -282,7 +302,10 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     c->grid = wgs < cap ? wgs : (cap > 0 ? cap : 1);
     c->lds_bytes = (int)lds;
     c->variant = 1 | ((unr & 3) << 1);
-    if (!(flags & QGEMV_FLAG_STREAM_META_CHUNK) && stream_meta_window(d, unr)) c->variant |= 8;
+    if (!(flags & QGEMV_FLAG_STREAM_META_CHUNK)) {
+        if (stream_meta_window(d, unr)) c->variant |= 8;
+        else if (stream_meta_dword(d)) c->variant |= 16;
+    }
     return true;
 }
 

@@ -111,8 +111,9 @@ enum qgemv_family {
 /* Flags (qgemv_desc.flags). Bits 0..3: forced family (0 = automatic choice).
  * Bits 4..6: forced number of K parts split across workgroups by qgemv_run_ws (v ->
  * 2^(v-1): 1, 2, 4 or 8 parts, at most one per K step of the MFMA family; 0 =
- * automatic). Bit 7: the persistent streaming kernel loads 8-bit codes' block metadata
- * per chunk, never as one window per round (for A/B comparisons).
+ * automatic). Bit 7: the persistent streaming kernel loads block metadata per chunk
+ * with narrow (8- and 16-bit) loads, never as one window per round (8-bit codes) or as
+ * the aligned dwords that hold it (for A/B comparisons).
  * Bits 8..11: forced K split of the MFMA family (0 = automatic; otherwise 1, 2, 4 or
  * 8 waves share the K range of a column tile). Bits 12..14: waves per workgroup of the
  * persistent streaming kernel with several rows per pass (v -> 4v, v = 1..4; 0 =
@@ -196,7 +197,8 @@ typedef struct qgemv_plan_info {
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4),
                                 bit 3 = block metadata loaded as one window per round (8-bit
-                                codes) */
+                                codes), bit 4 = as the aligned dwords that hold it (4-bit,
+                                8-bit and NVFP4 codes, where the rows are whole dwords) */
     int32_t kparts;          /* K parts split across workgroups (1 = none; only qgemv_run_ws
                                 splits, ABI version 3) */
     int32_t reserved;        /* 0 */
