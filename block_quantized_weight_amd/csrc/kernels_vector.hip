@@ -589,7 +589,9 @@ template <int FMT, int ACT, int MT>
 hipError_t go_stream1_c(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     switch (cfg.cols_per_wave) {
     case 1: return go_stream1_u<FMT, ACT, MT, 1>(cfg, a, s);
-    case 2: return go_stream1_u<FMT, ACT, MT, 2>(cfg, a, s);
+    case 2:
+        if constexpr (MT <= 4) return go_stream1_u<FMT, ACT, MT, 2>(cfg, a, s);
+        else return hipErrorInvalidValue;
     case 4:
         if constexpr (MT == 1) return go_stream1_u<FMT, ACT, MT, 4>(cfg, a, s);
         else return hipErrorInvalidValue;
@@ -603,6 +605,11 @@ hipError_t go_stream1(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     case 1: return go_stream1_c<FMT, ACT, 1>(cfg, a, s);
     case 2: return go_stream1_c<FMT, ACT, 2>(cfg, a, s);
     case 4: return go_stream1_c<FMT, ACT, 4>(cfg, a, s);
+    case 8:
+        // eight rows: FP8 only, one column per wave (the other formats' decode
+        // constants and metadata do not fit next to eight rows' accumulators)
+        if constexpr (FMT == FMT_FP8) return go_stream1_c<FMT, ACT, 8>(cfg, a, s);
+        else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

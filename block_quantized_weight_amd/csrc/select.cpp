@@ -229,15 +229,16 @@ static bool stream_meta_dword(const qgemv_desc *d) {
 //  - grid: one group per wave when that fits in 24 waves per CU (16 for several
 //    rows, whose waves hold more registers), else a persistent grid of as many.
 static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flags, LaunchCfg *c) {
-    if (M > 4) return false;
-    const int mt = M == 1 ? 1 : (M == 2 ? 2 : 4);  // rows per pass (one pass)
+    // eight rows per pass for FP8 only (the kernel fits them without spilling there)
+    if (M > 8 || (M > 4 && d->format != QGEMV_FMT_FP8)) return false;
+    const int mt = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));  // rows per pass (one pass)
     const int kpc = k_per_chunk(d->format);
     const int64_t nch = d->K / kpc;
     const int64_t nch64 = (nch + 63) / 64 * 64;
     const int nd = kpc == 32 ? 16 : 8;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
     const int64_t lds = mt * (nch64 * nd * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0));
-    if (lds > (mt > 1 ? 64 : 48) * 1024) return false;
+    if (lds > (mt == 8 ? kLdsBytes : (mt > 1 ? 64 : 48) * 1024)) return false;
     const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
     int unr = 0;
     const uint32_t fu = (flags & QGEMV_FLAG_STREAM_UNR_MASK) >> QGEMV_FLAG_STREAM_UNR_SHIFT;
@@ -257,6 +258,7 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     if (fc) cpw = fc == 3 ? 4 : (int)fc;
     else cpw = (mt > 1 || d->N <= 24LL * cu_count) ? 1 : 2;
     if (mt > 1 && cpw > 2) cpw = 2;
+    if (mt == 8) cpw = 1;
     const int64_t groups = (d->N + cpw - 1) / cpw;
     const uint32_t fw = (flags & QGEMV_FLAG_STREAM_WPC_MASK) >> QGEMV_FLAG_STREAM_WPC_SHIFT;
     int64_t wpc;
@@ -286,6 +288,12 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     const int max_wg = cpw == 2 ? 8 : ((u4_two_blocks && mt == 4) ? 12 : 16);
     if (mt > 1 && fn) {
         nwg = 4 * (int)fn < max_wg ? 4 * (int)fn : max_wg;
+    } else if (mt == 8) {
+        // eight staged rows leave room for few workgroups per CU: the fewest waves per
+        // workgroup that hold the CU's column groups, else the most, one round
+        nwg = 4;
+        while (nwg < max_wg && nwg * res < need) nwg += 4;
+        one_round = true;
     } else if (mt > 1 && !fw && max_wg * res >= need) {
         nwg = 4;
         while (nwg * res < need) nwg += 4;
@@ -467,7 +475,8 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // M = 12 95.3 -> 60.1.
         if (kp == 1 && rows_too_big && M > 8 && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON))) {
             LaunchCfg half;
-            if (select_plan(d, 8, cu_count, fast_ok, extra_flags, with_ws, &half) == QGEMV_OK &&
+            // (the matrix family's plan for 8 rows, whichever family 8 rows alone would take)
+            if (select_plan(d, 8, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_MFMA, with_ws, &half) == QGEMV_OK &&
                 half.family == QGEMV_FAMILY_MFMA && (half.variant & 1) && half.kparts == 1 && !(half.variant & 2)) {
                 half.passes = (M + 7) / 8;
                 *out = half;
@@ -524,6 +533,18 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // 36.0 -> 28.8; at M = 5 the two are even, 26.0 against 26.8). With more tile
         // groups the matrix family stays ahead (4-bit 2048 x 16384, 128 groups: M = 8
         // 37.1 against 43.5 us, M = 16 66.7 against 81.2).
+        // FP8 codes at M = 5..8 without K parts, where the tile groups fill at most half the
+        // CUs: one pass of eight rows in the persistent streaming kernel, a column per wave,
+        // loads every CU (matrix -> streaming: FP8 2048 x 4096 M = 8 9.73 -> 9.35 us; bf16
+        // 2048 x 8192 M = 8 13.6 -> 12.1). With more tile groups the matrix family stays
+        // ahead (FP8 5120 x 6144, 160 groups: M = 8 16.1 against 20.5 us, M = 5 14.8
+        // against 15.2; 8192 x 4096, 256 groups: M = 8 13.1 against 17.9).
+        if (forced == 0 && kp == 1 && d->format == QGEMV_FMT_FP8 && M >= 5 && M <= 8 && groups * 2 <= cu_count &&
+            stream_ok && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON | QGEMV_FLAG_STREAM_CLASSIC))) {
+            LaunchCfg rows8;
+            if (stream1_plan(d, M, cu_count, flags, &rows8))
+                return select_plan(d, M, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_STREAM, with_ws, out);
+        }
         if (forced == 0 && kp == 1 && !stage && groups * 4 <= cu_count && staged(1).lds > kLdsBytes && M >= 6 &&
             stream_ok && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON)))
             return select_plan(d, M, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_STREAM, with_ws, out);
@@ -633,7 +654,7 @@ int tune_candidates(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint
                                              3u << QGEMV_FLAG_STREAM_NWG_SHIFT, 4u << QGEMV_FLAG_STREAM_NWG_SHIFT});
         }
         add(QGEMV_FLAG_STREAM_WPC_MASK, {0u, 2u << QGEMV_FLAG_STREAM_WPC_SHIFT, 4u << QGEMV_FLAG_STREAM_WPC_SHIFT,
-                                         6u << QGEMV_FLAG_STREAM_WPC_SHIFT});
+                                         6u << QGEMV_FLAG_STREAM_WPC_SHIFT, 7u << QGEMV_FLAG_STREAM_WPC_SHIFT});
         if (d->format == QGEMV_FMT_U8) add(QGEMV_FLAG_STREAM_META_CHUNK, {0u, QGEMV_FLAG_STREAM_META_CHUNK});
     } else if (base.family == QGEMV_FAMILY_MFMA) {
         add(QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON, {0u, QGEMV_FLAG_STAGE_A_OFF, QGEMV_FLAG_STAGE_A_ON});

@@ -133,14 +133,44 @@ def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
                 assert all(len(v) == 1 for v in fams.values()), (fmt, ws, key, fams)
 
 
-def test_select_covers_the_machine():
-    # every automatic plan for the named shapes launches at least a full wave of
-    # work groups on 256 CUs, or is limited by the number of columns itself
-    for fmt, act, N, K, bs in [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128),
-                               ("nvfp4", "bf16", 248320, 2048, 16), ("u8", "f16", 4096, 4096, 128)]:
-        for M in (1, 4, 8):
-            p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)
-            assert p["grid"] * p["waves_per_wg"] >= 256 * 4 or p["grid"] * p["cols_per_wave"] * p["waves_per_wg"] >= N
+# Automatic plans that leave more than 10% of the CUs without a workgroup although the
+# work could be spread further, each with what was measured against the alternatives
+# (MI355X, cold weights, one session): the FP8 projection's 320 tiles make 160 8-wave
+# workgroups at K split 4 from M = 5; a K split of 8 (320 workgroups, 2 rounds at this
+# LDS) took 18.5-18.9 against 16.1-16.6 us at M = 8, K parts 17.5-64.9 us, unstaged
+# activations 27.9, one pass of eight rows in the streaming kernel (256 workgroups)
+# 20.5, 16-wave workgroups 16.8.
+UNDERFILLED = {("fp8", 5120, 6144, M) for M in range(5, 17)}
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+def test_select_covers_the_machine(cu):
+    """Every automatic plan for the named workloads (and M = 1, 2, 4, 8, 16, with and
+    without a workspace) puts a workgroup on at least 90% of the CUs, or has run out of
+    work to spread: every column has a wave of its own (streaming family), or, on 256 CUs,
+    every 16-column tile (and K part) has its own workgroup (matrix family); the one
+    exception is listed above with its measurements. On 80 and 304 CUs, where nothing
+    was measured, the matrix family's K split follows its cost model (ties go to the
+    smaller split), so there every tile group (and part) has its own workgroup."""
+    shapes = [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128), ("nvfp4", "bf16", 248320, 2048, 16),
+              ("u8", "f16", 4096, 4096, 128), ("nvfp4", "bf16", 2048, 2048, 16), ("u4", "f16", 1024, 2048, 32),
+              ("u4", "f16", 256, 512, 32), ("fp8", "f16", 1024, 16384, 128)]
+    for fmt, act, N, K, bs in shapes:
+        for M in (1, 2, 4, 8, 16):
+            for ws in (False, True):
+                p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=ws, cu_count=cu)
+                if p["grid"] >= 0.9 * cu:
+                    continue
+                if p["family"] == "stream":
+                    spread = p["grid"] * p["waves_per_wg"] * p["cols_per_wave"] >= N and p["cols_per_wave"] == 1
+                else:
+                    tiles = (N + 15) // 16
+                    groups = -(-tiles // (8 // p["ksplit"]))
+                    if cu == 256:
+                        spread = p["grid"] >= tiles * p["kparts"] or (fmt, N, K, M) in UNDERFILLED
+                    else:
+                        spread = p["grid"] >= groups * p["kparts"]
+                assert spread, (cu, fmt, N, K, M, ws, p)
 
 
 def test_k_parts_only_with_a_workspace_where_tile_groups_leave_cus_idle():
@@ -233,8 +263,10 @@ def test_three_and_four_rows_take_the_matrix_family_where_its_tile_groups_fill_t
 
 def test_small_weights_take_the_streaming_family_at_every_m():
     """Up to N x K = 4 Mi elements with K <= 4096, the streaming family serves every M
-    (the multi-pass kernel from M = 5), with or without a workspace; past either
-    bound, M >= 5 takes the matrix family."""
+    (from M = 5 the multi-pass kernel, or for FP8 codes up to M = 8 one persistent pass
+    of eight rows), with or without a workspace; past either bound, M >= 5 takes the
+    matrix family, except FP8 at M = 5..8 where the tile groups fill at most half the
+    CUs."""
     for fmt, act, N, K, bs in (("u4", "f16", 1024, 2048, 32), ("u4", "f16", 2048, 2048, 32),
                                ("fp8", "f16", 1024, 4096, 128), ("u8", "f16", 2048, 2048, 128),
                                ("nvfp4", "bf16", 2048, 2048, 16)):
@@ -242,11 +274,23 @@ def test_small_weights_take_the_streaming_family_at_every_m():
             for ws in (False, True):
                 p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=ws)
                 assert p["family"] == "stream" and p["kparts"] == 1, (fmt, N, K, M, ws, p)
-                assert p["rows_per_pass"] == 4 and p["passes"] == (M + 3) // 4
+                if fmt == "fp8" and M <= 8:
+                    assert p["rows_per_pass"] == 8 and p["passes"] == 1 and p["variant"] & 1, (M, p)
+                else:
+                    assert p["rows_per_pass"] == 4 and p["passes"] == (M + 3) // 4
     for fmt, act, N, K, bs in (("u4", "f16", 1536, 4096, 32), ("fp8", "f16", 2048, 4096, 128),
                                ("u4", "f16", 512, 8192, 32), ("fp8", "f16", 512, 8192, 128)):
         for M in (5, 8, 16):
-            assert _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)["family"] == "mfma"
+            p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M)
+            if fmt == "fp8" and M <= 8:
+                # 128 and 32 tile groups on 256 CUs: eight rows in one streaming pass
+                assert p["family"] == "stream" and p["rows_per_pass"] == 8, (N, K, M, p)
+            else:
+                assert p["family"] == "mfma", (fmt, N, K, M, p)
+    # FP8 5120 x 6144 (160 tile groups) and 8192 x 4096 (256) keep the matrix family
+    for N, K in ((5120, 6144), (8192, 4096)):
+        for M in (5, 8):
+            assert _sel(fmt="fp8", act="f16", N=N, K=K, block_size=128, M=M)["family"] == "mfma"
 
 
 def test_reduction_area_overlays_the_staged_rows_when_one_round_fits():
@@ -314,7 +358,10 @@ def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
         p = _sel(**kw, M=M)
         assert p["passes"] == passes and p["variant"] & 1, (M, p)
         if passes > 1:
-            assert p["rows_per_pass"] == 8 and p["kparts"] == 1 and p == _sel(**kw, M=8) | {"passes": passes}
+            # the passes are the matrix family's 8-row plan (8 rows alone take one
+            # streaming pass of eight rows on this shape: 128 tile groups)
+            assert p["rows_per_pass"] == 8 and p["kparts"] == 1 and p == _sel(**kw, M=8, flags=2) | {"passes": passes}
+    assert _sel(**kw, M=8)["family"] == "stream" and _sel(**kw, M=9)["family"] == "mfma"
     # with a workspace: 2 K parts in one launch instead
     p = _sel(**kw, M=16, with_workspace=True)
     assert p["passes"] == 1 and p["kparts"] == 2

@@ -253,6 +253,25 @@ def test_multi_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act
             assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, nwg, pa)
 
 
+@pytest.mark.parametrize("act,N,K", [("f16", 700, 128 * 41), ("bf16", 1234, 128 * 24), ("f16", 5120, 6144)])
+@pytest.mark.parametrize("M", [5, 6, 8])
+def test_eight_row_persistent_kernel_matches_the_classic_kernel_bitwise(act, N, K, M):
+    """FP8 codes at M = 5..8 in one pass of eight rows (the persistent streaming kernel's
+    largest row tile): each row equals the classic kernel's bits (two passes of four
+    rows), at every workgroup size, and the oracle bound holds."""
+    prob = synth.make_problem("fp8", act, N, K, 128, M, seed=33)
+    gu.say(f"[stream-8rows] fp8/{act} N={N} K={K} M={M}")
+    Yc, pc = gu.run_gpu(prob, M, flags=FAMILY_FLAG["stream_classic"])
+    assert pc["rows_per_pass"] == 4 and pc["passes"] == 2, pc
+    ok, ratio, _, _ = gu.check_full(prob, M, Yc, strict=False)
+    assert ok, ratio
+    for nwg in (0, 1, 2, 3, 4):
+        Ya, pa = gu.run_gpu(prob, M, flags=1 | (nwg << bqw.FLAG_STREAM_NWG_SHIFT))
+        assert pa["variant"] & 1 and pa["rows_per_pass"] == 8 and pa["passes"] == 1, pa
+        assert nwg == 0 or pa["waves_per_wg"] == 4 * nwg, pa
+        assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (nwg, pa)
+
+
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
 def test_repeated_runs_are_bitwise_equal(name, M):
     prob = synth.workload(name)

@@ -65,15 +65,19 @@ def kernel_lds(fmt, act, N, K, bs, rows, plan, zpp=False):
     return end + (4 if kp > 1 else 0)
 
 
-@pytest.mark.parametrize("zp", [False, True])
-@pytest.mark.parametrize("fmt,act,N,K,bs", SHAPES)
-def test_every_matrix_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs, zp):
-    if zp and fmt not in ("u4", "u8"):
-        pytest.skip("zero points are for the integer codes")
+CASES = [(fmt, act, N, K, bs, zp) for (fmt, act, N, K, bs) in SHAPES for zp in (False, True)
+         if not zp or fmt in ("u4", "u8")]  # zero points are for the integer codes
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+@pytest.mark.parametrize("fmt,act,N,K,bs,zp", CASES)
+def test_every_matrix_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs, zp, cu):
+    """At 80, 256 and 304 CUs (plans move with the CU count; the layouts must hold at
+    each)."""
     for M in (1, 2, 3, 4, 5, 8, 9, 12, 13, 16, 20, 37):
         for ws in (False, True):
-            p = bqw.select(fmt, act, N, K, bs, M, with_workspace=ws, zero_points=0x2000 if zp else None)
-            assert 1 <= p["grid"] and 0 <= p["lds_bytes"] <= LDS, (M, ws, p)
+            p = bqw.select(fmt, act, N, K, bs, M, cu_count=cu, with_workspace=ws, zero_points=0x2000 if zp else None)
+            assert 1 <= p["grid"] and 0 <= p["lds_bytes"] <= LDS, (M, ws, cu, p)
             rows = min(M, 16)
             # passes of rows_per_pass rows cover every row of each 16-row chunk
             chunks = (M + 15) // 16
