@@ -502,6 +502,72 @@ __device__ __forceinline__ void meta_decode_s(const KArgs &a, int c, const MetaS
     }
 }
 
+// The dword metadata of one lane's chunks, addressed the way the persistent streaming
+// kernel walks them: chunk c = base + lane with base a multiple of 64 (uniform), so a
+// block index splits into base * KPC / bs, a multiple of 8 (U4) or 4 (U8) blocks, plus
+// the lane's own part, and the dword offsets within a round and the fields' bit
+// positions are the lane's alone. Set once per kernel by meta_dw_lane; each load then
+// takes the round's uniform offset (meta_dw_round) as its scalar offset.
+template <int H>
+struct MetaDW {
+    uint32_t s_off[H], z_off[H];  // byte offsets of the lane's dwords within a round's window
+    uint32_t s_sh[H], z_sh[H];    // bit positions of the fields in them
+};
+
+template <int FMT, int H>
+__device__ __forceinline__ MetaDW<H> meta_dw_lane(const KArgs &a, int lane) {
+    MetaDW<H> d;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        if constexpr (FMT == FMT_NVFP4) {
+            d.s_off[h] = (uint32_t)(lane >> 1) * 4u;  // the chunk's two E4M3 scale bytes
+            d.s_sh[h] = (uint32_t)(lane & 1) << 4;
+            d.z_off[h] = 0u;
+            d.z_sh[h] = 0u;
+        } else {
+            const int bl = chunk_block<FMT>(a, lane, h);
+            d.s_off[h] = (uint32_t)(bl >> 1) * 4u;
+            d.s_sh[h] = (uint32_t)(bl & 1) << 4;
+            d.z_off[h] = (uint32_t)(FMT == FMT_U4 ? (bl >> 3) : (bl >> 2)) * 4u;
+            d.z_sh[h] = (uint32_t)(FMT == FMT_U4 ? (bl & 7) << 2 : (bl & 3) << 3);
+        }
+    }
+    return d;
+}
+
+// The uniform byte offsets of the scale and zero-point dwords for the chunks base +
+// lane (base a multiple of 64).
+template <int FMT>
+__device__ __forceinline__ void meta_dw_round(const KArgs &a, int base, uint32_t &s_off, uint32_t &z_off) {
+    if constexpr (FMT == FMT_NVFP4) {
+        s_off = (uint32_t)(base >> 1) * 4u;
+        z_off = 0u;
+    } else {
+        const int bu = chunk_block<FMT>(a, base, 0);
+        s_off = (uint32_t)(bu >> 1) * 4u;
+        z_off = (uint32_t)(FMT == FMT_U4 ? (bu >> 3) : (bu >> 2)) * 4u;
+    }
+}
+
+// Decode of dword metadata at the lane's bit positions (what meta_decode_s<.., true>
+// takes from the chunk index); zs.fill holds the midpoint in every field.
+template <int FMT, int H>
+__device__ __forceinline__ void meta_decode_dw(const MetaS<H> &m, const MetaDW<H> &d, ZSel zs, float sc[H],
+                                               uint32_t zr[H]) {
+    if constexpr (FMT == FMT_NVFP4) {
+        const uint32_t s2 = m.s[0] >> d.s_sh[0];
+        sc[0] = e4m3_to_float(s2 & 0xFFu);
+        sc[1] = e4m3_to_float((s2 >> 8) & 0xFFu);
+        zr[0] = zr[1] = 0u;
+    } else {
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            sc[h] = half_bits_to_float((uint16_t)(m.s[h] >> d.s_sh[h]));
+            zr[h] = (((m.z[h] & zs.keep) | zs.fill) >> d.z_sh[h]) & (FMT == FMT_U4 ? 0x0Fu : 0xFFu);
+        }
+    }
+}
+
 // Scale and integer zero point of each of the H halves of chunk c, loaded and decoded.
 template <int FMT, int H>
 __device__ __forceinline__ void chunk_meta(const KArgs &a, const ColPtrs &p, int c, float sc[H], uint32_t zr[H]) {

@@ -213,6 +213,10 @@ __device__ __forceinline__ void stage_rows(const KArgs &a, u4v *sP, float *sS, i
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG, int MD>
 __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     constexpr bool WM = MD == 1, DW = MD == 2;
+    // one row and up to two columns per wave: loads through buffer resources (below);
+    // the other shapes keep clamped global addresses (their accumulators, or four
+    // columns' resources, would not leave the scalar registers for them)
+    constexpr bool BUF = MT == 1 && CPW <= 2;
     using Ops = ChunkOps<FMT, ACT, H>;
     using B = SBatch<FMT, H, UNR, CPW>;
     constexpr int NQ = Ops::ND / 4;
@@ -231,27 +235,65 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
     const int mine = gw < ngroups ? (int)((ngroups - gw + nw - 1) / nw) : 0;
     const int total = mine * rounds;
     const ZSel zs = zsel(a.zp, FMT == FMT_U4 ? (DW ? 0x88888888u : 0x88u) : (DW ? 0x80808080u : 128u));
+    // Addressing (BUF): chunk c = base + lane of a column, base = round * 64 * UNR + 64 u
+    // (uniform). The codes, and with DW the metadata dwords, are loaded through a buffer
+    // resource per column with the lane's part as the vector offset and the base's as
+    // the scalar one: a chunk past the column reads zeros, which the select below
+    // discards, so no index needs clamping, and the per-chunk address arithmetic is a
+    // scalar one per round.
+    const uint32_t col_bytes = (uint32_t)a.col_bytes;
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    const MetaDW<H> mdw = meta_dw_lane<FMT, H>(a, lane);
+    // bytes of a column's scale row and zero-point row (the scale row again without
+    // zero points, as col_ptrs aliases it)
+    const uint32_t srow = (uint32_t)(FMT == FMT_NVFP4 ? (a.K >> 4) : (int64_t)a.nblk * (FMT == FMT_FP8 ? 4 : 2));
+    const uint32_t zrow = a.zp ? (uint32_t)a.zstride : srow;
 
     // issue cursor (group, round)
     int64_t ig = gw;
     int ir = 0;
     auto issue = [&](B &b) {
         ColPtrs cp[CPW];
+        __amdgpu_buffer_rsrc_t rw[CPW], rs[CPW], rz[CPW];
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int64_t n = ig * CPW + i;
             cp[i] = col_ptrs<FMT>(a, n < a.N ? n : a.N - 1);
+            if constexpr (BUF) {
+                rw[i] = buf_rsrc(cp[i].w, col_bytes);
+                if constexpr (DW) {
+                    rs[i] = buf_rsrc(cp[i].s, srow);
+                    rz[i] = buf_rsrc(cp[i].z, zrow);
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            const int c = ir * (64 * UNR) + 64 * u + lane;
-            const int cc = c < nch ? c : nch - 1;
+            const int base = ir * (64 * UNR) + 64 * u;
+            const int cc = base + lane < nch ? base + lane : nch - 1;
 #pragma unroll
-            for (int i = 0; i < CPW; ++i) b.w[u][i] = load16_stream(cp[i].w + (uint32_t)cc * 16u);
+            for (int i = 0; i < CPW; ++i) {
+                if constexpr (BUF) b.w[u][i] = buf_load16_stream(rw[i], lane16, (uint32_t)base * 16u);
+                else b.w[u][i] = load16_stream(cp[i].w + (uint32_t)cc * 16u);
+            }
         }
         if constexpr (WM) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) b.mw[i] = meta_window_load_u8<UNR>(a, cp[i], ir, lane);
+        } else if constexpr (DW && BUF) {
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                uint32_t so, zo;
+                meta_dw_round<FMT>(a, ir * (64 * UNR) + 64 * u, so, zo);
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+#pragma unroll
+                    for (int h = 0; h < H; ++h) {
+                        b.m[u][i].s[h] = buf_load4(rs[i], mdw.s_off[h], so);
+                        b.m[u][i].z[h] = FMT == FMT_NVFP4 ? 0u : buf_load4(rz[i], mdw.z_off[h], zo);
+                    }
+                }
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
@@ -283,18 +325,24 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
             const int c = cr * (64 * UNR) + 64 * u + lane;
             const bool valid = c < nch;
             const int cc = valid ? c : nch - 1;
+            // BUF: the staged pieces of the chunk are those of block blk = c / 64, clamped
+            // (uniformly) to the staged rows, which never clamps a valid chunk, and the
+            // lane (piece q at pbase + 64 q, sums at sbase); else those of the clamped chunk
+            const int blk = min(cr * UNR + u, (nch64 >> 6) - 1);
+            const int pbase = blk * (NQ * 64) + lane;
+            const int sbase = (blk * 64 + lane) * H;
             if constexpr (MT == 1) {
                 // one row: the activations are read once and each column's codes are
                 // decoded right before their dot products
                 ChunkAct act;
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) {
-                    const u4v v = sP[stage_index<NQ>(cc, q)];
+                    const u4v v = BUF ? sP[pbase + 64 * q] : sP[stage_index<NQ>(cc, q)];
                     act.p[4 * q] = v.x; act.p[4 * q + 1] = v.y; act.p[4 * q + 2] = v.z; act.p[4 * q + 3] = v.w;
                 }
                 if constexpr (Ops::ASUM) {
 #pragma unroll
-                    for (int h = 0; h < H; ++h) act.asum[h] = sS[cc * H + h];
+                    for (int h = 0; h < H; ++h) act.asum[h] = BUF ? sS[sbase + h] : sS[cc * H + h];
                 }
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
@@ -304,7 +352,8 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                     if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
                     else mu = b.m[u][i];
                     pin_meta(mu);
-                    meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc, zr);
+                    if constexpr (DW && BUF) meta_decode_dw<FMT, H>(mu, mdw, zs, sc, zr);
+                    else meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc, zr);
                     chunk_dot<FMT, ACT, H>(b.w[u][i], zr, act, part);
                     float t = acc[i][0];
 #pragma unroll
@@ -322,7 +371,8 @@ __global__ void __launch_bounds__(64 * NWG) k_stream1(KArgs a) {
                     if constexpr (WM) meta_from_window_u8<UNR>(a, b.mw[i], 64 * u + lane, mu);
                     else mu = b.m[u][i];
                     pin_meta(mu);
-                    meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc[i], zr[i]);
+                    if constexpr (DW && BUF) meta_decode_dw<FMT, H>(mu, mdw, zs, sc[i], zr[i]);
+                    else meta_decode_s<FMT, H, DW>(a, cc, mu, zs, sc[i], zr[i]);
                     Ops::decode(b.w[u][i], zr[i], wd[i]);
                 }
 #pragma unroll

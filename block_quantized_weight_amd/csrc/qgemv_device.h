@@ -211,4 +211,22 @@ __device__ __forceinline__ u4v load16_stream(const void *p) {
     return __builtin_nontemporal_load((const u4v *)p);
 }
 
+// A raw buffer resource over the n bytes at p (gfx9 descriptor word 3: no swizzle,
+// stride 0). Loads through it are range-checked against n: one that reaches past n
+// returns zeros instead of touching memory. The base is uniform (a column's start), so
+// the resource lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, 0x00020000);
+}
+
+// 16 bytes at voff + soff of r, nontemporal (the weight stream; cache policy NT).
+__device__ __forceinline__ u4v buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+}
+
+// The dword at voff + soff of r (zero past the range).
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
 }  // namespace qgemv
