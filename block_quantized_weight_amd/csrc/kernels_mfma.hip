@@ -1098,10 +1098,15 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
 
     int64_t ctile = gw;
     int csl = 0, cring = 0;
-    In cur, nxt;
+    // two operand sets, by step parity: step st computes on opd[st & 1] while the next
+    // step is read into the other; a slot has an even number of steps, so the next
+    // slot's first step lands in opd[0], where the loop expects it (no copy of the
+    // operands across the loop's back edge)
+    static_assert(SS % 2 == 0, "the operand sets alternate by step parity");
+    In opd[2];
     if (total > 0) {
         wait_slot(0);
-        read_step(ring, 0, 0, win_ssub(0), win_zsub(0), cur);
+        read_step(ring, 0, 0, win_ssub(0), win_zsub(0), opd[0]);
     }
 #pragma unroll 1
     for (int64_t i = 0; i < total; ++i) {
@@ -1113,6 +1118,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
         const int ssub = win_ssub(csl), zsub = win_zsub(csl);
 #pragma unroll
         for (int st = 0; st < SS; ++st) {
+            In &nxt = opd[(st + 1) & 1];
             if (st + 1 < SS) {
                 read_step(slot, st + 1, csl * CS + 4 * (st + 1), ssub, zsub, nxt);
             } else if (i + 1 < total) {
@@ -1121,8 +1127,7 @@ __global__ void __launch_bounds__(512, 1) k_mfma_dma(KArgs a) {
                 wait_slot(i + 1);
                 read_step(ring + nring * SLOT, 0, nsl * CS, win_ssub(nsl), win_zsub(nsl), nxt);
             }
-            compute(cur, st, csl * CS + 4 * st < nch);
-            cur = nxt;
+            compute(opd[st & 1], st, csl * CS + 4 * st < nch);
         }
         cring = nring;
         if (++csl == nslots) {
