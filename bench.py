@@ -26,6 +26,7 @@ Profiling helpers (no GPU needed):
   --calib-copy-mib X      also run one plain copy kernel of X MiB (torch.neg on fp32)
                           before the warmup, so a counter run can scale its readings
   --trace-summary DIR     per-kernel durations from a rocprofv3 --kernel-trace database
+  --counter-summary DIR   per-kernel counter means per dispatch from a rocprofv3 --pmc database
   --traffic-record F W    FETCH_SIZE run dir F and WRITE_SIZE run dir W -> traffic record
 """
 
@@ -81,6 +82,7 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain copy kernel of this many MiB before the warmup (counter calibration)")
     p.add_argument("--trace-summary", metavar="DIR", default=None)
+    p.add_argument("--counter-summary", metavar="DIR", default=None)
     p.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     return p.parse_args()
 
@@ -149,6 +151,15 @@ def counter_means(d):
         for name, ctr, v in rows:
             acc.setdefault(name, {}).setdefault(ctr, []).append(float(v))
     return {k: {c: (sum(v) / len(v), len(v)) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def print_counter_summary(d):
+    """One line per qgemv kernel: each counter's mean per dispatch."""
+    for name, cs in sorted(counter_means(d).items()):
+        if _is_qgemv(name):
+            n = max(x[1] for x in cs.values())
+            vals = ", ".join(f"{c} {v[0]:.1f}" for c, v in sorted(cs.items()))
+            print(f"{name}: {vals} ({n} dispatches)")
 
 
 def print_trace_summary(d):
@@ -442,6 +453,9 @@ def measure(prob, ms, args, dev, stream):
 
 def main():
     args = parse()
+    if args.counter_summary:
+        print_counter_summary(args.counter_summary)
+        return
     if args.trace_summary:
         print_trace_summary(args.trace_summary)
         return
