@@ -82,6 +82,11 @@ def test_committed_profiles_name_their_commands():
     assert files
     for f in files:
         txt = open(os.path.join(pdir, f)).read()
-        assert "rocprofv3 --kernel-trace --stats" in txt and "rocprofv3 --pmc FETCH_SIZE" in txt, f
+        if f.startswith("counters_"):
+            # instruction / occupancy counter summaries: the --pmc runs and their reader
+            assert "rocprofv3 --pmc SQ_" in txt and "bench.py --counter-summary" in txt, f
+        else:
+            # per-kernel summaries: the kernel trace and the two traffic counter runs
+            assert "rocprofv3 --kernel-trace --stats" in txt and "rocprofv3 --pmc FETCH_SIZE" in txt, f
         assert "_work" not in txt, f
         assert len(txt) < 16 * 1024, f
