@@ -402,6 +402,21 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         family = QGEMV_FAMILY_MFMA;
     } else if (mfma_ok && M >= 2 && !stream_rows_win(d, M, stream_ok, cu_count, flags)) {
         family = QGEMV_FAMILY_MFMA;
+    } else if (mfma_ok && M == 1 && d->format == QGEMV_FMT_NVFP4 && !(flags & QGEMV_FLAG_STREAM_CLASSIC)) {
+        // NVFP4 at one row: the matrix family where its plan is the DMA ring (wide N),
+        // else the streaming kernel. Measured (M = 1, one session): NVFP4 248320 x 2048
+        // 68.8 -> 53.5 us, 65536 x 2048 19.9 -> 16.2; for 4-bit, 8-bit and FP8 codes the
+        // streaming kernel stays ahead (4-bit 151936 x 4096 64.4 against 74.5 us, 8-bit
+        // 151936 x 2048 61.4 against 65.5, FP8 65536 x 4096 44.1 against 61.7).
+        LaunchCfg ring;
+        const bool takes_ring = select_plan(d, 1, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_MFMA, with_ws, &ring) ==
+                                    QGEMV_OK &&
+                                ring.family == QGEMV_FAMILY_MFMA && (ring.variant & 2);
+        if (takes_ring) {
+            *out = ring;
+            return QGEMV_OK;
+        }
+        family = stream_ok ? QGEMV_FAMILY_STREAM : QGEMV_FAMILY_GENERIC;
     } else if (stream_ok) {
         family = QGEMV_FAMILY_STREAM;
     } else {

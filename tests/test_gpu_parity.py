@@ -74,13 +74,29 @@ def test_u4_lm_head_full_parity(lm_head_u4, M):
     assert ok, (M, ratio, plan)
 
 
-def test_nvfp4_lm_head_full_parity(lm_head_nvfp4):
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_nvfp4_lm_head_full_parity(lm_head_nvfp4, M):
+    """Every output at M = 1, 2 and 4 (the DMA ring at each: NVFP4 takes it from one row
+    where N is wide)."""
     prob, Yr, S = lm_head_nvfp4
-    gu.say("[parity] nvfp4 lm_head M=4")
-    Y, plan = gu.run_gpu(prob, 4)
-    ok, ratio = oracle.within_tolerance(Y, Yr, S)
+    gu.say(f"[parity] nvfp4 lm_head M={M}")
+    Y, plan = gu.run_gpu(prob, M)
+    assert plan["family"] == "mfma" and plan["variant"] & 2, plan
+    ok, ratio = oracle.within_tolerance(Y, Yr[:M], S[:M])
     gu.say(f"   plan={plan} max err/tol={ratio:.3e}")
-    assert ok, (ratio, plan)
+    assert ok, (M, ratio, plan)
+
+
+def test_nvfp4_one_row_rows_match_the_four_row_launch():
+    """NVFP4 on a wide weight runs the matrix family from one row, so a row's bits do not
+    depend on M (the family's row invariance): rows of M = 1 and 2 equal the same rows of
+    a four-row launch, bit for bit (65536 x 2048, the DMA ring at every M)."""
+    prob = synth.make_problem("nvfp4", "bf16", 65536, 2048, 16, 4, seed=52)
+    Y4, p4 = gu.run_gpu(prob, 4)
+    for M in (1, 2):
+        Ym, pm = gu.run_gpu(prob, M)
+        assert pm["family"] == "mfma" and pm["variant"] & 2 and p4["variant"] & 2, (pm, p4)
+        assert np.array_equal(Ym.view(np.int64), Y4[:M].view(np.int64)), M
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
