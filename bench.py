@@ -8,7 +8,12 @@ rotates through R copies of the weight (R * weight bytes >= 1 GiB, four times th
 256 MB last-level cache; R <= 4096, copies held in one device buffer per array), and
 the rotation continues from the warmup, so every call streams a weight last touched
 at least 1 GiB of traffic earlier (310 MB for the 75 KB tiny case, still past the
-cache). Inputs are resident in HBM before the timed region starts.
+cache). Inputs are resident in HBM before the timed region starts. Before the W warmup
+calls of every timed loop, untimed calls run in synchronized chunks until --settle-ms
+(default 100) of wall time have passed, the rotation continuing through them: from
+idle the GPU needs some 30 ms of load (about 500 calls of the 4-bit lm_head) before a
+call settles at its steady time, and the first hundred run some 15% slower, so a
+short warmup alone would time the clocks' ramp, not the kernel.
 
 The default workload is the 4-bit lm_head (K = 4096, N = 151936, bf16): `value` is its
 achieved GB/s at M = 1 = weight bytes (codes + block scales + zero points) per call /
@@ -26,6 +31,8 @@ Profiling helpers (no GPU needed):
   --calib-copy-mib X      also run one plain copy kernel of X MiB (torch.neg on fp32)
                           before the warmup, so a counter run can scale its readings
   --trace-summary DIR     per-kernel durations from a rocprofv3 --kernel-trace database
+                          (with --steps K, also each kernel's mean over its last K
+                          launches: the timed calls of a profiled bench run)
   --counter-summary DIR   per-kernel counter means per dispatch from a rocprofv3 --pmc database
   --traffic-record F W    FETCH_SIZE run dir F and WRITE_SIZE run dir W -> traffic record
 """
@@ -61,6 +68,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="untimed calls before each timed loop's warmup, in synchronized chunks, until this "
+                        "much wall time has passed (the GPU clocks' ramp from idle; 0 = none)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--shape", default=None, metavar="FMT:ACT:N:K:BS",
                    help="time an arbitrary shape instead of a named workload (e.g. fp8:f16:8192:4096:128), "
@@ -131,13 +141,16 @@ def _dbs(d):
 
 
 def trace_durations(d):
-    """{kernel name: [durations in ns]} from --kernel-trace databases under d."""
-    res = {}
+    """{kernel name: [durations in ns], in launch order} from --kernel-trace databases
+    under d."""
+    rows = []
     for db in _dbs(d):
         con = sqlite3.connect(db)
-        for name, start, end in con.execute("select name, start, end from kernels"):
-            res.setdefault(name, []).append(end - start)
+        rows += con.execute("select name, start, end from kernels").fetchall()
         con.close()
+    res = {}
+    for name, start, end in sorted(rows, key=lambda r: r[1]):
+        res.setdefault(name, []).append(end - start)
     return res
 
 
@@ -162,12 +175,16 @@ def print_counter_summary(d):
             print(f"{name}: {vals} ({n} dispatches)")
 
 
-def print_trace_summary(d):
+def print_trace_summary(d, last=0):
+    """One line per kernel: launches, mean / min / max duration, share of the time;
+    with last > 0 also the mean over the kernel's last `last` launches."""
     rows = sorted(trace_durations(d).items(), key=lambda kv: -sum(kv[1]))
     tot = sum(sum(v) for _, v in rows) or 1
-    print(f"{'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'time %':>7}  kernel")
+    tail = f" {'last ' + str(last):>9}" if last else ""
+    print(f"{'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9}{tail} {'time %':>7}  kernel")
     for name, v in rows:
-        print(f"{len(v):6d} {sum(v) / len(v) / 1e3:9.3f} {min(v) / 1e3:9.3f} {max(v) / 1e3:9.3f} "
+        t = f" {sum(v[-last:]) / len(v[-last:]) / 1e3:9.3f}" if last else ""
+        print(f"{len(v):6d} {sum(v) / len(v) / 1e3:9.3f} {min(v) / 1e3:9.3f} {max(v) / 1e3:9.3f}{t} "
               f"{100.0 * sum(v) / tot:7.2f}  {name}")
 
 
@@ -327,22 +344,44 @@ class Rotation:
             q.close()
 
 
-def time_calls(hs, A, Y, M, stream, ws, warmup, steps):
+def settle(call, settle_ms, chunk=32):
+    """Untimed call(i), i = 0, 1, ..., in chunks of `chunk` each followed by a device
+    synchronize, until settle_ms of wall time have passed (so the host never runs far
+    ahead of the GPU). Returns the number of calls made."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(chunk):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def time_calls(hs, A, Y, M, stream, ws, warmup, steps, settle_ms=0.0):
     """(ms per call from HIP events on the launch stream, wall seconds of the timed
-    loop), the calls rotating over the handles hs (one per weight copy). The rotation
-    continues from the warmup into the timed loop."""
+    loop), the calls rotating over the handles hs (one per weight copy). Settle calls
+    (settle_ms), then the warmup, then the timed loop: the rotation runs on through
+    all three."""
     import torch
 
     R = len(hs)
-    for i in range(warmup):
+
+    def call(i):
         hs[i % R].run(A, Y, M, stream, workspace=ws)
+
+    i0 = settle(call, settle_ms)
+    for i in range(i0, i0 + warmup):
+        call(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(warmup, warmup + steps):
-        hs[i % R].run(A, Y, M, stream, workspace=ws)
+    for i in range(i0 + warmup, i0 + warmup + steps):
+        call(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
@@ -352,9 +391,9 @@ READ_CONTROL_SHAPES = ((2048, 4), (4096, 4), (4096, 8), (8192, 4), (8192, 8), (1
                        (2048, 16))
 
 
-def time_read_control(nbytes, dev, stream, warmup, steps):
-    """The plain streaming read of nbytes, cold like the GEMV (copies rotated, the
-    rotation continuing from the warmup), for each (workgroups, loads in flight per
+def time_read_control(nbytes, dev, stream, warmup, steps, settle_ms=0.0):
+    """The plain streaming read of nbytes, cold like the GEMV (settle calls and warmup
+    as for the GEMV, the rotation continuing into the timed loop), for each (workgroups, loads in flight per
     lane) of READ_CONTROL_SHAPES: the fastest, as the control is a ceiling. Returns
     (ms per read, GB/s, shape, {shape: GB/s})."""
     import ctypes
@@ -379,13 +418,14 @@ def time_read_control(nbytes, dev, stream, warmup, steps):
             if rc:
                 raise RuntimeError(f"read control launch failed ({rc})")
 
-        for i in range(warmup):
+        i0 = settle(go, settle_ms)
+        for i in range(i0, i0 + warmup):
             go(i)
         torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for i in range(warmup, warmup + steps):
+        for i in range(i0 + warmup, i0 + warmup + steps):
             go(i)
         ev1.record(stream)
         torch.cuda.synchronize()
@@ -410,7 +450,7 @@ def tuned_calls(rot, A, Y, M, stream, ws, args, wbytes, auto_ms):
         msc = auto_ms  # the automatic launch was kept: its cold time stands
     else:
         hs = [rot.handle_with(args.flags | f, i) for i in range(rot.copies)]
-        msc, _ = time_calls(hs, A, Y, M, stream, ws, args.warmup, args.steps)
+        msc, _ = time_calls(hs, A, Y, M, stream, ws, args.warmup, args.steps, args.settle_ms)
         for h in hs:
             h.close()
     q.close()
@@ -438,7 +478,8 @@ def measure(prob, ms, args, dev, stream):
             ws = torch.zeros(max(256, plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
         A = A_all[:M].contiguous()
         Y = torch.empty((M, prob.N), dtype=tdt, device=dev)
-        msc, wall = time_calls(rot.handles, A, Y, M, stream, ws if use_ws else None, args.warmup, args.steps)
+        msc, wall = time_calls(rot.handles, A, Y, M, stream, ws if use_ws else None, args.warmup, args.steps,
+                               args.settle_ms)
         out[M] = {"us_per_call": round(msc * 1e3, 3), "gbs": round(wbytes / (msc * 1e-3) / 1e9, 2),
                   "ms_per_step": msc, "wall_s": round(wall, 4), "plan": plan}
         if args.tune:
@@ -457,7 +498,7 @@ def main():
         print_counter_summary(args.counter_summary)
         return
     if args.trace_summary:
-        print_trace_summary(args.trace_summary)
+        print_trace_summary(args.trace_summary, args.steps)
         return
     if args.traffic_record:
         traffic_record(*args.traffic_record, args)
@@ -515,7 +556,7 @@ def main():
 
     read = None
     if not args.no_read_control:
-        rms, rgbs, shape, table = time_read_control(wbytes, dev, stream, args.warmup, args.steps)
+        rms, rgbs, shape, table = time_read_control(wbytes, dev, stream, args.warmup, args.steps, args.settle_ms)
         read = {"bytes": wbytes, "us_per_read": round(rms * 1e3, 3), "gbs": round(rgbs, 2),
                 "kernel": f"k_read_control (libreadctl.so): 16-byte nontemporal loads, {shape[1]} in flight per "
                           f"lane, {shape[0]} workgroups of 256 threads (fastest of the shapes tried)",
@@ -533,6 +574,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per, 6),
         "us_per_call": head["us_per_call"],
         "higher_is_better": True,

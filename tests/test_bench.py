@@ -47,6 +47,35 @@ def test_trace_durations_and_counter_means(tmp_path):
     assert cm["void qgemv::k(x)"]["FETCH_SIZE"] == (12.0, 2)
 
 
+def test_trace_summary_means_the_last_launches(tmp_path, capsys):
+    """Durations come back in launch order, across databases, and the summary's last-K
+    column averages the kernel's last K launches (a profiled run's timed calls)."""
+    d = tmp_path / "run"
+    d.mkdir()
+    _rocpd(str(d / "a_results.db"), kernels=[("k", 300, 1300), ("k", 0, 5000)])
+    _rocpd(str(d / "b_results.db"), kernels=[("k", 100, 3100)])
+    assert bench.trace_durations(str(d))["k"] == [5000, 3000, 1000]
+    bench.print_trace_summary(str(d), last=2)
+    head, row = capsys.readouterr().out.splitlines()
+    assert "last 2" in head
+    assert row.split()[:5] == ["3", "3.000", "1.000", "5.000", "2.000"]
+
+
+def test_settle_runs_whole_synchronized_chunks_until_the_time_is_up(monkeypatch):
+    import time
+
+    import torch
+
+    syncs = []
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: syncs.append(1))
+    seen = []
+    assert bench.settle(seen.append, 0.0) == 0 and not seen and not syncs
+    t0 = time.perf_counter()
+    n = bench.settle(lambda i: (seen.append(i), time.sleep(0.0005)), 20.0, chunk=8)
+    assert (time.perf_counter() - t0) * 1e3 >= 20.0
+    assert n > 0 and n % 8 == 0 and seen == list(range(n)) and len(syncs) == n // 8
+
+
 def test_traffic_lookup_is_gated_on_the_source_hash(tmp_path, monkeypatch):
     rec = {"workload": "w", "M": 4, "flags": 0, "ws": True, "src_hash": bench.kernel_source_hash(),
            "traffic_bytes": 1234}
