@@ -439,8 +439,8 @@ def time_read_control(nbytes, dev, stream, warmup, steps, settle_ms=0.0):
 
 
 def tuned_calls(rot, A, Y, M, stream, ws, args, wbytes, auto_ms):
-    """qgemv_tune on the first copy's handle (warm: it times one weight), then the kept
-    flags timed cold like the automatic plan, over the same copies."""
+    """qgemv_tune on the first copy's handle (it times every call cold, after a cache
+    sweep), then the kept flags timed like the automatic plan, over the same copies."""
     q = rot.handle_with(args.flags)
     info = q.tune(A, Y, M=M, with_workspace=ws is not None, workspace=ws)
     f = info["chosen_flags"]

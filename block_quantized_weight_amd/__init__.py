@@ -266,8 +266,9 @@ class QGemv:
              workspace_bytes: Optional[int] = None, rounds: int = 0, reps: int = 0,
              stream: Any = None) -> Dict[str, Any]:
         """qgemv_tune: time the launches that give the automatic plan's bits for M rows
-        on these buffers and keep the fastest in the handle (for qgemv_run, or with a
-        workspace for qgemv_run_ws / qgemv_run_noalloc). Waits for its work."""
+        on these buffers, each call cold (after a read sweep over a 512 MiB buffer the
+        call allocates and frees), and keep the fastest in the handle (for qgemv_run, or
+        with a workspace for qgemv_run_ws / qgemv_run_noalloc). Waits for its work."""
         if M is None:
             M = int(A.shape[0])
         if workspace is not None and workspace_bytes is None:

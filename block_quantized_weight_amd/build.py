@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libqgemv.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "qgemv")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "select.cpp", "kernels_vector.hip", "kernels_mfma.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "select.cpp", "kernels_vector.hip", "kernels_mfma.hip", "scratch.hip", "sweep.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]

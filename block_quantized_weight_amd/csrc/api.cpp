@@ -376,8 +376,22 @@ int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspac
     const int nc = (int)plans.size();
     if (nc == 0) return QGEMV_E_ARG;  // plans[0], with no extra flags, is the automatic launch
     hipStream_t s = (hipStream_t)hip_stream;
-    std::vector<hipEvent_t> ev(2 * (size_t)nc, nullptr);
-    std::vector<double> us((size_t)nc * rounds, 0.0);
+    // Cold timing: before every timed call a read sweep over twice the last-level cache
+    // (sweep.hip) evicts the weight, so that each candidate is timed fetching it from
+    // HBM, as a decode step does; each call is timed alone between two events.
+    constexpr size_t kSweepBytes = (size_t)512 << 20;
+    void *sweep = nullptr;
+    {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess) return QGEMV_E_DEVICE;
+        if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return QGEMV_E_DEVICE;
+        const bool ok = hipMalloc(&sweep, kSweepBytes + 256) == hipSuccess;
+        if (prev != h->device) hipSetDevice(prev);
+        if (!ok) return QGEMV_E_ALLOC;
+    }
+    uint32_t *sink = (uint32_t *)((unsigned char *)sweep + kSweepBytes);
+    std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+    std::vector<double> us((size_t)nc * rounds * reps, 0.0);  // [candidate][round][rep]
     int status = QGEMV_OK;
     for (size_t i = 0; i < ev.size() && status == QGEMV_OK; ++i)
         if (hipEventCreate(&ev[i]) != hipSuccess) status = QGEMV_E_LAUNCH;
@@ -386,23 +400,28 @@ int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspac
         status = enqueue(h, plans[i], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
     for (int r = 0; r < rounds && status == QGEMV_OK; ++r) {
         for (int i = 0; i < nc && status == QGEMV_OK; ++i) {
-            if (hipEventRecord(ev[2 * i], s) != hipSuccess) status = QGEMV_E_LAUNCH;
-            for (int k = 0; k < reps && status == QGEMV_OK; ++k)
-                status = enqueue(h, plans[i], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
-            if (status == QGEMV_OK && hipEventRecord(ev[2 * i + 1], s) != hipSuccess) status = QGEMV_E_LAUNCH;
-        }
-        if (status == QGEMV_OK && hipEventSynchronize(ev[2 * nc - 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
-        for (int i = 0; i < nc && status == QGEMV_OK; ++i) {
-            float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
-            us[(size_t)i * rounds + r] = 1000.0 * (double)ms / reps;
+            for (int k = 0; k < reps && status == QGEMV_OK; ++k) {
+                if (qgemv::launch_sweep(sweep, kSweepBytes, sink, s) != hipSuccess ||
+                    hipEventRecord(ev[2 * k], s) != hipSuccess)
+                    status = QGEMV_E_LAUNCH;
+                if (status == QGEMV_OK)
+                    status = enqueue(h, plans[i], A, Y, M, workspace, workspace_bytes, s, QGEMV_E_WORKSPACE);
+                if (status == QGEMV_OK && hipEventRecord(ev[2 * k + 1], s) != hipSuccess) status = QGEMV_E_LAUNCH;
+            }
+            if (status == QGEMV_OK && hipEventSynchronize(ev[2 * reps - 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
+            for (int k = 0; k < reps && status == QGEMV_OK; ++k) {
+                float ms = 0.0f;
+                if (hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]) != hipSuccess) status = QGEMV_E_LAUNCH;
+                us[((size_t)i * rounds + r) * reps + k] = 1000.0 * (double)ms;
+            }
         }
     }
     int best = 0;
     std::vector<double> med((size_t)nc, 0.0);
     if (status == QGEMV_OK) {
         for (int i = 0; i < nc; ++i) {
-            std::vector<double> v(us.begin() + (size_t)i * rounds, us.begin() + (size_t)(i + 1) * rounds);
+            const size_t per = (size_t)rounds * reps;
+            std::vector<double> v(us.begin() + (size_t)i * per, us.begin() + (size_t)(i + 1) * per);
             std::sort(v.begin(), v.end());
             med[i] = v[v.size() / 2];
         }
@@ -418,6 +437,7 @@ int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspac
     }
     for (hipEvent_t e : ev)
         if (e) hipEventDestroy(e);
+    hipFree(sweep);  // (synchronizes with the device: nothing of this call reads it after)
     if (status != QGEMV_OK) return status;
     h->plan[w][f][M - 1] = plans[best];
     if (out) {

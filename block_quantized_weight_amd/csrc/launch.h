@@ -94,5 +94,6 @@ inline hipError_t lds_limit_once(const void *kern, int device, int lds_bytes, st
 hipError_t launch_stream(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
 hipError_t launch_generic(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
 hipError_t launch_mfma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s);
+hipError_t launch_sweep(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);  // sweep.hip
 
 }  // namespace qgemv

@@ -93,7 +93,7 @@ enum qgemv_status {
     QGEMV_E_DEVICE = 5,   /* no usable device, or the device is not gfx950 */
     QGEMV_E_LAUNCH = 6,   /* the kernel launch reported an error */
     QGEMV_E_ARG = 7,      /* other invalid argument (struct size, flags, plan request) */
-    QGEMV_E_ALLOC = 8,    /* host memory for the handle could not be allocated */
+    QGEMV_E_ALLOC = 8,    /* host memory for the handle (or qgemv_tune's device buffer) could not be allocated */
     QGEMV_E_WORKSPACE = 9, /* qgemv_run_ws: the plan needs a workspace and none, or too small
                               or misaligned a one, was given */
     QGEMV_E_SCRATCH = 10   /* qgemv_run_noalloc: the plan needs more workspace than
@@ -316,7 +316,7 @@ typedef struct qgemv_tune_info {
                                (0 = the automatic one); a handle created with them in
                                qgemv_desc.flags plans the same launch for this M */
     int32_t reserved;       /* 0 */
-    double auto_us;         /* median of the rounds' mean time per call, automatic launch */
+    double auto_us;         /* median time of the automatic launch's timed calls (each cold) */
     double chosen_us;       /* the same for the kept launch */
 } qgemv_tune_info;
 
@@ -341,25 +341,29 @@ int qgemv_tune_candidates(const qgemv_desc *d, int M, int cu_count, int with_wor
  * small-M GEMV for MatMulNBits (4-bit/8-bit)", review). Times every launch that
  * qgemv_tune_candidates lists for this handle's device (after the create-time
  * residency cut; launches that come out equal are timed once) on the caller's A, Y
- * and workspace, `rounds` rounds of `reps` back-to-back calls each (0 for either: 5
- * and 10), interleaved so that every candidate sees the same conditions, and keeps
- * the launch with the least median time in the handle, for qgemv_run (with_workspace
+ * and workspace, `rounds` rounds of `reps` calls each (0 for either: 5 and 10),
+ * interleaved so that every candidate sees the same conditions, and keeps the launch
+ * with the least median time per call in the handle, for qgemv_run (with_workspace
  * = 0) or qgemv_run_ws and qgemv_run_noalloc (with_workspace != 0), for the pointer
  * alignment that A and Y have. The automatic launch is kept unless another is faster
  * by more than 2%. Every launch listed gives the same bits, so results do not change;
  * only the time does. Calls with more than 16 rows use the 16-row plan and so follow a
  * tuning of M = 16.
  *
- * The timing sees the memory system as the calls leave it: a weight small enough to
- * stay in the last-level cache is timed warm. A, Y, workspace and workspace_bytes are
- * as for qgemv_run_ws (the workspace only when with_workspace != 0 and the plan has K
- * parts); Y is written many times and holds the kept launch's product on return. The
- * call waits for its own work on hip_stream (HIP events) and returns after it; it
- * creates and destroys HIP events but allocates no device memory. It changes the
- * handle: no other call on the same handle may overlap it. *out (may be NULL) receives
- * what was measured. Returns QGEMV_E_SHAPE for M outside [1, QGEMV_MAX_M],
- * QGEMV_E_WORKSPACE when the plan needs a workspace that is not given, QGEMV_E_LAUNCH
- * when a launch or an event fails (the handle keeps the plan it had). */
+ * Every timed call is cold, as in a decode step, where each weight is read once per
+ * token among many times the caches' size of others: before it, a read sweep over a
+ * 512 MiB device buffer (twice MI355X's 256 MB last-level cache) evicts the weight,
+ * and the call alone is timed between two HIP events. A, Y, workspace and
+ * workspace_bytes are as for qgemv_run_ws (the workspace only when with_workspace != 0
+ * and the plan has K parts); Y is written many times and holds the kept launch's
+ * product on return. The call waits for its own work on hip_stream (HIP events) and
+ * returns after it; it allocates the sweep buffer on the handle's device for its
+ * duration and frees it before returning. It changes the handle: no other call on the
+ * same handle may overlap it. *out (may be NULL) receives what was measured. Returns
+ * QGEMV_E_SHAPE for M outside [1, QGEMV_MAX_M], QGEMV_E_WORKSPACE when the plan needs
+ * a workspace that is not given, QGEMV_E_ALLOC when the sweep buffer cannot be
+ * allocated, QGEMV_E_LAUNCH when a launch or an event fails (the handle keeps the plan
+ * it had in each case). */
 int qgemv_tune(qgemv_handle *h, const void *A, void *Y, int M, int with_workspace, void *workspace,
                size_t workspace_bytes, int rounds, int reps, void *hip_stream, qgemv_tune_info *out);
 

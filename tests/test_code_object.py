@@ -66,7 +66,8 @@ def _gfx950_objects(blob):
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
     objs = _gfx950_objects(_section(LIB, ".hip_fatbin"))
-    assert len(objs) == 3, "one gfx950 code object per HIP source expected (two kernel files, the scratch array)"
+    assert len(objs) == 4, ("one gfx950 code object per HIP source expected (two kernel files, the scratch array, "
+                            "the tuner's cache sweep)")
     recs = {}
     for i, obj in enumerate(objs):
         path = tmp_path_factory.mktemp("co") / f"co{i}.o"
@@ -91,6 +92,7 @@ def test_every_kernel_family_is_built(kernels):
     names = " ".join(kernels)
     for fam in ("k_stream1", "k_stream", "k_generic", "k_mfma", "k_mfma_dma"):
         assert re.search(rf"\d{fam}I", names), fam
+    assert re.search(r"\d+k_sweep", names), "k_sweep"
     assert len(kernels) > 100
 
 
