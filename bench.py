@@ -18,7 +18,11 @@ short warmup alone would time the clocks' ramp, not the kernel.
 The default workload is the 4-bit lm_head (K = 4096, N = 151936, bf16): `value` is its
 achieved GB/s at M = 1 = weight bytes (codes + block scales + zero points) per call /
 average time per call; the same line carries the M sweep 1, 2, 4, 8, 16 of that weight
-(us/call, GB/s, t(M)/t(1), plan) and the FP8 5120 x 6144 projection at M = 1, 4, 8.
+(us/call, GB/s, t(M)/t(1), plan), then every other named workload timed the same way
+(`extra_workloads`: the FP8 5120 x 6144 projection at M = 1, 4, 8, the 8-bit 4096 x 4096
+weight at M = 1, the NVFP4 lm_head at M = 1 and 4, NVFP4 2048 x 2048 at M = 4, the 4-bit
+1024 x 2048 split-K case at M = 8 and the tiny 4-bit case at M = 1), each with the plain
+read control of its own weight bytes unless --no-read-control.
 `roofline` reports the M = 1 figure against the 8 TB/s HBM peak and against a plain
 streaming read of the same bytes (the control kernel in libreadctl.so, timed with the
 same cold rotation); its `traffic` is the HBM bytes per launch that two rocprofv3
@@ -54,7 +58,9 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "u4_k4096_n151936"
 # second workload of the default line: the FP8 projection at the metric's M = 1, 4, 8
-EXTRA_WORKLOADS = (("fp8_k6144_n5120", (1, 4, 8)),)
+# the other named workloads, each at its own row counts (the NVFP4 lm_head also at M = 1)
+EXTRA_WORKLOADS = (("fp8_k6144_n5120", (1, 4, 8)), ("u8_m1_k4096_n4096", (1,)), ("nvfp4_m4_k2048_n248320", (1, 4)),
+                   ("nvfp4_m4_k2048_n2048", (4,)), ("u4_m8_k2048_n1024", (8,)), ("u4_m1_k512_n256", (1,)))
 METRIC = "achieved HBM GB/s (weight bytes/kernel time) and us/call at M=1,4,8"
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 1 << 30
@@ -78,7 +84,7 @@ def parse():
     p.add_argument("--seed", type=int, default=7, help="seed for --shape")
     p.add_argument("--m", type=int, default=None,
                    help="rows of A (default: the workload's M sweep, the first M as the headline; 1 for --shape)")
-    p.add_argument("--no-extra", action="store_true", help="skip the FP8 projection's M = 1, 4, 8 lines")
+    p.add_argument("--no-extra", action="store_true", help="skip the other named workloads' lines")
     p.add_argument("--no-read-control", action="store_true", help="skip the plain streaming read control")
     p.add_argument("--no-tune", dest="tune", action="store_false",
                    help="skip qgemv_tune (by default each M is also tuned and the kept launch timed cold)")
@@ -549,9 +555,15 @@ def main():
         for name, ems in EXTRA_WORKLOADS:
             p2 = synth.workload(name)
             res, c2 = measure(p2, ems, args, dev, stream)
-            extra[name] = {"weight_bytes": p2.weight_bytes(), "cold_copies": c2,
-                           "by_m": {str(m): {k: v for k, v in r.items() if k != "ms_per_step"}
-                                    for m, r in res.items()}}
+            e = {"weight_bytes": p2.weight_bytes(), "cold_copies": c2,
+                 "by_m": {str(m): {k: v for k, v in r.items() if k != "ms_per_step"} for m, r in res.items()}}
+            if not args.no_read_control:
+                rms2, rgbs2, _, _ = time_read_control(p2.weight_bytes(), dev, stream, args.warmup, args.steps,
+                                                      args.settle_ms)
+                e["read_control"] = {"us_per_read": round(rms2 * 1e3, 3), "gbs": round(rgbs2, 2)}
+                for r in e["by_m"].values():
+                    r["frac_of_read_control"] = round(r["gbs"] / rgbs2, 4)
+            extra[name] = e
             del p2
 
     read = None
