@@ -743,7 +743,14 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         const int t0 = kslice + is * ks;
         const int c4 = 4 * (pbeg + (t0 < nsteps ? t0 : nsteps - 1));
         const int c = c4 + g;
-        wb[p] = load16_stream(col.w + (uint32_t)(c4 + (lane & 3)) * 16u);
+        // A step reads 64 bytes of each column, half of a 128-byte line whose other half
+        // the next step reads. Ordinary loads keep the line in the L2 for it; with
+        // nontemporal ones about a third of the pairs both went to HBM (4-bit lm_head,
+        // M = 16: 1.32x the weight bytes fetched, 1.008x with ordinary loads; 137.9 ->
+        // 132.4 us; FP8 5120 x 6144 M = 8 16.0 -> 14.3 us). With K parts, nontemporal
+        // loads measured faster (FP8 1024 x 16384 M = 8: 14.5 against 15.1 us).
+        const u4v *wp = (const u4v *)(col.w + (uint32_t)(c4 + (lane & 3)) * 16u);
+        wb[p] = KP ? load16_stream(wp) : load16(wp);
         mb[p] = load_meta_raw<FMT, H>(a, col, c4 + (lane & 3));
         if constexpr (!LDSA) load_a_ops<FMT, ACT, RG>(a, c, ar, ab[p]);
         if (++is == S) {
