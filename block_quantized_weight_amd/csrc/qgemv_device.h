@@ -194,12 +194,13 @@ __device__ __forceinline__ void wait_slots(int64_t left) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land at
-// lds + l * BYTES (global_load_lds_dword / _dwordx4). Counted by vmcnt.
-template <int BYTES>
+// lds + l * BYTES (global_load_lds_dword / _dwordx4). Counted by vmcnt. NT: cache
+// policy nontemporal, for bytes read once (aux bit 1, as for the streaming buffer loads).
+template <int BYTES, bool NT = false>
 __device__ __forceinline__ void dma_to_lds(const void *src, void *lds) {
     static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4 copies");
-    if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 4, 0, 0);
-    else __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+    if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 4, 0, NT ? 2 : 0);
+    else __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, NT ? 2 : 0);
 }
 
 __device__ __forceinline__ u4v load16(const void *p) {
