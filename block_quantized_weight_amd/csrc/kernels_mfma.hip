@@ -830,7 +830,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
 // global -> LDS by DMA (global_load_lds) in slots of SS K steps (CS = 4 * SS chunks
 // of each of the 16 columns), R slots per wave and R - 1 in flight, so the prefetch
 // depth costs no VGPRs and the waits are exact load counts. The launcher takes SS = 4
-// and R = 2: the next slot loads while the current one computes.
+// and R = 2 (the next slot loads while the current one computes) or 3.
 //  - Coalescing: one code DMA instruction moves 64 / CS whole columns' CS chunks
 //    (CS * 16 contiguous bytes each, whole cache lines), not 16 columns' 64-byte
 //    pieces. Which lane fetches which chunk is permuted (chunk j of column n lands
@@ -1202,12 +1202,14 @@ hipError_t go_dma_rs(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     return launch_or_report(cfg, kern, 512, a, s);
 }
 
-// DMA ring: 4-step slots, double-buffered; one or two row groups only
+// DMA ring: 4-step slots, two or three per wave; one or two row groups only
 template <int FMT, int ACT, int RG, int H, bool ZPP>
 hipError_t go_dma(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     if (cfg.waves_per_wg != 8 || cfg.ksplit != 1) return hipErrorInvalidValue;
     if constexpr (RG <= 2) {
-        return go_dma_rs<FMT, ACT, RG, H, ZPP, 2, 4>(cfg, a, s);
+        // variant bit 2: three slots per wave (the dispatcher's depth rule), else two
+        return (cfg.variant & 4) ? go_dma_rs<FMT, ACT, RG, H, ZPP, 3, 4>(cfg, a, s)
+                                 : go_dma_rs<FMT, ACT, RG, H, ZPP, 2, 4>(cfg, a, s);
     } else {
         return hipErrorInvalidValue;
     }

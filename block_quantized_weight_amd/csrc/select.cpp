@@ -90,15 +90,12 @@ static bool needs_act_sums(const qgemv_desc *d) {
     return d->format == QGEMV_FMT_U4 && d->act_dtype == QGEMV_ACT_BF16;
 }
 
-// Whether the matrix family's DMA ring takes the problem, and its LDS bytes next to
-// abytes of staged activations. The ring is double-buffered with 4-step slots (16
-// chunks of each of a tile's 16 columns per slot). Measured on MI355X, this beat every
-// deeper ring (4-step x 3, 2-step x 4..7) on every workload that had the LDS for those:
-// the per-slot costs (the wait, the refill's DMA issue) weigh more than depth. It is
-// also the smallest of them in LDS. The scale (and zero-point) rows must be whole dwords
-// on 4-byte aligned arrays. A slot of 64 chunks per column holds whole blocks for
-// every block size the formats take.
-static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t *lds_out) {
+// Whether the matrix family's DMA ring takes the problem with `slots` 4-step slots per
+// wave (16 chunks of each of a tile's 16 columns per slot), and its LDS bytes next to
+// abytes of staged activations. The scale (and zero-point) rows must be whole dwords on
+// 4-byte aligned arrays. A slot of 64 chunks per column holds whole blocks for every
+// block size the formats take.
+static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int slots, int32_t *lds_out) {
     const int64_t nblk = d->K / d->block_size;
     const int sb = d->format == QGEMV_FMT_FP8 ? 4 : (d->format == QGEMV_FMT_NVFP4 ? 1 : 2);
     if ((nblk * sb) % 4 || (uintptr_t)d->scales % 4) return false;
@@ -107,10 +104,10 @@ static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int32_t
         if (zrow % 4 || (uintptr_t)d->zero_points % 4) return false;
     }
     // slot: 4 KiB of codes, the scale window (4 DMAs of 256 B where 16-wide blocks or
-    // FP8 need them, else 2), the zero-point window (256 B); 8 waves x 2 slots
+    // FP8 need them, else 2), the zero-point window (256 B); 8 waves x `slots` slots
     const bool wide_meta = d->format == QGEMV_FMT_FP8 || (d->format == QGEMV_FMT_U4 && d->block_size == 16);
     const int64_t slot = 4 * 1024 + 256 * (wide_meta ? 4 : 2) + (zpp ? 256 : 0);
-    const int64_t lds = abytes + 8 * 2 * slot;
+    const int64_t lds = abytes + 8 * (int64_t)slots * slot;
     if (lds > kLdsBytes) return false;
     *lds_out = (int32_t)lds;
     return true;
@@ -510,13 +507,27 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // 8 waves per CU, each with R slots of SS K steps; the largest prefetch that
         // fits in LDS next to the staged activations.
         const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
-        const bool ring_fits = dma_ring_fits(d, abytes16, zpp, &c.lds_bytes);
+        const bool ring_fits = dma_ring_fits(d, abytes16, zpp, 2, &c.lds_bytes);
+        // Ring depth: 2 slots per wave (the next slot loads while the current one
+        // computes), 3 for the formats with 16 k per chunk (FP8, 8-bit codes), whose slot
+        // holds half the arithmetic of a 4-bit one, where the LDS holds the third. Measured
+        // with nontemporal code copies (2 -> 3 slots): FP8 65536 x 4096 M = 3 / 4 56.7 /
+        // 57.0 -> 50.2 / 50.4 us, 8-bit 56.4 / 56.7 -> 49.4 / 49.7, 8-bit on bf16 M = 4
+        // 57.2 -> 52.2, FP8 151936 x 4096 M = 4 124.2 -> 118.8, but FP8 131072 x 2048
+        // (bf16) M = 4 43.4 -> 44.1; 4-bit and NVFP4 lm_heads 2-4% slower with 3. Deeper
+        // rings of shorter slots lost everywhere (the per-slot wait and DMA issue). The
+        // depth flag forces 2 (value 1) or 3 (value 2) slots where they fit.
+        const uint32_t rdep = (flags & QGEMV_FLAG_MFMA_DEPTH_MASK) >> QGEMV_FLAG_MFMA_DEPTH_SHIFT;
+        int32_t lds3 = 0;
+        const bool three = (rdep == 2 || (rdep == 0 && k_per_chunk(d->format) == 16)) &&
+                           dma_ring_fits(d, abytes16, zpp, 3, &lds3);
         bool ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits && groups > cu_count;
         if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {
             c.waves_per_wg = 8;
-            c.variant = 2;
+            c.variant = 2 | (three ? 4 : 0);
+            if (three) c.lds_bytes = lds3;
             const int64_t wgs = (tiles + 7) / 8;
             c.grid = wgs < cu_count ? wgs : cu_count;
             *out = c;

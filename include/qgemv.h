@@ -129,8 +129,8 @@ enum qgemv_family {
  * columns per wave (1 -> 1, 2 -> 2, 3 -> 4), bits 23..24 the chunks per lane per
  * batch (1 -> 2, 2 -> 3, 3 -> 4), bits 25..27 the resident waves per CU the grid is
  * sized for (v -> 4v); 0 = automatic. Bit 28: use the non-persistent streaming kernel
- * at M = 1 as well. Bits 29..30: MFMA register-ring depth (1 -> 4 slots, 2 -> 8;
- * 0 = automatic). Bit 31: 16-wave workgroups for the one-row streaming kernel with one
+ * at M = 1 as well. Bits 29..30: MFMA ring depth (register ring: 1 -> 4 slots, 2 -> 8;
+ * DMA ring: 1 -> 2 slots per wave, 2 -> 3 where they fit in LDS; 0 = automatic). Bit 31: 16-wave workgroups for the one-row streaming kernel with one
  * column per wave (also chosen automatically when the columns fill 8 to 16 waves per
  * CU and neither bits 21..22 nor 25..27 are set). None of these changes a result's
  * bits except the family choice, the K split and the K parts; they exist for A/B
@@ -192,8 +192,9 @@ typedef struct qgemv_plan_info {
     int32_t lds_bytes;       /* dynamic LDS per workgroup */
     int32_t variant;         /* family-specific variant bits. MFMA: bit 0 = activations staged in
                                 LDS, bit 1 = weights through the LDS DMA ring (4-step slots,
-                                double-buffered), bit 3 = 8-slot register ring (else 4, or fewer
-                                where the registers do not allow 4).
+                                two per wave), bit 2 = three DMA-ring slots per wave, bit 3 =
+                                8-slot register ring (else 4, or fewer where the registers do
+                                not allow 4).
                                 Streaming: bit 0 = persistent kernel (1, 2 or 4 rows per pass),
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4),
                                 bit 3 = block metadata loaded as one window per round (8-bit

@@ -114,6 +114,25 @@ def test_dma_ring_walks_several_rounds(act, M):
     assert ok, (ratio, plan)
 
 
+@pytest.mark.parametrize("fmt,act", [("fp8", "f16"), ("u8", "f16"), ("u8", "bf16"), ("u4", "bf16")])
+@pytest.mark.parametrize("M", [3, 4])
+def test_three_slot_dma_ring(fmt, act, M):
+    """The DMA ring with three slots per wave (the automatic depth for FP8 and 8-bit
+    codes, forced for 4-bit ones) on a ragged N that walks several tiles per wave:
+    every output against the oracle, and the same bits as the two-slot ring."""
+    depth = 29  # QGEMV_FLAG_MFMA_DEPTH_SHIFT
+    ring = 2 | bqw.FLAG_RING_ON | (1 << 8)  # the matrix family, no K split, the DMA ring
+    prob = synth.make_problem(fmt, act, 20003, 2048, 32 if fmt == "u4" else 128, M, seed=91)
+    gu.say(f"[parity] three-slot dma ring {fmt}/{act} 20003x2048 M={M}")
+    Y3, p3 = gu.run_gpu(prob, M, flags=ring | (2 << depth))
+    Y2, p2 = gu.run_gpu(prob, M, flags=ring | (1 << depth))
+    assert p3["variant"] & 6 == 6 and p2["variant"] & 6 == 2, (p3, p2)
+    ok, ratio, _, _ = gu.check_full(prob, M, Y3)
+    gu.say(f"   plan={p3} max err/tol={ratio:.3e}")
+    assert ok, (ratio, p3)
+    assert np.array_equal(Y3.view(np.int64), Y2.view(np.int64))
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "u4"])
 @pytest.mark.parametrize("M,family", [(5, "mfma"), (6, "stream"), (16, "stream")])
 def test_tall_narrow_shapes_without_workspace(fmt, M, family):

@@ -8,7 +8,7 @@ other formats with zero points form q - z in the decode), then the K-split
 reduction area (8 waves x row groups x 4 x 64 fp32), which overlays the staged rows from
 byte 0 when the workgroup holds a single tile group (always with K parts), and, with K
 parts, a 4-byte completion flag after both. The DMA-ring kernel (k_mfma_dma) stages
-all of K the same way and follows it with two slots per wave. The host must launch
+all of K the same way and follows it with two (variant bit 2: three) slots per wave. The host must launch
 with at least that much. This recomputes the kernels' layouts for every automatic
 plan over a grid of shapes, every M, with and without a workspace and zero points,
 and checks them against the plan, with the plan's other invariants.
@@ -47,7 +47,7 @@ def kernel_lds(fmt, act, N, K, bs, rows, plan, zpp=False):
         sums = nch * rg * h * 16 if (fmt, act) == ("u4", "bf16") else 0
         nsd = 4 if (fmt == "fp8" or (fmt == "u4" and h == 2)) else 2
         slot = 4096 + 256 * nsd + (256 if zpp else 0)
-        return 64 + rows_b + sums + 8 * 2 * slot
+        return 64 + rows_b + sums + 8 * (3 if plan["variant"] & 4 else 2) * slot
     steps = K // (4 * KPC[fmt])
     smax = (steps + kp - 1) // kp
     staged = bool(plan["variant"] & 1)
@@ -91,3 +91,27 @@ def test_every_matrix_plan_holds_the_kernels_lds_layout(fmt, act, N, K, bs, zp, 
                 continue  # the streaming kernels' staged rows are sized by the same formula
             need = kernel_lds(fmt, act, N, K, bs, min(p["rows_per_pass"], rows), p, zpp=zp)
             assert need <= p["lds_bytes"], (fmt, N, K, bs, M, ws, p, need)
+
+
+DEPTH = 29  # QGEMV_FLAG_MFMA_DEPTH_SHIFT
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+def test_dma_ring_depth_rule(cu):
+    """Three DMA-ring slots per wave for the 16-k-per-chunk formats (FP8, 8-bit codes)
+    where the LDS holds them, two for 4-bit and NVFP4 codes; the depth flag forces two
+    (1) or three (2, where they fit). The plan's LDS covers the slots it launches with."""
+    def ring(fmt, act, N, K, bs, M, flags=0, zp=False):
+        p = bqw.select(fmt, act, N, K, bs, M, cu_count=cu, flags=flags, zero_points=0x2000 if zp else None)
+        assert p["family"] == "mfma" and p["variant"] & 2, p
+        assert kernel_lds(fmt, act, N, K, bs, min(p["rows_per_pass"], M), p, zpp=zp) <= p["lds_bytes"] <= LDS
+        return 3 if p["variant"] & 4 else 2
+
+    assert ring("fp8", "f16", 65536, 4096, 128, 4) == 3
+    assert ring("u8", "f16", 65536, 4096, 128, 4, zp=True) == 3
+    assert ring("fp8", "f16", 65536, 4096, 128, 8) == 2  # eight staged rows leave no room for a third
+    assert ring("u4", "bf16", 151936, 4096, 32, 4, zp=True) == 2
+    assert ring("nvfp4", "bf16", 248320, 2048, 16, 4) == 2
+    assert ring("fp8", "f16", 65536, 4096, 128, 4, flags=1 << DEPTH) == 2
+    assert ring("u4", "bf16", 151936, 4096, 32, 4, flags=2 << DEPTH, zp=True) == 3
+    assert ring("u4", "bf16", 151936, 4096, 32, 8, flags=2 << DEPTH, zp=True) == 2  # does not fit: two
