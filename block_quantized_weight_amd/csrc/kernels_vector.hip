@@ -562,7 +562,8 @@ template <int FMT, int ACT, int MT, int CPW, int UNR, int H, int NWG>
 hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     // variant bit 3: the round's metadata windows (8-bit codes); bit 4: metadata as
     // the dwords that hold it (4-bit, 8-bit and NVFP4 codes; FP8 scales are dwords)
-    constexpr bool can_wm = FMT == FMT_U8, can_dw = FMT != FMT_FP8;
+    // (8-bit windows next to eight rows would spill scalar registers: not built)
+    constexpr bool can_wm = FMT == FMT_U8 && MT < 8, can_dw = FMT != FMT_FP8;
     const bool wm = (cfg.variant >> 3) & 1, dw = (cfg.variant >> 4) & 1;
     if ((wm && !can_wm) || (dw && !can_dw) || (wm && dw)) return hipErrorInvalidValue;
     void (*kern)(KArgs) = k_stream1<FMT, ACT, MT, CPW, UNR, H, NWG, 0>;
@@ -585,7 +586,8 @@ hipError_t go_stream1_w(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
 // two columns per wave, 12 for four rows of 4-bit codes with two blocks per chunk.
 template <int FMT, int MT, int CPW, int H>
 constexpr int stream_rows_max_wg() {
-    return CPW == 2 ? 8 : ((FMT == FMT_U4 && H == 2 && MT == 4) ? 12 : 16);
+    return (CPW == 2 || (MT == 8 && (FMT == FMT_U4 || FMT == FMT_NVFP4))) ? 8
+                                                                         : ((FMT == FMT_U4 && H == 2 && MT == 4) ? 12 : 16);
 }
 
 template <int FMT, int ACT, int MT, int CPW, int UNR, int H>
@@ -659,9 +661,9 @@ hipError_t go_stream1(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
     case 2: return go_stream1_c<FMT, ACT, 2>(cfg, a, s);
     case 4: return go_stream1_c<FMT, ACT, 4>(cfg, a, s);
     case 8:
-        // eight rows: FP8 only, one column per wave (the other formats' decode
-        // constants and metadata do not fit next to eight rows' accumulators)
-        if constexpr (FMT == FMT_FP8) return go_stream1_c<FMT, ACT, 8>(cfg, a, s);
+        // eight rows, one column per wave: every format but 4-bit codes on bf16 (whose
+        // per-row activation sums would spill scalar registers next to eight rows)
+        if constexpr (!(FMT == FMT_U4 && ACT == ACT_BF16)) return go_stream1_c<FMT, ACT, 8>(cfg, a, s);
         else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }

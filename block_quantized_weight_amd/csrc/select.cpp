@@ -226,8 +226,17 @@ static bool stream_meta_dword(const qgemv_desc *d) {
 //  - grid: one group per wave when that fits in 24 waves per CU (16 for several
 //    rows, whose waves hold more registers), else a persistent grid of as many.
 static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flags, LaunchCfg *c) {
-    // eight rows per pass for FP8 only (the kernel fits them without spilling there)
-    if (M > 8 || (M > 4 && d->format != QGEMV_FMT_FP8)) return false;
+    // Eight rows per pass: FP8 codes; and 4-bit (on fp16), 8-bit and NVFP4 codes with
+    // K >= 2048, one pass against the classic kernel's two (classic -> one pass at M = 8:
+    // 4-bit 1024 x 2048 6.22 -> 5.54 us, M = 5 5.51 -> 4.65; 4-bit 1024 x 4096 9.11 ->
+    // 6.21; 8-bit 2048 x 2048 6.88 -> 6.13, 8-bit 1024 x 4096 M = 6 8.34 -> 6.57; NVFP4
+    // 2048 x 2048 7.42 -> 6.49; but 4-bit 4096 x 1024 8.48 -> 9.47, whose short columns
+    // spend the pass on eight rows' reductions). Not 4-bit codes on bf16, whose per-row
+    // activation sums leave the scalar registers no room for eight rows.
+    if (M > 8) return false;
+    if (M > 4 && d->format != QGEMV_FMT_FP8 &&
+        (d->K < 2048 || (d->format == QGEMV_FMT_U4 && d->act_dtype == QGEMV_ACT_BF16)))
+        return false;
     const int mt = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));  // rows per pass (one pass)
     const int kpc = k_per_chunk(d->format);
     const int64_t nch = d->K / kpc;
@@ -282,7 +291,10 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     // the most waves per workgroup the kernel fits without spilling (kernel side:
     // stream_rows_max_wg)
     const bool u4_two_blocks = d->format == QGEMV_FMT_U4 && d->block_size == 16;
-    const int max_wg = cpw == 2 ? 8 : ((u4_two_blocks && mt == 4) ? 12 : 16);
+    // (eight rows of 4-bit or NVFP4 codes take 177-184 VGPRs: two waves per SIMD, so at
+    // most 8 per workgroup)
+    const bool wide8 = mt == 8 && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_NVFP4);
+    const int max_wg = (cpw == 2 || wide8) ? 8 : ((u4_two_blocks && mt == 4) ? 12 : 16);
     if (mt > 1 && fn) {
         nwg = 4 * (int)fn < max_wg ? 4 * (int)fn : max_wg;
     } else if (mt == 8) {
@@ -313,7 +325,7 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     c->lds_bytes = (int)lds;
     c->variant = 1 | ((unr & 3) << 1);
     if (!(flags & QGEMV_FLAG_STREAM_META_CHUNK)) {
-        if (stream_meta_window(d, unr)) c->variant |= 8;
+        if (mt < 8 && stream_meta_window(d, unr)) c->variant |= 8;  // (no windows next to eight rows)
         else if (stream_meta_dword(d)) c->variant |= 16;
     }
     return true;

@@ -262,22 +262,25 @@ def test_three_and_four_rows_take_the_matrix_family_where_its_tile_groups_fill_t
 
 
 def test_small_weights_take_the_streaming_family_at_every_m():
-    """Up to N x K = 4 Mi elements with K <= 4096, the streaming family serves every M
-    (from M = 5 the multi-pass kernel, or for FP8 codes up to M = 8 one persistent pass
-    of eight rows), with or without a workspace; past either bound, M >= 5 takes the
-    matrix family, except FP8 at M = 5..8 where the tile groups fill at most half the
-    CUs."""
+    """Up to N x K = 4 Mi elements with K <= 4096, the streaming family serves every M,
+    with or without a workspace: up to M = 8 one persistent pass of eight rows (FP8
+    codes; 4-bit on fp16, 8-bit and NVFP4 codes with K >= 2048), else the multi-pass
+    kernel; past either bound, M >= 5 takes the matrix family, except FP8 at M = 5..8
+    where the tile groups fill at most half the CUs."""
     for fmt, act, N, K, bs in (("u4", "f16", 1024, 2048, 32), ("u4", "f16", 2048, 2048, 32),
                                ("fp8", "f16", 1024, 4096, 128), ("u8", "f16", 2048, 2048, 128),
-                               ("nvfp4", "bf16", 2048, 2048, 16)):
+                               ("nvfp4", "bf16", 2048, 2048, 16), ("u4", "bf16", 1024, 2048, 32),
+                               ("u4", "f16", 4096, 1024, 32), ("u8", "bf16", 1024, 4096, 128)):
+        one_pass = fmt == "fp8" or (K >= 2048 and (fmt, act) != ("u4", "bf16"))
         for M in (5, 8, 12, 16):
             for ws in (False, True):
                 p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=M, with_workspace=ws)
                 assert p["family"] == "stream" and p["kparts"] == 1, (fmt, N, K, M, ws, p)
-                if fmt == "fp8" and M <= 8:
-                    assert p["rows_per_pass"] == 8 and p["passes"] == 1 and p["variant"] & 1, (M, p)
+                if one_pass and M <= 8:
+                    assert p["rows_per_pass"] == 8 and p["passes"] == 1 and p["variant"] & 1, (fmt, M, p)
+                    assert p["waves_per_wg"] <= (8 if fmt in ("u4", "nvfp4") else 16), p
                 else:
-                    assert p["rows_per_pass"] == 4 and p["passes"] == (M + 3) // 4
+                    assert p["rows_per_pass"] == 4 and p["passes"] == (M + 3) // 4, (fmt, K, M, p)
     for fmt, act, N, K, bs in (("u4", "f16", 1536, 4096, 32), ("fp8", "f16", 2048, 4096, 128),
                                ("u4", "f16", 512, 8192, 32), ("fp8", "f16", 512, 8192, 128)):
         for M in (5, 8, 16):

@@ -307,6 +307,27 @@ def test_eight_row_persistent_kernel_matches_the_classic_kernel_bitwise(act, N, 
         assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (nwg, pa)
 
 
+@pytest.mark.parametrize("fmt,act,N,K,bs", [("u4", "f16", 1001, 2080, 32), ("u4", "f16", 777, 4096, 16),
+                                             ("u8", "f16", 999, 2048, 128), ("u8", "bf16", 1234, 4096, 64),
+                                             ("nvfp4", "bf16", 1111, 2048, 16), ("nvfp4", "f16", 999, 3104, 16)])
+@pytest.mark.parametrize("M", [5, 8])
+def test_eight_row_pass_of_other_formats_matches_the_classic_kernel_bitwise(fmt, act, N, K, bs, M):
+    """4-bit (fp16), 8-bit and NVFP4 codes with K >= 2048 at M = 5..8 in one pass of eight
+    rows: each row equals the classic kernel's bits (two passes of four rows) at every
+    workgroup size the kernel takes, and the oracle bound holds."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=35)
+    gu.say(f"[stream-8rows] {fmt}/{act} N={N} K={K} bs={bs} M={M}")
+    Yc, pc = gu.run_gpu(prob, M, flags=FAMILY_FLAG["stream_classic"])
+    assert pc["rows_per_pass"] == 4 and pc["passes"] == 2, pc
+    ok, ratio, _, _ = gu.check_full(prob, M, Yc, strict=False)
+    assert ok, ratio
+    for nwg in ((0, 1, 2) if fmt in ("u4", "nvfp4") else (0, 1, 2, 3, 4)):
+        Ya, pa = gu.run_gpu(prob, M, flags=1 | (nwg << bqw.FLAG_STREAM_NWG_SHIFT))
+        assert pa["variant"] & 1 and pa["rows_per_pass"] == 8 and pa["passes"] == 1, pa
+        assert nwg == 0 or pa["waves_per_wg"] == 4 * nwg, pa
+        assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (nwg, pa)
+
+
 @pytest.mark.parametrize("name,M", [("u4_m8_k2048_n1024", 8), ("fp8_k6144_n5120", 4), ("u8_m1_k4096_n4096", 1)])
 def test_repeated_runs_are_bitwise_equal(name, M):
     prob = synth.workload(name)
