@@ -272,11 +272,20 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     else wpc = mt > 1 ? 16 : 24;
     // 16-wave workgroups (one row, one column per wave) when asked for, or when the
     // column groups fill 8..16 waves per CU: one workgroup per CU then stages the
-    // activation row once for 16 columns instead of once per 4 (measured 7% faster on
-    // 4096 x 4096 8-bit codes); past 16 per CU the 16-wave groups no longer spread
-    // evenly over the CUs and lose.
+    // activation row once for 16 columns instead of once per 4; past 16 per CU the
+    // 16-wave groups no longer spread evenly over the CUs and lose. Not for 8-bit codes:
+    // there four 4-wave workgroups per CU with two chunks per lane per batch are faster
+    // (cold, steady clocks, 16-wave -> 4-wave x 4 with batches of 2: 8-bit 4096 x 4096
+    // 5.50 -> 5.15 us, on bf16 6.37 -> 5.77, 2048 x 4096 4.73 -> 4.44; 4-bit 4096 x 4096
+    // the other way, 4.42 -> 4.72; FP8 and NVFP4 even).
     const bool wide_auto = !fc && !fw && groups >= 8LL * cu_count && groups <= 16LL * cu_count;
-    int nwg = ((flags & QGEMV_FLAG_STREAM_WIDE_WG) || wide_auto) && mt == 1 && cpw == 1 ? 16 : 4;
+    const bool u8_quads = wide_auto && mt == 1 && cpw == 1 && d->format == QGEMV_FMT_U8 &&
+                          !(flags & QGEMV_FLAG_STREAM_WIDE_WG);
+    if (u8_quads) {
+        wpc = 16;
+        if (!fu) unr = 2;
+    }
+    int nwg = ((flags & QGEMV_FLAG_STREAM_WIDE_WG) || (wide_auto && !u8_quads)) && mt == 1 && cpw == 1 ? 16 : 4;
     // Several rows: 4, 8, 12 or 16 waves share one staged copy of the rows. The staged
     // rows bound the workgroups resident per CU (res); when 16-wave workgroups would
     // hold every column group at once, the fewest waves per workgroup that do are

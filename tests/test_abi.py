@@ -448,3 +448,21 @@ def test_streaming_metadata_windows_where_they_fit():
     assert not _sel(**dict(u8, flags=bqw.FLAG_STREAM_META_CHUNK))["variant"] & 8
     assert not _sel()["variant"] & 8                                      # 4-bit lm_head
     assert not _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128)["variant"] & 8
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+def test_one_row_workgroups_where_columns_fill_8_to_16_waves_per_cu(cu):
+    """One row, one column per wave, columns for 8..16 waves per CU: 16-wave workgroups
+    (at most one per CU), except for 8-bit codes, which take four 4-wave workgroups per CU and two
+    chunks per lane per batch; a forced 16-wave flag still gives 16 waves."""
+    for fmt, act, bs in (("u8", "f16", 128), ("u8", "bf16", 128), ("u4", "f16", 32), ("fp8", "f16", 128),
+                         ("nvfp4", "bf16", 16)):
+        N = 12 * cu  # 12 columns per CU
+        p = _sel(fmt=fmt, act=act, N=N, K=4096, block_size=bs, M=1, cu_count=cu)
+        assert p["family"] == "stream" and p["cols_per_wave"] == 1, p
+        if fmt == "u8":
+            assert p["waves_per_wg"] == 4 and p["grid"] == min(4 * cu, (N + 3) // 4) and (p["variant"] >> 1) & 3 == 2, p
+            f = _sel(fmt=fmt, act=act, N=N, K=4096, block_size=bs, M=1, cu_count=cu, flags=bqw.FLAG_STREAM_WIDE_WG)
+            assert f["waves_per_wg"] == 16, f
+        else:
+            assert p["waves_per_wg"] == 16 and p["grid"] == (N + 15) // 16, p
