@@ -113,8 +113,50 @@ static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int slo
     return true;
 }
 
-// Waves that share one 16-column tile's K range. Chosen from N and K only so that
-// the summation order of a row never depends on M. A workgroup holds 8 / ksplit tiles
+// The matrix family's staged activations for `rows` rows over `sm` K steps: a 64-byte
+// zero block, the rows (stride sm x 4 chunks + 8 elements, 2 bytes each, rounded up to
+// 16 bytes) and, for 4-bit codes on bf16, one 16-byte activation-sum entry per chunk,
+// row group and scale block of the chunk.
+static int64_t staged_act_bytes(const qgemv_desc *d, int rows, int64_t sm) {
+    const int64_t la = (int64_t)rows * (sm * 4 * k_per_chunk(d->format) + 8) * 2;
+    const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
+    return 64 + ((la + 15) & ~15LL) + (needs_act_sums(d) ? 4 * sm * ((rows + 3) / 4) * hh * 16 : 0);
+}
+
+// Whether `groups` tile groups of the DMA ring (8 tiles each, no K split) fill enough
+// of the CUs for the ring to win: from 3/4 of them for the formats with 32 k per chunk
+// (4-bit, NVFP4), from 7/8 for those with 16 (FP8, 8-bit), whose slots hold half the
+// arithmetic. Measured on MI355X (ring against the best other plan, cold weights):
+// 4-bit on bf16 24576 x 4096 (192 groups) M = 2 / 4 / 8 15.6 / 15.8 / 20.3 us against
+// 15.9 / 16.6 / 23.5, 28672 x 4096 (224) M = 4 16.2 against 26.0, 32768 x 4096 (256)
+// M = 4 17.2 against 24.6; NVFP4 24576 x 2048 M = 1 / 4 8.5 / 8.8 against 8.9 / 20.4;
+// 4-bit on f16 32768 x 2048 M = 2 10.7 against 17.7; FP8 28672 x 4096 (224) M = 3 /
+// 4 / 8 28.1 / 28.2 / 28.5 against 30.6 / 30.8 / 40.3, 8-bit 28672 x 4096 M = 4 / 8
+// 27.8 / 28.4 against 31.0 / 45.2; with more groups, where the earlier rule took the
+// streaming kernel or the register ring: 4-bit on f16 49152 x 2048 M = 2 16.3 against
+// 25.2, FP8 49152 x 1024 M = 4 12.8 against 23.6, 8-bit 32768 x 2048 M = 4 14.8 against
+// 18.1, 4-bit on bf16 32768 x 16384 M = 2 62.6 against 98.4. But FP8 24576 x 4096 (192
+// groups) M = 4 26.9 against 23.9, and 4-bit on bf16 16384 x 4096 (128) M = 2 / 4
+// 19.3 / 20.0 against 12.2 / 13.7.
+static bool ring_groups_fill(const qgemv_desc *d, int64_t groups, int cu_count) {
+    return k_per_chunk(d->format) == 32 ? 4 * groups >= 3LL * cu_count : 8 * groups >= 7LL * cu_count;
+}
+
+// Whether the DMA ring takes this weight at every M up to 8: its tile groups fill the
+// CUs (above) and eight staged rows fit in LDS next to two slots per wave. Such a
+// weight takes no K split in the matrix family (the ring has none, and the split may
+// not depend on M).
+static bool ring_band(const qgemv_desc *d, int cu_count) {
+    const int64_t groups = ((d->N + 15) / 16 + 7) / 8;
+    if (!ring_groups_fill(d, groups, cu_count) || d->K % (4 * k_per_chunk(d->format))) return false;
+    const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
+    int32_t lds = 0;
+    return dma_ring_fits(d, staged_act_bytes(d, 8, d->K / (4 * k_per_chunk(d->format))), zpp, 2, &lds);
+}
+
+// Waves that share one 16-column tile's K range. Chosen from the weight (format, N, K,
+// block size, zero points) and the CU count only, so that the summation order of a
+// row never depends on M. A workgroup holds 8 / ksplit tiles
 // of ksplit waves, so the split sets both the number of workgroups and the K steps
 // each wave walks. While the workgroups do not fill the CUs, the split taken is the
 // one with the least work on the busiest CU, (workgroups per CU, rounded up) x (K
@@ -128,7 +170,12 @@ static bool dma_ring_fits(const qgemv_desc *d, int64_t abytes, bool zpp, int slo
 // 15.4 -> 14.4 (4 -> 8); a finer split than this rule's measured slower on FP8
 // 5120 x 6144 (16.7 us at 4, 19.3 at 8), NVFP4 and 4-bit 4096 x 4096 (10.1 / 12.5 us
 // at 4, 12.9 / 13.8 at 8) and 4-bit 12288 x 4096 (17.3 us at 2, 19.1 at 4). At least
-// two K steps per wave, and at most 8, the waves of one workgroup.
+// two K steps per wave, and at most 8, the waves of one workgroup. No split where the
+// DMA ring takes the weight at every M up to 8: from 9 rows the register ring then runs
+// unsplit, which measured about as fast or faster there (4-bit on bf16 24576 x 4096
+// M = 12 30.4 us unsplit against 29.3 at 4, M = 16 33.4 against 96.7 with unstaged
+// rows; FP8 28672 x 4096 M = 12 42.7 against 52.0 at 8; 8-bit 28672 x 4096 M = 12 / 16
+// 39.0 / 41.4 against 56.0 / 131.0).
 static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     const uint32_t forced = (flags & QGEMV_FLAG_KSPLIT_MASK) >> QGEMV_FLAG_KSPLIT_SHIFT;
     const int64_t tiles = (d->N + 15) / 16;
@@ -136,7 +183,7 @@ static int mfma_ksplit(const qgemv_desc *d, int cu_count, uint32_t flags) {
     int ks = 1;
     if (forced) {
         ks = (int)forced;
-    } else {
+    } else if (!ring_band(d, cu_count)) {
         auto groups = [&](int k) { return (tiles + 8 / k - 1) / (8 / k); };
         auto cost = [&](int k) { return (groups(k) + cu_count - 1) / cu_count * ((steps + k - 1) / k); };
         for (int k = 2; k <= 8 && 2 * k <= steps && groups(ks) < cu_count; k *= 2) {
@@ -345,7 +392,9 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 //    and FP8 codes, and for 4-bit codes while the weight is small enough (under
 //    64 MB) that the call is latency-bound rather than bandwidth-bound. Wide 4-bit
 //    weights take the matrix family's DMA ring from M = 2 (4-bit lm_head, M = 2:
-//    90 us against 101 us). At M = 3..4, where the matrix family's tile groups fill
+//    90 us against 101 us), and so do all weights whose ring tile groups fill the
+//    CUs (ring_band), but 1-byte codes at M = 2, where two rows leave the streaming
+//    kernel ahead (FP8 28672 x 4096: 22.1 against 28.0 us; 8-bit 24.0 against 27.4). At M = 3..4, where the matrix family's tile groups fill
 //    the CUs, it wins for 4-bit codes and, from 64 MB of codes, for 1-byte ones
 //    (streaming -> matrix at M = 4: 4-bit 16384 x 4096 22.9 -> 15.9 us, 4-bit
 //    8192 x 4096 12.5 -> 10.9 (M = 3: 11.2 -> 10.3), NVFP4 8192 x 4096 12.7 -> 9.1,
@@ -372,12 +421,14 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
 static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_count, uint32_t flags) {
     if (!stream_ok || M < 2) return false;
     if (M > 4) return d->K <= 4096 && (int64_t)d->N * d->K <= 4LL * 1024 * 1024;
+    const bool bytes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
+    // the weights the DMA ring takes at every M up to 8, but for 1-byte codes at two rows
+    if (ring_band(d, cu_count) && !(flags & QGEMV_FLAG_RING_OFF) && !(bytes && M == 2)) return false;
     if (M >= 3) {
         // four rows per pass: the matrix family wins once its tile groups fill the CUs,
         // for 1-byte codes only from 64 MB of codes on
         const int ks = mfma_ksplit(d, cu_count, flags);
         const int64_t groups = ((d->N + 15) / 16 + 8 / ks - 1) / (8 / ks);
-        const bool bytes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
         if (groups >= cu_count && (!bytes || (int64_t)d->N * d->K >= 64LL * 1024 * 1024)) return false;
     }
     const int kpc = k_per_chunk(d->format);
@@ -426,13 +477,16 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
     } else if (mfma_ok && M >= 2 && !stream_rows_win(d, M, stream_ok, cu_count, flags)) {
         family = QGEMV_FAMILY_MFMA;
     } else if (mfma_ok && M == 1 && d->format == QGEMV_FMT_NVFP4 && !(flags & QGEMV_FLAG_STREAM_CLASSIC)) {
-        // NVFP4 at one row: the matrix family where its plan is the DMA ring (wide N),
-        // else the streaming kernel. Measured (M = 1, one session): NVFP4 248320 x 2048
-        // 68.8 -> 53.5 us, 65536 x 2048 19.9 -> 16.2; for 4-bit, 8-bit and FP8 codes the
-        // streaming kernel stays ahead (4-bit 151936 x 4096 64.4 against 74.5 us, 8-bit
+        // NVFP4 at one row: the matrix family where its plan is the DMA ring and its tile
+        // groups outnumber the CUs, else the streaming kernel. Measured (M = 1, one
+        // session): NVFP4 248320 x 2048 68.8 -> 53.5 us, 65536 x 2048 19.9 -> 16.2; with
+        // fewer groups the streaming kernel holds on longer rows (24576 x 4096: 11.3
+        // against 13.0 us on the ring; 28672 x 6144: 17.8 against 19.6); for 4-bit, 8-bit
+        // and FP8 codes it stays ahead (4-bit 151936 x 4096 64.4 against 74.5 us, 8-bit
         // 151936 x 2048 61.4 against 65.5, FP8 65536 x 4096 44.1 against 61.7).
         LaunchCfg ring;
-        const bool takes_ring = select_plan(d, 1, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_MFMA, with_ws, &ring) ==
+        const bool takes_ring = ((d->N + 15) / 16 + 7) / 8 > cu_count &&
+                                select_plan(d, 1, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_MFMA, with_ws, &ring) ==
                                     QGEMV_OK &&
                                 ring.family == QGEMV_FAMILY_MFMA && (ring.variant & 2);
         if (takes_ring) {
@@ -470,13 +524,9 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         // then, and else follows them (FP8 8192 x 4096 at M = 16: 131 KB of staged rows
         // and 32 KB of reduction area fit only overlaid); then, with K parts, the
         // 16-byte last-workgroup flag (lds).
-        const bool zp_fmt = needs_act_sums(d);
-        const int hh = (d->format == QGEMV_FMT_U4 && d->block_size == 16) ? 2 : 1;
         struct Staged { int64_t abytes, lds; };
         auto staged = [&](int kpv) {
-            const int64_t sm = (steps + kpv - 1) / kpv;
-            const int64_t la = (int64_t)M * (sm * 4 * k_per_chunk(d->format) + 8) * 2;
-            const int64_t ab = 64 + ((la + 15) & ~15LL) + (zp_fmt ? 4 * sm * rg * hh * 16 : 0);
+            const int64_t ab = staged_act_bytes(d, M, (steps + kpv - 1) / kpv);
             const int64_t fb = kpv > 1 ? 16 : 0;
             const int64_t ovl = (ab > lds_red ? ab : lds_red) + fb;
             int64_t pc = kLdsBytes / ovl;
@@ -503,19 +553,27 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         if (with_ws && kp == 1 && !(flags & QGEMV_FLAG_KPARTS_MASK) && rows_too_big && steps >= 4LL * c.ksplit &&
             2LL * QGEMV_MAX_M * d->N < (1LL << 31))
             kp = 2;
-        // Otherwise (no workspace, or a forced single part), the same case with more
-        // than 8 rows runs as passes of 8 rows, one launch each on the caller's stream,
-        // when 8 rows stage: every row's arithmetic is that of the single launch (the
-        // K split does not depend on M, and staged and unstaged activations give the
-        // same bits), the weight is read once per pass. Measured on MI355X, one launch
-        // -> two passes: FP8 5120 x 6144 M = 16 49.2 -> 32.5 us; FP8 2048 x 8192 M = 16
-        // 36.9 -> 27.3, M = 12 28.9 -> 24.5; 4-bit 16384 x 8192 M = 16 122.3 -> 65.0,
-        // M = 12 95.3 -> 60.1.
-        if (kp == 1 && rows_too_big && M > 8 && !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON))) {
+        // Otherwise (no workspace, or a forced single part), more than 8 rows whose
+        // activations do not stage at this M run as passes of 8 rows, one launch each on
+        // the caller's stream, when 8 rows stage (or take the DMA ring): every row's
+        // arithmetic is that of the single launch (the K split does not depend on M, and
+        // staged and unstaged activations give the same bits), the weight is read once
+        // per pass. Unstaged rows travel with the codes in the register ring, 16 rows of
+        // activations per 16 columns of codes, which costs more than a second read of
+        // the weight. Measured on MI355X, one launch -> passes: FP8 5120 x 6144 M = 16
+        // 49.2 -> 32.5 us; FP8 2048 x 8192 M = 16 36.9 -> 27.3, M = 12 28.9 -> 24.5;
+        // 4-bit 16384 x 8192 M = 16 122.3 -> 65.0, M = 12 95.3 -> 60.1; 4-bit
+        // 24576 x 8192 M = 9 112.6 -> 67.8, M = 16 184.8 -> 77.2; 4-bit 5120 x 6144 M = 16
+        // 49.3 -> 29.9; 8-bit 4096 x 8192 M = 16 37.7 -> 30.7, M = 12 30.1 -> 26.9;
+        // FP8 24576 x 4096 M = 16 97.0 -> 51.0; 4-bit 151936 x 8192 M = 16 1164.8 ->
+        // 478.1; FP8 65536 x 8192 M = 16 475.8 -> 289.5, M = 10 309.6 -> 282.1.
+        if (kp == 1 && staged(1).lds > kLdsBytes && M > 8 &&
+            !(flags & (QGEMV_FLAG_STAGE_A_OFF | QGEMV_FLAG_STAGE_A_ON))) {
             LaunchCfg half;
-            // (the matrix family's plan for 8 rows, whichever family 8 rows alone would take)
+            // (the matrix family's plan for 8 rows, whichever family 8 rows alone would
+            // take: staged rows in the register ring, or the DMA ring)
             if (select_plan(d, 8, cu_count, fast_ok, extra_flags | QGEMV_FAMILY_MFMA, with_ws, &half) == QGEMV_OK &&
-                half.family == QGEMV_FAMILY_MFMA && (half.variant & 1) && half.kparts == 1 && !(half.variant & 2)) {
+                half.family == QGEMV_FAMILY_MFMA && (half.variant & 3) && half.kparts == 1) {
                 half.passes = (M + 7) / 8;
                 *out = half;
                 return QGEMV_OK;
@@ -542,7 +600,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         int32_t lds3 = 0;
         const bool three = (rdep == 2 || (rdep == 0 && k_per_chunk(d->format) == 16)) &&
                            dma_ring_fits(d, abytes16, zpp, 3, &lds3);
-        bool ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits && groups > cu_count;
+        bool ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits && ring_groups_fill(d, groups, cu_count);
         if (flags & QGEMV_FLAG_RING_ON) ring = c.ksplit == 1 && kp == 1 && rg <= 2 && ring_fits;
         if (flags & QGEMV_FLAG_RING_OFF) ring = false;
         if (ring) {

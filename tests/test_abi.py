@@ -353,9 +353,9 @@ def test_two_k_parts_where_the_unsplit_rows_do_not_fit_in_lds():
 
 
 def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
-    """Without K parts, the case where 2 parts would be taken with a workspace runs
-    more than 8 rows as passes of 8 (one launch each), each staging its rows; a forced
-    staging choice keeps one launch."""
+    """Without K parts, more than 8 rows whose activations do not stage run as passes
+    of 8 (one launch each), each staging its rows or taking the DMA ring, whatever the
+    tile groups; a forced staging choice keeps one launch."""
     kw = dict(fmt="fp8", act="f16", N=2048, K=8192, block_size=128)
     for M, passes in ((8, 1), (9, 1), (12, 2), (13, 2), (16, 2)):
         p = _sel(**kw, M=M)
@@ -376,9 +376,19 @@ def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
     # FP8 5120 x 6144 at M = 16 (160 tile groups, 24 K steps per wave): passes
     p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=16)
     assert p["passes"] == 2 and p["grid"] == 160
-    # 8-bit 4096 x 8192 (16 K steps per wave): one launch, unstaged
-    p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16)
-    assert p["passes"] == 1 and not (p["variant"] & 1)
+    # 8-bit 4096 x 8192 (16 K steps per wave; 2 K parts lose here): passes with or
+    # without a workspace
+    for ws in (False, True):
+        p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=ws)
+        assert p["passes"] == 2 and p["kparts"] == 1 and p["variant"] & 1, p
+    # the same at any number of tile groups: FP8 65536 x 8192 (512 groups) from M = 10
+    kw8 = dict(fmt="fp8", act="f16", N=65536, K=8192, block_size=128)
+    assert [_sel(**kw8, M=M)["passes"] for M in (9, 10, 16)] == [1, 2, 2]
+    # where the 8-row plan is the DMA ring, the passes are ring launches: 4-bit on f16
+    # 28672 x 5120 (224 tile groups) at M = 16
+    kwr = dict(fmt="u4", act="f16", N=28672, K=5120, block_size=32)
+    p = _sel(**kwr, M=16)
+    assert p["passes"] == 2 and p["variant"] & 2 and p == _sel(**kwr, M=8) | {"passes": 2}, p
     # 4-bit 2048 x 16384: 8 rows do not fit either: one unstaged matrix launch (128 tile
     # groups: the streaming fallback is for a quarter of the CUs or fewer)
     kw = dict(fmt="u4", act="bf16", N=2048, K=16384, block_size=32)
@@ -466,3 +476,39 @@ def test_one_row_workgroups_where_columns_fill_8_to_16_waves_per_cu(cu):
             assert f["waves_per_wg"] == 16, f
         else:
             assert p["waves_per_wg"] == 16 and p["grid"] == (N + 15) // 16, p
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+def test_dma_ring_band(cu):
+    """The DMA ring takes a weight at every M up to 8 once its tile groups (8 tiles of
+    16 columns, no K split) reach 3/4 of the CUs for 4-bit and NVFP4 codes, 7/8 for FP8
+    and 8-bit codes, where eight staged rows fit next to its slots; such a weight takes
+    no K split at any M (the split never depends on M), and 1-byte codes keep the
+    streaming kernel at M = 2. Below the band the K split and the other families stay."""
+    def shape(fmt, groups, K):
+        return dict(fmt=fmt, act="f16", N=groups * 128, K=K, block_size=32 if fmt in ("u4",) else
+                    (16 if fmt == "nvfp4" else 128), cu_count=cu)
+
+    for fmt, frac in (("u4", (3, 4)), ("nvfp4", (3, 4)), ("fp8", (7, 8)), ("u8", (7, 8))):
+        g_in = (cu * frac[0] + frac[1] - 1) // frac[1]  # the fewest groups in the band
+        kw = shape(fmt, g_in, 2048)
+        for M in range(2, 9):
+            p = _sel(**kw, M=M)
+            if fmt in ("fp8", "u8") and M == 2:
+                assert p["family"] == "stream", (fmt, cu, p)
+            else:
+                assert p["family"] == "mfma" and p["variant"] & 2 and p["ksplit"] == 1, (fmt, cu, M, p)
+                assert p["grid"] == min(g_in, cu)
+        for M in range(9, 17):
+            p = _sel(**kw, M=M)
+            assert p["family"] == "mfma" and p["ksplit"] == 1 and not p["variant"] & 2, (fmt, cu, M, p)
+        # one group fewer: no ring at M = 4 (a K split where it pays, or the streaming kernel)
+        p = _sel(**shape(fmt, g_in - 1, 2048), M=4)
+        assert not (p["family"] == "mfma" and p["variant"] & 2), (fmt, cu, p)
+    # a K range whose eight rows do not fit next to the ring: the weight keeps its K split
+    kw = dict(fmt="u4", act="bf16", N=24576 * cu // 256, K=8192, block_size=32, cu_count=cu)
+    assert all(_sel(**kw, M=M)["ksplit"] > 1 for M in (4, 8, 16))
+    # NVFP4 at one row: the ring only where its groups outnumber the CUs
+    kw = dict(fmt="nvfp4", act="bf16", K=2048, block_size=16, cu_count=cu)
+    assert _sel(**kw, N=cu * 128, M=1)["family"] == "stream"
+    assert _sel(**kw, N=(cu + 1) * 128, M=1)["variant"] & 2

@@ -133,6 +133,57 @@ def test_three_slot_dma_ring(fmt, act, M):
     assert np.array_equal(Y3.view(np.int64), Y2.view(np.int64))
 
 
+@pytest.mark.parametrize("fmt,act,N,K,bs,variant", [
+    ("u4", "f16", 28672, 5120, 32, 2),     # 8 rows take the DMA ring
+    ("fp8", "f16", 24576, 4096, 128, 1),   # 8 rows stage in the register ring, K split 4
+    ("u8", "bf16", 4096, 8192, 128, 1),    # K split 8, 256 tile groups
+])
+def test_row_passes_where_the_rows_do_not_stage(fmt, act, N, K, bs, variant):
+    """More than 8 rows whose activations do not fit in LDS run as passes of 8 rows, one
+    launch each (M = 16 here; M = 9 stages its rows in one launch on the first two):
+    sampled outputs against the oracle at M = 9 and 16, and every row's bits equal to
+    those of the 8-row launch (rows 0..7) and across M (row 8)."""
+    prob = synth.make_problem(fmt, act, N, K, bs, 16, seed=93)
+    gu.say(f"[parity] row passes {fmt}/{act} {N}x{K}")
+    Y8, p8 = gu.run_gpu(prob, 8)
+    assert p8["family"] == "mfma" and p8["variant"] & 3 == variant, p8
+    Ys = {}
+    for M in (9, 16):
+        Ys[M], p = gu.run_gpu(prob, M)
+        assert p["family"] == "mfma" and p["ksplit"] == p8["ksplit"], (M, p)
+        if M == 16:
+            assert p["passes"] == 2 and p["rows_per_pass"] == 8 and p["variant"] == p8["variant"], (M, p)
+        ok, ratio = gu.check_points(prob, M, Ys[M], count=4000, seed=M)
+        gu.say(f"   M={M} plan={p} max err/tol={ratio:.3e}")
+        assert ok, (M, ratio)
+        assert np.array_equal(Ys[M][:8].view(np.int64), Y8.view(np.int64)), M
+    assert np.array_equal(Ys[16][8].view(np.int64), Ys[9][8].view(np.int64))
+
+
+@pytest.mark.parametrize("fmt,act,N,bs", [("u4", "bf16", 24576, 32), ("fp8", "f16", 28672, 128)])
+def test_dma_ring_band_takes_no_k_split_at_any_m(fmt, act, N, bs):
+    """A weight whose ring tile groups fill 3/4 (4-bit) or 7/8 (FP8) of the CUs: the DMA
+    ring from M = 2 or 3 up to 8, the unsplit register ring above, one summation order
+    throughout. Sampled outputs against the oracle and a row's bits across M."""
+    import torch
+
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if ((N + 15) // 16 + 7) // 8 * (4 if fmt == "u4" else 8) < (3 if fmt == "u4" else 7) * cu:
+        pytest.skip(f"{N} columns are below the band on {cu} CUs")
+    prob = synth.make_problem(fmt, act, N, 4096, bs, 16, seed=95)
+    gu.say(f"[parity] ring band {fmt}/{act} {N}x4096")
+    rows = {}
+    for M in (4, 8, 12, 16):
+        Y, p = gu.run_gpu(prob, M)
+        assert p["family"] == "mfma" and p["ksplit"] == 1 and bool(p["variant"] & 2) == (M <= 8), (M, p)
+        ok, ratio = gu.check_points(prob, M, Y, count=3000, seed=M)
+        gu.say(f"   M={M} plan={p} max err/tol={ratio:.3e}")
+        assert ok, (M, ratio)
+        rows[M] = Y[:4]
+    for M in (8, 12, 16):
+        assert np.array_equal(rows[M].view(np.int64), rows[4].view(np.int64)), M
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "u4"])
 @pytest.mark.parametrize("M,family", [(5, "mfma"), (6, "stream"), (16, "stream")])
 def test_tall_narrow_shapes_without_workspace(fmt, M, family):
