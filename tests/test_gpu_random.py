@@ -79,3 +79,37 @@ def test_random_case_against_the_oracle(i, fmt, act, bs, N, K, M, flags, ws):
         assert got["ws_zero"], got
     ok, ratio, _, _ = gu.check_full(prob, M, Y, strict=False)
     assert ok, (i, ratio, got)
+
+
+def draw_wide_cases(n, seed=2025):
+    """Wide weights (N from 20000 to 70000, ragged), where the dispatcher's choices turn
+    on how many tile groups fill the CUs: the DMA ring and its band, the K split, row
+    passes, the streaming kernel at one or two rows. The automatic plan, K a whole number
+    of four chunks (so the matrix family can take every case) up to 4096, M up to 16."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        fmt, bs = FORMATS[rng.integers(len(FORMATS))]
+        act = "bf16" if rng.random() < 0.5 else "f16"
+        N = int(rng.integers(20000, 70001))
+        unit = int(np.lcm(4 * KPC[fmt], bs))
+        K = unit * int(rng.integers(1, 4096 // unit + 1))
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 9, 12, 16]))
+        ws = bool(rng.random() < 0.5)
+        cases.append((i, fmt, act, bs, N, K, M, ws))
+    return cases
+
+
+@pytest.mark.parametrize("i,fmt,act,bs,N,K,M,ws", draw_wide_cases(40))
+def test_random_wide_case_against_the_oracle(i, fmt, act, bs, N, K, M, ws):
+    """3000 sampled outputs and the first and last 40 columns of every row, against the
+    oracle (plus a bf16 output's final rounding, as for the cases above)."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=5000 + i)
+    gu.say(f"[random wide {i}] {fmt}/{act} bs={bs} N={N} K={K} M={M} ws={ws}")
+    Y, got = gu.run_gpu(prob, M, ws=ws)
+    if ws:
+        assert got["ws_zero"], got
+    ms, ns = gu.sample_points(M, N, 3000, i)
+    yr, s = gu.oracle.gemv_points(prob, ms, ns, M=M)
+    ok, ratio = gu.oracle.within_tolerance(Y[ms, ns], yr, s, out_dtype=prob.act)
+    assert ok, (i, ratio, got)
