@@ -224,6 +224,34 @@ static int mfma_kparts(const qgemv_desc *d, int cu_count, uint32_t flags, int ks
     return kp;
 }
 
+// Long rows with a workspace: where the unsplit tile groups fill between 1/8 of the CUs
+// and all of them, and neither eight rows nor this M's rows of the whole K fit in LDS,
+// the matrix family splits K across workgroups only (no split inside one; K parts,
+// below). An in-workgroup split stages the activations of the whole K range per
+// 16 x (8 / ksplit) columns, and at these lengths the rows do not stage at all; K parts
+// stage only their part. Like the K parts, this choice depends on M: the K split then
+// does too, so rows of qgemv_run_ws's automatic plans are bit-identical across M only
+// where no such rule applies (a forced split or part count turns it off). Measured on
+// MI355X with a workspace (µs, automatic before -> after): 4-bit 8192 x 28672 M = 8 / 16
+// 124.2 / 224.2 -> 60.5 / 83.9 (M = 4 55.9 -> 56.4); FP8 8192 x 28672 M = 4 / 8 / 16
+// 73.3 / 129.7 / 226.7 -> 69.3 / 79.7 / 99.9; 4-bit 4096 x 14336 M = 8 / 16 32.4 /
+// 58.5 -> 22.1 / 27.1; FP8 4096 x 14336 36.3 / 73.9 -> 25.7 / 28.6; 4-bit 5120 x 16384
+// M = 16 134.6 -> 47.8; NVFP4 8192 x 28672 M = 4 / 8 / 16 46.1 / 121.9 / 220.3 -> 38.4
+// / 43.3 / 71.3; K = 16384, M = 8 / 16: 4-bit 16384 x 16384 74.0 / 255.6 -> 69.0 /
+// 92.7, FP8 4096 x 16384 38.7 / 83.4 -> 34.7 / 39.8, NVFP4 24576 x 16384 181.7 / 355.8
+// -> 96.6 / 121.5; but 8-bit 8192 x 16384 M = 8 69.1 -> 73.3 (M = 16 142.5 -> 78.7),
+// 8-bit 28672 x 16384 M = 5 183.7 -> 222.7 (M = 8 / 16 249.7 / 456.8 -> 225.1 / 257.2).
+// Where the rows stage, the in-workgroup split stays ahead (4-bit 5120 x 16384 M = 4:
+// 24.0 against 38.8 us with 8 parts; 8-bit 8192 x 16384 M = 4 40.7 against 71.7).
+static bool long_rows(const qgemv_desc *d, int M, int cu_count, uint32_t flags, bool with_ws) {
+    if (!with_ws || (flags & (QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_KPARTS_MASK))) return false;
+    if (d->K % (4 * k_per_chunk(d->format))) return false;
+    const int64_t groups = ((d->N + 15) / 16 + 7) / 8;
+    if (groups >= cu_count || groups * 8 < cu_count) return false;
+    const int64_t steps = d->K / (4 * k_per_chunk(d->format));
+    return staged_act_bytes(d, M < 8 ? M : 8, steps) > kLdsBytes;
+}
+
 // Whether the persistent streaming kernel takes a round's block metadata as one window
 // dword per lane per column (variant bit 3) with unr chunks per lane: 8-bit codes
 // only, where the round's scale and zero-point windows are whole dwords within 64 of
@@ -290,8 +318,13 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     const int64_t nch64 = (nch + 63) / 64 * 64;
     const int nd = kpc == 32 ? 16 : 8;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
+    // The staged rows, at most 64 KB below eight rows (two 4-wave workgroups per CU at
+    // the most). Past it the classic kernel, which re-reads the activations from L2 per
+    // column. One row of 28672 (57-61 KB) measured on MI355X with the 48 KB bound of
+    // before -> 64 KB (classic -> persistent): 4-bit 8192 x 28672 35.4 -> 24.6 us, FP8
+    // 53.1 -> 38.6, NVFP4 36.6 -> 23.5, 8-bit 4096 x 28672 34.6 -> 22.2.
     const int64_t lds = mt * (nch64 * nd * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0));
-    if (lds > (mt == 8 ? kLdsBytes : (mt > 1 ? 64 : 48) * 1024)) return false;
+    if (lds > (mt == 8 ? kLdsBytes : 64 * 1024)) return false;
     const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
     int unr = 0;
     const uint32_t fu = (flags & QGEMV_FLAG_STREAM_UNR_MASK) >> QGEMV_FLAG_STREAM_UNR_SHIFT;
@@ -507,7 +540,8 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         c.rows_per_pass = 4 * rg;
         c.passes = 1;
         c.cols_per_wave = 16;
-        c.ksplit = mfma_ksplit(d, cu_count, flags);
+        const bool lrows = long_rows(d, M, cu_count, flags, with_ws);
+        c.ksplit = lrows ? 1 : mfma_ksplit(d, cu_count, flags);
         // a workgroup holds 8 / ksplit tiles of ksplit waves each
         const int nw = 8;
         c.waves_per_wg = nw;
@@ -535,6 +569,14 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
             return Staged{ab, overlay ? ovl : ab + lds_red + fb};
         };
         int kp = with_ws ? mfma_kparts(d, cu_count, flags, c.ksplit, groups) : 1;
+        if (lrows) {
+            // the fewest parts that give every CU a workgroup, then more (up to 8) until
+            // this M's rows stage
+            kp = 2;
+            while (kp < 8 && groups * kp < cu_count) kp *= 2;
+            while (kp < 8 && staged(kp).lds > kLdsBytes) kp *= 2;
+            while (kp > 1 && (steps < 2LL * kp || (int64_t)kp * QGEMV_MAX_M * d->N >= (1LL << 31))) kp /= 2;
+        }
         // With a workspace, where the unsplit plan's activations do not fit in LDS at
         // this M, 2 parts: twice the workgroups, each staging half the K range where that
         // fits. The one choice of the K parts that depends on M. Taken where the tile

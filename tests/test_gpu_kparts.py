@@ -68,6 +68,29 @@ def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K,
     assert np.array_equal(Y.view(np.int64), Yf.view(np.int64))
 
 
+@pytest.mark.parametrize("fmt,act,N,K,bs,M,kp", [("u4", "bf16", 4096, 14336, 32, 8, 8),
+                                                 ("u4", "bf16", 4096, 14336, 32, 16, 8),
+                                                 ("fp8", "f16", 8192, 28672, 128, 4, 4),
+                                                 ("nvfp4", "bf16", 8192, 28672, 16, 16, 8)])
+def test_long_rows_take_k_parts_without_an_in_workgroup_split(fmt, act, N, K, bs, M, kp):
+    """Long rows that do not stage at this M, with 32 to 64 unsplit tile groups: no K
+    split inside a workgroup, parts enough to fill the CUs and stage the rows. Sampled
+    outputs against the oracle, the workspace left zero, and bit for bit the run with
+    the same split and part count forced."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=27)
+    gu.say(f"[kparts] long rows {fmt} {N}x{K} M={M}")
+    Y, plan = gu.run_gpu(prob, M, ws=True)
+    gu.say(f"   plan={plan}")
+    assert plan["family"] == "mfma" and plan["ksplit"] == 1 and plan["kparts"] == kp and plan["variant"] & 1, plan
+    assert plan["ws_zero"]
+    ok, ratio = gu.check_points(prob, M, Y, count=4000, seed=M)
+    gu.say(f"   max err/tol={ratio:.3e}")
+    assert ok, ratio
+    Yf, pf = gu.run_gpu(prob, M, flags=2 | (1 << 8) | kp_flags(kp), ws=True)
+    assert pf["kparts"] == kp and pf["ksplit"] == 1
+    assert np.array_equal(Y.view(np.int64), Yf.view(np.int64))
+
+
 def test_more_than_sixteen_rows_share_the_workspace_chunk_by_chunk():
     """M = 20 with K parts (FP8 1024 x 16384, 4 parts): chunks of 16 and 4 rows run
     through the same workspace in turn, which ends all zero; outputs against the
