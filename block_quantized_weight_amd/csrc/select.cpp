@@ -143,15 +143,25 @@ static bool ring_groups_fill(const qgemv_desc *d, int64_t groups, int cu_count) 
 }
 
 // Whether the DMA ring takes this weight at every M up to 8: its tile groups fill the
-// CUs (above) and eight staged rows fit in LDS next to two slots per wave. Such a
-// weight takes no K split in the matrix family (the ring has none, and the split may
-// not depend on M).
+// CUs (above) and eight staged rows fit in LDS next to two slots per wave; or, for
+// 4-bit and NVFP4 codes whose tile groups reach 7/8 of the CUs, at every M up to 4,
+// where four staged rows fit next to them. Such a weight takes no K split in the
+// matrix family (the ring has none, and the split may not depend on M), and the
+// register ring takes the rows the ring does not at no loss there (µs, K split 8 ->
+// unsplit, 28672 x 8192, ring at M <= 4: 4-bit on bf16 M = 2 / 4 / 8 / 16 38.6 / 39.4
+// / 56.0 / 110.6 -> 30.7 / 31.8 / 56.3 / 103.2; NVFP4 33.8 / 35.3 / 51.0 / 100.5 ->
+// 27.4 / 28.3 / 41.7 / 76.0), but not with fewer groups (4-bit 24576 x 8192, 192
+// groups, M = 8: 39.9 us at a split of 4, 54.9 unsplit) nor for 1-byte codes (FP8
+// 28672 x 8192 M = 8: 57.3 at 8, 73.3 unsplit).
 static bool ring_band(const qgemv_desc *d, int cu_count) {
     const int64_t groups = ((d->N + 15) / 16 + 7) / 8;
     if (!ring_groups_fill(d, groups, cu_count) || d->K % (4 * k_per_chunk(d->format))) return false;
     const bool zpp = d->zero_points && (d->format == QGEMV_FMT_U4 || d->format == QGEMV_FMT_U8);
+    const int64_t steps = d->K / (4 * k_per_chunk(d->format));
     int32_t lds = 0;
-    return dma_ring_fits(d, staged_act_bytes(d, 8, d->K / (4 * k_per_chunk(d->format))), zpp, 2, &lds);
+    if (dma_ring_fits(d, staged_act_bytes(d, 8, steps), zpp, 2, &lds)) return true;
+    return k_per_chunk(d->format) == 32 && 8 * groups >= 7LL * cu_count &&
+           dma_ring_fits(d, staged_act_bytes(d, 4, steps), zpp, 2, &lds);
 }
 
 // Waves that share one 16-column tile's K range. Chosen from the weight (format, N, K,
@@ -455,7 +465,7 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_c
     if (!stream_ok || M < 2) return false;
     if (M > 4) return d->K <= 4096 && (int64_t)d->N * d->K <= 4LL * 1024 * 1024;
     const bool bytes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
-    // the weights the DMA ring takes at every M up to 8, but for 1-byte codes at two rows
+    // the weights in the DMA ring's band (ring_band), but for 1-byte codes at two rows
     if (ring_band(d, cu_count) && !(flags & QGEMV_FLAG_RING_OFF) && !(bytes && M == 2)) return false;
     if (M >= 3) {
         // four rows per pass: the matrix family wins once its tile groups fill the CUs,

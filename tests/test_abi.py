@@ -506,7 +506,16 @@ def test_dma_ring_band(cu):
         p = _sel(**shape(fmt, g_in - 1, 2048), M=4)
         assert not (p["family"] == "mfma" and p["variant"] & 2), (fmt, cu, p)
     # a K range whose eight rows do not fit next to the ring: the weight keeps its K split
+    # at 3/4 of the CUs; from 7/8 of them 4-bit codes take the ring up to four rows and
+    # no K split at any M, 1-byte codes keep theirs
     kw = dict(fmt="u4", act="bf16", N=24576 * cu // 256, K=8192, block_size=32, cu_count=cu)
+    assert all(_sel(**kw, M=M)["ksplit"] > 1 for M in (4, 8, 16))
+    g78 = (7 * cu + 7) // 8
+    kw = dict(fmt="u4", act="bf16", N=g78 * 128, K=8192, block_size=32, cu_count=cu)
+    for M in (2, 3, 4, 5, 8, 16):
+        p = _sel(**kw, M=M)
+        assert p["family"] == "mfma" and p["ksplit"] == 1 and bool(p["variant"] & 2) == (M <= 4), (cu, M, p)
+    kw = dict(fmt="fp8", act="f16", N=g78 * 128, K=8192, block_size=128, cu_count=cu)
     assert all(_sel(**kw, M=M)["ksplit"] > 1 for M in (4, 8, 16))
     # NVFP4 at one row: the ring only where its groups outnumber the CUs
     kw = dict(fmt="nvfp4", act="bf16", K=2048, block_size=16, cu_count=cu)

@@ -160,22 +160,25 @@ def test_row_passes_where_the_rows_do_not_stage(fmt, act, N, K, bs, variant):
     assert np.array_equal(Ys[16][8].view(np.int64), Ys[9][8].view(np.int64))
 
 
-@pytest.mark.parametrize("fmt,act,N,bs", [("u4", "bf16", 24576, 32), ("fp8", "f16", 28672, 128)])
-def test_dma_ring_band_takes_no_k_split_at_any_m(fmt, act, N, bs):
-    """A weight whose ring tile groups fill 3/4 (4-bit) or 7/8 (FP8) of the CUs: the DMA
-    ring from M = 2 or 3 up to 8, the unsplit register ring above, one summation order
-    throughout. Sampled outputs against the oracle and a row's bits across M."""
+@pytest.mark.parametrize("fmt,act,N,K,bs,ring_max,frac", [("u4", "bf16", 24576, 4096, 32, 8, (3, 4)),
+                                                           ("fp8", "f16", 28672, 4096, 128, 8, (7, 8)),
+                                                           ("u4", "bf16", 28672, 8192, 32, 4, (7, 8))])
+def test_dma_ring_band_takes_no_k_split_at_any_m(fmt, act, N, K, bs, ring_max, frac):
+    """A weight whose ring tile groups fill 3/4 (4-bit) or 7/8 (FP8; 4-bit where only
+    four rows fit next to the ring) of the CUs: the DMA ring from M = 2 or 3 up to 8 (or
+    4), the unsplit register ring above, one summation order throughout. Sampled
+    outputs against the oracle and a row's bits across M."""
     import torch
 
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    if ((N + 15) // 16 + 7) // 8 * (4 if fmt == "u4" else 8) < (3 if fmt == "u4" else 7) * cu:
+    if ((N + 15) // 16 + 7) // 8 * frac[1] < frac[0] * cu:
         pytest.skip(f"{N} columns are below the band on {cu} CUs")
-    prob = synth.make_problem(fmt, act, N, 4096, bs, 16, seed=95)
-    gu.say(f"[parity] ring band {fmt}/{act} {N}x4096")
+    prob = synth.make_problem(fmt, act, N, K, bs, 16, seed=95)
+    gu.say(f"[parity] ring band {fmt}/{act} {N}x{K}")
     rows = {}
     for M in (4, 8, 12, 16):
         Y, p = gu.run_gpu(prob, M)
-        assert p["family"] == "mfma" and p["ksplit"] == 1 and bool(p["variant"] & 2) == (M <= 8), (M, p)
+        assert p["family"] == "mfma" and p["ksplit"] == 1 and bool(p["variant"] & 2) == (M <= ring_max), (M, p)
         ok, ratio = gu.check_points(prob, M, Y, count=3000, seed=M)
         gu.say(f"   M={M} plan={p} max err/tol={ratio:.3e}")
         assert ok, (M, ratio)
