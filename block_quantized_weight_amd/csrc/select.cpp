@@ -235,31 +235,34 @@ static int mfma_kparts(const qgemv_desc *d, int cu_count, uint32_t flags, int ks
 }
 
 // Long rows with a workspace: where the unsplit tile groups fill between 1/8 of the CUs
-// and all of them, and neither eight rows nor this M's rows of the whole K fit in LDS,
-// the matrix family splits K across workgroups only (no split inside one; K parts,
-// below). An in-workgroup split stages the activations of the whole K range per
-// 16 x (8 / ksplit) columns, and at these lengths the rows do not stage at all; K parts
-// stage only their part. Like the K parts, this choice depends on M: the K split then
-// does too, so rows of qgemv_run_ws's automatic plans are bit-identical across M only
-// where no such rule applies (a forced split or part count turns it off). Measured on
-// MI355X with a workspace (µs, automatic before -> after): 4-bit 8192 x 28672 M = 8 / 16
-// 124.2 / 224.2 -> 60.5 / 83.9 (M = 4 55.9 -> 56.4); FP8 8192 x 28672 M = 4 / 8 / 16
-// 73.3 / 129.7 / 226.7 -> 69.3 / 79.7 / 99.9; 4-bit 4096 x 14336 M = 8 / 16 32.4 /
-// 58.5 -> 22.1 / 27.1; FP8 4096 x 14336 36.3 / 73.9 -> 25.7 / 28.6; 4-bit 5120 x 16384
-// M = 16 134.6 -> 47.8; NVFP4 8192 x 28672 M = 4 / 8 / 16 46.1 / 121.9 / 220.3 -> 38.4
-// / 43.3 / 71.3; K = 16384, M = 8 / 16: 4-bit 16384 x 16384 74.0 / 255.6 -> 69.0 /
-// 92.7, FP8 4096 x 16384 38.7 / 83.4 -> 34.7 / 39.8, NVFP4 24576 x 16384 181.7 / 355.8
-// -> 96.6 / 121.5; but 8-bit 8192 x 16384 M = 8 69.1 -> 73.3 (M = 16 142.5 -> 78.7),
-// 8-bit 28672 x 16384 M = 5 183.7 -> 222.7 (M = 8 / 16 249.7 / 456.8 -> 225.1 / 257.2).
-// Where the rows stage, the in-workgroup split stays ahead (4-bit 5120 x 16384 M = 4:
-// 24.0 against 38.8 us with 8 parts; 8-bit 8192 x 16384 M = 4 40.7 against 71.7).
+// and all of them, and this M's rows of the whole K do not fit in LDS, the matrix
+// family splits K across workgroups only (no split inside one; K parts, below). An
+// in-workgroup split stages the activations of the whole K range per 16 x (8 / ksplit)
+// columns, and here the rows do not stage at all; K parts stage only their part. Like
+// the K parts, this choice depends on M: the K split then does too, so rows of
+// qgemv_run_ws's automatic plans are bit-identical across M only where no such rule
+// applies (a forced split or part count turns it off). Measured on MI355X with a
+// workspace (µs, automatic before -> after): 4-bit 8192 x 28672 M = 8 / 16 124.2 /
+// 224.2 -> 60.5 / 83.9 (M = 4 55.9 -> 56.4); FP8 8192 x 28672 M = 4 / 8 / 16 73.3 /
+// 129.7 / 226.7 -> 69.3 / 79.7 / 99.9; 4-bit 4096 x 14336 M = 8 / 16 32.4 / 58.5 ->
+// 22.1 / 27.1; NVFP4 8192 x 28672 M = 4 / 8 / 16 46.1 / 121.9 / 220.3 -> 38.4 / 43.3 /
+// 71.3; NVFP4 24576 x 16384 M = 8 181.7 -> 96.6; at K = 8192, M = 12 / 16 (row passes or
+// a split of 4 or 8 before): 4-bit 8192 x 8192 32.2 / 37.2 -> 23.4 / 26.3, 4-bit
+// 10240 x 8192 48.0 / 55.9 -> 35.3 / 40.3, 8-bit 8192 x 8192 42.7 / 45.8 -> 32.2 /
+// 33.8, FP8 4096 x 8192 24.4 / 28.1 -> 18.5 / 20.4; at K = 6144, M = 16: FP8 5120 x 6144
+// 34.3 -> 24.9, 4-bit 8192 x 6144 30.9 -> 23.7. But 8-bit 8192 x 16384 M = 8 69.1 ->
+// 73.3 and 8-bit 28672 x 16384 M = 5 183.7 -> 222.7. The parts: one round of
+// workgroups, not more (FP8 5120 x 6144 M = 16: 24.9 us in 4 parts, 34.5 in 8; 4-bit
+// 10240 x 8192: 40.3 in 2, 46.0 in 4). Where the rows stage, the in-workgroup split
+// stays ahead (4-bit 5120 x 16384 M = 4: 24.0 against 38.8 us in 8 parts; FP8
+// 5120 x 6144 M = 12: 18.0 against 22.9 in 4).
 static bool long_rows(const qgemv_desc *d, int M, int cu_count, uint32_t flags, bool with_ws) {
     if (!with_ws || (flags & (QGEMV_FLAG_KSPLIT_MASK | QGEMV_FLAG_KPARTS_MASK))) return false;
     if (d->K % (4 * k_per_chunk(d->format))) return false;
     const int64_t groups = ((d->N + 15) / 16 + 7) / 8;
     if (groups >= cu_count || groups * 8 < cu_count) return false;
     const int64_t steps = d->K / (4 * k_per_chunk(d->format));
-    return staged_act_bytes(d, M < 8 ? M : 8, steps) > kLdsBytes;
+    return staged_act_bytes(d, M < QGEMV_MAX_M ? M : QGEMV_MAX_M, steps) > kLdsBytes;
 }
 
 // Whether the persistent streaming kernel takes a round's block metadata as one window
@@ -580,10 +583,10 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
         };
         int kp = with_ws ? mfma_kparts(d, cu_count, flags, c.ksplit, groups) : 1;
         if (lrows) {
-            // the fewest parts that give every CU a workgroup, then more (up to 8) until
-            // this M's rows stage
+            // the most parts (2 to 8) that keep the workgroups to one round over the CUs,
+            // then more (up to 8) until this M's rows stage
             kp = 2;
-            while (kp < 8 && groups * kp < cu_count) kp *= 2;
+            while (kp < 8 && groups * 2 * kp <= cu_count) kp *= 2;
             while (kp < 8 && staged(kp).lds > kLdsBytes) kp *= 2;
             while (kp > 1 && (steps < 2LL * kp || (int64_t)kp * QGEMV_MAX_M * d->N >= (1LL << 31))) kp /= 2;
         }

@@ -250,10 +250,10 @@ int qgemv_run(const qgemv_handle *h, const void *A, void *Y, int M, void *hip_st
  * formats. The order of the fp32 sums depends on (format, N, K, block size, flags)
  * and the device's compute-unit count, and on M where the activation rows of this M
  * do not fit in LDS: with tile groups for at most half the compute units the K range
- * is then cut in 2 parts; for long rows (eight rows of the whole K do not fit either,
- * and the unsplit tile groups fill between an eighth of the compute units and all of
- * them) the split inside a workgroup is dropped and 2 to 8 parts taken, as many as
- * stage this M's rows. Rows stay
+ * is then cut in 2 parts; where instead the unsplit tile groups fill between an
+ * eighth of the compute units and all of them, the split inside a workgroup is dropped
+ * and 2 to 8 parts taken (one round of workgroups, more where this M's rows need them
+ * to stage). Rows stay
  * bit-identical whatever tile carries them within a call. Across M they stay so only
  * when the flags force both the kernel family (the automatic choice takes the
  * streaming family at small M and the matrix family above it, and the two add in

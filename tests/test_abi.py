@@ -115,18 +115,18 @@ def test_select_families_and_fallback():
 
 
 def test_select_parameters_that_shape_row_arithmetic_do_not_depend_on_m():
-    """The K split orders each row's fp32 sums, so it may depend on N and K only; so do
-    the K parts on these shapes while their unsplit activation rows fit in LDS (up to
-    M = 12 here; FP8 5120 x 6144 takes 2 parts at M = 16, see the test below). (The
-    matrix family's variants, register ring, LDS-staged activations or LDS DMA ring,
-    feed identical MFMA operands in the same order; the GPU tests check that they
-    agree bit for bit.)"""
+    """The K split orders each row's fp32 sums, so it may depend on the weight only; so
+    do the K parts on these shapes while their activation rows fit in LDS (up to M = 12
+    here). With a workspace, FP8 5120 x 6144 at M = 16 is long rows: no split inside a
+    workgroup and 4 parts (the tests below). (The matrix family's variants, register
+    ring, LDS-staged activations or LDS DMA ring, feed identical MFMA operands in the
+    same order; the GPU tests check that they agree bit for bit.)"""
     for fmt, act, N, K, bs in [("u4", "bf16", 151936, 4096, 32), ("fp8", "f16", 5120, 6144, 128),
                                ("nvfp4", "bf16", 248320, 2048, 16), ("u8", "f16", 4096, 4096, 128),
                                ("u4", "f16", 1024, 2048, 32)]:
         for ws in (False, True):
             plans = [_sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=m, with_workspace=ws) for m in range(1, 17)]
-            for key, upto in (("ksplit", 16), ("kparts", 12)):
+            for key, upto in (("ksplit", 12 if ws else 16), ("kparts", 12)):
                 fams = {}
                 for p in plans[:upto]:
                     fams.setdefault(p["family"], set()).add(p[key])
@@ -346,10 +346,16 @@ def test_two_k_parts_where_the_unsplit_rows_do_not_fit_in_lds():
     # past half the CUs, only while each unsplit wave walks 24 K steps or more: FP8
     # 5120 x 6144 (160 tile groups, 96 steps, split 4: 24 per wave) at M = 16; not at
     # M = 12, where the rows fit
+    # M = 12, where the rows fit; at M = 16 the long-rows rule takes it instead: no split
+    # inside a workgroup, 4 parts (40 unsplit tile groups: one round of 160 workgroups)
     kw = dict(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, with_workspace=True)
-    assert _sel(**kw, M=16)["kparts"] == 2 and _sel(**kw, M=12)["kparts"] == 1
-    # 8-bit 4096 x 8192 (256 tile groups, 128 steps, split 8: 16 per wave): never
-    assert _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=True)["kparts"] == 1
+    p = _sel(**kw, M=16)
+    assert p["ksplit"] == 1 and p["kparts"] == 4 and p["variant"] & 1, p
+    assert _sel(**kw, M=12)["kparts"] == 1 and _sel(**kw, M=12)["ksplit"] == 4
+    # 8-bit 4096 x 8192 (256 tile groups, 128 steps, split 8: 16 per wave): not the
+    # 2-part rule; long rows at M = 16 (32 unsplit groups: 8 parts)
+    p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=True)
+    assert p["ksplit"] == 1 and p["kparts"] == 8 and p["variant"] & 1, p
 
 
 def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
@@ -376,11 +382,10 @@ def test_row_passes_where_the_rows_do_not_fit_and_there_are_no_k_parts():
     # FP8 5120 x 6144 at M = 16 (160 tile groups, 24 K steps per wave): passes
     p = _sel(fmt="fp8", act="f16", N=5120, K=6144, block_size=128, M=16)
     assert p["passes"] == 2 and p["grid"] == 160
-    # 8-bit 4096 x 8192 (16 K steps per wave; 2 K parts lose here): passes with or
-    # without a workspace
-    for ws in (False, True):
-        p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16, with_workspace=ws)
-        assert p["passes"] == 2 and p["kparts"] == 1 and p["variant"] & 1, p
+    # 8-bit 4096 x 8192 (16 K steps per wave; 2 K parts at a split of 8 lose here):
+    # passes without a workspace (with one, the long-rows parts above)
+    p = _sel(fmt="u8", act="f16", N=4096, K=8192, block_size=128, M=16)
+    assert p["passes"] == 2 and p["kparts"] == 1 and p["variant"] & 1, p
     # the same at any number of tile groups: FP8 65536 x 8192 (512 groups) from M = 10
     kw8 = dict(fmt="fp8", act="f16", N=65536, K=8192, block_size=128)
     assert [_sel(**kw8, M=M)["passes"] for M in (9, 10, 16)] == [1, 2, 2]

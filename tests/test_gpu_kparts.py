@@ -50,11 +50,10 @@ def test_tall_k_fp8_with_automatic_k_parts(M):
 
 @pytest.mark.parametrize("fmt,act,N,K,bs,M,staged", [("fp8", "f16", 2048, 8192, 128, 16, True),
                                                       ("u4", "bf16", 2048, 16384, 32, 8, True),
-                                                      ("u4", "bf16", 2048, 16384, 32, 12, False),
-                                                      ("fp8", "f16", 5120, 6144, 128, 16, True)])
+                                                      ("u4", "bf16", 2048, 16384, 32, 12, False)])
 def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K, bs, M, staged):
     """Where the unsplit plan's activation rows do not fit in LDS at this M (128 tile
-    groups; or 160 with 24 K steps per unsplit wave), the automatic plan takes 2 parts;
+    groups, too few unsplit groups for the long-rows rule), the automatic plan takes 2 parts;
     sampled outputs against the oracle, and bit for bit the run with 2 parts forced."""
     prob = synth.make_problem(fmt, act, N, K, bs, M, seed=26)
     gu.say(f"[kparts] {fmt} {N}x{K} M={M} automatic 2 parts")
@@ -71,10 +70,14 @@ def test_two_automatic_k_parts_where_the_unsplit_rows_do_not_fit(fmt, act, N, K,
 @pytest.mark.parametrize("fmt,act,N,K,bs,M,kp", [("u4", "bf16", 4096, 14336, 32, 8, 8),
                                                  ("u4", "bf16", 4096, 14336, 32, 16, 8),
                                                  ("fp8", "f16", 8192, 28672, 128, 4, 4),
-                                                 ("nvfp4", "bf16", 8192, 28672, 16, 16, 8)])
+                                                 ("nvfp4", "bf16", 8192, 28672, 16, 16, 8),
+                                                 ("fp8", "f16", 5120, 6144, 128, 16, 4),
+                                                 ("u8", "f16", 4096, 8192, 128, 16, 8),
+                                                 ("u4", "bf16", 10240, 8192, 128, 12, 2)])
 def test_long_rows_take_k_parts_without_an_in_workgroup_split(fmt, act, N, K, bs, M, kp):
-    """Long rows that do not stage at this M, with 32 to 64 unsplit tile groups: no K
-    split inside a workgroup, parts enough to fill the CUs and stage the rows. Sampled
+    """Rows of the whole K that do not stage at this M, with 32 to 80 unsplit tile
+    groups: no K split inside a workgroup, the most parts that keep one round of
+    workgroups, more where the rows need them to stage. Sampled
     outputs against the oracle, the workspace left zero, and bit for bit the run with
     the same split and part count forced."""
     prob = synth.make_problem(fmt, act, N, K, bs, M, seed=27)
