@@ -331,13 +331,14 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     const int64_t nch64 = (nch + 63) / 64 * 64;
     const int nd = kpc == 32 ? 16 : 8;
     const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
-    // The staged rows, at most 64 KB below eight rows (two 4-wave workgroups per CU at
-    // the most). Past it the classic kernel, which re-reads the activations from L2 per
-    // column. One row of 28672 (57-61 KB) measured on MI355X with the 48 KB bound of
-    // before -> 64 KB (classic -> persistent): 4-bit 8192 x 28672 35.4 -> 24.6 us, FP8
-    // 53.1 -> 38.6, NVFP4 36.6 -> 23.5, 8-bit 4096 x 28672 34.6 -> 22.2.
+    // The staged rows: one row up to 64 KB (two 4-wave workgroups per CU at the least;
+    // past it the classic kernel, which re-reads the activations from L2 per column),
+    // several up to the whole LDS. One row of 28672 (57-61 KB) measured on MI355X with
+    // the 48 KB bound of before -> 64 KB (classic -> persistent): 4-bit 8192 x 28672
+    // 35.4 -> 24.6 us, FP8 53.1 -> 38.6, NVFP4 36.6 -> 23.5, 8-bit 4096 x 28672 34.6 ->
+    // 22.2. Several rows past 64 KB run as one round of the widest workgroups (below).
     const int64_t lds = mt * (nch64 * nd * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0));
-    if (lds > (mt == 8 ? kLdsBytes : 64 * 1024)) return false;
+    if (lds > (mt == 1 ? 64 * 1024 : kLdsBytes)) return false;
     const int64_t cpl = (nch + 63) / 64;  // chunks per lane per column
     int unr = 0;
     const uint32_t fu = (flags & QGEMV_FLAG_STREAM_UNR_MASK) >> QGEMV_FLAG_STREAM_UNR_SHIFT;
@@ -399,9 +400,13 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     const int max_wg = (cpw == 2 || wide8) ? 8 : ((u4_two_blocks && mt == 4) ? 12 : 16);
     if (mt > 1 && fn) {
         nwg = 4 * (int)fn < max_wg ? 4 * (int)fn : max_wg;
-    } else if (mt == 8) {
-        // eight staged rows leave room for few workgroups per CU: the fewest waves per
-        // workgroup that hold the CU's column groups, else the most, one round
+    } else if (mt == 8 || lds > 64 * 1024) {
+        // eight staged rows, or fewer past 64 KB, leave room for few workgroups per CU:
+        // the fewest waves per workgroup that hold the CU's column groups, else the
+        // most, one round (16-wave workgroups, one per CU, against 8-wave ones, two, at
+        // 115-131 KB of rows: 4-bit 8192 x 28672 M = 2 30.2 against 32.7 us, FP8
+        // 4096 x 14336 M = 4 15.3 against 16.5, 8-bit 8192 x 16384 M = 4 34.7 against
+        // 38.6)
         nwg = 4;
         while (nwg < max_wg && nwg * res < need) nwg += 4;
         one_round = true;
@@ -470,6 +475,23 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_c
     const bool bytes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;
     // the weights in the DMA ring's band (ring_band), but for 1-byte codes at two rows
     if (ring_band(d, cu_count) && !(flags & QGEMV_FLAG_RING_OFF) && !(bytes && M == 2)) return false;
+    const int kpc = k_per_chunk(d->format);
+    const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
+    const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
+    const int mt = M == 2 ? 2 : 4;
+    const int64_t lds = mt * (nch64 * (kpc == 32 ? 16 : 8) * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0));
+    if (lds > kLdsBytes) return false;
+    // Rows past 64 KB (one round of 16-wave workgroups): the streaming kernel for 1-byte
+    // codes, and for 4-bit and NVFP4 codes where one workgroup per CU holds them (past
+    // 80 KB). Streaming against the matrix family's plan (us): FP8 4096 x 14336 M = 4
+    // 15.3 against 17.7, 8192 x 28672 M = 2 41.0 against 53.8, 65536 x 16384 M = 4 204.9
+    // against 269.0; 8-bit 8192 x 16384 M = 3 / 4 32.4 / 34.7 against 40.2 / 40.6; 4-bit
+    // on bf16 8192 x 28672 M = 2 30.2 against 38.5, 4096 x 14336 M = 3 / 4 13.8 / 16.0
+    // against 16.8 / 17.1, 16384 x 16384 M = 4 46.1 against 48.1 (but NVFP4 16384 x 16384
+    // M = 4 41.7 against 38.4). Between 64 and 80 KB of 4-bit rows the matrix family
+    // holds on wide weights (4-bit on bf16 24576 x 8192 M = 4 32.2 against 37.0 us,
+    // 65536 x 16384 M = 2 113.1 against 123.4).
+    if (lds > 64 * 1024) return bytes || lds > kLdsBytes / 2;
     if (M >= 3) {
         // four rows per pass: the matrix family wins once its tile groups fill the CUs,
         // for 1-byte codes only from 64 MB of codes on
@@ -477,11 +499,6 @@ static bool stream_rows_win(const qgemv_desc *d, int M, bool stream_ok, int cu_c
         const int64_t groups = ((d->N + 15) / 16 + 8 / ks - 1) / (8 / ks);
         if (groups >= cu_count && (!bytes || (int64_t)d->N * d->K >= 64LL * 1024 * 1024)) return false;
     }
-    const int kpc = k_per_chunk(d->format);
-    const int64_t nch64 = (d->K / kpc + 63) / 64 * 64;
-    const int h = (d->format == QGEMV_FMT_NVFP4 || (d->format == QGEMV_FMT_U4 && d->block_size == 16)) ? 2 : 1;
-    const int mt = M == 2 ? 2 : 4;
-    if (mt * (nch64 * (kpc == 32 ? 16 : 8) * 4 + (needs_act_sums(d) ? nch64 * h * 4 : 0)) > 64 * 1024) return false;
     const double wbytes = (double)d->N * d->K * (kpc == 32 ? 0.5 : 1.0);
     const bool small = wbytes < 64.0 * 1024 * 1024;
     const bool byte_codes = d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8;

@@ -342,6 +342,25 @@ def test_multi_row_persistent_kernel_matches_the_classic_kernel_bitwise(fmt, act
             assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (cpw, nwg, pa)
 
 
+@pytest.mark.parametrize("fmt,act,bs,N,K,M", [("u4", "bf16", 32, 4096, 14336, 3), ("fp8", "bf16", 128, 3001, 28672, 2),
+                                              ("u8", "f16", 128, 2500, 16384, 4), ("u4", "bf16", 32, 1024, 16384, 4),
+                                              ("u4", "bf16", 32, 8192, 28672, 1)])
+def test_long_rows_in_the_persistent_streaming_kernel(fmt, act, bs, N, K, M):
+    """Rows past 64 KB of LDS in the persistent streaming kernel (one round of
+    workgroups of up to 16 waves holding them; one row up to 64 KB): the automatic
+    plan, every row equal to the classic kernel's bits, sampled outputs against the
+    oracle."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=34)
+    gu.say(f"[stream-rows] long {fmt}/{act} N={N} K={K} M={M}")
+    Ya, pa = gu.run_gpu(prob, M)
+    gu.say(f"   plan={pa}")
+    assert pa["family"] == "stream" and pa["variant"] & 1 and pa["lds_bytes"] > (48 if M == 1 else 64) * 1024, pa
+    Yc, pc = gu.run_gpu(prob, M, flags=FAMILY_FLAG["stream_classic"])
+    assert np.array_equal(Ya.view(np.int64), Yc.view(np.int64)), (pa, pc)
+    ok, ratio = gu.check_points(prob, M, Ya, count=3000, seed=M)
+    assert ok, ratio
+
+
 @pytest.mark.parametrize("act,N,K", [("f16", 700, 128 * 41), ("bf16", 1234, 128 * 24), ("f16", 5120, 6144)])
 @pytest.mark.parametrize("M", [5, 6, 8])
 def test_eight_row_persistent_kernel_matches_the_classic_kernel_bitwise(act, N, K, M):
