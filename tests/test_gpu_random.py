@@ -113,3 +113,37 @@ def test_random_wide_case_against_the_oracle(i, fmt, act, bs, N, K, M, ws):
     yr, s = gu.oracle.gemv_points(prob, ms, ns, M=M)
     ok, ratio = gu.oracle.within_tolerance(Y[ms, ns], yr, s, out_dtype=prob.act)
     assert ok, (i, ratio, got)
+
+
+def draw_long_cases(n, seed=2026):
+    """Long rows (K from 8192 to 32768), where the activation rows outgrow the LDS: the
+    streaming kernel's wide workgroups, the long-rows K parts, row passes. The automatic
+    plan, N from 1000 to 40000 (at most 200 M weight elements), M up to 16."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        fmt, bs = FORMATS[rng.integers(len(FORMATS))]
+        act = "bf16" if rng.random() < 0.5 else "f16"
+        N = int(rng.integers(1000, 40001))
+        unit = int(np.lcm(4 * KPC[fmt], bs))
+        K = unit * int(rng.integers(8192 // unit, 32768 // unit + 1))
+        N = min(N, 200_000_000 // K)  # at most 200 M weight elements to draw on the host
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+        ws = bool(rng.random() < 0.5)
+        cases.append((i, fmt, act, bs, N, K, M, ws))
+    return cases
+
+
+@pytest.mark.parametrize("i,fmt,act,bs,N,K,M,ws", draw_long_cases(30))
+def test_random_long_case_against_the_oracle(i, fmt, act, bs, N, K, M, ws):
+    """3000 sampled outputs and the first and last 40 columns of every row, against the
+    oracle (plus a bf16 output's final rounding)."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=7000 + i)
+    gu.say(f"[random long {i}] {fmt}/{act} bs={bs} N={N} K={K} M={M} ws={ws}")
+    Y, got = gu.run_gpu(prob, M, ws=ws)
+    if ws:
+        assert got["ws_zero"], got
+    ms, ns = gu.sample_points(M, N, 3000, i)
+    yr, s = gu.oracle.gemv_points(prob, ms, ns, M=M)
+    ok, ratio = gu.oracle.within_tolerance(Y[ms, ns], yr, s, out_dtype=prob.act)
+    assert ok, (i, ratio, got)
