@@ -393,7 +393,7 @@ def time_calls(hs, A, Y, M, stream, ws, warmup, steps, settle_ms=0.0):
     return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
 
 
-READ_CONTROL_SHAPES = ((2048, 4), (4096, 4), (4096, 8), (8192, 4), (8192, 8), (16384, 4), (32768, 4),
+READ_CONTROL_SHAPES = ((2048, 4), (4096, 4), (4096, 8), (8192, 4), (8192, 8), (16384, 4), (32768, 4), (65536, 4), (131072, 4),
                        (2048, 16))
 
 
