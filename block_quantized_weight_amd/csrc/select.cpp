@@ -417,6 +417,17 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     }
     const int64_t wgs = (groups + nwg - 1) / nwg;
     int64_t cap = one_round ? res * cu_count : (int64_t)cu_count * wpc / nwg;
+    // One row of 1-byte codes: a grid of every column group, one per wave, which the
+    // hardware starts as resident workgroups finish, in place of the persistent walk
+    // (variant bit 5; not cut to the resident workgroups at create). Measured on MI355X
+    // (persistent -> whole grid, us): 8-bit 151936 x 2048 50.1 -> 48.0, 65536 x 8192
+    // 86.0 -> 82.3, 32768 x 4096 23.6 -> 22.5, 12288 x 4096 13.3 -> 12.8; FP8
+    // 65536 x 4096 42.0 -> 40.4, 131072 x 2048 42.7 -> 41.3, 16384 x 8192 23.9 -> 23.5,
+    // 28672 x 4096 20.1 -> 20.0; but 4-bit codes lose (lm_head 55.9 -> 60.7, 28672 x 4096
+    // 13.7 -> 14.4), their wave's walk staying ahead of a new workgroup's activation copy.
+    const bool whole = mt == 1 && (d->format == QGEMV_FMT_U8 || d->format == QGEMV_FMT_FP8) && !fw && !fc &&
+                       !(flags & QGEMV_FLAG_STREAM_WIDE_WG);
+    if (whole) cap = wgs;
     // several rows: a grid past one workgroup per CU is cut to a whole number of them per
     // CU, and the persistent walk carries the rest, so that every CU holds as many
     // workgroups (FP8 5120 x 6144 at M = 4: 640 8-wave workgroups, 2.5 per CU, 11.85 us;
@@ -430,7 +441,7 @@ static bool stream1_plan(const qgemv_desc *d, int M, int cu_count, uint32_t flag
     c->waves_per_wg = nwg;
     c->grid = wgs < cap ? wgs : (cap > 0 ? cap : 1);
     c->lds_bytes = (int)lds;
-    c->variant = 1 | ((unr & 3) << 1);
+    c->variant = 1 | ((unr & 3) << 1) | (whole ? 32 : 0);
     if (!(flags & QGEMV_FLAG_STREAM_META_CHUNK)) {
         if (mt < 8 && stream_meta_window(d, unr)) c->variant |= 8;  // (no windows next to eight rows)
         else if (stream_meta_dword(d)) c->variant |= 16;
@@ -771,7 +782,7 @@ int select_plan(const qgemv_desc *d, int M, int cu_count, bool fast_ok, uint32_t
 
 bool persistent(const LaunchCfg &c) {
     if (c.family == QGEMV_FAMILY_MFMA) return c.kparts == 1;
-    if (c.family == QGEMV_FAMILY_STREAM) return (c.variant & 1) != 0;
+    if (c.family == QGEMV_FAMILY_STREAM) return (c.variant & 1) && !(c.variant & 32);
     return c.family == QGEMV_FAMILY_GENERIC;
 }
 

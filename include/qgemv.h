@@ -199,7 +199,9 @@ typedef struct qgemv_plan_info {
                                 bits 1..2 = chunks per lane per batch (2 -> 2, 3 -> 3, 0 -> 4),
                                 bit 3 = block metadata loaded as one window per round (8-bit
                                 codes), bit 4 = as the aligned dwords that hold it (4-bit,
-                                8-bit and NVFP4 codes, where the rows are whole dwords) */
+                                8-bit and NVFP4 codes, where the rows are whole dwords),
+                                bit 5 = a grid of every column group, one per wave, instead
+                                of a persistent grid (one row of 1-byte codes) */
     int32_t kparts;          /* K parts split across workgroups (1 = none; only qgemv_run_ws
                                 splits, ABI version 3) */
     int32_t reserved;        /* 0 */
