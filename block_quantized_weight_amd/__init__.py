@@ -24,7 +24,7 @@ FAMILY_NAMES = {v: k for k, v in FAMILIES.items()}
 QGEMV_OK = 0
 QGEMV_E_WORKSPACE = 9
 QGEMV_E_SCRATCH = 10
-NOALLOC_SCRATCH_BYTES = 8 << 20  # QGEMV_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20  # QGEMV_NOALLOC_SCRATCH_BYTES
 FLAG_FAMILY_MASK = 0x0000000F
 FLAG_KPARTS_SHIFT = 4
 FLAG_STREAM_META_CHUNK = 0x00000080

@@ -65,7 +65,7 @@ extern "C" {
 #define QGEMV_MAX_ROWS 65536
 /* Bytes of the library's own device scratch array that qgemv_run_noalloc uses in place
  * of a workspace (one copy per device, held until the process ends). */
-#define QGEMV_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define QGEMV_NOALLOC_SCRATCH_BYTES (16u << 20)
 /* Most launches qgemv_tune_candidates lists (and qgemv_tune times) for one M. */
 #define QGEMV_TUNE_MAX_CANDIDATES 256
 
@@ -278,13 +278,14 @@ int qgemv_run_ws(const qgemv_handle *h, const void *A, void *Y, int M, void *wor
 /* qgemv_run_ws without a caller workspace and without any allocation, for callers that
  * cannot allocate device memory: code being captured into a HIP graph, tight serving
  * loops, harnesses that forbid hipMalloc. The same plans and kernels as qgemv_run_ws,
- * with the library's own device array of QGEMV_NOALLOC_SCRATCH_BYTES (8 MiB, one per
+ * with the library's own device array of QGEMV_NOALLOC_SCRATCH_BYTES (16 MiB, one per
  * device, set up and zeroed when the first handle for that device is created, held
  * until the process ends) as the workspace; the result is bit-identical to
  * qgemv_run_ws's. The call allocates nothing and frees nothing. Returns
  * QGEMV_E_SCRATCH, before any launch, when the plan for M rows needs more workspace
  * than the array holds (qgemv_workspace_size reports the need; automatic plans on a
- * 256-CU device need at most 4 MiB), and QGEMV_E_DEVICE when the array could not be
+ * 256-CU device need at most 16 MiB: long rows over nearly 32768 columns at 16 rows,
+ * in 8 K parts; 4 MiB elsewhere), and QGEMV_E_DEVICE when the array could not be
  * set up. Every completed call leaves the area it used zero again, which is how the
  * next call finds its counters. All calls on one device share the one array: calls
  * that overlap in time on one device (different streams, or threads) race on it and

@@ -526,3 +526,16 @@ def test_dma_ring_band(cu):
     kw = dict(fmt="nvfp4", act="bf16", K=2048, block_size=16, cu_count=cu)
     assert _sel(**kw, N=cu * 128, M=1)["family"] == "stream"
     assert _sel(**kw, N=(cu + 1) * 128, M=1)["variant"] & 2
+
+
+def test_automatic_workspaces_fit_the_noalloc_array():
+    """On 256 CUs every automatic plan of up to 16 rows needs at most the no-allocation
+    entry point's array (16 MiB): the largest are the long-rows K parts over nearly
+    32768 columns."""
+    worst = 0
+    for fmt, act, bs in [("u4", "bf16", 32), ("fp8", "f16", 128), ("u8", "f16", 128), ("nvfp4", "bf16", 16)]:
+        for K in (4096, 16384, 20480, 32768, 65536):
+            for N in (1024, 4096, 8192, 20480, 30720, 32256, 32768, 151936):
+                p = _sel(fmt=fmt, act=act, N=N, K=K, block_size=bs, M=16, with_workspace=True)
+                worst = max(worst, p["workspace_bytes"])
+    assert 8 << 20 < worst <= bqw.NOALLOC_SCRATCH_BYTES == 16 << 20, worst

@@ -65,9 +65,9 @@ def test_noalloc_with_more_than_16_rows():
 
 
 def test_noalloc_rejects_a_plan_larger_than_its_array():
-    # 8 forced K parts on 32768 columns: 8 x 16 x 32768 x 4 bytes of partials at M = 16,
-    # 16 MiB, twice the array; the same handle at M = 1 needs 1 MiB and runs
-    prob = synth.make_problem("fp8", "f16", 32768, 1024, 128, 16, seed=8)
+    # 8 forced K parts on 65536 columns: 8 x 16 x 65536 x 4 bytes of partials at M = 16,
+    # 32 MiB, twice the array; the same handle at M = 1 needs 2 MiB and runs
+    prob = synth.make_problem("fp8", "f16", 65536, 1024, 128, 16, seed=8)
     flags = 2 | (4 << 4)
     q, t = bqw.upload(prob, flags=flags)
     assert q.workspace_size(16) > bqw.NOALLOC_SCRATCH_BYTES >= q.workspace_size(1)
