@@ -8,14 +8,16 @@
 // unit is the wave64 and the machine is cu_count compute units (256 on MI355X).
 //
 // Within a kernel family, every parameter that changes per-row arithmetic (the lanes
-// that own a column, the K split) is chosen from (format, N, K, block size, flags and
-// the CU count) only, never from M, so a row's bits do not depend on how many rows
-// travel with it in that family. The family itself is chosen from M as well (the
-// streaming family at M = 1, the matrix family from M = 2 or 3 on wide weights, and
-// the fallbacks below), as are the K parts of qgemv_run_ws in one case; the families
-// sum in different fp32 orders, so a row's bits can change where M moves a shape
-// from one family to the other (both within the same bound). A caller who needs the
-// same bits for a row at every M forces one family (and the part count) in the flags.
+// that own a column, the K split) is chosen from the weight (format, N, K, block size,
+// zero points), the flags and the CU count only, never from M, so a row's bits do not
+// depend on how many rows travel with it in that family. The family itself is chosen
+// from M as well (the streaming family at M = 1, the matrix family from M = 2 or 3 on
+// wide weights, and the fallbacks below), and so are qgemv_run_ws's K parts where this
+// M's rows do not fit in LDS, with the K split beside them for long rows; the families
+// sum in different fp32 orders, so a row's bits can change where M moves a shape from
+// one family or part count to another (all within the same bound). A caller who needs
+// the same bits for a row at every M forces one family (and the part count) in the
+// flags.
 #include "select.h"
 
 #include <initializer_list>
