@@ -661,8 +661,9 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
 }
 
 // Register-ring kernel. A workgroup of 8 waves holds 8 / ksplit tiles of ksplit waves
-// each. Without K parts (KP false) it walks tile groups blockIdx.x, + gridDim.x, ...
-// over all of K. With K parts (KP, a.kparts > 1; the grid is one workgroup per tile
+// each. Without K parts (KP 0) it walks tile groups blockIdx.x, + gridDim.x, ...
+// over all of K. With K parts (KP 1 with a K split inside the workgroup, 2 without;
+// a.kparts > 1; the grid is one workgroup per tile
 // group and part), workgroup b takes tile group b / kparts and part b mod kparts of
 // its K steps (a contiguous range, parts as even as whole steps allow), and the
 // cross-workgroup finish runs once, after the ring has drained. Within a tile,
@@ -683,7 +684,7 @@ __device__ __forceinline__ void finish_tile(const KArgs &a, f4 acc[RG], float *s
 // flight.
 // Register budget: four waves per SIMD (<= 128 VGPRs) for one row group, two waves
 // per SIMD (<= 256) beyond.
-template <int FMT, int ACT, int RG, int H, bool LDSA, int P, bool KP>
+template <int FMT, int ACT, int RG, int H, bool LDSA, int P, int KP>
 __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     constexpr int NW = 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -698,7 +699,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     const bool a_live_grp = ((lane & 15) >> 2) == g;
     // K part of this workgroup: steps pbeg .. pbeg + nsteps - 1 (nsteps >= 1, as the
     // dispatcher takes at most one part per step); the tile-group walk of the part
-    const uint32_t kp = KP ? (uint32_t)a.kparts : 1u;
+    const uint32_t kp = KP != 0 ? (uint32_t)a.kparts : 1u;
     const uint32_t part = blockIdx.x % kp;
     const int64_t gx = blockIdx.x / kp;
     const int64_t gdim = gridDim.x / kp;
@@ -721,7 +722,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     f4 *sSum = (f4 *)(smem + kZeroBytes + rows_b);
     const size_t abytes = LDSA ? kZeroBytes + rows_b + sums_bytes<FMT, ACT, RG, H>((size_t)4 * smax) : 0;
     const size_t red_b = ks > 1 ? (size_t)NW * RG * 4 * 64 * 4 : 0;
-    const bool red_alias = LDSA && ks > 1 && (KP || gdim >= ngroups);
+    const bool red_alias = LDSA && ks > 1 && (KP != 0 || gdim >= ngroups);
     float *sR = (float *)(red_alias ? smem : smem + abytes);
     uint32_t *sFlag = (uint32_t *)(smem + (red_alias ? (abytes > red_b ? abytes : red_b) : abytes + red_b));
 
@@ -748,9 +749,13 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
         // nontemporal ones about a third of the pairs both went to HBM (4-bit lm_head,
         // M = 16: 1.32x the weight bytes fetched, 1.008x with ordinary loads; 137.9 ->
         // 132.4 us; FP8 5120 x 6144 M = 8 16.0 -> 14.3 us). With K parts, nontemporal
-        // loads measured faster (FP8 1024 x 16384 M = 8: 14.5 against 15.1 us).
+        // loads measured faster where K is also split inside the workgroup (KP = 1: FP8
+        // 1024 x 16384 M = 8: 14.5 against 15.1 us), whose waves walk strided steps;
+        // without that split (KP = 2) a wave reads both halves itself and the ordinary
+        // loads win again (FP8 8192 x 28672 M = 4 / 8: 69.6 / 80.1 -> 63.3 / 74.5 us;
+        // 4-bit 8192 x 28672 M = 8 57.6 -> 53.9; 8-bit 8192 x 8192 M = 16 34.0 -> 31.7).
         const u4v *wp = (const u4v *)(col.w + (uint32_t)(c4 + (lane & 3)) * 16u);
-        wb[p] = KP ? load16_stream(wp) : load16(wp);
+        wb[p] = KP == 1 ? load16_stream(wp) : load16(wp);
         mb[p] = load_meta_raw<FMT, H>(a, col, c4 + (lane & 3));
         if constexpr (!LDSA) load_a_ops<FMT, ACT, RG>(a, c, ar, ab[p]);
         if (++is == S) {
@@ -775,7 +780,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     // One ring turn = P slots. Every turn but the last consumes and refills each slot;
     // the last turn only drains the ring, so nothing is fetched past the wave's work.
     // Tile boundaries fall on turn boundaries (S is a multiple of P).
-    const int64_t G = KP ? (gx < ngroups ? 1 : 0) : (gx < ngroups ? (ngroups - gx + gdim - 1) / gdim : 0);
+    const int64_t G = KP != 0 ? (gx < ngroups ? 1 : 0) : (gx < ngroups ? (ngroups - gx + gdim - 1) / gdim : 0);
     const int64_t turns = G * (S / P);
     const int tpt = S / P;  // turns per tile
     int64_t tg = gx;
@@ -802,7 +807,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
                 issue(p);
             }
         }
-        if constexpr (!KP) {
+        if constexpr (KP == 0) {
             if (++tt == tpt) {
                 finish_tile<ACT, RG, false>(a, acc, sR, wave, lane, ks, kslice, g, tile_ok, tile * 16 + (lane & 15), 0,
                                             0, nullptr, red_alias);
@@ -817,7 +822,7 @@ __global__ void __launch_bounds__(512, (RG == 1 ? 4 : 2)) k_mfma(KArgs a) {
     };
     for (int64_t i = 0; i + 1 < turns; ++i) turn(true);
     if (turns > 0) turn(false);
-    if constexpr (KP) {
+    if constexpr (KP != 0) {
         // one tile group per workgroup: its finish, with nothing left in flight
         const int64_t tile = gx * tpw + slot;
         finish_tile<ACT, RG, true>(a, acc, sR, wave, lane, ks, kslice, g, tile < ntiles, tile * 16 + (lane & 15),
@@ -1155,10 +1160,13 @@ namespace {
 
 template <int FMT, int ACT, int RG, int H, bool LDSA, int P>
 hipError_t go_p(const LaunchCfg &cfg, const KArgs &a, hipStream_t s) {
-    const bool kp = a.kparts > 1;
-    auto kern = kp ? k_mfma<FMT, ACT, RG, H, LDSA, P, true> : k_mfma<FMT, ACT, RG, H, LDSA, P, false>;
-    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};  // per kernel: without / with K parts
-    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[kp ? 1 : 0]);
+    // K parts: with a K split inside the workgroup (1) or without (2)
+    const int kp = a.kparts > 1 ? (a.ksplit > 1 ? 1 : 2) : 0;
+    auto kern = kp == 1   ? k_mfma<FMT, ACT, RG, H, LDSA, P, 1>
+                : kp == 2 ? k_mfma<FMT, ACT, RG, H, LDSA, P, 2>
+                          : k_mfma<FMT, ACT, RG, H, LDSA, P, 0>;
+    static std::atomic<uint64_t> lds_set[3] = {{0}, {0}, {0}};  // per kernel
+    hipError_t e = lds_limit_once((const void *)kern, cfg.device, cfg.lds_bytes, lds_set[kp]);
     if (e != hipSuccess) return e;
     return launch_or_report(cfg, kern, 512, a, s);
 }
