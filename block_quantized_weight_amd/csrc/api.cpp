@@ -202,6 +202,17 @@ void fit_residency(const qgemv_handle *h, qgemv::LaunchCfg *c, int m, uint32_t e
         per_cu < 1)
         return;
     const int64_t cap = (int64_t)per_cu * h->cu_count;
+    // A staged register-ring plan with a K split inside the workgroup whose grid holds
+    // every tile group lays its reduction area over the staged activations (the kernel
+    // overlays them only when gridDim covers the tile groups, and the plan's LDS is the
+    // overlaid size): a grid cut below the tile groups would make the kernel lay the
+    // area after the activations, past the LDS the launch provides. Such a grid keeps
+    // its size; the workgroups past the resident ones start as the first finish.
+    if (c->family == QGEMV_FAMILY_MFMA && c->kparts == 1 && c->ksplit > 1 && (c->variant & 1) && !(c->variant & 2)) {
+        const int64_t tiles = ((int64_t)h->d.N + 15) / 16;
+        const int64_t groups = (tiles + 8 / c->ksplit - 1) / (8 / c->ksplit);
+        if (c->grid >= groups && cap < groups) return;
+    }
     if (c->grid > cap) c->grid = cap;
 }
 

@@ -187,6 +187,26 @@ def test_dma_ring_band_takes_no_k_split_at_any_m(fmt, act, N, K, bs, ring_max, f
         assert np.array_equal(rows[M].view(np.int64), rows[4].view(np.int64)), M
 
 
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_overlaid_reduction_keeps_one_tile_group_per_workgroup(M):
+    """4-bit 16446 x 9600 (block size 64): a K split of 4 over 514 tile groups. At two
+    rows the staged rows leave room for the reduction area over them, which needs one
+    tile group per workgroup; the kernel's registers leave fewer workgroups resident
+    than that, and the create-time residency cut must keep the grid (a cut grid made
+    the kernel lay the area past the launch's LDS: wrong outputs). At three and four
+    rows the area follows the rows in a persistent grid. Sampled outputs against the
+    oracle."""
+    prob = synth.make_problem("u4", "f16", 16446, 9600, 64, M, seed=148)
+    gu.say(f"[parity] overlaid reduction u4/f16 16446x9600 M={M}")
+    for ws in (False, True):
+        Y, plan = gu.run_gpu(prob, M, ws=ws)
+        assert plan["family"] == "mfma" and plan["ksplit"] == 4 and plan["variant"] & 1, plan
+        assert M > 2 or plan["grid"] >= (16446 + 15) // 16 // 2, plan
+        ok, ratio = gu.check_points(prob, M, Y, count=4000, seed=M)
+        gu.say(f"   ws={ws} plan={plan} max err/tol={ratio:.3e}")
+        assert ok, (ws, ratio)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "u4"])
 @pytest.mark.parametrize("M,family", [(5, "mfma"), (6, "stream"), (16, "stream")])
 def test_tall_narrow_shapes_without_workspace(fmt, M, family):
