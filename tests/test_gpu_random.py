@@ -147,3 +147,46 @@ def test_random_long_case_against_the_oracle(i, fmt, act, bs, N, K, M, ws):
     yr, s = gu.oracle.gemv_points(prob, ms, ns, M=M)
     ok, ratio = gu.oracle.within_tolerance(Y[ms, ns], yr, s, out_dtype=prob.act)
     assert ok, (i, ratio, got)
+
+
+def draw_mid_cases(n, seed=2027):
+    """Mid-size weights (N from 2048 to 20000, K from 1024 to 16384, at most 150 M weight
+    elements), where the K split, its reduction area over the staged rows, K parts, row
+    passes and the residency cut meet: the automatic plan or a forced K split, part
+    count, DMA ring or unstaged rows, M up to 20."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        fmt, bs = FORMATS[rng.integers(len(FORMATS))]
+        act = "bf16" if rng.random() < 0.5 else "f16"
+        N = int(rng.integers(2048, 20001))
+        kind = rng.integers(5)
+        flags = 0
+        if kind == 1:
+            flags = 2 | (int(rng.choice([1, 2, 4, 8])) << 8)
+        elif kind == 2:
+            flags = 2 | (int(rng.integers(1, 5)) << 4)
+        elif kind == 3:
+            flags = 2 | int(rng.choice([bqw.FLAG_RING_ON | (1 << 8), bqw.FLAG_STAGE_A_OFF]))
+        unit = int(np.lcm(4 * KPC[fmt], bs))
+        K = unit * int(rng.integers(max(1, 1024 // unit), 16384 // unit + 1))
+        N = min(N, 150_000_000 // K)
+        M = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 9, 12, 16, 20]))
+        ws = bool(rng.random() < 0.5)
+        cases.append((i, fmt, act, bs, N, K, M, flags, ws))
+    return cases
+
+
+@pytest.mark.parametrize("i,fmt,act,bs,N,K,M,flags,ws", draw_mid_cases(40))
+def test_random_mid_case_against_the_oracle(i, fmt, act, bs, N, K, M, flags, ws):
+    """3000 sampled outputs and the first and last 40 columns of every row, against the
+    oracle (plus a bf16 output's final rounding)."""
+    prob = synth.make_problem(fmt, act, N, K, bs, M, seed=9000 + i)
+    gu.say(f"[random mid {i}] {fmt}/{act} bs={bs} N={N} K={K} M={M} flags={flags:#x} ws={ws}")
+    Y, got = gu.run_gpu(prob, M, flags=flags, ws=ws)
+    if ws:
+        assert got["ws_zero"], got
+    ms, ns = gu.sample_points(M, N, 3000, i)
+    yr, s = gu.oracle.gemv_points(prob, ms, ns, M=M)
+    ok, ratio = gu.oracle.within_tolerance(Y[ms, ns], yr, s, out_dtype=prob.act)
+    assert ok, (i, ratio, got)
