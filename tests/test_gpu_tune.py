@@ -70,7 +70,13 @@ EVERY = [("fp8_k6144_n5120", 1, False), ("fp8_k6144_n5120", 4, False), ("fp8_k61
          ("nvfp4_m4_k2048_n2048", 4, False), (("nvfp4", "bf16", 999, 3104, 16), 1, False),
          ("u4_m8_k2048_n1024", 8, False), (("u4", "bf16", 8192, 4096, 32), 8, False),
          (("u4", "bf16", 8192, 4096, 32), 16, False), (("fp8", "f16", 1024, 16384, 128), 8, True),
-         (("u8", "f16", 2048, 8192, 128), 13, False)]
+         (("u8", "f16", 2048, 8192, 128), 13, False),
+         # the DMA ring's band (ring up to 8 rows, the unsplit register ring above), long rows
+         # with a workspace (K parts, no split inside a workgroup), several long streaming rows,
+         # one row of 1-byte codes on a grid of every column group
+         (("u4", "bf16", 24576, 4096, 32), 4, False), (("u4", "bf16", 24576, 4096, 32), 12, False),
+         (("u4", "bf16", 4096, 14336, 32), 8, True), (("u4", "bf16", 4096, 14336, 32), 3, False),
+         (("u8", "f16", 12288, 4096, 128), 1, False)]
 
 
 @pytest.mark.parametrize("spec,M,ws", EVERY)
